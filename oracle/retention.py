@@ -1,0 +1,317 @@
+"""Float64 reference implementation of retention and the gated MSR layer.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).  Plain numpy, float64,
+no blocking or fusion beyond what each definition states.
+
+Pages cited (titles as printed on them):
+
+* [RN-zh]  "Transformer取代者登場！微軟、清華剛推出RetNet：成本低、速度快、
+  性能強（2）" -- the RetNet method section.  Its displayed equations are
+  stripped by the extraction; each function below states the definition it
+  implements in words and names the equation number the page refers to.
+* [RN-ja]  "[論文レビュー] Retentive Network: A Successor to Transformer for
+  Large Language Models" -- abstract and method bullets.
+* [RN-ru]  "Retentive Network: архитектурный прорыв или временный успех?" --
+  decay-masked causal mask, per-head gamma, chunkwise recursion.
+
+Tensor layout everywhere: [batch, seqlen, heads, head_dim] (token-major, the
+natural output of X @ W).  gamma is a float64 array with one value per head.
+"""
+from __future__ import annotations
+
+import math
+from fractions import Fraction
+
+import numpy as np
+
+F64 = np.float64
+
+
+def _f64(x):
+    return np.asarray(x, dtype=F64)
+
+
+# --------------------------------------------------------------------------
+# Relative-position rotation (xPos / rotary)
+# --------------------------------------------------------------------------
+def rotary(x, pos0: int = 0, base: float = 10000.0):
+    """Rotate interleaved pairs of ``x`` [B, N, H, d] by position.
+
+    [RN-zh] section "Retention", Eq. (3)-(4): diagonalising the state matrix
+    gives the factor e^{i n theta} on Q_n (and its conjugate on K_m) so the
+    score depends on the relative position n - m (the page calls it xPos).
+    Real form: pair j = (x[2j], x[2j+1]) read as the complex number
+    x[2j] + i x[2j+1] is multiplied by e^{i p theta_j}, with p = pos0 + n and
+    theta_j = base^(-2j/d).  The same rotation is applied to Q and to K.
+    ``base <= 0`` means no rotation.
+    """
+    x = _f64(x)
+    if base is None or base <= 0:
+        return x.copy()
+    B, N, H, d = x.shape
+    if d % 2:
+        raise ValueError("rotary needs an even head dimension")
+    j = np.arange(d // 2, dtype=F64)
+    theta = base ** (-2.0 * j / d)                       # [d/2]
+    p = (pos0 + np.arange(N, dtype=F64))[:, None]        # [N, 1]
+    ang = p * theta[None, :]                             # [N, d/2]
+    c = np.cos(ang)[None, :, None, :]
+    s = np.sin(ang)[None, :, None, :]
+    xe, xo = x[..., 0::2], x[..., 1::2]
+    out = np.empty_like(x)
+    out[..., 0::2] = xe * c - xo * s
+    out[..., 1::2] = xe * s + xo * c
+    return out
+
+
+# --------------------------------------------------------------------------
+# Decay mask and the three forms of retention
+# --------------------------------------------------------------------------
+def decay_mask(N: int, gamma: float):
+    """D[n, m] = gamma^(n-m) for n >= m, else 0.
+
+    [RN-zh] section "1) Retention 的並行表征", Eq. (5); [RN-ru] "Causal Mask
+    с затуханием".  gamma = 0 gives the identity (0^0 = 1 on the diagonal).
+    """
+    n = np.arange(N)
+    diff = n[:, None] - n[None, :]
+    D = np.zeros((N, N), dtype=F64)
+    low = diff >= 0
+    D[low] = np.power(F64(gamma), diff[low].astype(F64))
+    return D
+
+
+def retention_parallel(q, k, v, gamma, scale: float = 1.0):
+    """Parallel form: O = ((Q K^T) * scale  (.)  D) V per (batch, head).
+
+    [RN-zh] section "1) Retention 的並行表征", Eq. (5), Fig. 3a.
+    q, k: [B, N, H, dk]; v: [B, N, H, dv]; gamma: [H].  Returns [B, N, H, dv].
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, N, H, _ = q.shape
+    out = np.zeros(v.shape, dtype=F64)
+    for h in range(H):
+        D = decay_mask(N, float(gamma[h]))
+        for b in range(B):
+            scores = (q[b, :, h, :] @ k[b, :, h, :].T) * scale
+            out[b, :, h, :] = (scores * D) @ v[b, :, h, :]
+    return out
+
+
+def retention_recurrent(q, k, v, gamma, scale: float = 1.0, S0=None):
+    """Recurrent form, token by token.
+
+    [RN-zh] section "2) Retention 的循環表征", Eq. (6), Fig. 3b:
+    S_n = gamma * S_{n-1} + K_n^T V_n, then o_n = scale * Q_n S_n (the state is
+    updated before it is read, so token n sees itself with weight gamma^0).
+    S0: optional initial state [B, H, dk, dv] (zeros if None).
+    Returns (O [B, N, H, dv], S_final [B, H, dk, dv]).
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, N, H, dk = q.shape
+    dv = v.shape[-1]
+    S = np.zeros((B, H, dk, dv), dtype=F64) if S0 is None else _f64(S0).copy()
+    g = _f64(gamma)[None, :, None, None]
+    out = np.zeros((B, N, H, dv), dtype=F64)
+    for n in range(N):
+        S = g * S + k[:, n, :, :, None] * v[:, n, :, None, :]
+        out[:, n] = scale * np.einsum("bhi,bhij->bhj", q[:, n], S)
+    return out, S
+
+
+def retention_chunkwise(q, k, v, gamma, chunk: int, scale: float = 1.0, S0=None):
+    """Chunkwise recurrent form.
+
+    [RN-zh] section "3) Retention 分塊循環表征", Eq. (7); [RN-ru]
+    "Chunk-wise рекурсия": inside a chunk the parallel form (Eq. 5) is used,
+    across chunks the state is passed on as in the recurrent form (Eq. 6).
+    Chunks are the contiguous slices [i*B, (i+1)*B); the last one may be short
+    (length L).  With rows t, s indexed from 0 inside the chunk:
+
+      O_[i] = ((Q_[i] K_[i]^T) * scale (.) D_L) V_[i]
+              + scale * (Q_[i] R_{i-1}) (.) xi,     xi_t   = gamma^(t+1)
+      R_i   = gamma^L R_{i-1} + K_[i]^T (V_[i] (.) zeta),  zeta_s = gamma^(L-1-s)
+
+    R_{-1} = S0 (zeros if None).  Returns (O, R_last).
+    """
+    if chunk < 1:
+        raise ValueError("chunk must be >= 1")
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, N, H, dk = q.shape
+    dv = v.shape[-1]
+    R = np.zeros((B, H, dk, dv), dtype=F64) if S0 is None else _f64(S0).copy()
+    out = np.zeros((B, N, H, dv), dtype=F64)
+    for c0 in range(0, N, chunk):
+        L = min(chunk, N - c0)
+        qc, kc, vc = q[:, c0:c0 + L], k[:, c0:c0 + L], v[:, c0:c0 + L]
+        for h in range(H):
+            gam = F64(gamma[h])
+            D = decay_mask(L, gam)
+            t = np.arange(L, dtype=F64)
+            xi = np.power(gam, t + 1.0)                  # [L]
+            zeta = np.power(gam, L - 1.0 - t)            # [L]
+            for b in range(B):
+                Qb, Kb, Vb = qc[b, :, h], kc[b, :, h], vc[b, :, h]
+                inner = ((Qb @ Kb.T) * scale * D) @ Vb
+                cross = scale * (Qb @ R[b, h]) * xi[:, None]
+                out[b, c0:c0 + L, h] = inner + cross
+                R[b, h] = np.power(gam, L) * R[b, h] + Kb.T @ (Vb * zeta[:, None])
+    return out, R
+
+
+def retention_bruteforce(q, k, v, gamma, scale=1.0):
+    """Scalar double loop, exact in rational arithmetic when the inputs are
+    Fractions or integers (tiny inputs only).
+
+    o[b,n,h,:] = sum_{m <= n} gamma^(n-m) * scale * (q_n . k_m) * v_m.
+    Nested Python lists or numpy object arrays of shape [B, N, H, d].
+    """
+    q = np.asarray(q, dtype=object)
+    k = np.asarray(k, dtype=object)
+    v = np.asarray(v, dtype=object)
+    B, N, H, dk = q.shape
+    dv = v.shape[-1]
+    out = np.empty((B, N, H, dv), dtype=object)
+    for b in range(B):
+        for h in range(H):
+            g = gamma[h]
+            for n in range(N):
+                acc = [0] * dv
+                for m in range(n + 1):
+                    dot = 0
+                    for i in range(dk):
+                        dot += q[b, n, h, i] * k[b, m, h, i]
+                    w = (g ** (n - m)) * scale * dot
+                    for j in range(dv):
+                        acc[j] += w * v[b, m, h, j]
+                out[b, n, h, :] = acc
+    return out
+
+
+def retention_parallel_normalized(q, k, v, gamma):
+    """Parallel form with the three normalisation factors of [RN-zh] section
+    "Retention Score 歸一化":
+
+      1. scores Q K^T / sqrt(dk);
+      2. D~[n, m] = D[n, m] / sqrt(sum_{i<=n} D[n, i]);
+      3. R = (Q K^T / sqrt(dk)) (.) D~, R~[n, m] = R[n, m] / max(|sum_{i<=n} R[n, i]|, 1).
+
+    Output R~ V.  The page prints only the first factor; factors 2 and 3 are
+    the reading stated here (both are positive per-row factors, so GroupNorm
+    removes them exactly).
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, N, H, dk = q.shape
+    out = np.zeros(v.shape, dtype=F64)
+    for h in range(H):
+        D = decay_mask(N, float(gamma[h]))
+        Dn = D / np.sqrt(D.sum(axis=1, keepdims=True))
+        for b in range(B):
+            R = (q[b, :, h] @ k[b, :, h].T) / math.sqrt(dk) * Dn
+            R = R / np.maximum(np.abs(R.sum(axis=1, keepdims=True)), 1.0)
+            out[b, :, h] = R @ v[b, :, h]
+    return out
+
+
+def recurrent_step(S, q, k, v, gamma, scale=1.0, pos=None, base=0.0):
+    """One decode step of Eq. (6) for every (batch, head).
+
+    S: [B, H, dk, dv]; q, k: [B, H, dk]; v: [B, H, dv].  When ``base > 0``
+    q and k are first rotated at absolute position ``pos``.
+    Returns (o [B, H, dv], S_new).
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    if base is not None and base > 0:
+        q = rotary(q[:, None], pos, base)[:, 0]
+        k = rotary(k[:, None], pos, base)[:, 0]
+    g = _f64(gamma)[None, :, None, None]
+    S_new = g * _f64(S) + k[..., :, None] * v[..., None, :]
+    o = scale * np.einsum("bhi,bhij->bhj", q, S_new)
+    return o, S_new
+
+
+# --------------------------------------------------------------------------
+# GroupNorm, swish gate, the gated MSR layer
+# --------------------------------------------------------------------------
+def group_norm_heads(O, eps: float):
+    """GroupNorm with one group per head ([RN-zh] "門控多尺度 Retention":
+    each head's output is normalised on its own because heads with different
+    gamma have different variance).  Statistics per (token, head) over the
+    head's d_v channels, biased variance, identity affine.
+    """
+    O = _f64(O)
+    mu = O.mean(axis=-1, keepdims=True)
+    var = ((O - mu) ** 2).mean(axis=-1, keepdims=True)
+    return (O - mu) / np.sqrt(var + eps)
+
+
+def swish(x):
+    """swish(x) = x * sigmoid(x) (beta = 1)."""
+    x = _f64(x)
+    return x / (1.0 + np.exp(-x))
+
+
+def msr_layer(X, WQ, WK, WV, WG, WO, gamma, heads, d_k, d_v, chunk=None,
+              rope_base=10000.0, eps=1e-5, form="chunkwise", normalized=False,
+              scale=None):
+    """Gated multi-scale retention layer, [RN-zh] "門控多尺度 Retention", Eq. (8):
+
+      Q^ = X W_Q, K^ = X W_K, V = X W_V (heads = contiguous column blocks)
+      Q, K = rotary(Q^), rotary(K^) at positions 0..N-1
+      head_h = Retention_h(Q, K, V) with gamma_h, score scale 1/sqrt(d_k)
+      Y = GroupNorm_h(Concat_h head_h)
+      MSR(X) = (swish(X W_G) (.) Y) W_O
+
+    X: [B, N, d_model]; W_Q, W_K: [d_model, H*d_k]; W_V, W_G: [d_model, H*d_v];
+    W_O: [H*d_v, d_model].  ``form`` picks the retention form
+    ("parallel", "recurrent", "chunkwise"); ``normalized=True`` uses the
+    three score-normalisation factors instead (parallel form).
+    """
+    X = _f64(X)
+    B, N, _ = X.shape
+    q = (X @ _f64(WQ)).reshape(B, N, heads, d_k)
+    k = (X @ _f64(WK)).reshape(B, N, heads, d_k)
+    v = (X @ _f64(WV)).reshape(B, N, heads, d_v)
+    g = X @ _f64(WG)
+    q = rotary(q, 0, rope_base)
+    k = rotary(k, 0, rope_base)
+    s = 1.0 / math.sqrt(d_k) if scale is None else scale
+    if normalized:
+        o = retention_parallel_normalized(q, k, v, gamma)
+    elif form == "parallel":
+        o = retention_parallel(q, k, v, gamma, s)
+    elif form == "recurrent":
+        o, _ = retention_recurrent(q, k, v, gamma, s)
+    elif form == "chunkwise":
+        o, _ = retention_chunkwise(q, k, v, gamma, chunk or N, s)
+    else:
+        raise ValueError(form)
+    y = group_norm_heads(o, eps).reshape(B, N, heads * d_v)
+    return (swish(g) * y) @ _f64(WO)
+
+
+# --------------------------------------------------------------------------
+# Error measures
+# --------------------------------------------------------------------------
+def max_rel_err(got, ref):
+    """max|got - ref| / max|ref| over the whole tensor."""
+    got, ref = _f64(got), _f64(ref)
+    den = np.max(np.abs(ref))
+    return float(np.max(np.abs(got - ref)) / (den if den > 0 else 1.0))
+
+
+def max_rel_err_per_head(got, ref):
+    """max over (batch, head) slices of max|got - ref| / max|ref| for raw
+    retention outputs [B, N, H, d] (heads differ in scale by an order of
+    magnitude, so a tensor-wide denominator would hide the small ones)."""
+    got, ref = _f64(got), _f64(ref)
+    worst = 0.0
+    for b in range(ref.shape[0]):
+        for h in range(ref.shape[2]):
+            worst = max(worst, max_rel_err(got[b, :, h], ref[b, :, h]))
+    return worst
+
+
+def exact_fraction(x):
+    """Helper for the rational brute force: Fraction of a float, exactly."""
+    return Fraction(x)

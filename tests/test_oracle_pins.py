@@ -1,0 +1,314 @@
+"""Pins of the float64 oracle against facts fixed by the pages and by
+mathematics, independent of the oracle's own formulas.
+
+Pages: [RN-zh] = "Transformer取代者登場！微軟、清華剛推出RetNet：成本低、速度快、
+性能強（2）"; [RN-ru] = "Retentive Network: архитектурный прорыв или временный
+успех?"; [RN-it] = "This article on AI proposes Retentive Networks (RetNet)
+as a fundamental architecture for large language models ...".
+"""
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+from hypothesis import given, settings, strategies as st
+from scipy.special import expit
+
+import oracle
+from oracle.retention import decay_mask
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rnd(seed, *shape):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+def close(a, b, tol=1e-12):
+    a, b = np.asarray(a, float), np.asarray(b, float)
+    den = max(np.max(np.abs(b)), 1e-300)
+    return np.max(np.abs(a - b)) / den <= tol
+
+
+# ---------------------------------------------------------------- P1 -------
+@pytest.mark.parametrize("gamma", [Fraction(0), Fraction(1, 2), Fraction(97, 100), Fraction(1)])
+def test_parallel_equals_exact_bruteforce(gamma):
+    """Eq. (5) evaluated in float64 equals the exact rational double loop
+    o_n = sum_{m<=n} gamma^(n-m) (q_n . k_m) v_m on small integer inputs."""
+    rng = np.random.default_rng(1)
+    B, N, H, dk, dv = 2, 6, 2, 3, 2
+    q = rng.integers(-3, 4, (B, N, H, dk))
+    k = rng.integers(-3, 4, (B, N, H, dk))
+    v = rng.integers(-3, 4, (B, N, H, dv))
+    gam = [gamma, Fraction(1, 3)]
+    exact = oracle.retention_bruteforce(q.tolist(), k.tolist(), v.tolist(), gam)
+    exact = np.array(exact.tolist(), dtype=float)
+    got = oracle.retention_parallel(q, k, v, np.array([float(g) for g in gam]))
+    assert close(got, exact, 1e-13)
+
+
+def test_chunkwise_ragged_equals_exact_bruteforce():
+    """Eq. (7) with a ragged last chunk (N=7, B=3) against the exact double
+    loop: catches an off-by-one in zeta, xi or the gamma^L carry."""
+    rng = np.random.default_rng(2)
+    B, N, H, dk, dv = 1, 7, 1, 2, 3
+    q = rng.integers(-2, 3, (B, N, H, dk))
+    k = rng.integers(-2, 3, (B, N, H, dk))
+    v = rng.integers(-2, 3, (B, N, H, dv))
+    exact = oracle.retention_bruteforce(q.tolist(), k.tolist(), v.tolist(), [Fraction(3, 4)], Fraction(1, 2))
+    exact = np.array(exact.tolist(), dtype=float)
+    for chunk in (1, 2, 3, 4, 7, 9):
+        got, _ = oracle.retention_chunkwise(q, k, v, np.array([0.75]), chunk, 0.5)
+        assert close(got, exact, 1e-13), chunk
+
+
+# ---------------------------------------------------------------- P2 -------
+def test_gamma_one_is_causal_linear_attention():
+    """gamma = 1, no rotation, scale 1: retention is plain causal linear
+    attention (the softmax-free attention of [RN-ru] / [RN-it]),
+    o_n = q_n (sum_{m<=n} k_m^T v_m), computed here with a running sum."""
+    B, N, H, dk, dv = 2, 9, 3, 4, 5
+    q, k, v = rnd(3, B, N, H, dk), rnd(4, B, N, H, dk), rnd(5, B, N, H, dv)
+    kv = np.cumsum(k[..., :, None] * v[..., None, :], axis=1)   # [B,N,H,dk,dv]
+    lin = np.einsum("bnhi,bnhij->bnhj", q, kv)
+    g = np.ones(H)
+    assert close(oracle.retention_parallel(q, k, v, g), lin)
+    assert close(oracle.retention_recurrent(q, k, v, g)[0], lin)
+    assert close(oracle.retention_chunkwise(q, k, v, g, 4)[0], lin)
+
+
+# ---------------------------------------------------------------- P3 -------
+@settings(max_examples=40, deadline=None)
+@given(
+    N=st.integers(1, 24),
+    extra=st.integers(0, 3),
+    chunk_frac=st.floats(0.0, 1.0),
+    dk=st.sampled_from([2, 4, 6]),
+    dv=st.sampled_from([1, 3, 4]),
+    H=st.integers(1, 3),
+    seed=st.integers(0, 10_000),
+    gsel=st.lists(st.sampled_from([0.0, 0.5, 1 - 2.0 ** -5, 1 - 2.0 ** -12, 1.0]), min_size=3, max_size=3),
+    use_s0=st.booleans(),
+)
+def test_three_forms_agree(N, extra, chunk_frac, dk, dv, H, seed, gsel, use_s0):
+    """The parallel, recurrent and chunkwise forms are one function ([RN-zh]
+    sections 1)-3): Eq. (5) is derived from Eq. (6), Eq. (7) runs Eq. (5)
+    inside chunks and Eq. (6) across them), for every chunk length
+    1 <= B <= N + 3, ragged last chunks included, and with an initial state."""
+    chunk = 1 + int(chunk_frac * (N + 2 + extra - 1))
+    B = 2
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, N, H, dk))
+    k = rng.standard_normal((B, N, H, dk))
+    v = rng.standard_normal((B, N, H, dv))
+    g = np.array(gsel[:H])
+    s = 0.7
+    S0 = rng.standard_normal((B, H, dk, dv)) if use_s0 else None
+    o_r, S_r = oracle.retention_recurrent(q, k, v, g, s, S0)
+    o_c, S_c = oracle.retention_chunkwise(q, k, v, g, chunk, s, S0)
+    assert close(o_c, o_r, 1e-11)
+    assert close(S_c, S_r, 1e-11)
+    if S0 is None:
+        assert close(oracle.retention_parallel(q, k, v, g, s), o_r, 1e-11)
+
+
+def test_chunk_extremes_reduce_to_other_forms():
+    """B = N is the parallel form; B = 1 is the recurrent form."""
+    B, N, H, d = 1, 11, 2, 3
+    q, k, v = rnd(6, B, N, H, d), rnd(7, B, N, H, d), rnd(8, B, N, H, d)
+    g = np.array([0.9, 0.5])
+    assert close(oracle.retention_chunkwise(q, k, v, g, N)[0], oracle.retention_parallel(q, k, v, g))
+    assert close(oracle.retention_chunkwise(q, k, v, g, 1)[0], oracle.retention_recurrent(q, k, v, g)[0])
+
+
+# ---------------------------------------------------------------- P4 -------
+def test_gamma_zero_keeps_only_the_diagonal():
+    """gamma = 0: D is the identity, so o_n = s (q_n . k_n) v_n."""
+    B, N, H, dk, dv = 2, 7, 1, 3, 4
+    q, k, v = rnd(9, B, N, H, dk), rnd(10, B, N, H, dk), rnd(11, B, N, H, dv)
+    want = 0.3 * np.sum(q * k, axis=-1, keepdims=True) * v
+    for got in (oracle.retention_parallel(q, k, v, [0.0], 0.3),
+                oracle.retention_recurrent(q, k, v, [0.0], 0.3)[0],
+                oracle.retention_chunkwise(q, k, v, [0.0], 3, 0.3)[0]):
+        assert close(got, want)
+
+
+# ---------------------------------------------------------------- P5 -------
+def test_geometric_series_golden():
+    rows = [l.split() for l in open(os.path.join(GOLDEN, "geometric_series.txt")) if not l.startswith("#")]
+    for gamma in sorted({float(r[0]) for r in rows}):
+        want = np.array([float(r[2]) for r in rows if float(r[0]) == gamma])
+        N = len(want)
+        one = np.ones((1, N, 1, 1))
+        for got in (oracle.retention_parallel(one, one, one, [gamma])[0, :, 0, 0],
+                    oracle.retention_recurrent(one, one, one, [gamma])[0][0, :, 0, 0],
+                    oracle.retention_chunkwise(one, one, one, [gamma], 5)[0][0, :, 0, 0]):
+            np.testing.assert_allclose(got, want, rtol=1e-14, atol=0)
+
+
+def test_decay_mask_entries():
+    D = decay_mask(4, 0.5)
+    assert D[3, 0] == 0.125 and D[0, 3] == 0.0 and D[2, 2] == 1.0 and D[2, 1] == 0.5
+
+
+# ---------------------------------------------------------------- P6 -------
+def test_split_sequence_continuation():
+    """The state is the whole memory of the prefix ([RN-zh] Eq. (6)-(7)):
+    chunkwise over [0, M) -> S_out -> chunkwise over [M, N) from S_in equals
+    one pass; a prefill followed by single recurrent steps (with rotation at
+    the absolute position) equals one pass over all tokens."""
+    B, N, H, dk, dv, M = 2, 20, 2, 4, 3, 13
+    g = np.array([0.8, 0.99])
+    base = 100.0
+    q0, k0, v = rnd(12, B, N, H, dk), rnd(13, B, N, H, dk), rnd(14, B, N, H, dv)
+    q, k = oracle.rotary(q0, 0, base), oracle.rotary(k0, 0, base)
+    full, S_full = oracle.retention_chunkwise(q, k, v, g, 4, 0.5)
+    a, Sa = oracle.retention_chunkwise(q[:, :M], k[:, :M], v[:, :M], g, 4, 0.5)
+    b, Sb = oracle.retention_chunkwise(q[:, M:], k[:, M:], v[:, M:], g, 4, 0.5, Sa)
+    assert close(np.concatenate([a, b], 1), full) and close(Sb, S_full)
+    # rotation of the continuation computed at its own offset
+    q2 = oracle.rotary(q0[:, M:], M, base)
+    assert close(q2, q[:, M:])
+    # prefill M tokens, then decode the rest one token at a time
+    S = Sa
+    for n in range(M, N):
+        o, S = oracle.recurrent_step(S, q0[:, n], k0[:, n], v[:, n], g, 0.5, pos=n, base=base)
+        assert close(o, full[:, n])
+    assert close(S, S_full)
+
+
+# ---------------------------------------------------------------- P7 -------
+def test_rotary_golden_and_properties():
+    rows = [l.split() for l in open(os.path.join(GOLDEN, "rotary_unit.txt")) if not l.startswith("#")]
+    for base, d, j, p, c, s in rows:
+        base, d, j, p, c, s = float(base), int(d), int(j), int(p), float(c), float(s)
+        x = np.zeros((1, 1, 1, d))
+        x[..., 2 * j] = 1.0
+        y = oracle.rotary(x, p, base)
+        assert abs(y[0, 0, 0, 2 * j] - c) < 1e-12 and abs(y[0, 0, 0, 2 * j + 1] - s) < 1e-12
+        x2 = np.zeros((1, 1, 1, d))
+        x2[..., 2 * j + 1] = 1.0                    # i * e^{i a} = (-sin a, cos a)
+        y2 = oracle.rotary(x2, p, base)
+        assert abs(y2[0, 0, 0, 2 * j] + s) < 1e-12 and abs(y2[0, 0, 0, 2 * j + 1] - c) < 1e-12
+    x = rnd(15, 2, 9, 3, 8)
+    y = oracle.rotary(x, 5, 10000.0)
+    assert close(np.linalg.norm(y, axis=-1), np.linalg.norm(x, axis=-1))
+    assert np.array_equal(oracle.rotary(x, 5, 0.0), x)
+
+
+def test_rotation_is_relative():
+    """With the same rotation on Q and K the scores depend on n - m only
+    ([RN-zh] "Retention": xPos is a relative position embedding): shifting the
+    absolute origin leaves the retention output unchanged."""
+    B, N, H, d = 1, 10, 2, 6
+    q, k, v = rnd(16, B, N, H, d), rnd(17, B, N, H, d), rnd(18, B, N, H, d)
+    g = np.array([1.0, 0.9])
+    outs = [oracle.retention_parallel(oracle.rotary(q, p0, 50.0), oracle.rotary(k, p0, 50.0), v, g)
+            for p0 in (0, 3, 1000)]
+    assert close(outs[1], outs[0], 1e-10) and close(outs[2], outs[0], 1e-10)
+    assert not close(outs[0], oracle.retention_parallel(q, k, v, g), 1e-3)
+
+
+# ---------------------------------------------------------------- P8/P9 ----
+def test_groupnorm_scale_invariance_and_moments():
+    O = rnd(19, 2, 5, 3, 16)
+    alpha = np.exp(rnd(20, 2, 5, 3, 1))          # positive per-row factors
+    y = oracle.group_norm_heads(O, 0.0)
+    assert close(oracle.group_norm_heads(alpha * O, 0.0), y, 1e-12)
+    np.testing.assert_allclose(y.mean(-1), 0.0, atol=1e-14)
+    np.testing.assert_allclose(y.var(-1), 1.0, rtol=1e-12)
+    # a constant row normalises to 0 when eps > 0
+    assert np.all(oracle.group_norm_heads(np.ones((1, 1, 1, 4)), 1e-5) == 0.0)
+
+
+def test_normalisation_tricks_leave_layer_unchanged():
+    """[RN-zh] "Retention Score 歸一化": QK^T/sqrt(d), D~ and R~ do not change
+    the layer output because GroupNorm is scale invariant (eps = 0)."""
+    B, N, dm, H, dk, dv = 1, 12, 16, 2, 4, 6
+    rng = np.random.default_rng(21)
+    X = rng.standard_normal((B, N, dm))
+    W = [rng.standard_normal(s) / 4 for s in ((dm, H * dk), (dm, H * dk), (dm, H * dv), (dm, H * dv), (H * dv, dm))]
+    g = np.array([0.9, 0.6])
+    plain = oracle.msr_layer(X, *W, g, H, dk, dv, rope_base=30.0, eps=0.0, form="parallel", scale=1.0)
+    tricks = oracle.msr_layer(X, *W, g, H, dk, dv, rope_base=30.0, eps=0.0, normalized=True)
+    assert close(tricks, plain, 1e-11)
+    # at eps > 0 the deviation is small but not zero
+    a = oracle.msr_layer(X, *W, g, H, dk, dv, rope_base=30.0, eps=1e-5, form="parallel", scale=1.0)
+    assert close(a, plain, 1e-3)
+
+
+# ---------------------------------------------------------------- P10 ------
+def test_linearity_and_independence():
+    B, N, H, dk, dv = 2, 8, 3, 4, 5
+    q, k, v, v2 = rnd(22, B, N, H, dk), rnd(23, B, N, H, dk), rnd(24, B, N, H, dv), rnd(25, B, N, H, dv)
+    g = np.array([0.5, 0.9, 1.0])
+    f = lambda q, k, v: oracle.retention_chunkwise(q, k, v, g, 3)[0]
+    assert close(f(q, k, 2 * v - v2), 2 * f(q, k, v) - f(q, k, v2))
+    assert close(f(3 * q, k, v), 3 * f(q, k, v)) and close(f(q, -2 * k, v), -2 * f(q, k, v))
+    # heads are independent: permuting heads (with their gamma) permutes outputs
+    perm = [2, 0, 1]
+    out_p = oracle.retention_chunkwise(q[:, :, perm], k[:, :, perm], v[:, :, perm], g[perm], 3)[0]
+    assert close(out_p, f(q, k, v)[:, :, perm])
+    # batch rows are independent
+    assert close(oracle.retention_chunkwise(q[1:], k[1:], v[1:], g, 3)[0], f(q, k, v)[1:])
+
+
+# ---------------------------------------------------------------- P11 ------
+def test_swish():
+    x = np.linspace(-30, 30, 1001)
+    np.testing.assert_allclose(oracle.swish(x), x * expit(x), rtol=1e-13, atol=1e-300)
+    assert oracle.swish(0.0) == 0.0
+    assert abs(oracle.swish(40.0) - 40.0) < 1e-12
+
+
+# ---------------------------------------------------------------- layer ----
+def _layer_case(seed, B=1, N=10, dm=12, H=3, dk=4, dv=4):
+    rng = np.random.default_rng(seed)
+    X = rng.standard_normal((B, N, dm))
+    W = [rng.standard_normal(s) / 3 for s in ((dm, H * dk), (dm, H * dk), (dm, H * dv), (dm, H * dv), (H * dv, dm))]
+    return X, W, np.array([0.5, 0.8, 0.95][:H])
+
+
+def test_layer_decomposes_over_heads():
+    """Heads are contiguous column blocks of the projections and GroupNorm
+    is per head, so the layer equals the sum over heads of one-head layers
+    built from the matching weight slices ([RN-zh] Eq. (8))."""
+    X, (WQ, WK, WV, WG, WO), g = _layer_case(26)
+    H, dk, dv = 3, 4, 4
+    full = oracle.msr_layer(X, WQ, WK, WV, WG, WO, g, H, dk, dv, chunk=3)
+    acc = 0
+    for h in range(H):
+        sk, sv = slice(h * dk, (h + 1) * dk), slice(h * dv, (h + 1) * dv)
+        acc = acc + oracle.msr_layer(X, WQ[:, sk], WK[:, sk], WV[:, sv], WG[:, sv], WO[sv, :], g[h:h + 1], 1, dk, dv, chunk=3)
+    assert close(full, acc)
+
+
+def test_layer_forms_agree_and_gate():
+    X, W, g = _layer_case(27)
+    outs = [oracle.msr_layer(X, *W, g, 3, 4, 4, chunk=c, form=f)
+            for f, c in (("parallel", None), ("recurrent", None), ("chunkwise", 3), ("chunkwise", 4))]
+    for o in outs[1:]:
+        assert close(o, outs[0], 1e-11)
+    WQ, WK, WV, WG, WO = W
+    zero_gate = oracle.msr_layer(X, WQ, WK, WV, np.zeros_like(WG), WO, g, 3, 4, 4, chunk=3)
+    assert np.all(zero_gate == 0.0)
+
+
+def test_layer_rectangular_heads():
+    """d_v != d_k and H*d_v != d_model (the block shape with v head dim 512):
+    weight shapes follow the projections, W_O is [H*d_v, d_model]."""
+    X, W, g = _layer_case(28, dm=8, H=2, dk=2, dv=6)
+    o = oracle.msr_layer(X, *W, g[:2], 2, 2, 6, chunk=4)
+    assert o.shape == (1, 10, 8)
+    assert close(o, oracle.msr_layer(X, *W, g[:2], 2, 2, 6, form="recurrent"), 1e-11)
+
+
+def test_error_measures():
+    ref = np.zeros((1, 3, 2, 2))
+    ref[0, :, 0] = 100.0
+    ref[0, :, 1] = 1.0
+    got = ref.copy()
+    got[0, 0, 1, 0] += 0.05
+    assert oracle.max_rel_err(got, ref) == pytest.approx(0.0005)
+    assert oracle.max_rel_err_per_head(got, ref) == pytest.approx(0.05)
