@@ -1,0 +1,338 @@
+#!/usr/bin/env python3
+"""Benchmark of libmsr on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--only a,b,...] [--no-cpu]
+
+Headline (the JSON line's "value"): forward of one gated multi-scale
+retention layer (bf16, fp32 accumulate) on batch 8 x 2048 tokens,
+d_model 2048, 8 heads of 256, chunk 256 -- tokens per second, inputs and
+weights resident in HBM, W untimed warm-up steps then exactly K timed steps
+between two stream synchronisations.  The same line carries:
+
+* roofline   -- the dominant kernel's achieved rate over the timed steps,
+                from HIP events bracketing each of its launches (msr_trace)
+                against the MI355X peak;
+* kernels    -- the same for every kernel of the step;
+* decode     -- recurrent decode, batch 128, 16 heads of 256, fp32 state
+                (512 MiB) prefilled from an 8192-token context, 512 timed
+                steps: steps/s and fraction of HBM peak; also a 1024-token
+                context for the length-independence check;
+* long       -- chunkwise core (batch 2, 16384 tokens, 10 heads of 256,
+                chunk 512) and a sequence-length sweep of chunkwise vs
+                parallel form, plus that layer;
+* block      -- the gated MSR block (batch 4, 8192 tokens, d_model 4096,
+                16 heads, q/k 256, v 512, chunk 512);
+* cpu_baseline -- the float64 oracle timed on this host on a bounded sample.
+
+There is one GPU: --gpus above 1 exits with a message.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16 = 256 * 2.4e9 * 4096        # dense MFMA flop/s: 2516.6 TFLOP/s
+PEAK_F32_MFMA = 157.3e12
+PEAK_HBM = 8.0e12                      # bytes/s
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+# --------------------------------------------------------------------------
+def gpu_time(fn, steps, warmup):
+    """Average seconds per call of fn over `steps` calls after `warmup`."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(steps):
+        fn()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) * 1e-3 / steps
+
+
+def traced(fn, steps):
+    """Per-kernel (total s, launches) over `steps` calls, from HIP events the
+    library records around each launch on its stream."""
+    import torch
+    import linear_recurrence_sequence_amd as msr
+    torch.cuda.synchronize()
+    msr.msr_trace_enable(True)
+    for _ in range(steps):
+        fn()
+    tot = msr.trace_totals()
+    msr.msr_trace_enable(False)
+    return {k: (ms * 1e-3, n) for k, (ms, n) in tot.items()}
+
+
+def roof(name, work_per_step, bound, trace, steps, launches_per_step=None):
+    """Roofline entry for one kernel: work_per_step is flops (mfma) or bytes
+    (hbm) of algorithmic work in one step."""
+    t, n = trace[name]
+    per_launch_t = t / n
+    lps = n / steps if launches_per_step is None else launches_per_step
+    per_launch_work = work_per_step / lps
+    peak, unit = (PEAK_BF16, "TFLOP/s") if bound == "mfma" else (PEAK_HBM, "GB/s")
+    scale = 1e12 if bound == "mfma" else 1e9
+    ach = per_launch_work / per_launch_t
+    return {"kernel": name, "bound": bound, "achieved": round(ach / scale, 2), "peak": round(peak / scale, 1),
+            "unit": unit, "frac": round(ach / peak, 4), "traffic": None,
+            "avg_launch_us": round(per_launch_t * 1e6, 2), "launches_per_step": lps}
+
+
+def layer_flops(B, N, dm, H, dk, dv, C):
+    proj = 2 * dm * (2 * H * dk + 2 * H * dv) + 2 * H * dv * dm
+    core = H * (C * (dk + dv) + 4 * dk * dv)
+    return B * N * proj, B * N * core
+
+
+def make_layer(w, device_inputs):
+    """Device tensors X, W_Q, W_K, W_V, W_G, W_O (bf16) for workload w."""
+    import numpy as np
+    import torch
+    import workloads
+    if not device_inputs:
+        arrs = workloads.layer_inputs(w)
+        return [torch.from_numpy(a).cuda().to(torch.bfloat16) for a in arrs]
+    s = 1.0 / math.sqrt(w.d_model)
+    hk, hv = w.heads * w.d_k, w.heads * w.d_v
+    shapes = [(w.batch, w.seqlen, w.d_model), (w.d_model, hk), (w.d_model, hk), (w.d_model, hv), (w.d_model, hv),
+              (hv, w.d_model)]
+    out = []
+    for i, shp in enumerate(shapes):
+        t = workloads.device_normal(shp, seed=1000 * (w.seed + 1) + i)
+        out.append((t if i == 0 else t * s).to(torch.bfloat16))
+    return out
+
+
+def bench_layer(w, steps, warmup, device_inputs=False):
+    import torch
+    import linear_recurrence_sequence_amd as msr
+    import workloads
+    X, WQ, WK, WV, WG, WO = make_layer(w, device_inputs)
+    g = workloads.gammas(w.heads)
+    out = torch.empty_like(X)
+    ws = torch.empty(msr.msr_layer_workspace_bytes(1, w.batch, w.seqlen, w.d_model, w.heads, w.d_k, w.d_v, w.chunk),
+                     dtype=torch.uint8, device="cuda")
+    fn = lambda: msr.msr_layer_fwd(X, WQ, WK, WV, WG, WO, g, w.heads, w.d_k, w.d_v, w.chunk, rope_base=w.rope_base,
+                                   gn_eps=1e-5, out=out, workspace=ws)
+    t = gpu_time(fn, steps, warmup)
+    tr = traced(fn, steps)
+    proj, core = layer_flops(w.batch, w.seqlen, w.d_model, w.heads, w.d_k, w.d_v, w.chunk)
+    B, N, H, dk, dv, C = w.batch, w.seqlen, w.heads, w.d_k, w.d_v, w.chunk
+    nc = -(-N // C)
+    es = 2
+    kern = {
+        "k_gemm_nt": roof("k_gemm_nt", proj, "mfma", tr, steps),
+        "k_chunk_out": roof("k_chunk_out", B * N * H * (C * (dk + dv) + 2 * dk * dv), "mfma", tr, steps),
+        "k_chunk_state": roof("k_chunk_state", B * N * H * 2 * dk * dv, "mfma", tr, steps),
+        "k_chunk_scan": roof("k_chunk_scan", B * H * nc * dk * dv * (4 + es), "hbm", tr, steps),
+        "k_rope_apply": roof("k_rope_apply", 2 * 2 * B * N * H * dk * es, "hbm", tr, steps),
+        "k_transpose": roof("k_transpose", 2 * es * w.d_model * (2 * H * dk + 3 * H * dv), "hbm", tr, steps),
+    }
+    del X, WQ, WK, WV, WG, WO, out, ws
+    torch.cuda.empty_cache()
+    res = {"s_per_step": t, "tokens_per_s": B * N / t, "flops_per_step": proj + core,
+           "tflops": (proj + core) / t / 1e12, "mfma_frac": (proj + core) / t / PEAK_BF16, "kernels": kern,
+           "trace_s_per_step": {k: v[0] / steps for k, v in tr.items()}}
+    return res
+
+
+def bench_core(B, N, H, d, C, steps, warmup, parallel=False):
+    import torch
+    import linear_recurrence_sequence_amd as msr
+    import workloads
+    Q, K, V = (workloads.device_normal((B, N, H, d), seed=7 + i, dtype=torch.bfloat16) for i in range(3))
+    O = torch.empty_like(Q)
+    g = workloads.gammas(H)
+    s = 1 / math.sqrt(d)
+    if parallel:
+        fn = lambda: msr.msr_parallel_fwd(Q, K, V, g, qk_scale=s, O=O)
+        flops = B * N * H * N * 2 * d       # causal: N(dk + dv) per token on average
+    else:
+        ws = torch.empty(msr.msr_chunkwise_workspace_bytes(1, B, N, H, d, d, C, 0.0), dtype=torch.uint8,
+                         device="cuda")
+        fn = lambda: msr.msr_chunkwise_fwd(Q, K, V, g, C, qk_scale=s, O=O, workspace=ws)
+        flops = B * N * H * (C * 2 * d + 4 * d * d)
+    t = gpu_time(fn, steps, warmup)
+    res = {"N": N, "s": t, "tokens_per_s": B * N / t, "tflops": flops / t / 1e12, "mfma_frac": flops / t / PEAK_BF16}
+    if not parallel:
+        tr = traced(fn, steps)
+        nc = -(-N // C)
+        res["kernels"] = {
+            "k_chunk_out": roof("k_chunk_out", B * N * H * (C * 2 * d + 2 * d * d), "mfma", tr, steps),
+            "k_chunk_state": roof("k_chunk_state", B * N * H * 2 * d * d, "mfma", tr, steps),
+            "k_chunk_scan": roof("k_chunk_scan", B * H * nc * d * d * 6, "hbm", tr, steps),
+        }
+    return res
+
+
+def bench_decode(steps_timed, warmup):
+    import torch
+    import linear_recurrence_sequence_amd as msr
+    import workloads
+    w = workloads.WORKLOADS["decode_fp32_b128_h16"]
+    B, H, d, C = w.batch, w.heads, w.d_k, w.chunk
+    g = workloads.gammas(H)
+    s = 1 / math.sqrt(d)
+    out = {}
+    for ctx in (w.context, 1024):
+        S = torch.empty((B, H, d, d), device="cuda")
+        sl = 16
+        ws = torch.empty(msr.msr_chunkwise_workspace_bytes(0, sl, ctx, H, d, d, C, w.rope_base), dtype=torch.uint8,
+                         device="cuda")
+        for b0 in range(0, B, sl):  # prefill in batch slices (inputs drawn on the device, seeded)
+            q, k, v = (workloads.device_normal((sl, ctx, H, d), seed=100000 * i + b0 + ctx) for i in range(1, 4))
+            msr.msr_chunkwise_fwd(q, k, v, g, C, rope_base=w.rope_base, qk_scale=s, S_out=S[b0:b0 + sl],
+                                  workspace=ws)
+            del q, k, v
+        del ws
+        n = steps_timed if ctx == w.context else max(64, steps_timed // 8)
+        qs, ks, vs = (workloads.device_normal((n, B, H, d), seed=200000 * i + ctx) for i in range(1, 4))
+        o = torch.empty((B, H, d), device="cuda")
+        Sw = S.clone()
+        for t in range(warmup):
+            msr.msr_recurrent_step(qs[t % n], ks[t % n], vs[t % n], Sw, g, pos=ctx, rope_base=w.rope_base,
+                                   qk_scale=s, o=o)
+        del Sw
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for t in range(n):
+            msr.msr_recurrent_step(qs[t], ks[t], vs[t], S, g, pos=ctx + t, rope_base=w.rope_base, qk_scale=s, o=o)
+        e1.record()
+        torch.cuda.synchronize()
+        ts = e0.elapsed_time(e1) * 1e-3 / n
+        byts = B * H * (2 * d * d * 4 + 4 * d * 4)
+        entry = {"context": ctx, "steps": n, "us_per_step": round(ts * 1e6, 2), "steps_per_s": round(1 / ts, 1),
+                 "tokens_per_s": round(B / ts, 1), "GB_per_s": round(byts / ts / 1e9, 1),
+                 "hbm_frac": round(byts / ts / PEAK_HBM, 4), "bytes_per_step": byts}
+        if ctx == w.context:
+            tr = traced(lambda: msr.msr_recurrent_step(qs[0], ks[0], vs[0], S, g, pos=ctx + n, rope_base=w.rope_base,
+                                                       qk_scale=s, o=o), min(n, 128))
+            entry["roofline"] = roof("k_recurrent_step", byts, "hbm", tr, min(n, 128))
+        out[str(ctx)] = entry
+        del S, qs, ks, vs, o
+        torch.cuda.empty_cache()
+    a, b = out[str(w.context)]["us_per_step"], out["1024"]["us_per_step"]
+    out["length_ratio_8192_vs_1024"] = round(a / b, 4)
+    return out
+
+
+def cpu_baseline(budget_s=12.0):
+    """The float64 oracle on a bounded sample of the headline workload: the
+    layer on one batch element at a time (2048 tokens) until budget_s."""
+    import numpy as np
+    import oracle
+    import workloads
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = None
+    w = workloads.WORKLOADS["layer_bf16_b8_n2048"]
+    X, WQ, WK, WV, WG, WO = workloads.layer_inputs(w)
+    g = workloads.gammas(w.heads)
+    t0 = time.perf_counter()
+    done = 0
+    for b in range(w.batch):
+        oracle.msr_layer(X[b:b + 1], WQ, WK, WV, WG, WO, g, w.heads, w.d_k, w.d_v, w.chunk, rope_base=w.rope_base,
+                         eps=1e-5)
+        done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    t = time.perf_counter() - t0
+    return {"value": round(done * w.seqlen / t, 1), "unit": "tokens/s", "cores": threads,
+            "host_cpus": len(os.sched_getaffinity(0)), "kind": "oracle",
+            "sample": f"{done} of {w.batch} batch elements ({done * w.seqlen} tokens) of the layer workload, "
+                      f"float64 numpy, {t:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--only", default="layer,decode,long,block,cpu")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for {max(args.gpus, world)}): this library has no "
+              f"multi-GPU path; the sharding design is described in DESIGN.md.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import workloads
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    parts = set(args.only.split(","))
+    if args.no_cpu:
+        parts.discard("cpu")
+    props = torch.cuda.get_device_properties(0)
+    log(f"device {props.name} CUs={props.multi_processor_count}")
+
+    w = workloads.WORKLOADS["layer_bf16_b8_n2048"]
+    line = {"metric": "MSR fwd tokens/s + %MFMA peak (chunkwise); decode steps/s + %HBM peak",
+            "value": None, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": None, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic (seeded Gaussian inputs and random-init weights)",
+            "config": {"workload": w.name, "batch": w.batch, "seqlen": w.seqlen, "d_model": w.d_model,
+                       "heads": w.heads, "d_k": w.d_k, "d_v": w.d_v, "chunk": w.chunk, "form": "chunkwise"}}
+    if "layer" in parts:
+        log("layer", w.name)
+        r = bench_layer(w, args.steps, args.warmup)
+        line["value"] = round(r["tokens_per_s"], 1)
+        line["ms_per_step"] = round(r["s_per_step"] * 1e3, 4)
+        line["mfma_frac"] = round(r["mfma_frac"], 4)
+        line["tflops"] = round(r["tflops"], 1)
+        k = r["kernels"]
+        dom = max(k, key=lambda n: r["trace_s_per_step"].get(n, 0))
+        line["roofline"] = {x: k[dom][x] for x in ("bound", "achieved", "peak", "unit", "frac", "traffic")}
+        line["roofline"]["kernel"] = dom
+        line["kernels"] = k
+        line["trace_ms_per_step"] = {n: round(v * 1e3, 4) for n, v in r["trace_s_per_step"].items()}
+    if "decode" in parts:
+        log("decode")
+        line["decode"] = bench_decode(512, 16)
+    if "long" in parts:
+        log("long")
+        lw = workloads.WORKLOADS["long_bf16_b2_n16384"]
+        long = {"core_chunkwise": bench_core(lw.batch, lw.seqlen, lw.heads, lw.d_k, lw.chunk, args.steps,
+                                             args.warmup)}
+        sweep = []
+        for N in (1024, 2048, 4096, 8192, 16384):
+            c = bench_core(lw.batch, N, lw.heads, lw.d_k, lw.chunk, 5, 2)
+            p = bench_core(lw.batch, N, lw.heads, lw.d_k, lw.chunk, 3, 1, parallel=True)
+            sweep.append({"N": N, "chunkwise_us": round(c["s"] * 1e6, 1), "parallel_us": round(p["s"] * 1e6, 1),
+                          "chunkwise_tflops": round(c["tflops"], 1), "parallel_tflops": round(p["tflops"], 1)})
+        long["sweep"] = sweep
+        lr = bench_layer(lw, max(3, args.steps // 4), 2, device_inputs=True)
+        long["layer"] = {"tokens_per_s": round(lr["tokens_per_s"], 1), "mfma_frac": round(lr["mfma_frac"], 4),
+                         "ms_per_step": round(lr["s_per_step"] * 1e3, 3)}
+        line["long"] = long
+    if "block" in parts:
+        log("block")
+        bw = workloads.WORKLOADS["block_bf16_b4_n8192"]
+        br = bench_layer(bw, max(3, args.steps // 4), 2, device_inputs=True)
+        line["block"] = {"tokens_per_s": round(br["tokens_per_s"], 1), "mfma_frac": round(br["mfma_frac"], 4),
+                         "ms_per_step": round(br["s_per_step"] * 1e3, 3), "tflops": round(br["tflops"], 1),
+                         "kernels": br["kernels"]}
+    if "cpu" in parts:
+        log("cpu baseline")
+        line["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

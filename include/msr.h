@@ -1,0 +1,157 @@
+/*
+ * msr.h -- C ABI of libmsr: multi-scale retention (MSR) on AMD Instinct
+ * MI355X (gfx950).
+ *
+ * Pages cited:
+ *   [RN-zh] "Transformer取代者登場！微軟、清華剛推出RetNet：成本低、速度快、
+ *           性能強（2）" -- the RetNet method: retention in three forms
+ *           (sections "1) Retention 的並行表征" Eq. (5), "2) Retention 的循環
+ *           表征" Eq. (6), "3) Retention 分塊循環表征" Eq. (7)), the gated
+ *           multi-scale layer (section "門控多尺度 Retention", Eq. (8)) and the
+ *           score normalisation (section "Retention Score 歸一化").
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Layout.   Activations are token-major [batch, seqlen, heads, head_dim],
+ *           head_dim fastest (exactly what X @ W produces).  Weights are
+ *           row-major [in, out] so the layer computes X @ W.  The recurrent
+ *           state S is [batch, heads, d_k, d_v] float32, d_v fastest.
+ * dtype.    MSR_F32: float32 everywhere.  MSR_BF16: bfloat16 inputs and
+ *           outputs, float32 accumulation; the state S is always float32.
+ * gamma.    Host array of `heads` doubles, 0 <= gamma_h <= 1, the per-head
+ *           decay.  Powers of gamma are formed on the device as
+ *           exp2(k * log2(gamma_h)) from log2(gamma_h) computed on the host
+ *           in double precision.
+ * Rotation. rope_base > 0 rotates interleaved pairs (x[2j], x[2j+1]) of Q
+ *           and K by the angle p * theta_j, theta_j = rope_base^(-2j/d_k),
+ *           p = absolute token position ([RN-zh] section "Retention",
+ *           Eq. (3)-(4), xPos).  rope_base <= 0: no rotation.
+ * Memory.   Every pointer except `gamma` is device memory allocated by the
+ *           caller; the library allocates nothing and, apart from the
+ *           opt-in msr_trace_* diagnostics, keeps no mutable global state
+ *           (it is thread safe).  Outputs must not alias
+ *           inputs, except S of msr_recurrent_step, which is updated in
+ *           place.
+ * Streams.  `stream` is a hipStream_t (NULL = the null stream).  Every call
+ *           only enqueues work and returns without synchronising.
+ * Errors.   All arguments are validated on the host before anything is
+ *           launched; on error nothing is enqueued and a status is returned
+ *           (never an abort).  msr_last_error() gives a human-readable
+ *           reason for the last failure on the calling thread.  A launch
+ *           failure reported by the HIP runtime maps to MSR_ERR_HIP.
+ * Supported head dims (else MSR_ERR_UNSUPPORTED): (d_k, d_v) in
+ *           {(64,64), (128,128), (256,256), (256,512)}, the last one in
+ *           bf16 only except for msr_recurrent_step; heads <= 128; chunk a
+ *           positive multiple of 32; batch * seqlen < 2^31.
+ */
+#ifndef MSR_H
+#define MSR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MSR_OK = 0,
+  MSR_ERR_NULL = 1,         /* a required pointer is NULL */
+  MSR_ERR_SHAPE = 2,        /* negative / inconsistent sizes */
+  MSR_ERR_DTYPE = 3,        /* unknown dtype */
+  MSR_ERR_UNSUPPORTED = 4,  /* valid but not implemented (head dim, chunk) */
+  MSR_ERR_WORKSPACE = 5,    /* workspace missing or too small */
+  MSR_ERR_HIP = 6           /* the HIP runtime reported an error */
+} msr_status;
+
+typedef enum { MSR_F32 = 0, MSR_BF16 = 1 } msr_dtype;
+
+typedef struct {
+  int32_t batch, seqlen, heads, d_k, d_v;
+} msr_dims;
+
+/* Parallel form, [RN-zh] Eq. (5):
+ *   O = ((Q K^T) * qk_scale  (.)  D) V,  D[n,m] = gamma_h^(n-m) (n >= m), else 0,
+ * per (batch, head), with Q, K rotated at positions pos0 + n when
+ * rope_base > 0.  Q, K: [batch, seqlen, heads, d_k]; V, O: [.., d_v].
+ * Workspace: msr_parallel_workspace_bytes() bytes (0 when rope_base <= 0). */
+msr_status msr_parallel_fwd(msr_dtype dtype, msr_dims dims, const double* gamma,
+                            float rope_base, int64_t pos0, float qk_scale,
+                            const void* Q, const void* K, const void* V, void* O,
+                            void* workspace, size_t ws_bytes, void* stream);
+size_t msr_parallel_workspace_bytes(msr_dtype dtype, msr_dims dims, float rope_base);
+
+/* Chunkwise recurrent form, [RN-zh] Eq. (7).  Contiguous chunks of `chunk`
+ * tokens (the last may be short, length L); t, s index rows inside a chunk:
+ *   O_[i] = ((Q_[i] K_[i]^T) * qk_scale (.) D) V_[i]
+ *           + qk_scale * (Q_[i] R_{i-1}) (.) xi,       xi_t   = gamma^(t+1)
+ *   R_i   = gamma^L R_{i-1} + K_[i]^T (V_[i] (.) zeta), zeta_s = gamma^(L-1-s)
+ * R_{-1} = S_in (NULL: zeros); S_out (nullable) receives the last R.  The
+ * state is carried across chunks in float32.  S_in/S_out:
+ * [batch, heads, d_k, d_v] float32; S_out may not alias S_in.  pos0 is the
+ * absolute position of token 0 (the rotation of a continued sequence).
+ * Workspace: msr_chunkwise_workspace_bytes() bytes. */
+msr_status msr_chunkwise_fwd(msr_dtype dtype, msr_dims dims, int32_t chunk,
+                             const double* gamma, float rope_base, int64_t pos0,
+                             float qk_scale, const void* Q, const void* K,
+                             const void* V, const float* S_in, float* S_out,
+                             void* O, void* workspace, size_t ws_bytes,
+                             void* stream);
+size_t msr_chunkwise_workspace_bytes(msr_dtype dtype, msr_dims dims, int32_t chunk,
+                                     float rope_base);
+
+/* Recurrent form, one decode step, [RN-zh] Eq. (6), for every (batch, head):
+ *   S <- gamma_h S + k^T v ;  o = qk_scale * q S   (S updated in place)
+ * q, k: [batch, heads, d_k]; v, o: [batch, heads, d_v] (dtype); S:
+ * [batch, heads, d_k, d_v] float32.  q and k are rotated at position `pos`
+ * when rope_base > 0.  No workspace. */
+msr_status msr_recurrent_step(msr_dtype dtype, int32_t batch, int32_t heads,
+                              int32_t d_k, int32_t d_v, const double* gamma,
+                              float rope_base, int64_t pos, float qk_scale,
+                              const void* q, const void* k, const void* v,
+                              float* S, void* o, void* stream);
+
+/* Gated multi-scale retention layer, [RN-zh] Eq. (8):
+ *   Q^ = X W_Q, K^ = X W_K, V = X W_V, G = X W_G   (head h = column block h)
+ *   Q, K = rotation of Q^, K^ at positions 0..seqlen-1 (rope_base > 0)
+ *   head_h = chunkwise retention (chunk, gamma_h, score scale 1/sqrt(d_k))
+ *   Y = GroupNorm per (token, head) over d_v, biased variance, eps = gn_eps,
+ *       identity affine
+ *   out = (swish(G) (.) Y) W_O,  swish(x) = x * sigmoid(x)
+ * X: [batch, seqlen, d_model]; W_Q, W_K: [d_model, heads*d_k];
+ * W_V, W_G: [d_model, heads*d_v]; W_O: [heads*d_v, d_model];
+ * out: [batch, seqlen, d_model].  d_model must be a multiple of 64.
+ * Workspace: msr_layer_workspace_bytes() bytes. */
+msr_status msr_layer_fwd(msr_dtype dtype, int32_t batch, int32_t seqlen,
+                         int32_t d_model, int32_t heads, int32_t d_k, int32_t d_v,
+                         int32_t chunk, const double* gamma, float rope_base,
+                         float gn_eps, const void* X, const void* W_Q,
+                         const void* W_K, const void* W_V, const void* W_G,
+                         const void* W_O, void* out, void* workspace,
+                         size_t ws_bytes, void* stream);
+size_t msr_layer_workspace_bytes(msr_dtype dtype, int32_t batch, int32_t seqlen,
+                                 int32_t d_model, int32_t heads, int32_t d_k,
+                                 int32_t d_v, int32_t chunk);
+
+/* Diagnostics for benchmarks: per-kernel timing with HIP events.
+ * msr_trace_enable(1) clears earlier totals and from then on brackets every
+ * kernel the library launches with an event pair recorded on that launch's
+ * stream; msr_trace_enable(0) stops (and clears).  msr_trace_count() waits
+ * for all recorded events, folds them into per-kernel totals and returns the
+ * number of distinct kernels; msr_trace_get(i, ...) returns the i-th kernel's
+ * name (valid until the next msr_trace_* call), total milliseconds and launch
+ * count (MSR_ERR_SHAPE for i out of range).  Process-wide state, not thread
+ * safe; never enable it in a caller that must not synchronise. */
+void msr_trace_enable(int32_t on);
+int32_t msr_trace_count(void);
+msr_status msr_trace_get(int32_t i, const char** name, double* total_ms, int64_t* launches);
+
+/* Name of a status code. */
+const char* msr_status_str(msr_status s);
+/* Reason for the last non-OK status returned on the calling thread. */
+const char* msr_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MSR_H */

@@ -1,0 +1,254 @@
+"""Python binding of libmsr (multi-scale retention on MI355X / gfx950).
+
+Argument marshalling only: every function below validates nothing beyond
+what it needs to build the C call, and every step of the computation runs in
+the HIP kernels of ``libmsr.so``.  PyTorch supplies device memory and the
+current stream.  The C functions carry the same names; their contracts are
+documented in ``include/msr.h``.
+
+If ``libmsr.so`` has not been built, importing works but the first call
+raises ``MsrLibraryMissing`` -- there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "MSR_F32", "MSR_BF16", "MsrError", "MsrLibraryMissing", "library_path", "lib",
+    "msr_parallel_fwd", "msr_parallel_workspace_bytes",
+    "msr_chunkwise_fwd", "msr_chunkwise_workspace_bytes",
+    "msr_recurrent_step", "msr_layer_fwd", "msr_layer_workspace_bytes",
+    "msr_status_str", "msr_last_error", "msr_trace_enable", "msr_trace_count", "msr_trace_get",
+    "trace_totals",
+]
+
+MSR_F32, MSR_BF16 = 0, 1
+EXPORTS = (
+    "msr_parallel_fwd", "msr_parallel_workspace_bytes", "msr_chunkwise_fwd",
+    "msr_chunkwise_workspace_bytes", "msr_recurrent_step", "msr_layer_fwd",
+    "msr_layer_workspace_bytes", "msr_status_str", "msr_last_error",
+    "msr_trace_enable", "msr_trace_count", "msr_trace_get",
+)
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, "libmsr.so")
+
+
+class MsrError(RuntimeError):
+    def __init__(self, fn, status, detail):
+        super().__init__(f"{fn}: {msr_status_str(status)} ({status}): {detail}")
+        self.status = status
+
+
+class MsrLibraryMissing(ImportError):
+    pass
+
+
+class MsrDims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("seqlen", ctypes.c_int32), ("heads", ctypes.c_int32),
+                ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32)]
+
+
+_lib = None
+_P = ctypes.c_void_p
+_I32, _I64, _F, _SZ = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+_DP = ctypes.POINTER(ctypes.c_double)
+
+
+def lib():
+    """Load libmsr.so (once) and declare its signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise MsrLibraryMissing(
+            f"{path} is missing: build it with `python -m linear_recurrence_sequence_amd.build`")
+    L = ctypes.CDLL(path)
+    sig = {
+        "msr_parallel_fwd": (_I32, [_I32, MsrDims, _DP, _F, _I64, _F, _P, _P, _P, _P, _P, _SZ, _P]),
+        "msr_parallel_workspace_bytes": (_SZ, [_I32, MsrDims, _F]),
+        "msr_chunkwise_fwd": (_I32, [_I32, MsrDims, _I32, _DP, _F, _I64, _F, _P, _P, _P, _P, _P, _P, _P,
+                                     _SZ, _P]),
+        "msr_chunkwise_workspace_bytes": (_SZ, [_I32, MsrDims, _I32, _F]),
+        "msr_recurrent_step": (_I32, [_I32, _I32, _I32, _I32, _I32, _DP, _F, _I64, _F, _P, _P, _P, _P, _P,
+                                      _P]),
+        "msr_layer_fwd": (_I32, [_I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _DP, _F, _F, _P, _P, _P,
+                                 _P, _P, _P, _P, _P, _SZ, _P]),
+        "msr_layer_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32]),
+        "msr_trace_enable": (None, [_I32]),
+        "msr_trace_count": (_I32, []),
+        "msr_trace_get": (_I32, [_I32, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_double),
+                                 ctypes.POINTER(ctypes.c_int64)]),
+        "msr_status_str": (ctypes.c_char_p, [_I32]),
+        "msr_last_error": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(L, name)
+        f.restype, f.argtypes = res, args
+    _lib = L
+    return L
+
+
+def msr_status_str(status: int) -> str:
+    return lib().msr_status_str(int(status)).decode()
+
+
+def msr_last_error() -> str:
+    return lib().msr_last_error().decode()
+
+
+def _check(fn, status):
+    if status != 0:
+        raise MsrError(fn, status, msr_last_error())
+
+
+def msr_trace_enable(on: bool) -> None:
+    lib().msr_trace_enable(1 if on else 0)
+
+
+def msr_trace_count() -> int:
+    return lib().msr_trace_count()
+
+
+def msr_trace_get(i: int):
+    name, ms, n = ctypes.c_char_p(), ctypes.c_double(), ctypes.c_int64()
+    _check("msr_trace_get", lib().msr_trace_get(i, ctypes.byref(name), ctypes.byref(ms), ctypes.byref(n)))
+    return name.value.decode(), ms.value, n.value
+
+
+def trace_totals() -> dict:
+    """{kernel name: (total ms, launches)} recorded since msr_trace_enable(True)."""
+    return {name: (ms, n) for name, ms, n in (msr_trace_get(i) for i in range(msr_trace_count()))}
+
+
+# ---------------------------------------------------------------- helpers --
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return MSR_F32
+    if t.dtype == torch.bfloat16:
+        return MSR_BF16
+    raise TypeError(f"unsupported tensor dtype {t.dtype}; use float32 or bfloat16")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_cuda:
+        raise ValueError("tensors must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _gamma(gamma, heads):
+    import numpy as np
+    g = np.ascontiguousarray(np.asarray(gamma, dtype=np.float64).reshape(-1))
+    if g.size != heads:
+        raise ValueError(f"gamma has {g.size} values for {heads} heads")
+    return g, g.ctypes.data_as(_DP)
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    return _torch().cuda.current_stream().cuda_stream
+
+
+def _workspace(nbytes, workspace, device):
+    if nbytes == 0:
+        return workspace, 0
+    if workspace is None:
+        workspace = _torch().empty(nbytes, dtype=_torch().uint8, device=device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+# ------------------------------------------------------------ entry points --
+def msr_parallel_workspace_bytes(dtype: int, batch, seqlen, heads, d_k, d_v, rope_base) -> int:
+    return lib().msr_parallel_workspace_bytes(dtype, MsrDims(batch, seqlen, heads, d_k, d_v), rope_base)
+
+
+def msr_chunkwise_workspace_bytes(dtype: int, batch, seqlen, heads, d_k, d_v, chunk, rope_base) -> int:
+    return lib().msr_chunkwise_workspace_bytes(dtype, MsrDims(batch, seqlen, heads, d_k, d_v), chunk,
+                                               rope_base)
+
+
+def msr_layer_workspace_bytes(dtype: int, batch, seqlen, d_model, heads, d_k, d_v, chunk) -> int:
+    return lib().msr_layer_workspace_bytes(dtype, batch, seqlen, d_model, heads, d_k, d_v, chunk)
+
+
+def msr_parallel_fwd(Q, K, V, gamma, *, rope_base=0.0, pos0=0, qk_scale=1.0, O=None, workspace=None,
+                     stream=None):
+    """Parallel form (Eq. 5).  Q, K: [B, N, H, d_k]; V: [B, N, H, d_v]."""
+    B, N, H, dk = Q.shape
+    dv = V.shape[-1]
+    dt = _dtype_code(Q)
+    if O is None:
+        O = _torch().empty((B, N, H, dv), dtype=Q.dtype, device=Q.device)
+    _, gp = g = _gamma(gamma, H)
+    dims = MsrDims(B, N, H, dk, dv)
+    ws, wsb = _workspace(lib().msr_parallel_workspace_bytes(dt, dims, rope_base), workspace, Q.device)
+    _check("msr_parallel_fwd", lib().msr_parallel_fwd(dt, dims, gp, rope_base, pos0, qk_scale, _ptr(Q), _ptr(K),
+                                                      _ptr(V), _ptr(O), _ptr(ws), wsb, _stream(stream)))
+    return O
+
+
+def msr_chunkwise_fwd(Q, K, V, gamma, chunk, *, rope_base=0.0, pos0=0, qk_scale=1.0, S_in=None,
+                      S_out=None, O=None, workspace=None, stream=None):
+    """Chunkwise form (Eq. 7).  Returns O; S_out (if given) receives the
+    final state [B, H, d_k, d_v] float32."""
+    B, N, H, dk = Q.shape
+    dv = V.shape[-1]
+    dt = _dtype_code(Q)
+    if O is None:
+        O = _torch().empty((B, N, H, dv), dtype=Q.dtype, device=Q.device)
+    _, gp = g = _gamma(gamma, H)
+    dims = MsrDims(B, N, H, dk, dv)
+    ws, wsb = _workspace(lib().msr_chunkwise_workspace_bytes(dt, dims, chunk, rope_base), workspace, Q.device)
+    _check("msr_chunkwise_fwd", lib().msr_chunkwise_fwd(dt, dims, chunk, gp, rope_base, pos0, qk_scale, _ptr(Q),
+                                                        _ptr(K), _ptr(V), _ptr(S_in), _ptr(S_out), _ptr(O),
+                                                        _ptr(ws), wsb, _stream(stream)))
+    return O
+
+
+def msr_recurrent_step(q, k, v, S, gamma, *, pos, rope_base=0.0, qk_scale=1.0, o=None, stream=None):
+    """Recurrent form, one step (Eq. 6), S updated in place.
+    q, k: [B, H, d_k]; v: [B, H, d_v]; S: [B, H, d_k, d_v] float32."""
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = _dtype_code(q)
+    if o is None:
+        o = _torch().empty((B, H, dv), dtype=q.dtype, device=q.device)
+    _, gp = g = _gamma(gamma, H)
+    _check("msr_recurrent_step", lib().msr_recurrent_step(dt, B, H, dk, dv, gp, rope_base, pos, qk_scale,
+                                                          _ptr(q), _ptr(k), _ptr(v), _ptr(S), _ptr(o),
+                                                          _stream(stream)))
+    return o
+
+
+def msr_layer_fwd(X, W_Q, W_K, W_V, W_G, W_O, gamma, heads, d_k, d_v, chunk, *, rope_base=10000.0,
+                  gn_eps=1e-5, out=None, workspace=None, stream=None):
+    """Gated MSR layer (Eq. 8).  X: [B, N, d_model]; returns [B, N, d_model]."""
+    B, N, dm = X.shape
+    dt = _dtype_code(X)
+    if out is None:
+        out = _torch().empty((B, N, dm), dtype=X.dtype, device=X.device)
+    _, gp = g = _gamma(gamma, heads)
+    nbytes = lib().msr_layer_workspace_bytes(dt, B, N, dm, heads, d_k, d_v, chunk)
+    ws, wsb = _workspace(nbytes, workspace, X.device)
+    _check("msr_layer_fwd", lib().msr_layer_fwd(dt, B, N, dm, heads, d_k, d_v, chunk, gp, rope_base, gn_eps,
+                                                _ptr(X), _ptr(W_Q), _ptr(W_K), _ptr(W_V), _ptr(W_G), _ptr(W_O),
+                                                _ptr(out), _ptr(ws), wsb, _stream(stream)))
+    return out

@@ -1,0 +1,175 @@
+// Recurrent decode step and rotation kernels for gfx950.
+//
+// Decode ([RN-zh] = page "Transformer取代者登場！微軟、清華剛推出RetNet：成本低、
+// 速度快、性能強（2）", section "2) Retention 的循環表征", Eq. (6)): for every
+// (batch, head)
+//   S <- gamma S + k^T v ;   o = scale * q S
+// with q, k rotated at the absolute position (section "Retention", Eq. (3)-(4),
+// xPos).  The step reads and writes the d_k x d_v float32 state once, so it is
+// bound by HBM bandwidth: one workgroup per (batch, head) streams the state
+// row by row, each lane owning 4 contiguous d_v columns (16-byte accesses,
+// a wave covers 256 contiguous floats), with 8 rows in flight per lane.
+#include "msr_launch.h"
+
+namespace msr {
+
+// (cos, sin) of p * theta_j, theta_j = base^(-2j/d).  The angle is reduced in
+// double precision (p can be ~1e4 radians, where float32 would lose ~1e-3 of
+// absolute accuracy) and evaluated as sincospi of the reduced half-turns.
+__device__ __forceinline__ void rope_cs(int64_t p, int j, int d, float base, float* c, float* s) {
+  const double w = exp2(-2.0 * (double)j / (double)d * log2((double)base)) * 0.31830988618379067154;  // theta/pi
+  double t = (double)p * w;
+  t -= 2.0 * rint(0.5 * t);
+  sincospif((float)t, s, c);
+}
+
+template <class T> __device__ __forceinline__ float ld1(const T* p) { return (float)*p; }
+
+template <class T, int DK, int DV>
+__global__ __launch_bounds__(256) void k_recurrent_step(const T* __restrict__ q, const T* __restrict__ k,
+                                                        const T* __restrict__ v, float* __restrict__ S,
+                                                        T* __restrict__ o, int H, float scale, int64_t pos,
+                                                        float rope_base, HeadTab tab) {
+  constexpr int CPT = 4;               // d_v columns per lane
+  constexpr int TPR = DV / CPT;        // lanes per state row
+  constexpr int RG = 256 / TPR;        // rows processed in parallel
+  __shared__ float sq[DK], sk[DK];
+  __shared__ f32x4 red[RG][TPR];
+  const int bh = blockIdx.x, h = bh % H, tid = threadIdx.x;
+  const T* qb = q + (size_t)bh * DK;
+  const T* kb = k + (size_t)bh * DK;
+  for (int j = tid; j < DK / 2; j += 256) {
+    float q0 = ld1(qb + 2 * j), q1 = ld1(qb + 2 * j + 1), k0 = ld1(kb + 2 * j), k1 = ld1(kb + 2 * j + 1);
+    if (rope_base > 0.f) {
+      float c, s;
+      rope_cs(pos, j, DK, rope_base, &c, &s);
+      const float a0 = q0 * c - q1 * s, a1 = q0 * s + q1 * c;
+      const float b0 = k0 * c - k1 * s, b1 = k0 * s + k1 * c;
+      q0 = a0; q1 = a1; k0 = b0; k1 = b1;
+    }
+    sq[2 * j] = q0; sq[2 * j + 1] = q1;
+    sk[2 * j] = k0; sk[2 * j + 1] = k1;
+  }
+  __syncthreads();
+
+  const int rg = tid / TPR, c = (tid % TPR) * CPT;
+  const T* vb = v + (size_t)bh * DV + c;
+  const f32x4 vv = {ld1(vb), ld1(vb + 1), ld1(vb + 2), ld1(vb + 3)};
+  const float g = tab.gam[h];
+  float* Sb = S + (size_t)bh * DK * DV + c;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+  for (int i = rg; i < DK; i += RG) {
+    f32x4* p = reinterpret_cast<f32x4*>(Sb + (size_t)i * DV);
+    f32x4 s = *p;
+    const float ki = sk[i], qi = sq[i];
+    s = g * s + ki * vv;
+    *p = s;
+    acc += qi * s;
+  }
+  red[rg][tid % TPR] = acc;
+  __syncthreads();
+  if (rg == 0) {
+    f32x4 t = red[0][tid];
+#pragma unroll
+    for (int r = 1; r < RG; ++r) t += red[r][tid];
+    T* ob = o + (size_t)bh * DV + c;
+    ob[0] = (T)(scale * t[0]);
+    ob[1] = (T)(scale * t[1]);
+    ob[2] = (T)(scale * t[2]);
+    ob[3] = (T)(scale * t[3]);
+  }
+}
+
+template <class T, int DK, int DV>
+static hipError_t run_step(int batch, int heads, const void* q, const void* k, const void* v, float* S, void* o,
+                           float scale, int64_t pos, float base, const HeadTab& tab, hipStream_t st) {
+  TraceScope ts("k_recurrent_step", st);
+  hipLaunchKernelGGL((k_recurrent_step<T, DK, DV>), dim3(batch * heads), dim3(256), 0, st, (const T*)q,
+                     (const T*)k, (const T*)v, S, (T*)o, heads, scale, pos, base, tab);
+  return hipGetLastError();
+}
+
+hipError_t launch_recurrent_step(Elt elt, int d_k, int d_v, int batch, int heads, const void* q, const void* k,
+                                 const void* v, float* S, void* o, float scale, int64_t pos, float base,
+                                 const HeadTab& tab, hipStream_t st) {
+#define MSR_STEP(T)                                                                               \
+  if (d_k == 64 && d_v == 64) return run_step<T, 64, 64>(batch, heads, q, k, v, S, o, scale, pos, base, tab, st); \
+  if (d_k == 128 && d_v == 128) return run_step<T, 128, 128>(batch, heads, q, k, v, S, o, scale, pos, base, tab, st); \
+  if (d_k == 256 && d_v == 256) return run_step<T, 256, 256>(batch, heads, q, k, v, S, o, scale, pos, base, tab, st); \
+  if (d_k == 256 && d_v == 512) return run_step<T, 256, 512>(batch, heads, q, k, v, S, o, scale, pos, base, tab, st);
+  if (elt == kBF16) {
+    MSR_STEP(bf16)
+  } else {
+    MSR_STEP(float)
+  }
+#undef MSR_STEP
+  return hipErrorInvalidValue;
+}
+
+// ---------------------------------------------------------------------------
+// Rotation: a (cos, sin) table per call, then an elementwise pass.
+// ---------------------------------------------------------------------------
+__global__ void k_rope_table(float2* tab, int npos, int d, int64_t pos0, float base) {
+  const int half = d / 2;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)npos * half) return;
+  const int n = (int)(i / half), j = (int)(i % half);
+  float c, s;
+  rope_cs(pos0 + n, j, d, base, &c, &s);
+  tab[i] = make_float2(c, s);
+}
+
+hipError_t launch_rope_table(float2* tab, int npos, int d, int64_t pos0, float base, hipStream_t st) {
+  const int64_t n = (int64_t)npos * (d / 2);
+  if (n == 0) return hipSuccess;
+  TraceScope ts("k_rope_table", st);
+  hipLaunchKernelGGL(k_rope_table, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, tab, npos, d, pos0, base);
+  return hipGetLastError();
+}
+
+// One lane rotates 4 pairs (8 contiguous elements) of one (token, head).
+template <class T>
+__global__ void k_rope_apply(const T* src, int64_t lds, T* dst, int64_t ldd, int rows, int seqlen, int heads, int d,
+                             const float2* __restrict__ tab) {
+  const int groups = d / 8;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t per_row = (int64_t)heads * groups;
+  if (i >= (int64_t)rows * per_row) return;
+  const int row = (int)(i / per_row);
+  const int rem = (int)(i % per_row);
+  const int h = rem / groups, g = rem % groups;
+  const int n = row % seqlen;
+  const T* s = src + (size_t)row * lds + (size_t)h * d + 8 * g;
+  T* o = dst + (size_t)row * ldd + (size_t)h * d + 8 * g;
+  const float2* cs = tab + (size_t)n * (d / 2) + 4 * g;
+  float x[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = (float)s[e];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const float2 t = cs[p];
+    const float a = x[2 * p], b = x[2 * p + 1];
+    x[2 * p] = a * t.x - b * t.y;
+    x[2 * p + 1] = a * t.y + b * t.x;
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = (T)x[e];
+}
+
+hipError_t launch_rope_apply(Elt elt, const void* src, int64_t lds, void* dst, int64_t ldd, int rows, int seqlen,
+                             int heads, int d, const float2* tab, hipStream_t st) {
+  const int64_t n = (int64_t)rows * heads * (d / 8);
+  if (n == 0) return hipSuccess;
+  const dim3 grid((unsigned)((n + 255) / 256));
+  TraceScope ts("k_rope_apply", st);
+  if (elt == kBF16)
+    hipLaunchKernelGGL(k_rope_apply<bf16>, grid, dim3(256), 0, st, (const bf16*)src, lds, (bf16*)dst, ldd, rows,
+                       seqlen, heads, d, tab);
+  else
+    hipLaunchKernelGGL(k_rope_apply<float>, grid, dim3(256), 0, st, (const float*)src, lds, (float*)dst, ldd, rows,
+                       seqlen, heads, d, tab);
+  return hipGetLastError();
+}
+
+}  // namespace msr

@@ -1,0 +1,370 @@
+// libmsr C ABI: argument validation, workspace layout and dispatch.
+// The operations and their arguments are documented in include/msr.h.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/msr.h"
+#include "msr_launch.h"
+
+using namespace msr;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+msr_status fail(msr_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+msr_status fail(msr_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+msr_status ok() {
+  g_last_error.clear();
+  return MSR_OK;
+}
+
+msr_status from_hip(hipError_t e, const char* where) {
+  if (e == hipSuccess) return ok();
+  return fail(MSR_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+size_t elt_size(msr_dtype d) { return d == MSR_BF16 ? 2 : 4; }
+
+bool dims_supported(int dk, int dv) {
+  return (dk == 64 && dv == 64) || (dk == 128 && dv == 128) || (dk == 256 && dv == 256) ||
+         (dk == 256 && dv == 512);
+}
+
+msr_status check_dtype(msr_dtype d) {
+  if (d != MSR_F32 && d != MSR_BF16) return fail(MSR_ERR_DTYPE, "unknown dtype %d", (int)d);
+  return MSR_OK;
+}
+
+msr_status check_heads(int32_t batch, int32_t seqlen, int32_t heads, int32_t dk, int32_t dv) {
+  if (batch < 0 || seqlen < 0 || heads <= 0 || dk <= 0 || dv <= 0)
+    return fail(MSR_ERR_SHAPE, "invalid sizes batch=%d seqlen=%d heads=%d d_k=%d d_v=%d", batch, seqlen, heads, dk,
+                dv);
+  if (heads > kMaxHeads) return fail(MSR_ERR_UNSUPPORTED, "heads=%d exceeds %d", heads, kMaxHeads);
+  if (!dims_supported(dk, dv))
+    return fail(MSR_ERR_UNSUPPORTED, "(d_k, d_v) = (%d, %d) has no kernel; supported: (64,64) (128,128) (256,256) "
+                "(256,512)", dk, dv);
+  const int64_t tokens = (int64_t)batch * seqlen;
+  if (tokens > (int64_t)INT32_MAX) return fail(MSR_ERR_UNSUPPORTED, "batch*seqlen exceeds 2^31-1");
+  return MSR_OK;
+}
+
+// The matrix-core (chunkwise / parallel / layer) kernels have no float32
+// variant for 512-wide value heads: its accumulators and tiles do not fit.
+msr_status check_matrix_dims(msr_dtype dt, int dv) {
+  if (dt == MSR_F32 && dv > 256)
+    return fail(MSR_ERR_UNSUPPORTED, "d_v = %d has no float32 chunkwise/parallel kernel (bf16 only)", dv);
+  return MSR_OK;
+}
+
+msr_status check_gamma(const double* gamma, int heads) {
+  if (!gamma) return fail(MSR_ERR_NULL, "gamma is NULL");
+  for (int h = 0; h < heads; ++h)
+    if (!(gamma[h] >= 0.0 && gamma[h] <= 1.0))
+      return fail(MSR_ERR_SHAPE, "gamma[%d] = %g is outside [0, 1]", h, gamma[h]);
+  return MSR_OK;
+}
+
+msr_status check_chunk(int32_t chunk) {
+  if (chunk <= 0) return fail(MSR_ERR_SHAPE, "chunk = %d must be positive", chunk);
+  if (chunk % 32) return fail(MSR_ERR_UNSUPPORTED, "chunk = %d is not a multiple of 32", chunk);
+  return MSR_OK;
+}
+
+HeadTab make_tab(const double* gamma, int heads, int chunk, int seqlen) {
+  HeadTab t;
+  std::memset(&t, 0, sizeof t);
+  int last = seqlen > 0 && chunk > 0 ? seqlen - ((seqlen - 1) / chunk) * chunk : 0;
+  for (int h = 0; h < heads; ++h) {
+    const double g = gamma[h];
+    t.lg2[h] = g > 0.0 ? (float)std::log2(g) : -INFINITY;
+    t.gchunk[h] = (float)std::pow(g, (double)chunk);
+    t.glast[h] = (float)std::pow(g, (double)last);
+    t.gam[h] = (float)g;
+  }
+  return t;
+}
+
+struct ChunkWs {
+  size_t qr = 0, kr = 0, tab = 0, dr = 0, rx = 0, total = 0;
+};
+
+ChunkWs chunk_ws_layout(msr_dtype dt, const msr_dims& d, int32_t chunk, bool rope, bool with_state) {
+  ChunkWs w;
+  const size_t es = elt_size(dt);
+  const size_t tok = (size_t)d.batch * d.seqlen;
+  size_t off = 0;
+  if (rope) {
+    w.qr = off; off += align_up(tok * d.heads * d.d_k * es);
+    w.kr = off; off += align_up(tok * d.heads * d.d_k * es);
+    w.tab = off; off += align_up((size_t)d.seqlen * (d.d_k / 2) * sizeof(float2));
+  }
+  if (with_state) {
+    const size_t nc = chunk > 0 ? ((size_t)d.seqlen + chunk - 1) / chunk : 0;
+    const size_t st = (size_t)d.batch * d.heads * nc * d.d_k * d.d_v;
+    w.dr = off; off += align_up(st * sizeof(float));
+    w.rx = w.dr;
+    if (dt == MSR_BF16) { w.rx = off; off += align_up(st * 2); }
+  }
+  w.total = off;
+  return w;
+}
+
+struct LayerWs {
+  size_t wt = 0, wto = 0, qkvg = 0, z = 0, chunk = 0, total = 0;
+  ChunkWs cw;
+};
+LayerWs layer_ws_layout(msr_dtype dt, int32_t batch, int32_t seqlen, int32_t d_model, int32_t heads, int32_t dk,
+                        int32_t dv, int32_t chunk) {
+  LayerWs w;
+  const size_t es = elt_size(dt);
+  const size_t M = (size_t)batch * seqlen;
+  const size_t ntot = (size_t)heads * (2 * dk + 2 * dv);
+  size_t off = 0;
+  w.wt = off; off += align_up(ntot * d_model * es);
+  w.wto = off; off += align_up((size_t)d_model * heads * dv * es);
+  w.qkvg = off; off += align_up(M * ntot * es);
+  w.z = off; off += align_up(M * heads * dv * es);
+  msr_dims d{batch, seqlen, heads, dk, dv};
+  w.cw = chunk_ws_layout(dt, d, chunk, true, true);  // includes the rotation table
+  w.chunk = off; off += w.cw.total;
+  w.total = off;
+  return w;
+}
+
+template <class P> P* at(void* base, size_t off) { return reinterpret_cast<P*>(static_cast<char*>(base) + off); }
+
+}  // namespace
+
+extern "C" {
+
+const char* msr_status_str(msr_status s) {
+  switch (s) {
+    case MSR_OK: return "MSR_OK";
+    case MSR_ERR_NULL: return "MSR_ERR_NULL";
+    case MSR_ERR_SHAPE: return "MSR_ERR_SHAPE";
+    case MSR_ERR_DTYPE: return "MSR_ERR_DTYPE";
+    case MSR_ERR_UNSUPPORTED: return "MSR_ERR_UNSUPPORTED";
+    case MSR_ERR_WORKSPACE: return "MSR_ERR_WORKSPACE";
+    case MSR_ERR_HIP: return "MSR_ERR_HIP";
+  }
+  return "MSR_ERR_UNKNOWN";
+}
+
+const char* msr_last_error(void) { return g_last_error.c_str(); }
+
+size_t msr_chunkwise_workspace_bytes(msr_dtype dtype, msr_dims dims, int32_t chunk, float rope_base) {
+  if (dims.batch < 0 || dims.seqlen < 0 || dims.heads <= 0 || dims.d_k <= 0 || dims.d_v <= 0 || chunk <= 0) return 0;
+  return chunk_ws_layout(dtype, dims, chunk, rope_base > 0.f, true).total;
+}
+
+size_t msr_parallel_workspace_bytes(msr_dtype dtype, msr_dims dims, float rope_base) {
+  if (dims.batch < 0 || dims.seqlen < 0 || dims.heads <= 0 || dims.d_k <= 0 || dims.d_v <= 0) return 0;
+  return chunk_ws_layout(dtype, dims, 0, rope_base > 0.f, false).total;
+}
+
+static msr_status rotate_qk(msr_dtype dtype, const msr_dims& d, float rope_base, int64_t pos0, const void* Q,
+                            const void* K, void* ws, const ChunkWs& w, hipStream_t st, const void** Qo,
+                            const void** Ko) {
+  const Elt e = dtype == MSR_BF16 ? kBF16 : kF32;
+  float2* tab = at<float2>(ws, w.tab);
+  const int64_t ld = (int64_t)d.heads * d.d_k;
+  const int rows = d.batch * d.seqlen;
+  hipError_t err = launch_rope_table(tab, d.seqlen, d.d_k, pos0, rope_base, st);
+  if (err == hipSuccess)
+    err = launch_rope_apply(e, Q, ld, at<void>(ws, w.qr), ld, rows, d.seqlen, d.heads, d.d_k, tab, st);
+  if (err == hipSuccess)
+    err = launch_rope_apply(e, K, ld, at<void>(ws, w.kr), ld, rows, d.seqlen, d.heads, d.d_k, tab, st);
+  *Qo = at<void>(ws, w.qr);
+  *Ko = at<void>(ws, w.kr);
+  return from_hip(err, "rotation");
+}
+
+msr_status msr_parallel_fwd(msr_dtype dtype, msr_dims d, const double* gamma, float rope_base, int64_t pos0,
+                            float qk_scale, const void* Q, const void* K, const void* V, void* O, void* workspace,
+                            size_t ws_bytes, void* stream) {
+  msr_status s;
+  if ((s = check_dtype(dtype))) return s;
+  if ((s = check_heads(d.batch, d.seqlen, d.heads, d.d_k, d.d_v))) return s;
+  if ((s = check_matrix_dims(dtype, d.d_v))) return s;
+  if ((s = check_gamma(gamma, d.heads))) return s;
+  if (pos0 < 0) return fail(MSR_ERR_SHAPE, "pos0 = %lld is negative", (long long)pos0);
+  const size_t tok = (size_t)d.batch * d.seqlen;
+  if (tok == 0) return ok();
+  if (!Q || !K || !V || !O) return fail(MSR_ERR_NULL, "Q, K, V and O must be non-NULL");
+  const bool rope = rope_base > 0.f;
+  const ChunkWs w = chunk_ws_layout(dtype, d, 0, rope, false);
+  if (w.total > 0 && (!workspace || ws_bytes < w.total))
+    return fail(MSR_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", w.total, workspace ? ws_bytes : 0);
+  hipStream_t st = (hipStream_t)stream;
+  if (rope && (s = rotate_qk(dtype, d, rope_base, pos0, Q, K, workspace, w, st, &Q, &K))) return s;
+  ChunkArgs a{};
+  a.elt = dtype == MSR_BF16 ? kBF16 : kF32;
+  a.d_k = d.d_k; a.d_v = d.d_v; a.batch = d.batch; a.seqlen = d.seqlen; a.heads = d.heads;
+  a.Q = Q; a.K = K; a.V = V; a.O = O;
+  a.ldq = a.ldk = (int64_t)d.heads * d.d_k;
+  a.ldv = a.ldo = (int64_t)d.heads * d.d_v;
+  a.scale = qk_scale;
+  const HeadTab tab = make_tab(gamma, d.heads, 0, d.seqlen);
+  return from_hip(launch_parallel(a, tab, st), "msr_parallel_fwd");
+}
+
+msr_status msr_chunkwise_fwd(msr_dtype dtype, msr_dims d, int32_t chunk, const double* gamma, float rope_base,
+                             int64_t pos0, float qk_scale, const void* Q, const void* K, const void* V,
+                             const float* S_in, float* S_out, void* O, void* workspace, size_t ws_bytes,
+                             void* stream) {
+  msr_status s;
+  if ((s = check_dtype(dtype))) return s;
+  if ((s = check_heads(d.batch, d.seqlen, d.heads, d.d_k, d.d_v))) return s;
+  if ((s = check_matrix_dims(dtype, d.d_v))) return s;
+  if ((s = check_chunk(chunk))) return s;
+  if ((s = check_gamma(gamma, d.heads))) return s;
+  if (pos0 < 0) return fail(MSR_ERR_SHAPE, "pos0 = %lld is negative", (long long)pos0);
+  if (S_out && S_out == S_in) return fail(MSR_ERR_SHAPE, "S_out may not alias S_in");
+  hipStream_t st = (hipStream_t)stream;
+  const size_t tok = (size_t)d.batch * d.seqlen;
+  const size_t state_bytes = (size_t)d.batch * d.heads * d.d_k * d.d_v * sizeof(float);
+  if (d.batch == 0) return ok();
+  if (d.seqlen == 0) {  // no tokens: the state passes through unchanged
+    if (!S_out) return ok();
+    hipError_t e = S_in ? hipMemcpyAsync(S_out, S_in, state_bytes, hipMemcpyDeviceToDevice, st)
+                        : hipMemsetAsync(S_out, 0, state_bytes, st);
+    return from_hip(e, "msr_chunkwise_fwd(seqlen=0)");
+  }
+  if (!Q || !K || !V || !O) return fail(MSR_ERR_NULL, "Q, K, V and O must be non-NULL");
+  const bool rope = rope_base > 0.f;
+  const ChunkWs w = chunk_ws_layout(dtype, d, chunk, rope, true);
+  if (!workspace || ws_bytes < w.total)
+    return fail(MSR_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", w.total, workspace ? ws_bytes : 0);
+  (void)tok;
+  if (rope && (s = rotate_qk(dtype, d, rope_base, pos0, Q, K, workspace, w, st, &Q, &K))) return s;
+  ChunkArgs a{};
+  a.elt = dtype == MSR_BF16 ? kBF16 : kF32;
+  a.d_k = d.d_k; a.d_v = d.d_v; a.batch = d.batch; a.seqlen = d.seqlen; a.heads = d.heads;
+  a.chunk = chunk;
+  a.Q = Q; a.K = K; a.V = V; a.O = O;
+  a.ldq = a.ldk = (int64_t)d.heads * d.d_k;
+  a.ldv = a.ldo = (int64_t)d.heads * d.d_v;
+  a.scale = qk_scale;
+  a.S_in = S_in; a.S_out = S_out;
+  a.dR = at<float>(workspace, w.dr);
+  a.Rx = at<void>(workspace, w.rx);
+  const HeadTab tab = make_tab(gamma, d.heads, chunk, d.seqlen);
+  return from_hip(launch_chunkwise(a, tab, st), "msr_chunkwise_fwd");
+}
+
+msr_status msr_recurrent_step(msr_dtype dtype, int32_t batch, int32_t heads, int32_t d_k, int32_t d_v,
+                              const double* gamma, float rope_base, int64_t pos, float qk_scale, const void* q,
+                              const void* k, const void* v, float* S, void* o, void* stream) {
+  msr_status s;
+  if ((s = check_dtype(dtype))) return s;
+  if ((s = check_heads(batch, 1, heads, d_k, d_v))) return s;
+  if ((s = check_gamma(gamma, heads))) return s;
+  if (pos < 0) return fail(MSR_ERR_SHAPE, "pos = %lld is negative", (long long)pos);
+  if (batch == 0) return ok();
+  if (!q || !k || !v || !S || !o) return fail(MSR_ERR_NULL, "q, k, v, S and o must be non-NULL");
+  if ((int64_t)batch * heads > (int64_t)INT32_MAX) return fail(MSR_ERR_UNSUPPORTED, "batch*heads too large");
+  const HeadTab tab = make_tab(gamma, heads, 1, 1);
+  return from_hip(launch_recurrent_step(dtype == MSR_BF16 ? kBF16 : kF32, d_k, d_v, batch, heads, q, k, v, S, o,
+                                        qk_scale, pos, rope_base, tab, (hipStream_t)stream),
+                  "msr_recurrent_step");
+}
+
+
+size_t msr_layer_workspace_bytes(msr_dtype dtype, int32_t batch, int32_t seqlen, int32_t d_model, int32_t heads,
+                                 int32_t d_k, int32_t d_v, int32_t chunk) {
+  if (batch < 0 || seqlen < 0 || d_model <= 0 || heads <= 0 || d_k <= 0 || d_v <= 0 || chunk <= 0) return 0;
+  return layer_ws_layout(dtype, batch, seqlen, d_model, heads, d_k, d_v, chunk).total;
+}
+
+msr_status msr_layer_fwd(msr_dtype dtype, int32_t batch, int32_t seqlen, int32_t d_model, int32_t heads, int32_t d_k,
+                         int32_t d_v, int32_t chunk, const double* gamma, float rope_base, float gn_eps,
+                         const void* X, const void* W_Q, const void* W_K, const void* W_V, const void* W_G,
+                         const void* W_O, void* out, void* workspace, size_t ws_bytes, void* stream) {
+  msr_status s;
+  if ((s = check_dtype(dtype))) return s;
+  if ((s = check_heads(batch, seqlen, heads, d_k, d_v))) return s;
+  if ((s = check_matrix_dims(dtype, d_v))) return s;
+  if ((s = check_chunk(chunk))) return s;
+  if ((s = check_gamma(gamma, heads))) return s;
+  if (d_model <= 0) return fail(MSR_ERR_SHAPE, "d_model = %d must be positive", d_model);
+  if (d_model % 64) return fail(MSR_ERR_UNSUPPORTED, "d_model = %d is not a multiple of 64", d_model);
+  if (!(gn_eps >= 0.f)) return fail(MSR_ERR_SHAPE, "gn_eps must be >= 0");
+  const int64_t M = (int64_t)batch * seqlen;
+  if (M == 0) return ok();
+  if (!X || !W_Q || !W_K || !W_V || !W_G || !W_O || !out)
+    return fail(MSR_ERR_NULL, "X, W_Q, W_K, W_V, W_G, W_O and out must be non-NULL");
+  const LayerWs w = layer_ws_layout(dtype, batch, seqlen, d_model, heads, d_k, d_v, chunk);
+  if (!workspace || ws_bytes < w.total)
+    return fail(MSR_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", w.total, workspace ? ws_bytes : 0);
+  hipStream_t st = (hipStream_t)stream;
+  const Elt e = dtype == MSR_BF16 ? kBF16 : kF32;
+  const size_t es = elt_size(dtype);
+  const int hk = heads * d_k, hv = heads * d_v;
+  const int ntot = 2 * hk + 2 * hv;
+  char* wt = at<char>(workspace, w.wt);
+  char* wto = at<char>(workspace, w.wto);
+  char* qkvg = at<char>(workspace, w.qkvg);
+  char* z = at<char>(workspace, w.z);
+  void* cws = at<void>(workspace, w.chunk);
+
+  // 1. weights into K-contiguous layout: rows [Q | K | V | G] of W^T
+  hipError_t err = launch_transpose(e, W_Q, hk, wt, d_model, d_model, hk, st);
+  if (err == hipSuccess) err = launch_transpose(e, W_K, hk, wt + (size_t)hk * d_model * es, d_model, d_model, hk, st);
+  if (err == hipSuccess)
+    err = launch_transpose(e, W_V, hv, wt + (size_t)2 * hk * d_model * es, d_model, d_model, hv, st);
+  if (err == hipSuccess)
+    err = launch_transpose(e, W_G, hv, wt + (size_t)(2 * hk + hv) * d_model * es, d_model, d_model, hv, st);
+  if (err == hipSuccess) err = launch_transpose(e, W_O, d_model, wto, hv, hv, d_model, st);
+  // 2. [Q^ | K^ | V | G] = X W
+  if (err == hipSuccess) err = launch_gemm_nt(e, X, d_model, wt, d_model, qkvg, ntot, (int)M, ntot, d_model, st);
+  if (err != hipSuccess) return from_hip(err, "msr_layer_fwd(projections)");
+  // 3. rotation of Q^ and K^ in place
+  msr_dims d{batch, seqlen, heads, d_k, d_v};
+  float2* tab = at<float2>(cws, w.cw.tab);
+  if (rope_base > 0.f) {
+    err = launch_rope_table(tab, seqlen, d_k, 0, rope_base, st);
+    if (err == hipSuccess) err = launch_rope_apply(e, qkvg, ntot, qkvg, ntot, (int)M, seqlen, heads, d_k, tab, st);
+    if (err == hipSuccess)
+      err = launch_rope_apply(e, qkvg + (size_t)hk * es, ntot, qkvg + (size_t)hk * es, ntot, (int)M, seqlen, heads,
+                              d_k, tab, st);
+    if (err != hipSuccess) return from_hip(err, "msr_layer_fwd(rotation)");
+  }
+  // 4. chunkwise retention + per-head GroupNorm + swish gate -> Z
+  ChunkArgs a{};
+  a.elt = e;
+  a.d_k = d_k; a.d_v = d_v; a.batch = batch; a.seqlen = seqlen; a.heads = heads;
+  a.chunk = chunk;
+  a.Q = qkvg; a.ldq = ntot;
+  a.K = qkvg + (size_t)hk * es; a.ldk = ntot;
+  a.V = qkvg + (size_t)2 * hk * es; a.ldv = ntot;
+  a.G = qkvg + (size_t)(2 * hk + hv) * es; a.ldg = ntot;
+  a.O = z; a.ldo = hv;
+  a.scale = 1.0f / std::sqrt((float)d_k);
+  a.eps = gn_eps;
+  a.fuse_gn_gate = true;
+  a.dR = at<float>(cws, w.cw.dr);
+  a.Rx = at<void>(cws, w.cw.rx);
+  const HeadTab htab = make_tab(gamma, heads, chunk, seqlen);
+  err = launch_chunkwise(a, htab, st);
+  if (err != hipSuccess) return from_hip(err, "msr_layer_fwd(retention)");
+  // 5. out = Z W_O
+  err = launch_gemm_nt(e, z, hv, wto, hv, out, d_model, (int)M, d_model, hv, st);
+  return from_hip(err, "msr_layer_fwd(output projection)");
+}
+
+}  // extern "C"

@@ -1,0 +1,76 @@
+// Host-side launchers of the libmsr kernels (internal; the public ABI is
+// include/msr.h).  Every launcher only enqueues on `stream`.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "msr_device.h"
+
+namespace msr {
+
+enum Elt { kF32 = 0, kBF16 = 1 };
+
+// Brackets one kernel launch with HIP events on its stream while tracing is
+// enabled (msr_trace_enable); a no-op otherwise.
+class TraceScope {
+ public:
+  TraceScope(const char* name, hipStream_t stream);
+  ~TraceScope();
+  TraceScope(const TraceScope&) = delete;
+  TraceScope& operator=(const TraceScope&) = delete;
+
+ private:
+  const char* name_;
+  hipStream_t stream_;
+  hipEvent_t start_{}, stop_{};
+  bool active_ = false;
+};
+
+struct ChunkArgs {
+  Elt elt;
+  int d_k, d_v;
+  int batch, seqlen, heads;
+  int chunk;                 // tokens per chunk (multiple of 32)
+  const void* Q; int64_t ldq;   // token stride in elements
+  const void* K; int64_t ldk;
+  const void* V; int64_t ldv;
+  void* O; int64_t ldo;
+  const void* G; int64_t ldg;   // gate (only with fused GroupNorm + gate)
+  float scale, eps;
+  bool fuse_gn_gate;
+  const float* S_in; float* S_out;
+  float* dR;                 // [B, H, NC, d_v, d_k] float32
+  void* Rx;                  // [B, H, NC, d_v, d_k] elt (may alias dR for f32)
+};
+
+// Chunkwise retention: state contributions, fp32 scan, outputs.
+hipError_t launch_chunkwise(const ChunkArgs& a, const HeadTab& tab, hipStream_t stream);
+// Parallel form: one "chunk" spanning the whole sequence, no state.
+hipError_t launch_parallel(const ChunkArgs& a, const HeadTab& tab, hipStream_t stream);
+
+// One decode step: S <- gamma S + k^T v; o = scale q S (q, k rotated at pos).
+hipError_t launch_recurrent_step(Elt elt, int d_k, int d_v, int batch, int heads,
+                                 const void* q, const void* k, const void* v, float* S,
+                                 void* o, float scale, int64_t pos, float rope_base,
+                                 const HeadTab& tab, hipStream_t stream);
+
+// cos/sin table: tab[n * (d/2) + j] = (cos, sin)((pos0 + n) * theta_j),
+// theta_j = base^(-2j/d), n = 0..npos-1.
+hipError_t launch_rope_table(float2* tab, int npos, int d, int64_t pos0, float base,
+                             hipStream_t stream);
+// Rotate the first d columns of every head of a [rows, heads * d] block
+// (rows = batch * seqlen tokens, token n = row % seqlen) from src to dst
+// (dst may equal src).  Strides in elements.
+hipError_t launch_rope_apply(Elt elt, const void* src, int64_t lds, void* dst, int64_t ldd,
+                             int rows, int seqlen, int heads, int d, const float2* tab,
+                             hipStream_t stream);
+
+// C[M, N] = A[M, K] * Bt[N, K]^T (both operands K-contiguous), fp32
+// accumulation, C in elt.  K must be a multiple of 64.
+hipError_t launch_gemm_nt(Elt elt, const void* A, int64_t lda, const void* Bt, int64_t ldb,
+                          void* C, int64_t ldc, int M, int N, int K, hipStream_t stream);
+// dst[c, r] = src[r, c] for a rows x cols block.
+hipError_t launch_transpose(Elt elt, const void* src, int64_t lds, void* dst, int64_t ldd,
+                            int rows, int cols, hipStream_t stream);
+
+}  // namespace msr

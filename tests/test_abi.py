@@ -1,0 +1,137 @@
+"""The C ABI library loads, exports what include/msr.h declares, and rejects
+bad arguments with status codes before launching anything (CPU only: every
+call here fails validation, so no GPU is touched)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import linear_recurrence_sequence_amd as msr
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "msr.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(msr.library_path()),
+                                reason="libmsr.so not built (python -m linear_recurrence_sequence_amd.build)")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(msr_[a-z_]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert declared_functions() == sorted(msr.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported():
+    L = ctypes.CDLL(msr.library_path())
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_status_strings():
+    names = [msr.msr_status_str(i) for i in range(7)]
+    assert names == ["MSR_OK", "MSR_ERR_NULL", "MSR_ERR_SHAPE", "MSR_ERR_DTYPE", "MSR_ERR_UNSUPPORTED",
+                     "MSR_ERR_WORKSPACE", "MSR_ERR_HIP"]
+
+
+def _gamma(n):
+    g = np.full(n, 0.9)
+    return g, g.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+FAKE = 0x1000  # never dereferenced: every call below fails validation first
+
+
+def _chunkwise(dtype=0, dims=(1, 64, 2, 64, 64), chunk=32, gamma=True, ws=(FAKE, 1 << 40), Q=FAKE,
+               S_in=None, S_out=None, gam=None):
+    L = msr.lib()
+    g, gp = _gamma(dims[2]) if gam is None else gam
+    return L.msr_chunkwise_fwd(dtype, msr.MsrDims(*dims), chunk, gp if gamma else None, 10000.0, 0, 1.0, Q, FAKE,
+                               FAKE, S_in, S_out, FAKE, ws[0], ws[1], None)
+
+
+def test_chunkwise_validation():
+    assert _chunkwise(dtype=7) == 3                               # dtype
+    assert _chunkwise(dims=(1, 64, 2, 64, 96)) == 4               # unsupported head dims
+    assert _chunkwise(dims=(1, 64, 2, 48, 48)) == 4
+    assert _chunkwise(dims=(-1, 64, 2, 64, 64)) == 2              # negative size
+    assert _chunkwise(dims=(1, 64, 0, 64, 64)) == 2               # no heads
+    assert _chunkwise(dims=(1, 64, 129, 64, 64)) == 4             # too many heads
+    assert _chunkwise(chunk=0) == 2
+    assert _chunkwise(chunk=48) == 4                              # not a multiple of 32
+    assert _chunkwise(gamma=False) == 1                           # gamma NULL
+    assert _chunkwise(Q=None) == 1
+    assert _chunkwise(ws=(None, 0)) == 5                          # workspace missing
+    assert _chunkwise(ws=(FAKE, 16)) == 5                         # workspace too small
+    assert _chunkwise(S_in=FAKE, S_out=FAKE) == 2                 # S_out aliases S_in
+    g = np.array([0.5, 1.5])
+    assert _chunkwise(gam=(g, g.ctypes.data_as(ctypes.POINTER(ctypes.c_double)))) == 2   # gamma > 1
+    g = np.array([0.5, np.nan])
+    assert _chunkwise(gam=(g, g.ctypes.data_as(ctypes.POINTER(ctypes.c_double)))) == 2
+    assert "multiple of 32" in _last(lambda: _chunkwise(chunk=40))
+
+
+def _last(fn):
+    fn()
+    return msr.msr_last_error()
+
+
+def test_other_entry_points_validation():
+    L = msr.lib()
+    g, gp = _gamma(4)
+    d = msr.MsrDims(1, 16, 4, 64, 64)
+    assert L.msr_parallel_fwd(0, d, gp, 0.0, -1, 1.0, FAKE, FAKE, FAKE, FAKE, None, 0, None) == 2      # pos0 < 0
+    assert L.msr_parallel_fwd(0, d, gp, 0.0, 0, 1.0, None, FAKE, FAKE, FAKE, None, 0, None) == 1
+    assert L.msr_parallel_fwd(0, d, gp, 100.0, 0, 1.0, FAKE, FAKE, FAKE, FAKE, None, 0, None) == 5     # rotation needs ws
+    assert L.msr_recurrent_step(0, 2, 4, 64, 64, gp, 0.0, 0, 1.0, FAKE, FAKE, FAKE, None, FAKE, None) == 1
+    assert L.msr_recurrent_step(0, 2, 4, 32, 32, gp, 0.0, 0, 1.0, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 4
+    assert L.msr_recurrent_step(0, 2, 4, 64, 64, gp, 0.0, -3, 1.0, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 2
+    lay = lambda dm, chunk=64, ws=1 << 40, eps=1e-5: L.msr_layer_fwd(
+        1, 1, 128, dm, 4, 64, 64, chunk, gp, 10000.0, eps, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, None)
+    assert lay(100) == 4                    # d_model not a multiple of 64
+    assert lay(256, chunk=-32) == 2
+    assert lay(256, ws=10) == 5
+    assert lay(256, eps=-1.0) == 2
+
+
+def test_empty_inputs_are_no_ops():
+    """batch = 0 or seqlen = 0 (parallel / layer) returns OK without touching memory."""
+    L = msr.lib()
+    g, gp = _gamma(2)
+    assert L.msr_parallel_fwd(0, msr.MsrDims(0, 16, 2, 64, 64), gp, 0.0, 0, 1.0, None, None, None, None, None, 0,
+                              None) == 0
+    assert L.msr_parallel_fwd(1, msr.MsrDims(3, 0, 2, 64, 64), gp, 0.0, 0, 1.0, None, None, None, None, None, 0,
+                              None) == 0
+    assert L.msr_chunkwise_fwd(0, msr.MsrDims(0, 16, 2, 64, 64), 32, gp, 0.0, 0, 1.0, None, None, None, None, None,
+                               None, None, 0, None) == 0
+    assert L.msr_recurrent_step(0, 0, 2, 64, 64, gp, 0.0, 0, 1.0, None, None, None, None, None, None) == 0
+    assert L.msr_layer_fwd(1, 2, 0, 256, 2, 64, 64, 32, gp, 1.0, 1e-5, None, None, None, None, None, None, None, None,
+                           0, None) == 0
+    assert msr.msr_last_error() == ""
+
+
+def test_workspace_sizes():
+    # chunkwise, bf16: dR float32 + R_excl bf16, each [B, H, NC, dk, dv]; rotation adds Q, K copies and a table
+    B, N, H, dk, dv, C = 2, 1000, 3, 128, 128, 256
+    nc = -(-N // C)
+    st = B * H * nc * dk * dv
+    up = lambda x: -(-x // 256) * 256
+    assert msr.msr_chunkwise_workspace_bytes(1, B, N, H, dk, dv, C, 0.0) == up(st * 4) + up(st * 2)
+    assert msr.msr_chunkwise_workspace_bytes(0, B, N, H, dk, dv, C, 0.0) == up(st * 4)   # f32: in place
+    rot = 2 * up(B * N * H * dk * 2) + up(N * dk // 2 * 8)
+    assert msr.msr_chunkwise_workspace_bytes(1, B, N, H, dk, dv, C, 1e4) == rot + up(st * 4) + up(st * 2)
+    assert msr.msr_parallel_workspace_bytes(1, B, N, H, dk, dv, 0.0) == 0
+    assert msr.msr_layer_workspace_bytes(1, 2, 64, 256, 2, 64, 64, 32) > 0
+    assert msr.msr_layer_workspace_bytes(1, 2, 64, 256, 2, 64, 64, 0) == 0
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(msr, "_lib", None)
+    monkeypatch.setattr(msr, "library_path", lambda: str(tmp_path / "missing.so"))
+    with pytest.raises(msr.MsrLibraryMissing):
+        msr.lib()
