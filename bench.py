@@ -134,14 +134,14 @@ def bench_layer(w, steps, warmup, device_inputs=False):
     B, N, H, dk, dv, C = w.batch, w.seqlen, w.heads, w.d_k, w.d_v, w.chunk
     nc = -(-N // C)
     es = 2
-    kern = {
-        "k_gemm_nt": roof("k_gemm_nt", proj, "mfma", tr, steps),
-        "k_chunk_out": roof("k_chunk_out", B * N * H * (C * (dk + dv) + 2 * dk * dv), "mfma", tr, steps),
-        "k_chunk_state": roof("k_chunk_state", B * N * H * 2 * dk * dv, "mfma", tr, steps),
-        "k_chunk_scan": roof("k_chunk_scan", B * H * nc * dk * dv * (4 + es), "hbm", tr, steps),
-        "k_rope_apply": roof("k_rope_apply", 2 * 2 * B * N * H * dk * es, "hbm", tr, steps),
-        "k_transpose": roof("k_transpose", 2 * es * w.d_model * (2 * H * dk + 3 * H * dv), "hbm", tr, steps),
+    work = {  # algorithmic work per step: flops (mfma) or bytes (hbm)
+        "k_gemm": (proj, "mfma"),
+        "k_chunk_out": (B * N * H * (C * (dk + dv) + 2 * dk * dv), "mfma"),
+        "k_chunk_state": (B * N * H * 2 * dk * dv, "mfma"),
+        "k_chunk_scan": (B * H * nc * dk * dv * (4 + es), "hbm"),
+        "k_rope_table": (N * dk // 2 * 8, "hbm"),
     }
+    kern = {n: roof(n, wk, bd, tr, steps) for n, (wk, bd) in work.items() if n in tr}
     del X, WQ, WK, WV, WG, WO, out, ws
     torch.cuda.empty_cache()
     res = {"s_per_step": t, "tokens_per_s": B * N / t, "flops_per_step": proj + core,

@@ -12,10 +12,10 @@
 //
 // Three kernels per call:
 //   k_chunk_state : dR_i^T = (V_[i] (.) zeta)^T K_[i]   (matrix cores, one
-//                   workgroup per (batch, head, chunk, 128x128 state tile))
+//                   workgroup per (batch, head, chunk, state tile))
 //   k_chunk_scan  : R_i = gamma^L R_{i-1} + dR_i in float32, writing the
 //                   exclusive prefix R_{i-1} per chunk (as the input type)
-//   k_chunk_out   : per 128-row tile: Q R_{i-1} (.) xi, then the causal,
+//   k_chunk_out   : per row tile: Q R_{i-1} (.) xi, then the causal,
 //                   decay-weighted intra-chunk product, then either O or the
 //                   fused per-head GroupNorm + swish gate.
 // States are stored transposed, [d_v][d_k] (d_k contiguous), because that is
@@ -28,17 +28,33 @@ template <class T> constexpr int pad16() { return 16 / (int)sizeof(T); }
 
 // ---------------------------------------------------------------------------
 // k_chunk_state
+// One workgroup per (batch, head, chunk, TS x TS state tile), 4 waves of
+// (TS/2) x (TS/2).  K and zeta-weighted V are staged row-major ([key][col],
+// one key per row, plain 16-byte copies) and read as fragments with the
+// transposing LDS read.  The kernel is bound by reading K and V and writing
+// dR, so it keeps LDS small (about 40 KiB) for three workgroups per CU
+// rather than double-buffering.
 // ---------------------------------------------------------------------------
+template <class T, int DK, int DV>
+struct StateCfg {
+  static constexpr int TS = (DK >= 128 && DV >= 128) ? 128 : 64;  // state tile edge
+  static constexpr int WT = TS / 64;                              // 32x32 tiles per wave per dim
+  static constexpr int KB = sizeof(T) == 2 ? 64 : 32;             // keys per stage
+  static constexpr int LDT = TS + rm_pad<T>();
+  static constexpr int UNITS = KB * (TS / 8);                     // 8-element rows per operand
+  static constexpr int UPT = (UNITS + 255) / 256;
+  static constexpr int STAGE = 2 * KB * LDT;                      // elements (V then K)
+};
+
 template <class T, int DK, int DV>
 __global__ __launch_bounds__(256) void k_chunk_state(const T* __restrict__ K, const T* __restrict__ V,
                                                      int64_t ldk, int64_t ldv, float* __restrict__ dR,
                                                      int N, int H, int chunk, int NC, HeadTab tab) {
-  constexpr int TS = (DK >= 128 && DV >= 128) ? 128 : 64;  // state tile edge
-  constexpr int WT = TS / 64;                              // 32x32 tiles per wave per dim
-  constexpr int KB = 64;                                   // keys per stage
-  constexpr int LDT = KB + pad16<T>();
-  __shared__ __attribute__((aligned(16))) T sV[TS * LDT];  // (V (.) zeta)^T : [dv][key]
-  __shared__ __attribute__((aligned(16))) T sK[TS * LDT];  // K^T           : [dk][key]
+  using C = StateCfg<T, DK, DV>;
+  constexpr int TS = C::TS, WT = C::WT, KB = C::KB, LDT = C::LDT, UNITS = C::UNITS, UPT = C::UPT;
+  __shared__ __attribute__((aligned(16))) T smem[C::STAGE];
+  T* sV = smem;
+  T* sK = smem + KB * LDT;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 31, hh = lane >> 5;
   const int ci = blockIdx.x % NC;
@@ -52,6 +68,8 @@ __global__ __launch_bounds__(256) void k_chunk_state(const T* __restrict__ K, co
   const int wr = (wave >> 1) * 32 * WT;
   const int wc = (wave & 1) * 32 * WT;
   const size_t tok0 = (size_t)b * N + c0;
+  const T* Kb = K + (size_t)h * DK + tk * TS;
+  const T* Vb = V + (size_t)h * DV + tv * TS;
 
   f32x16 acc[WT][WT];
 #pragma unroll
@@ -59,32 +77,30 @@ __global__ __launch_bounds__(256) void k_chunk_state(const T* __restrict__ K, co
 #pragma unroll
     for (int j = 0; j < WT; ++j) acc[i][j] = (f32x16){};
 
-  constexpr int CG = TS / 8;                  // 8-column groups per row
-  constexpr int UNITS = (KB / 4) * CG;        // 4-key x 8-column units
   for (int kb = 0; kb < L; kb += KB) {
-    for (int u = tid; u < UNITS; u += 256) {
-      const int kg = u / CG, cg = u % CG;
-      Row8<T> rk[4], rv[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = kb + 4 * kg + i;
-        const bool ok = key < L;
-        const size_t tok = tok0 + (ok ? key : 0);
-        load_row8(rk[i], K + tok * ldk + (size_t)h * DK + tk * TS + 8 * cg, ok);
-        load_row8(rv[i], V + tok * ldv + (size_t)h * DV + tv * TS + 8 * cg, ok);
-        if (ok) scale_row8(rv[i], gpow(L - 1 - key, lg2));
+    for (int q = 0; q < UPT; ++q) {
+      const int u = tid + 256 * q;
+      const int key = u / (TS / 8), c8 = u % (TS / 8);
+      if (u < UNITS) {
+        const bool ok = kb + key < L;
+        const size_t tok = tok0 + (ok ? kb + key : 0);
+        Row8<T> rk, rv;
+        load_row8(rk, Kb + tok * ldk + 8 * c8, ok);
+        load_row8(rv, Vb + tok * ldv + 8 * c8, ok);
+        if (ok) scale_row8(rv, gpow(L - 1 - (kb + key), lg2));
+        store_row8(sK + key * LDT + 8 * c8, rk);
+        store_row8(sV + key * LDT + 8 * c8, rv);
       }
-      store_transposed4x8(sK + (8 * cg) * LDT + 4 * kg, LDT, rk);
-      store_transposed4x8(sV + (8 * cg) * LDT + 4 * kg, LDT, rv);
     }
     __syncthreads();
 #pragma unroll
     for (int s = 0; s < KB / 16; ++s) {
       Frag<T> a[WT], bb[WT];
 #pragma unroll
-      for (int i = 0; i < WT; ++i) a[i] = load_frag(sV + (wr + 32 * i + lr) * LDT + 16 * s + 8 * hh);
+      for (int i = 0; i < WT; ++i) a[i] = load_frag_rm<KMAP_CONTIG>(sV + 16 * s * LDT + wr + 32 * i, LDT);
 #pragma unroll
-      for (int j = 0; j < WT; ++j) bb[j] = load_frag(sK + (wc + 32 * j + lr) * LDT + 16 * s + 8 * hh);
+      for (int j = 0; j < WT; ++j) bb[j] = load_frag_rm<KMAP_CONTIG>(sK + 16 * s * LDT + wc + 32 * j, LDT);
 #pragma unroll
       for (int i = 0; i < WT; ++i)
 #pragma unroll
@@ -186,33 +202,47 @@ __global__ __launch_bounds__(256) void k_chunk_scan(const float* dR, T* Rx, cons
 
 // ---------------------------------------------------------------------------
 // k_chunk_out
+// One workgroup per (batch, head, chunk, row tile of 32*NW query rows); each
+// wave owns 32 query rows and the full d_v width of their outputs (the
+// accumulators), and keeps its Q rows in registers as matrix-core fragments.
+// Stages, in order: the d_k slabs of R_{i-1} (Q R), then the key blocks of
+// the chunk up to the tile's last row (causal, decay-weighted Q K^T, then
+// P V).  bf16 with 4 waves runs them as a two-stage pipeline: the next
+// stage's global loads are in flight in registers while the matrix cores
+// work on the current stage in LDS, then land in the other LDS buffer.
 // ---------------------------------------------------------------------------
-template <class T, int DK, int DV>
-struct OutSmem {
-  // Q stays in registers unless the accumulators of a 512-wide row need them.
-  static constexpr bool QREG = DV <= 256;
-  static constexpr int KB = 32;                       // keys per stage
-  static constexpr int LDK = DK + pad16<T>();
-  static constexpr int LDV = KB + pad16<T>();
-  static constexpr int SK = sizeof(T) == 2 ? 64 : 32;  // d_k rows of R per stage
-  static constexpr int LDR = SK + pad16<T>();
-  static constexpr int intra = (KB * LDK + DV * LDV) * (int)sizeof(T);
-  static constexpr int inter = DV * LDR * (int)sizeof(T);
-  static constexpr int qtile = QREG ? 0 : 128 * LDK * (int)sizeof(T);
-  static constexpr int bytes = (intra > inter ? intra : inter) + qtile;
+template <class T, int DK, int DV, int NW>
+struct OutCfg {
+  static constexpr int NT = 64 * NW;                               // threads
+  static constexpr bool PIPE = sizeof(T) == 2 && NW == 4;
+  static constexpr int KB = (sizeof(T) == 4 || DV > 256) ? 32 : 64; // keys per stage
+  static constexpr int SK = KB;                                    // d_k rows of R per stage
+  static constexpr int PAD = pad16<T>();
+  static constexpr int LDK = DK + PAD;                             // K block: [key][dk]
+  static constexpr int LDV = DV + rm_pad<T>();                     // V block: [key][dv]
+  static constexpr int LDR = SK + PAD;                             // R^T slab: [dv][dk]
+  static constexpr int KV = KB * LDK + KB * LDV;
+  static constexpr int RS = DV * LDR;
+  static constexpr int STAGE = KV > RS ? KV : RS;                  // elements per stage
+  static constexpr int NBUF = PIPE ? 2 : 1;
+  static constexpr int NR = DK / SK;                               // R slabs
+  // register staging (Row8 units per thread)
+  static constexpr int KU = (KB * (DK / 8) + NT - 1) / NT;         // K rows
+  static constexpr int VU = (KB * (DV / 8) + NT - 1) / NT;         // V rows
+  static constexpr int RU = (DV * (SK / 8) + NT - 1) / NT;         // R slab rows
+  static constexpr int PRE = (KU + VU) > RU ? (KU + VU) : RU;
 };
 
-template <class T, int DK, int DV, bool STATE, bool GN>
-__global__ __launch_bounds__(256) void k_chunk_out(
+template <class T, int DK, int DV, int NW, bool STATE, bool GN>
+__global__ __launch_bounds__(64 * NW) void k_chunk_out(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, int64_t ldq, int64_t ldk,
-    int64_t ldv, const T* __restrict__ Rx, const T* __restrict__ G, int64_t ldg, T* __restrict__ O,
-    int64_t ldo, int BH, int N, int H, int chunk, int NC, int TPC, int RT, float scale, float eps,
-    HeadTab tab) {
-  using SM = OutSmem<T, DK, DV>;
-  constexpr int KB = SM::KB, LDK = SM::LDK, LDV = SM::LDV, SK = SM::SK, LDR = SM::LDR;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[SM::bytes];
+    int64_t ldv, const T* __restrict__ Rx, int has_sin, const T* __restrict__ G, int64_t ldg, T* __restrict__ O,
+    int64_t ldo, int BH, int N, int H, int chunk, int NC, int TPC, float scale, float eps, HeadTab tab) {
+  using C = OutCfg<T, DK, DV, NW>;
+  constexpr int NT = C::NT, KB = C::KB, SK = C::SK, LDK = C::LDK, LDV = C::LDV, LDR = C::LDR;
+  constexpr int RT = 32 * NW;
+  __shared__ __attribute__((aligned(16))) T smem[C::NBUF * C::STAGE];
 
-  const int nthr = blockDim.x;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 31, hh = lane >> 5;
   // Heavy row tiles (late in their chunk) are scheduled first.
   const int per = NC * BH;
@@ -227,76 +257,97 @@ __global__ __launch_bounds__(256) void k_chunk_out(
   const float lg2 = tab.lg2[h];
   const size_t tokb = (size_t)b * N;
 
-  // This wave's 32 query rows as matrix-core fragments: element t of lane
-  // half hh of fragment s is column 16 s + 8 hh + t of query row q0 + lr.
-  // The same registers serve as the B operand of K Q^T and as the A operand
-  // of Q R.  For 512-wide value heads they live in LDS instead.
-  constexpr bool QREG = SM::QREG;
-  Frag<T> qf[QREG ? DK / 16 : 1];
-  T* sQ = reinterpret_cast<T*>(smem + (SM::bytes - SM::qtile)) + (32 * wave) * LDK;
+  // Query rows as fragments: element t of lane half hh of fragment s is
+  // column 16 s + 8 hh + t of query row q0 + lr.  They are the B operand of
+  // K Q^T and (times xs) the A operand of Q R.
+  Frag<T> qf[DK / 16];
   {
     const int q = q0 + lr;
     const bool ok = q < N;
     const T* p = Q + (tokb + (ok ? q : 0)) * ldq + (size_t)h * DK + 8 * hh;
-    if constexpr (QREG) {
 #pragma unroll
-      for (int s = 0; s < DK / 16; ++s) qf[s] = ok ? load_frag(p + 16 * s) : zero_frag<T>();
-    } else {
-#pragma unroll
-      for (int s = 0; s < DK / 16; ++s) {
-        Row8<T> r;
-        load_row8(r, p + 16 * s, ok);
-        store_row8(sQ + lr * LDK + 16 * s + 8 * hh, r);
-      }
-    }
+    for (int s = 0; s < DK / 16; ++s) qf[s] = ok ? load_frag(p + 16 * s) : zero_frag<T>();
   }
-  auto qfrag = [&](int s) -> Frag<T> {
-    if constexpr (QREG) return qf[s];
-    else return load_frag(sQ + lr * LDK + 16 * s + 8 * hh);
-  };
-
   f32x16 acc[DV / 32];
 #pragma unroll
   for (int j = 0; j < DV / 32; ++j) acc[j] = (f32x16){};
 
-  if constexpr (STATE) {
-    // acc = (xs (.) Q) R_{i-1}, xs_t = scale * xi_t for row t inside the
-    // chunk.  In the A-operand layout a lane holds one query row (lr), so the
-    // row factor is one scalar per lane folded into the Q fragment.
-    // R_{i-1} is stored [dv][dk].
-    const float xs = scale * gpow(q0 - c0 + lr + 1, lg2);
-    T* sR = reinterpret_cast<T*>(smem);
-    const T* Rt = Rx + ((size_t)bh * NC + ci) * DV * DK;
-    if constexpr (!QREG) __syncthreads();  // Q tile visible (rows are per wave, but be safe)
+  // ---- staging ----
+  Row8<T> pre[C::PRE];
+  const T* Rt = STATE ? Rx + ((size_t)bh * NC + ci) * DV * DK : nullptr;
+  const T* Kh = K + (size_t)h * DK;
+  const T* Vh = V + (size_t)h * DV;
+  auto load_R = [&](int k0) {
 #pragma unroll
-    for (int k0 = 0; k0 < DK; k0 += SK) {
-      for (int u = tid; u < DV * SK / 8; u += nthr) {
-        const int row = u / (SK / 8), c8 = u % (SK / 8);
-        Row8<T> r;
-        load_row8(r, Rt + (size_t)row * DK + k0 + 8 * c8, true);
-        store_row8(sR + row * LDR + 8 * c8, r);
-      }
-      __syncthreads();
-#pragma unroll
-      for (int s = 0; s < SK / 16; ++s) {
-        Frag<T> qa = qfrag(k0 / 16 + s);
-#pragma unroll
-        for (int t = 0; t < 8; ++t) qa.v[t] = (T)((float)qa.v[t] * xs);
-#pragma unroll
-        for (int j = 0; j < DV / 32; ++j) {
-          Frag<T> bfr = load_frag(sR + (32 * j + lr) * LDR + 16 * s + 8 * hh);
-          mma16(acc[j], qa, bfr);
-        }
-      }
-      __syncthreads();
+    for (int u = 0; u < C::RU; ++u) {
+      const int idx = tid + NT * u;
+      const int row = idx / (SK / 8), c8 = idx % (SK / 8);
+      load_row8(pre[u], Rt + (size_t)row * DK + k0 + 8 * c8, idx < DV * (SK / 8));
     }
-  }
+  };
+  auto store_R = [&](T* sR) {
+#pragma unroll
+    for (int u = 0; u < C::RU; ++u) {
+      const int idx = tid + NT * u;
+      if (idx >= DV * (SK / 8)) break;
+      const int row = idx / (SK / 8), c8 = idx % (SK / 8);
+      store_row8(sR + row * LDR + 8 * c8, pre[u]);
+    }
+  };
+  auto load_KV = [&](int kb) {
+#pragma unroll
+    for (int u = 0; u < C::KU; ++u) {
+      const int idx = tid + NT * u;
+      const int row = idx / (DK / 8), c8 = idx % (DK / 8);
+      const int key = kb + row;
+      const bool ok = idx < KB * (DK / 8) && key < N;
+      load_row8(pre[u], Kh + (tokb + (ok ? key : 0)) * ldk + 8 * c8, ok);
+    }
+#pragma unroll
+    for (int u = 0; u < C::VU; ++u) {
+      const int idx = tid + NT * u;
+      const int row = idx / (DV / 8), c8 = idx % (DV / 8);
+      const int key = kb + row;
+      const bool ok = idx < KB * (DV / 8) && key < N;
+      load_row8(pre[C::KU + u], Vh + (tokb + (ok ? key : 0)) * ldv + 8 * c8, ok);
+    }
+  };
+  auto store_KV = [&](T* sK) {
+    T* sV = sK + KB * LDK;
+#pragma unroll
+    for (int u = 0; u < C::KU; ++u) {
+      const int idx = tid + NT * u;
+      if (idx >= KB * (DK / 8)) break;
+      const int row = idx / (DK / 8), c8 = idx % (DK / 8);
+      store_row8(sK + row * LDK + 8 * c8, pre[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < C::VU; ++u) {
+      const int idx = tid + NT * u;
+      if (idx >= KB * (DV / 8)) break;
+      const int row = idx / (DV / 8), c8 = idx % (DV / 8);
+      store_row8(sV + row * LDV + 8 * c8, pre[C::KU + u]);
+    }
+  };
+  auto buf = [&](int i) { return smem + (C::PIPE ? (i & 1) : 0) * C::STAGE; };
 
-  // Decay factors of a 32x32 score tile (lane lr = query offset, register r
-  // = key offset kk = 8 (r/4) + 4 hh + r%4):
-  //   diagonal tile:  dd[r] = scale * gamma^(lr - kk) for lr >= kk, else 0;
-  //   tile kb < q0 :  scale * gamma^(q0-kb-31) * ab[r],
-  //                   ab[r] = gamma^lr * gamma^(31 - kk)   (all exponents >= 0).
+  // ---- compute ----
+  // rows scaled by xs = scale * xi_t = scale * gamma^(t+1), t = row inside the chunk
+  const float xs = scale * gpow(q0 - c0 + lr + 1, lg2);
+  auto compute_R = [&](const T* sR, int slab) {
+#pragma unroll
+    for (int s = 0; s < SK / 16; ++s) {
+      Frag<T> qa = qf[slab * (SK / 16) + s];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) qa.v[t] = (T)((float)qa.v[t] * xs);
+#pragma unroll
+      for (int j = 0; j < DV / 32; ++j) mma16(acc[j], qa, load_frag(sR + (32 * j + lr) * LDR + 16 * s + 8 * hh));
+    }
+  };
+  // Decay of a 32x32 score tile (lane lr = query offset, register r = key
+  // offset kk = 8 (r/4) + 4 hh + r%4): diagonal tile dd[r] = scale *
+  // gamma^(lr-kk) (lr >= kk, else 0); a tile ks < q0 uses scale *
+  // gamma^(q0-ks-31) * ab[r], ab[r] = gamma^lr gamma^(31-kk) (exponents >= 0).
   float dd[16], ab[16];
   {
     const float glr = gpow(lr, lg2);
@@ -308,59 +359,80 @@ __global__ __launch_bounds__(256) void k_chunk_out(
       ab[r] = glr * gpow(31 - kk, lg2);
     }
   }
-
-  T* sK = reinterpret_cast<T*>(smem);
-  T* sVt = sK + KB * LDK;
-  const int kend = min(r0 + RT, N);
-  for (int kb = c0; kb < kend; kb += KB) {
-    // K block row-major [key][dk]
-    for (int u = tid; u < KB * (DK / 8); u += nthr) {
-      const int row = u / (DK / 8), c8 = u % (DK / 8);
-      const int key = kb + row;
-      Row8<T> r;
-      load_row8(r, K + (tokb + (key < N ? key : 0)) * ldk + (size_t)h * DK + 8 * c8, key < N);
-      store_row8(sK + row * LDK + 8 * c8, r);
-    }
-    // V block transposed [dv][key]
-    for (int u = tid; u < (KB / 4) * (DV / 8); u += nthr) {
-      const int kg = u / (DV / 8), cg = u % (DV / 8);
-      Row8<T> rv[4];
+  auto compute_KV = [&](const T* sK, int kb) {
+    const T* sV = sK + KB * LDK;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = kb + 4 * kg + i;
-        load_row8(rv[i], V + (tokb + (key < N ? key : 0)) * ldv + (size_t)h * DV + 8 * cg, key < N);
-      }
-      store_transposed4x8(sVt + (8 * cg) * LDV + 4 * kg, LDV, rv);
-    }
-    __syncthreads();
-    if (kb <= q0 && q0 < N) {
+    for (int u = 0; u < KB / 32; ++u) {
+      const int ks = kb + 32 * u;
+      if (ks > q0 || q0 >= N) continue;  // wave-uniform: keys all in this wave's future
       f32x16 st = (f32x16){};
 #pragma unroll
-      for (int s = 0; s < DK / 16; ++s) {
-        Frag<T> a = load_frag(sK + lr * LDK + 16 * s + 8 * hh);
-        mma16(st, a, qfrag(s));
-      }
+      for (int s = 0; s < DK / 16; ++s) mma16(st, load_frag(sK + (32 * u + lr) * LDK + 16 * s + 8 * hh), qf[s]);
       float p[16];
-      if (kb == q0) {
+      if (ks == q0) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) p[r] = st[r] * dd[r];
       } else {
-        const float c = scale * gpow(q0 - kb - 31, lg2);
+        const float c = scale * gpow(q0 - ks - 31, lg2);
 #pragma unroll
         for (int r = 0; r < 16; ++r) p[r] = st[r] * (c * ab[r]);
       }
       const Frag<T> pa0 = frag_from<T>(p), pa1 = frag_from<T>(p + 8);
+      // P's element t of lane half hh is key 8 (t/4) + 4 hh + t%4 of each
+      // 16-key step: the V fragment is read in that (KMAP_ACC) order.
 #pragma unroll
       for (int j = 0; j < DV / 32; ++j) {
-        const T* vr = sVt + (32 * j + lr) * LDV + 4 * hh;
-        mma16(acc[j], pa0, load_frag2(vr, vr + 8));
-        mma16(acc[j], pa1, load_frag2(vr + 16, vr + 24));
+        const T* vr = sV + (32 * u) * LDV + 32 * j;
+        mma16(acc[j], pa0, load_frag_rm<KMAP_ACC>(vr, LDV));
+        mma16(acc[j], pa1, load_frag_rm<KMAP_ACC>(vr + 16 * LDV, LDV));
       }
+    }
+  };
+
+  // ---- the pipeline ----
+  const bool inter = STATE && (ci > 0 || has_sin);
+  const int kend = min(r0 + RT, N);
+  const int nkb = (kend - c0 + KB - 1) / KB;
+  int stage = 0;
+  if constexpr (C::PIPE) {
+    if (inter) load_R(0); else load_KV(c0);
+    if (inter) store_R(buf(0)); else store_KV(buf(0));
+    __syncthreads();
+  }
+  if (inter) {
+#pragma unroll
+    for (int sl = 0; sl < C::NR; ++sl, ++stage) {
+      if constexpr (C::PIPE) {
+        if (sl + 1 < C::NR) load_R((sl + 1) * SK);
+        else if (nkb > 0) load_KV(c0);
+        compute_R(buf(stage), sl);
+        if (sl + 1 < C::NR) store_R(buf(stage + 1));
+        else if (nkb > 0) store_KV(buf(stage + 1));
+      } else {
+        load_R(sl * SK);
+        store_R(buf(0));
+        __syncthreads();
+        compute_R(buf(0), sl);
+      }
+      __syncthreads();
+    }
+  }
+  for (int i = 0; i < nkb; ++i, ++stage) {
+    const int kb = c0 + i * KB;
+    if constexpr (C::PIPE) {
+      if (i + 1 < nkb) load_KV(kb + KB);
+      compute_KV(buf(stage), kb);
+      if (i + 1 < nkb) store_KV(buf(stage + 1));
+    } else {
+      load_KV(kb);
+      store_KV(buf(0));
+      __syncthreads();
+      compute_KV(buf(0), kb);
     }
     __syncthreads();
   }
 
-  // Epilogue.  Lane owns column 32 j + lr of rows q0 + 8 (r/4) + 4 hh + r%4.
+  // ---- epilogue: lane owns column 32 j + lr of rows q0 + 8 (r/4) + 4 hh + r%4 ----
   if constexpr (GN) {
     float mu[16], rs[16];
 #pragma unroll
@@ -410,23 +482,33 @@ __global__ __launch_bounds__(256) void k_chunk_out(
 // ---------------------------------------------------------------------------
 // Host launchers
 // ---------------------------------------------------------------------------
-static int row_tile(int chunk) {
-  if (chunk % 128 == 0) return 128;
-  if (chunk % 64 == 0) return 64;
-  return 32;
+template <class T, int DK, int DV, int NW, bool STATE>
+static void launch_out(const ChunkArgs& a, int chunk, int NC, int TPC, int has_sin, const HeadTab& tab,
+                       hipStream_t st) {
+  const int BH = a.batch * a.heads;
+  dim3 grid(TPC * NC * BH);
+  if (a.fuse_gn_gate)
+    hipLaunchKernelGGL((k_chunk_out<T, DK, DV, NW, STATE, true>), grid, dim3(64 * NW), 0, st, (const T*)a.Q,
+                       (const T*)a.K, (const T*)a.V, a.ldq, a.ldk, a.ldv, (const T*)a.Rx, has_sin, (const T*)a.G,
+                       a.ldg, (T*)a.O, a.ldo, BH, a.seqlen, a.heads, chunk, NC, TPC, a.scale, a.eps, tab);
+  else
+    hipLaunchKernelGGL((k_chunk_out<T, DK, DV, NW, STATE, false>), grid, dim3(64 * NW), 0, st, (const T*)a.Q,
+                       (const T*)a.K, (const T*)a.V, a.ldq, a.ldk, a.ldv, (const T*)a.Rx, has_sin,
+                       (const T*)nullptr, (int64_t)0, (T*)a.O, a.ldo, BH, a.seqlen, a.heads, chunk, NC, TPC,
+                       a.scale, a.eps, tab);
 }
 
 template <class T, int DK, int DV>
 static hipError_t run_chunkwise(const ChunkArgs& a, const HeadTab& tab, hipStream_t st) {
-  const int B = a.batch, N = a.seqlen, H = a.heads, C = a.chunk;
-  const int NC = (N + C - 1) / C;
+  const int B = a.batch, N = a.seqlen, H = a.heads, Cn = a.chunk;
+  const int NC = (N + Cn - 1) / Cn;
   const int BH = B * H;
-  constexpr int TS = (DK >= 128 && DV >= 128) ? 128 : 64;
+  constexpr int TS = StateCfg<T, DK, DV>::TS;
   {
     TraceScope ts("k_chunk_state", st);
     dim3 grid(BH * NC, (DV / TS) * (DK / TS));
     hipLaunchKernelGGL((k_chunk_state<T, DK, DV>), grid, dim3(256), 0, st, (const T*)a.K, (const T*)a.V,
-                       a.ldk, a.ldv, a.dR, N, H, C, NC, tab);
+                       a.ldk, a.ldv, a.dR, N, H, Cn, NC, tab);
   }
   {
     TraceScope ts("k_chunk_scan", st);
@@ -436,38 +518,20 @@ static hipError_t run_chunkwise(const ChunkArgs& a, const HeadTab& tab, hipStrea
   }
   {
     TraceScope ts("k_chunk_out", st);
-    const int RT = row_tile(C);
-    const int TPC = C / RT;
-    dim3 grid(TPC * NC * BH);
-    dim3 block(RT * 2);  // RT / 32 waves of 64 lanes
-    if (a.fuse_gn_gate)
-      hipLaunchKernelGGL((k_chunk_out<T, DK, DV, true, true>), grid, block, 0, st, (const T*)a.Q, (const T*)a.K,
-                         (const T*)a.V, a.ldq, a.ldk, a.ldv, (const T*)a.Rx, (const T*)a.G, a.ldg, (T*)a.O,
-                         a.ldo, BH, N, H, C, NC, TPC, RT, a.scale, a.eps, tab);
+    const int has_sin = a.S_in != nullptr;
+    if (Cn % 128 == 0)
+      launch_out<T, DK, DV, 4, true>(a, Cn, NC, Cn / 128, has_sin, tab, st);
     else
-      hipLaunchKernelGGL((k_chunk_out<T, DK, DV, true, false>), grid, block, 0, st, (const T*)a.Q,
-                         (const T*)a.K, (const T*)a.V, a.ldq, a.ldk, a.ldv, (const T*)a.Rx, (const T*)nullptr,
-                         (int64_t)0, (T*)a.O, a.ldo, BH, N, H, C, NC, TPC, RT, a.scale, a.eps, tab);
+      launch_out<T, DK, DV, 1, true>(a, Cn, NC, Cn / 32, has_sin, tab, st);
   }
   return hipGetLastError();
 }
 
 template <class T, int DK, int DV>
 static hipError_t run_parallel(const ChunkArgs& a, const HeadTab& tab, hipStream_t st) {
-  const int B = a.batch, N = a.seqlen, H = a.heads;
-  const int BH = B * H;
-  constexpr int RT = 128;
-  const int TPC = (N + RT - 1) / RT;
-  dim3 grid(TPC * BH);
+  const int TPC = (a.seqlen + 127) / 128;
   TraceScope ts("k_chunk_out", st);
-  if (a.fuse_gn_gate)
-    hipLaunchKernelGGL((k_chunk_out<T, DK, DV, false, true>), grid, dim3(256), 0, st, (const T*)a.Q,
-                       (const T*)a.K, (const T*)a.V, a.ldq, a.ldk, a.ldv, (const T*)nullptr, (const T*)a.G,
-                       a.ldg, (T*)a.O, a.ldo, BH, N, H, TPC * RT, 1, TPC, RT, a.scale, a.eps, tab);
-  else
-    hipLaunchKernelGGL((k_chunk_out<T, DK, DV, false, false>), grid, dim3(256), 0, st, (const T*)a.Q,
-                       (const T*)a.K, (const T*)a.V, a.ldq, a.ldk, a.ldv, (const T*)nullptr, (const T*)nullptr,
-                       (int64_t)0, (T*)a.O, a.ldo, BH, N, H, TPC * RT, 1, TPC, RT, a.scale, a.eps, tab);
+  launch_out<T, DK, DV, 4, false>(a, TPC * 128, 1, TPC, 0, tab, st);
   return hipGetLastError();
 }
 

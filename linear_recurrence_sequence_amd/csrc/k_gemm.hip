@@ -4,56 +4,112 @@
 // 性能強（2）", section "門控多尺度 Retention", Eq. (8): the layer projects X with
 // W_Q, W_K, W_V, W_G and the gated, normalised heads with W_O.
 //
-// C[M, N] = A[M, K] * Bt[N, K]^T with both operands K-contiguous (the weights
-// are transposed once per call into that layout).  bf16: 256x256 output tile
-// per workgroup, 4 waves of 128x128 (16 accumulator tiles of 32x32 each), a
-// 64-deep K slab double-buffered in LDS (2 x 72 KiB) with the next slab's
-// global loads in flight during the current slab's matrix-core work.  f32:
-// 128x128 tile, 32-deep slab.
+// C[M, N] = A[M, K] * B[K, N], both row-major (the weights exactly as the
+// layer stores them, [in, out]).  B may be split into up to four column
+// segments with their own base pointer and row stride (W_Q | W_K | W_V |
+// W_G in one launch).  The matrix-core B operand wants the reduction index
+// contiguous: B tiles are copied into LDS as they are ([k][n]) and read
+// with the transposing LDS read (see load_frag_rm).  Leading segments can get the
+// rotation epilogue: output column pairs (2j, 2j+1) of each head are rotated
+// by the (cos, sin) of their row's position (row % seqlen) before the single
+// rounding to the output type.
+//
+// bf16: 256x256 output tile, 4 waves of 128x128 (16 accumulator tiles each,
+// held in the accumulation registers; a 128x128 wave tile reads 64 bytes of
+// LDS per clock at the matrix-core peak, a 128x64 one 96), 64-deep K slabs
+// double-buffered in LDS (2 x 72 KiB), the next slab's global loads in
+// flight during the current slab's matrix-core work.  f32: 128x128 tile,
+// 4 waves, 32-deep slabs.
 #include "msr_launch.h"
 
 namespace msr {
 
-template <class T, int BM, int BN, int BK>
-__global__ __launch_bounds__(256) void k_gemm_nt(const T* __restrict__ A, int64_t lda, const T* __restrict__ Bt,
-                                                 int64_t ldb, T* __restrict__ C, int64_t ldc, int M, int N, int K) {
-  constexpr int EPU = 16 / (int)sizeof(T);    // elements per 16-byte unit
-  constexpr int LDS_LD = BK + EPU;            // padded row (16 bytes)
-  constexpr int TM = BM / 64, TN = BN / 64;   // 32x32 tiles per wave per dim
-  constexpr int UPR = BK / EPU;               // units per row
-  constexpr int AU = BM * UPR / 256, BU = BN * UPR / 256;
-  __shared__ __attribute__((aligned(16))) T smem[2][(BM + BN) * LDS_LD];
+template <class T, int BM, int BN, int BK, int WM, int WN>
+__global__ __launch_bounds__(64 * WM * WN) void k_gemm(const T* __restrict__ A, int64_t lda, GemmB bp,
+                                                       T* __restrict__ C, int64_t ldc, int M, int N, int K) {
+  constexpr int NT = 64 * WM * WN;
+  constexpr int LDA = BK + 16 / (int)sizeof(T);         // A tile [BM][LDA], k contiguous
+  constexpr int LDB = BN + rm_pad<T>();                 // B tile [BK][LDB], n contiguous
+  constexpr int TM = BM / WM / 32, TN = BN / WN / 32;   // 32x32 tiles per wave
+  constexpr int AUNITS = BM * BK / 8, AU = (AUNITS + NT - 1) / NT;
+  constexpr int BUNITS = BK * BN / 8, BU = (BUNITS + NT - 1) / NT;
+  constexpr int STAGE = BM * LDA + BK * LDB;
+  __shared__ __attribute__((aligned(16))) T smem[2][STAGE];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 31, hh = lane >> 5;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WN, wn = wave % WN;
   const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+  auto seg_of = [&](int n) { return (n >= bp.start[1]) + (n >= bp.start[2]) + (n >= bp.start[3]); };
 
-  uint4 ra[AU], rb[BU];
+  // Global loads: uniform base (scalar registers) + loop-invariant 32-bit
+  // per-thread offset + uniform K offset.  Rows of A past M and columns of B
+  // past N are clamped to valid addresses instead of masked: they only feed
+  // output rows / columns that are never stored.
+  Row8<T> ra[AU], rb[BU];
+  const T* Ab = A + (size_t)m0 * lda;
+  uint32_t aoff[AU];
+#pragma unroll
+  for (int u = 0; u < AU; ++u) {
+    const int idx = min(tid + NT * u, AUNITS - 1);
+    const int row = min(idx / (BK / 8), M - 1 - m0), c8 = idx % (BK / 8);
+    aoff[u] = (uint32_t)(row * lda + 8 * c8);
+  }
+  // B: the whole tile inside one weight segment (the usual case) -> one base.
+  const int seg0 = seg_of(n0), seg1 = seg_of(min(n0 + BN, N) - 1);
+  const bool uni = seg0 == seg1;
+  const T* s0 = reinterpret_cast<const T*>(bp.ptr[0]);
+  const T* s1 = reinterpret_cast<const T*>(bp.ptr[1]);
+  const T* s2 = reinterpret_cast<const T*>(bp.ptr[2]);
+  const T* s3 = reinterpret_cast<const T*>(bp.ptr[3]);
+  auto sel = [&](int sg, auto a0, auto a1, auto a2, auto a3) {
+    return sg == 0 ? a0 : (sg == 1 ? a1 : (sg == 2 ? a2 : a3));
+  };
+  const T* Bb = sel(seg0, s0, s1, s2, s3) + (n0 - sel(seg0, bp.start[0], bp.start[1], bp.start[2], bp.start[3]));
+  const int64_t ldb0 = sel(seg0, bp.ld[0], bp.ld[1], bp.ld[2], bp.ld[3]);
+  uint32_t boff[BU];
+  int bcol[BU];
+#pragma unroll
+  for (int u = 0; u < BU; ++u) {
+    const int idx = min(tid + NT * u, BUNITS - 1);
+    const int row = idx / (BN / 8), c8 = idx % (BN / 8);
+    bcol[u] = min(n0 + 8 * c8, N - 8);           // N is a multiple of 8
+    boff[u] = (uint32_t)(row * ldb0 + (bcol[u] - n0));
+  }
   auto gload = [&](int k0) {
+    const T* Ak = Ab + k0;
 #pragma unroll
-    for (int u = 0; u < AU; ++u) {
-      const int idx = tid + 256 * u, row = idx / UPR, c = idx % UPR;
-      const int gm = m0 + row;
-      ra[u] = gm < M ? *reinterpret_cast<const uint4*>(A + (size_t)gm * lda + k0 + c * EPU) : make_uint4(0, 0, 0, 0);
-    }
+    for (int u = 0; u < AU; ++u) load_row8(ra[u], Ak + aoff[u], true);
+    if (uni) {
+      const T* Bk = Bb + (size_t)k0 * ldb0;
 #pragma unroll
-    for (int u = 0; u < BU; ++u) {
-      const int idx = tid + 256 * u, row = idx / UPR, c = idx % UPR;
-      const int gn = n0 + row;
-      rb[u] = gn < N ? *reinterpret_cast<const uint4*>(Bt + (size_t)gn * ldb + k0 + c * EPU) : make_uint4(0, 0, 0, 0);
+      for (int u = 0; u < BU; ++u) load_row8(rb[u], Bk + boff[u], true);
+    } else {
+#pragma unroll
+      for (int u = 0; u < BU; ++u) {
+        const int idx = min(tid + NT * u, BUNITS - 1);
+        const int row = idx / (BN / 8);
+        const int sg = seg_of(bcol[u]);
+        const T* src = sel(sg, s0, s1, s2, s3) + (bcol[u] - sel(sg, bp.start[0], bp.start[1], bp.start[2], bp.start[3]));
+        load_row8(rb[u], src + (size_t)(k0 + row) * sel(sg, bp.ld[0], bp.ld[1], bp.ld[2], bp.ld[3]), true);
+      }
     }
   };
   auto sstore = [&](int buf) {
-    T* s = smem[buf];
+    T* sA = smem[buf];
+    T* sB = sA + BM * LDA;
 #pragma unroll
     for (int u = 0; u < AU; ++u) {
-      const int idx = tid + 256 * u, row = idx / UPR, c = idx % UPR;
-      *reinterpret_cast<uint4*>(s + row * LDS_LD + c * EPU) = ra[u];
+      const int idx = tid + NT * u;
+      if (idx >= AUNITS) break;
+      const int row = idx / (BK / 8), c8 = idx % (BK / 8);
+      store_row8(sA + row * LDA + 8 * c8, ra[u]);
     }
 #pragma unroll
     for (int u = 0; u < BU; ++u) {
-      const int idx = tid + 256 * u, row = idx / UPR, c = idx % UPR;
-      *reinterpret_cast<uint4*>(s + (BM + row) * LDS_LD + c * EPU) = rb[u];
+      const int idx = tid + NT * u;
+      if (idx >= BUNITS) break;
+      const int row = idx / (BN / 8), c8 = idx % (BN / 8);
+      store_row8(sB + row * LDB + 8 * c8, rb[u]);
     }
   };
 
@@ -70,14 +126,14 @@ __global__ __launch_bounds__(256) void k_gemm_nt(const T* __restrict__ A, int64_
   for (int kt = 0; kt < KT; ++kt) {
     if (kt + 1 < KT) gload((kt + 1) * BK);
     const T* sA = smem[kt & 1];
-    const T* sB = sA + BM * LDS_LD;
+    const T* sB = sA + BM * LDA;
 #pragma unroll
     for (int s = 0; s < BK / 16; ++s) {
       Frag<T> af[TM], bfr[TN];
 #pragma unroll
-      for (int i = 0; i < TM; ++i) af[i] = load_frag(sA + (wm * (BM / 2) + 32 * i + lr) * LDS_LD + 16 * s + 8 * hh);
+      for (int i = 0; i < TM; ++i) af[i] = load_frag(sA + (wm * (BM / WM) + 32 * i + lr) * LDA + 16 * s + 8 * hh);
 #pragma unroll
-      for (int j = 0; j < TN; ++j) bfr[j] = load_frag(sB + (wn * (BN / 2) + 32 * j + lr) * LDS_LD + 16 * s + 8 * hh);
+      for (int j = 0; j < TN; ++j) bfr[j] = load_frag_rm<KMAP_CONTIG>(sB + 16 * s * LDB + wn * (BN / WN) + 32 * j, LDB);
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -87,66 +143,65 @@ __global__ __launch_bounds__(256) void k_gemm_nt(const T* __restrict__ A, int64_
     __syncthreads();
   }
 
+  // Epilogue through LDS (free after the main loop): each wave stages 32 of
+  // its rows at a time in float32, then every lane takes 8 consecutive
+  // columns of one row -- a rotation pair lives in one lane -- applies the
+  // rotation if the columns belong to a rotated segment, rounds once and
+  // writes 16 contiguous bytes.
+  constexpr int WCOLS = BN / WN;                 // columns per wave
+  constexpr int SLD = WCOLS + 4;                 // staged row stride (floats)
+  float* stg = reinterpret_cast<float*>(&smem[0][0]) + wave * 32 * SLD;
+  const int cw0 = n0 + wn * WCOLS;               // first column of this wave
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
+  for (int i = 0; i < TM; ++i) {
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int col = n0 + wn * (BN / 2) + 32 * j + lr;
-      if (col >= N) continue;
+    for (int j = 0; j < TN; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm * (BM / 2) + 32 * i + 8 * (r >> 2) + 4 * hh + (r & 3);
-        if (row < M) C[(size_t)row * ldc + col] = (T)acc[i][j][r];
+      for (int r = 0; r < 16; ++r) stg[(8 * (r >> 2) + 4 * hh + (r & 3)) * SLD + 32 * j + lr] = acc[i][j][r];
+    __syncthreads();
+    const int rbase = m0 + wm * (BM / WM) + 32 * i;
+#pragma unroll 1
+    for (int g = lane; g < 32 * (WCOLS / 8); g += 64) {
+      const int rr = g / (WCOLS / 8), c8 = g % (WCOLS / 8);
+      const int row = rbase + rr, col = cw0 + 8 * c8;
+      if (row >= M || col >= N) continue;
+      const float* src = stg + rr * SLD + 8 * c8;
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = src[e];
+      const int sg = seg_of(col);
+      if (sg < bp.rope_segs) {
+        const float2* cs = bp.rope_tab + (size_t)(row % bp.seqlen) * (bp.rope_d / 2) +
+                           (((col - bp.start[sg]) % bp.rope_d) >> 1);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const float2 t = cs[p];
+          const float x = v[2 * p], y = v[2 * p + 1];
+          v[2 * p] = x * t.x - y * t.y;
+          v[2 * p + 1] = x * t.y + y * t.x;
+        }
       }
+      Row8<T> o;
+      pack_row8(o, v);
+      store_row8(C + (size_t)row * ldc + col, o);
     }
+    __syncthreads();
+  }
 }
 
-hipError_t launch_gemm_nt(Elt elt, const void* A, int64_t lda, const void* Bt, int64_t ldb, void* C, int64_t ldc,
-                          int M, int N, int K, hipStream_t st) {
+hipError_t launch_gemm(Elt elt, const void* A, int64_t lda, const GemmB& b, void* C, int64_t ldc, int M, int N,
+                       int K, hipStream_t st) {
   if (M == 0 || N == 0) return hipSuccess;
-  TraceScope ts("k_gemm_nt", st);
+  TraceScope ts("k_gemm", st);
   if (elt == kBF16) {
     dim3 grid((N + 255) / 256, (M + 255) / 256);
-    hipLaunchKernelGGL((k_gemm_nt<bf16, 256, 256, 64>), grid, dim3(256), 0, st, (const bf16*)A, lda,
-                       (const bf16*)Bt, ldb, (bf16*)C, ldc, M, N, K);
+    hipLaunchKernelGGL((k_gemm<bf16, 256, 256, 64, 2, 2>), grid, dim3(256), 0, st, (const bf16*)A, lda, b, (bf16*)C,
+                       ldc, M, N, K);
   } else {
     dim3 grid((N + 127) / 128, (M + 127) / 128);
-    hipLaunchKernelGGL((k_gemm_nt<float, 128, 128, 32>), grid, dim3(256), 0, st, (const float*)A, lda,
-                       (const float*)Bt, ldb, (float*)C, ldc, M, N, K);
+    hipLaunchKernelGGL((k_gemm<float, 128, 128, 32, 2, 2>), grid, dim3(256), 0, st, (const float*)A, lda, b,
+                       (float*)C, ldc, M, N, K);
   }
-  return hipGetLastError();
-}
-
-// ---------------------------------------------------------------------------
-// 64x64-tile transpose through LDS.
-// ---------------------------------------------------------------------------
-template <class T>
-__global__ __launch_bounds__(256) void k_transpose(const T* __restrict__ src, int64_t lds, T* __restrict__ dst,
-                                                   int64_t ldd, int rows, int cols) {
-  __shared__ T t[64][65];
-  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int i = ty; i < 64; i += 4) {
-    const int r = r0 + i, c = c0 + tx;
-    if (r < rows && c < cols) t[i][tx] = src[(size_t)r * lds + c];
-  }
-  __syncthreads();
-  for (int i = ty; i < 64; i += 4) {
-    const int c = c0 + i, r = r0 + tx;
-    if (r < rows && c < cols) dst[(size_t)c * ldd + r] = t[tx][i];
-  }
-}
-
-hipError_t launch_transpose(Elt elt, const void* src, int64_t lds, void* dst, int64_t ldd, int rows, int cols,
-                            hipStream_t st) {
-  if (rows == 0 || cols == 0) return hipSuccess;
-  dim3 grid((cols + 63) / 64, (rows + 63) / 64);
-  TraceScope ts("k_transpose", st);
-  if (elt == kBF16)
-    hipLaunchKernelGGL(k_transpose<bf16>, grid, dim3(256), 0, st, (const bf16*)src, lds, (bf16*)dst, ldd, rows, cols);
-  else
-    hipLaunchKernelGGL(k_transpose<float>, grid, dim3(256), 0, st, (const float*)src, lds, (float*)dst, ldd, rows,
-                       cols);
   return hipGetLastError();
 }
 

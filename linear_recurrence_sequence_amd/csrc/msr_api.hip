@@ -125,22 +125,22 @@ ChunkWs chunk_ws_layout(msr_dtype dt, const msr_dims& d, int32_t chunk, bool rop
 }
 
 struct LayerWs {
-  size_t wt = 0, wto = 0, qkvg = 0, z = 0, chunk = 0, total = 0;
+  size_t qkvg = 0, z = 0, tab = 0, chunk = 0, total = 0;
   ChunkWs cw;
 };
 LayerWs layer_ws_layout(msr_dtype dt, int32_t batch, int32_t seqlen, int32_t d_model, int32_t heads, int32_t dk,
                         int32_t dv, int32_t chunk) {
+  (void)d_model;
   LayerWs w;
   const size_t es = elt_size(dt);
   const size_t M = (size_t)batch * seqlen;
   const size_t ntot = (size_t)heads * (2 * dk + 2 * dv);
   size_t off = 0;
-  w.wt = off; off += align_up(ntot * d_model * es);
-  w.wto = off; off += align_up((size_t)d_model * heads * dv * es);
   w.qkvg = off; off += align_up(M * ntot * es);
   w.z = off; off += align_up(M * heads * dv * es);
+  w.tab = off; off += align_up((size_t)seqlen * (dk / 2) * sizeof(float2));
   msr_dims d{batch, seqlen, heads, dk, dv};
-  w.cw = chunk_ws_layout(dt, d, chunk, true, true);  // includes the rotation table
+  w.cw = chunk_ws_layout(dt, d, chunk, false, true);
   w.chunk = off; off += w.cw.total;
   w.total = off;
   return w;
@@ -316,35 +316,26 @@ msr_status msr_layer_fwd(msr_dtype dtype, int32_t batch, int32_t seqlen, int32_t
   const size_t es = elt_size(dtype);
   const int hk = heads * d_k, hv = heads * d_v;
   const int ntot = 2 * hk + 2 * hv;
-  char* wt = at<char>(workspace, w.wt);
-  char* wto = at<char>(workspace, w.wto);
   char* qkvg = at<char>(workspace, w.qkvg);
   char* z = at<char>(workspace, w.z);
+  float2* tab = at<float2>(workspace, w.tab);
   void* cws = at<void>(workspace, w.chunk);
+  const bool rope = rope_base > 0.f;
 
-  // 1. weights into K-contiguous layout: rows [Q | K | V | G] of W^T
-  hipError_t err = launch_transpose(e, W_Q, hk, wt, d_model, d_model, hk, st);
-  if (err == hipSuccess) err = launch_transpose(e, W_K, hk, wt + (size_t)hk * d_model * es, d_model, d_model, hk, st);
-  if (err == hipSuccess)
-    err = launch_transpose(e, W_V, hv, wt + (size_t)2 * hk * d_model * es, d_model, d_model, hv, st);
-  if (err == hipSuccess)
-    err = launch_transpose(e, W_G, hv, wt + (size_t)(2 * hk + hv) * d_model * es, d_model, d_model, hv, st);
-  if (err == hipSuccess) err = launch_transpose(e, W_O, d_model, wto, hv, hv, d_model, st);
-  // 2. [Q^ | K^ | V | G] = X W
-  if (err == hipSuccess) err = launch_gemm_nt(e, X, d_model, wt, d_model, qkvg, ntot, (int)M, ntot, d_model, st);
+  // 1. (cos, sin) table of the positions 0..seqlen-1
+  hipError_t err = rope ? launch_rope_table(tab, seqlen, d_k, 0, rope_base, st) : hipSuccess;
+  // 2. [Q | K | V | G] = X [W_Q | W_K | W_V | W_G], Q and K rotated in the epilogue
+  GemmB bq{};
+  bq.ptr[0] = W_Q; bq.ptr[1] = W_K; bq.ptr[2] = W_V; bq.ptr[3] = W_G;
+  bq.ld[0] = hk; bq.ld[1] = hk; bq.ld[2] = hv; bq.ld[3] = hv;
+  bq.start[0] = 0; bq.start[1] = hk; bq.start[2] = 2 * hk; bq.start[3] = 2 * hk + hv;
+  bq.rope_segs = rope ? 2 : 0;
+  bq.rope_d = d_k;
+  bq.seqlen = seqlen;
+  bq.rope_tab = tab;
+  if (err == hipSuccess) err = launch_gemm(e, X, d_model, bq, qkvg, ntot, (int)M, ntot, d_model, st);
   if (err != hipSuccess) return from_hip(err, "msr_layer_fwd(projections)");
-  // 3. rotation of Q^ and K^ in place
-  msr_dims d{batch, seqlen, heads, d_k, d_v};
-  float2* tab = at<float2>(cws, w.cw.tab);
-  if (rope_base > 0.f) {
-    err = launch_rope_table(tab, seqlen, d_k, 0, rope_base, st);
-    if (err == hipSuccess) err = launch_rope_apply(e, qkvg, ntot, qkvg, ntot, (int)M, seqlen, heads, d_k, tab, st);
-    if (err == hipSuccess)
-      err = launch_rope_apply(e, qkvg + (size_t)hk * es, ntot, qkvg + (size_t)hk * es, ntot, (int)M, seqlen, heads,
-                              d_k, tab, st);
-    if (err != hipSuccess) return from_hip(err, "msr_layer_fwd(rotation)");
-  }
-  // 4. chunkwise retention + per-head GroupNorm + swish gate -> Z
+  // 3. chunkwise retention + per-head GroupNorm + swish gate -> Z
   ChunkArgs a{};
   a.elt = e;
   a.d_k = d_k; a.d_v = d_v; a.batch = batch; a.seqlen = seqlen; a.heads = heads;
@@ -362,8 +353,11 @@ msr_status msr_layer_fwd(msr_dtype dtype, int32_t batch, int32_t seqlen, int32_t
   const HeadTab htab = make_tab(gamma, heads, chunk, seqlen);
   err = launch_chunkwise(a, htab, st);
   if (err != hipSuccess) return from_hip(err, "msr_layer_fwd(retention)");
-  // 5. out = Z W_O
-  err = launch_gemm_nt(e, z, hv, wto, hv, out, d_model, (int)M, d_model, hv, st);
+  // 4. out = Z W_O
+  GemmB bo{};
+  bo.ptr[0] = W_O; bo.ld[0] = d_model;
+  bo.start[0] = 0; bo.start[1] = bo.start[2] = bo.start[3] = INT32_MAX;
+  err = launch_gemm(e, z, hv, bo, out, d_model, (int)M, d_model, hv, st);
   return from_hip(err, "msr_layer_fwd(output projection)");
 }
 

@@ -128,6 +128,14 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
 }
 
+__device__ __forceinline__ void pack_row8(Row8<bf16>& r, const float* v) {
+  r.u = make_uint4(pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]), pack_bf16(v[4], v[5]), pack_bf16(v[6], v[7]));
+}
+__device__ __forceinline__ void pack_row8(Row8<float>& r, const float* v) {
+  r.lo = make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3]));
+  r.hi = make_uint4(__float_as_uint(v[4]), __float_as_uint(v[5]), __float_as_uint(v[6]), __float_as_uint(v[7]));
+}
+
 // Multiply the 8 elements of a row by s (rounding back to the storage type).
 __device__ __forceinline__ void scale_row8(Row8<bf16>& r, float s) {
   uint32_t w[4] = {r.u.x, r.u.y, r.u.z, r.u.w};
@@ -142,35 +150,59 @@ __device__ __forceinline__ void scale_row8(Row8<float>& r, float s) {
                     __float_as_uint(__uint_as_float(r.hi.z) * s), __float_as_uint(__uint_as_float(r.hi.w) * s));
 }
 
-// Transposing store: rows r[0..3] are 4 consecutive source rows (k, k+1,
-// k+2, k+3) of 8 consecutive columns c..c+7.  Writes dst[(c+e)*ld + k + 0..3]
-// for e = 0..7, i.e. the tile lands column-major (the reduction index k
-// contiguous) as the matrix-core fragments want it.
-__device__ __forceinline__ void store_transposed4x8(bf16* dst, int ld, const Row8<bf16>* r) {
-  const uint32_t w0[4] = {r[0].u.x, r[0].u.y, r[0].u.z, r[0].u.w};
-  const uint32_t w1[4] = {r[1].u.x, r[1].u.y, r[1].u.z, r[1].u.w};
-  const uint32_t w2[4] = {r[2].u.x, r[2].u.y, r[2].u.z, r[2].u.w};
-  const uint32_t w3[4] = {r[3].u.x, r[3].u.y, r[3].u.z, r[3].u.w};
+// ---------------------------------------------------------------------------
+// Fragments of a matrix stored row-major [k][n] (n contiguous) in LDS, i.e.
+// with the reduction index strided.  This lane receives column lr of the
+// 32-column tile starting at `tile` and, as element t = 4p + j, row
+// koff(p, hh) + j, where koff = 8 hh + 4 p (KMAP_CONTIG: the same order as a
+// k-contiguous fragment) or 8 p + 4 hh (KMAP_ACC: the key order of a 32x32
+// accumulator tile reused as an A operand, see k_chunk_out).
+//
+// bf16 uses the gfx950 transposing LDS read ds_read_b64_tr_b16: within each
+// group of 16 lanes, lane i receives as element j the (i % 4)-th 16-bit value
+// of the 8 bytes addressed by lane 4 j + i / 4.  So lane 4 j + q of group g
+// (hh = g / 2, column half c = g % 2) addresses row koff + j, columns
+// 16 c + 4 q .. + 3; two reads (p = 0, 1) give the 8 elements.  With a row
+// stride of 16 or 48 banks (mod 64) the 32 lanes serviced together touch 64
+// distinct banks.  f32 has no such instruction: 8 scalar reads.
+// ---------------------------------------------------------------------------
+enum { KMAP_CONTIG = 0, KMAP_ACC = 1 };
+
+template <int KM>
+__device__ __forceinline__ Frag<bf16> load_frag_rm(const bf16* tile, int ld) {
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4, i = lane & 15;
+  const int hh = g >> 1, c = g & 1, j = i >> 2, q = i & 3;
+  Frag<bf16> f;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    uint2 even, odd;
-    even.x = (w0[i] & 0xffffu) | (w1[i] << 16);
-    even.y = (w2[i] & 0xffffu) | (w3[i] << 16);
-    odd.x = (w0[i] >> 16) | (w1[i] & 0xffff0000u);
-    odd.y = (w2[i] >> 16) | (w3[i] & 0xffff0000u);
-    *reinterpret_cast<uint2*>(dst + (2 * i) * ld) = even;
-    *reinterpret_cast<uint2*>(dst + (2 * i + 1) * ld) = odd;
+  for (int p = 0; p < 2; ++p) {
+    const int koff = KM == KMAP_CONTIG ? 8 * hh + 4 * p : 8 * p + 4 * hh;
+    const bf16* a = tile + (koff + j) * ld + 16 * c + 4 * q;
+    const bf16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)a);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) f.v[4 * p + e] = r[e];
   }
+  return f;
 }
-__device__ __forceinline__ void store_transposed4x8(float* dst, int ld, const Row8<float>* r) {
-  const uint32_t* a = reinterpret_cast<const uint32_t*>(&r[0]);
-  const uint32_t* b = reinterpret_cast<const uint32_t*>(&r[1]);
-  const uint32_t* c = reinterpret_cast<const uint32_t*>(&r[2]);
-  const uint32_t* d = reinterpret_cast<const uint32_t*>(&r[3]);
+
+template <int KM>
+__device__ __forceinline__ Frag<float> load_frag_rm(const float* tile, int ld) {
+  const int lane = threadIdx.x & 63;
+  const int lr = lane & 31, hh = lane >> 5;
+  Frag<float> f;
 #pragma unroll
-  for (int e = 0; e < 8; ++e)
-    *reinterpret_cast<uint4*>(dst + e * ld) = make_uint4(a[e], b[e], c[e], d[e]);
+  for (int t = 0; t < 8; ++t) {
+    const int p = t >> 2, j = t & 3;
+    const int koff = KM == KMAP_CONTIG ? 8 * hh + 4 * p : 8 * p + 4 * hh;
+    f.v[t] = tile[(koff + j) * ld + lr];
+  }
+  return f;
 }
+
+// Row padding (elements) of a row-major tile read with load_frag_rm: bf16
+// rows of a multiple of 128 bytes get 64 bytes more, making the stride 16 or
+// 48 banks mod 64.
+template <class T> constexpr int rm_pad() { return sizeof(T) == 2 ? 32 : 4; }
 
 // Butterfly sum over the 32 lanes of one half-wave (xor masks < 32 stay
 // inside the half).

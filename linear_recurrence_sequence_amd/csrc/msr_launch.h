@@ -65,12 +65,23 @@ hipError_t launch_rope_apply(Elt elt, const void* src, int64_t lds, void* dst, i
                              int rows, int seqlen, int heads, int d, const float2* tab,
                              hipStream_t stream);
 
-// C[M, N] = A[M, K] * Bt[N, K]^T (both operands K-contiguous), fp32
-// accumulation, C in elt.  K must be a multiple of 64.
-hipError_t launch_gemm_nt(Elt elt, const void* A, int64_t lda, const void* Bt, int64_t ldb,
-                          void* C, int64_t ldc, int M, int N, int K, hipStream_t stream);
-// dst[c, r] = src[r, c] for a rows x cols block.
-hipError_t launch_transpose(Elt elt, const void* src, int64_t lds, void* dst, int64_t ldd,
-                            int rows, int cols, hipStream_t stream);
+// B operand of launch_gemm: up to four column segments, segment s covering
+// output columns [start[s], start[s+1]) (start[0] = 0, unused entries set to
+// INT_MAX), each a row-major [K, width] block at ptr[s] with row stride
+// ld[s] (elements; multiples of 8).  The first rope_segs segments get the
+// rotation epilogue with head dim rope_d and table rope_tab ([seqlen][rope_d/2]
+// (cos, sin)); output row m is token m % seqlen.
+struct GemmB {
+  const void* ptr[4];
+  int64_t ld[4];
+  int start[4];
+  int rope_segs, rope_d, seqlen;
+  const float2* rope_tab;
+};
+
+// C[M, N] = A[M, K] * B[K, N] (row-major A and B segments), fp32
+// accumulation, C (row stride ldc) in elt.  K must be a multiple of 64.
+hipError_t launch_gemm(Elt elt, const void* A, int64_t lda, const GemmB& b, void* C, int64_t ldc, int M, int N,
+                       int K, hipStream_t stream);
 
 }  // namespace msr
