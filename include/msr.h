@@ -42,7 +42,8 @@
  * Supported head dims (else MSR_ERR_UNSUPPORTED): (d_k, d_v) in
  *           {(64,64), (128,128), (256,256), (256,512)}, the last one in
  *           bf16 only except for msr_recurrent_step; heads <= 128; chunk a
- *           positive multiple of 32; batch * seqlen < 2^31.
+ *           positive multiple of 32, at most 4096; batch * seqlen < 2^31;
+ *           heads * (2 d_k + 2 d_v) * 4096 < 2^31.
  */
 #ifndef MSR_H
 #define MSR_H

@@ -67,9 +67,11 @@ __global__ __launch_bounds__(256) void k_chunk_state(const T* __restrict__ K, co
   const float lg2 = tab.lg2[h];
   const int wr = (wave >> 1) * 32 * WT;
   const int wc = (wave & 1) * 32 * WT;
+  // uniform bases + small per-thread offsets; keys past the chunk end are
+  // clamped to a valid row and get zeta = 0, so they add nothing.
   const size_t tok0 = (size_t)b * N + c0;
-  const T* Kb = K + (size_t)h * DK + tk * TS;
-  const T* Vb = V + (size_t)h * DV + tv * TS;
+  const T* Kb = K + (size_t)h * DK + tk * TS + tok0 * ldk;
+  const T* Vb = V + (size_t)h * DV + tv * TS + tok0 * ldv;
 
   f32x16 acc[WT][WT];
 #pragma unroll
@@ -82,13 +84,13 @@ __global__ __launch_bounds__(256) void k_chunk_state(const T* __restrict__ K, co
     for (int q = 0; q < UPT; ++q) {
       const int u = tid + 256 * q;
       const int key = u / (TS / 8), c8 = u % (TS / 8);
-      if (u < UNITS) {
-        const bool ok = kb + key < L;
-        const size_t tok = tok0 + (ok ? kb + key : 0);
+      if (UNITS % 256 == 0 || u < UNITS) {
+        const int kk = kb + key;
+        const int kc = min(kk, L - 1);
         Row8<T> rk, rv;
-        load_row8(rk, Kb + tok * ldk + 8 * c8, ok);
-        load_row8(rv, Vb + tok * ldv + 8 * c8, ok);
-        if (ok) scale_row8(rv, gpow(L - 1 - (kb + key), lg2));
+        load_row8(rk, Kb + (uint32_t)(kc * (int)ldk + 8 * c8), true);
+        load_row8(rv, Vb + (uint32_t)(kc * (int)ldv + 8 * c8), true);
+        scale_row8(rv, kk < L ? gpow(L - 1 - kk, lg2) : 0.f);
         store_row8(sK + key * LDT + 8 * c8, rk);
         store_row8(sV + key * LDT + 8 * c8, rv);
       }
@@ -262,11 +264,10 @@ __global__ __launch_bounds__(64 * NW) void k_chunk_out(
   // K Q^T and (times xs) the A operand of Q R.
   Frag<T> qf[DK / 16];
   {
-    const int q = q0 + lr;
-    const bool ok = q < N;
-    const T* p = Q + (tokb + (ok ? q : 0)) * ldq + (size_t)h * DK + 8 * hh;
+    // rows past the end are clamped (their outputs are never stored)
+    const T* p = Q + (tokb + min(q0 + lr, N - 1)) * ldq + (size_t)h * DK + 8 * hh;
 #pragma unroll
-    for (int s = 0; s < DK / 16; ++s) qf[s] = ok ? load_frag(p + 16 * s) : zero_frag<T>();
+    for (int s = 0; s < DK / 16; ++s) qf[s] = load_frag(p + 16 * s);
   }
   f32x16 acc[DV / 32];
 #pragma unroll
@@ -275,14 +276,16 @@ __global__ __launch_bounds__(64 * NW) void k_chunk_out(
   // ---- staging ----
   Row8<T> pre[C::PRE];
   const T* Rt = STATE ? Rx + ((size_t)bh * NC + ci) * DV * DK : nullptr;
-  const T* Kh = K + (size_t)h * DK;
-  const T* Vh = V + (size_t)h * DV;
+  // Keys past the end of the sequence are clamped to the last row: they are
+  // in the future of every stored query, so their P entries are exactly 0.
+  const T* Kh = K + (size_t)h * DK + tokb * ldk;
+  const T* Vh = V + (size_t)h * DV + tokb * ldv;
   auto load_R = [&](int k0) {
 #pragma unroll
     for (int u = 0; u < C::RU; ++u) {
-      const int idx = tid + NT * u;
+      const int idx = min(tid + NT * u, DV * (SK / 8) - 1);
       const int row = idx / (SK / 8), c8 = idx % (SK / 8);
-      load_row8(pre[u], Rt + (size_t)row * DK + k0 + 8 * c8, idx < DV * (SK / 8));
+      load_row8(pre[u], Rt + k0 + row * DK + 8 * c8, true);
     }
   };
   auto store_R = [&](T* sR) {
@@ -294,22 +297,24 @@ __global__ __launch_bounds__(64 * NW) void k_chunk_out(
       store_row8(sR + row * LDR + 8 * c8, pre[u]);
     }
   };
+  // 32-bit per-thread offsets inside a KB-row block (row < KB, so
+  // row * stride fits easily); the block base is a uniform 64-bit pointer.
+  const int ldk32 = (int)ldk, ldv32 = (int)ldv;
   auto load_KV = [&](int kb) {
+    const int lim = N - 1 - kb;
+    const T* Kk = Kh + (size_t)kb * ldk;
+    const T* Vk = Vh + (size_t)kb * ldv;
 #pragma unroll
     for (int u = 0; u < C::KU; ++u) {
-      const int idx = tid + NT * u;
+      const int idx = min(tid + NT * u, KB * (DK / 8) - 1);
       const int row = idx / (DK / 8), c8 = idx % (DK / 8);
-      const int key = kb + row;
-      const bool ok = idx < KB * (DK / 8) && key < N;
-      load_row8(pre[u], Kh + (tokb + (ok ? key : 0)) * ldk + 8 * c8, ok);
+      load_row8(pre[u], Kk + (uint32_t)(min(row, lim) * ldk32 + 8 * c8), true);
     }
 #pragma unroll
     for (int u = 0; u < C::VU; ++u) {
-      const int idx = tid + NT * u;
+      const int idx = min(tid + NT * u, KB * (DV / 8) - 1);
       const int row = idx / (DV / 8), c8 = idx % (DV / 8);
-      const int key = kb + row;
-      const bool ok = idx < KB * (DV / 8) && key < N;
-      load_row8(pre[C::KU + u], Vh + (tokb + (ok ? key : 0)) * ldv + 8 * c8, ok);
+      load_row8(pre[C::KU + u], Vk + (uint32_t)(min(row, lim) * ldv32 + 8 * c8), true);
     }
   };
   auto store_KV = [&](T* sK) {

@@ -24,7 +24,7 @@
 
 namespace msr {
 
-template <class T, int BM, int BN, int BK, int WM, int WN>
+template <class T, int BM, int BN, int BK, int WM, int WN, bool UNI>
 __global__ __launch_bounds__(64 * WM * WN) void k_gemm(const T* __restrict__ A, int64_t lda, GemmB bp,
                                                        T* __restrict__ C, int64_t ldc, int M, int N, int K) {
   constexpr int NT = 64 * WM * WN;
@@ -38,7 +38,20 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm(const T* __restrict__ A, 
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 31, hh = lane >> 5;
   const int wm = wave / WN, wn = wave % WN;
-  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+  // Tile order: blocks are dispatched round-robin over the 8 XCDs (each with
+  // its own L2).  Give every XCD a contiguous range of tiles in grouped order
+  // (8 tile-rows at a time, N fastest), so the tiles in flight on one XCD
+  // share A row panels and B column panels in that XCD's L2.
+  // XCD x (= bid % 8) takes q + (x < r) consecutive tiles starting at
+  // x q + min(x, r), q = total / 8, r = total % 8: a permutation of 0..total-1.
+  const int Mt = gridDim.y, Nt = gridDim.x, total = Mt * Nt;
+  const int bid = blockIdx.y * Nt + blockIdx.x;
+  const int xcd = bid % 8, q8 = total / 8, r8 = total % 8;
+  const int t = xcd * q8 + min(xcd, r8) + bid / 8;
+  constexpr int GM = 8;
+  const int grp = t / (GM * Nt), first = grp * GM, gm = min(GM, Mt - first);
+  const int w = t % (GM * Nt);
+  const int m0 = (first + w % gm) * BM, n0 = (w / gm) * BN;
   auto seg_of = [&](int n) { return (n >= bp.start[1]) + (n >= bp.start[2]) + (n >= bp.start[3]); };
 
   // Global loads: uniform base (scalar registers) + loop-invariant 32-bit
@@ -55,8 +68,8 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm(const T* __restrict__ A, 
     aoff[u] = (uint32_t)(row * lda + 8 * c8);
   }
   // B: the whole tile inside one weight segment (the usual case) -> one base.
-  const int seg0 = seg_of(n0), seg1 = seg_of(min(n0 + BN, N) - 1);
-  const bool uni = seg0 == seg1;
+  // UNI: the launcher checked that no tile straddles two segments.
+  const int seg0 = seg_of(n0);
   const T* s0 = reinterpret_cast<const T*>(bp.ptr[0]);
   const T* s1 = reinterpret_cast<const T*>(bp.ptr[1]);
   const T* s2 = reinterpret_cast<const T*>(bp.ptr[2]);
@@ -79,7 +92,7 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm(const T* __restrict__ A, 
     const T* Ak = Ab + k0;
 #pragma unroll
     for (int u = 0; u < AU; ++u) load_row8(ra[u], Ak + aoff[u], true);
-    if (uni) {
+    if constexpr (UNI) {
       const T* Bk = Bb + (size_t)k0 * ldb0;
 #pragma unroll
       for (int u = 0; u < BU; ++u) load_row8(rb[u], Bk + boff[u], true);
@@ -192,15 +205,27 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm(const T* __restrict__ A, 
 hipError_t launch_gemm(Elt elt, const void* A, int64_t lda, const GemmB& b, void* C, int64_t ldc, int M, int N,
                        int K, hipStream_t st) {
   if (M == 0 || N == 0) return hipSuccess;
+  const int BN = elt == kBF16 ? 256 : 128;
+  bool uni = true;  // every segment boundary on a tile boundary
+  for (int sgi = 1; sgi < 4; ++sgi)
+    if (b.start[sgi] < N && b.start[sgi] % BN) uni = false;
   TraceScope ts("k_gemm", st);
   if (elt == kBF16) {
     dim3 grid((N + 255) / 256, (M + 255) / 256);
-    hipLaunchKernelGGL((k_gemm<bf16, 256, 256, 64, 2, 2>), grid, dim3(256), 0, st, (const bf16*)A, lda, b, (bf16*)C,
-                       ldc, M, N, K);
+    if (uni)
+      hipLaunchKernelGGL((k_gemm<bf16, 256, 256, 64, 2, 2, true>), grid, dim3(256), 0, st, (const bf16*)A, lda, b,
+                         (bf16*)C, ldc, M, N, K);
+    else
+      hipLaunchKernelGGL((k_gemm<bf16, 256, 256, 64, 2, 2, false>), grid, dim3(256), 0, st, (const bf16*)A, lda, b,
+                         (bf16*)C, ldc, M, N, K);
   } else {
     dim3 grid((N + 127) / 128, (M + 127) / 128);
-    hipLaunchKernelGGL((k_gemm<float, 128, 128, 32, 2, 2>), grid, dim3(256), 0, st, (const float*)A, lda, b,
-                       (float*)C, ldc, M, N, K);
+    if (uni)
+      hipLaunchKernelGGL((k_gemm<float, 128, 128, 32, 2, 2, true>), grid, dim3(256), 0, st, (const float*)A, lda, b,
+                         (float*)C, ldc, M, N, K);
+    else
+      hipLaunchKernelGGL((k_gemm<float, 128, 128, 32, 2, 2, false>), grid, dim3(256), 0, st, (const float*)A, lda, b,
+                         (float*)C, ldc, M, N, K);
   }
   return hipGetLastError();
 }

@@ -60,6 +60,10 @@ msr_status check_heads(int32_t batch, int32_t seqlen, int32_t heads, int32_t dk,
                 "(256,512)", dk, dv);
   const int64_t tokens = (int64_t)batch * seqlen;
   if (tokens > (int64_t)INT32_MAX) return fail(MSR_ERR_UNSUPPORTED, "batch*seqlen exceeds 2^31-1");
+  // in-chunk offsets are 32-bit: a chunk of rows of the widest token stride
+  // (the fused projection buffer) must stay below 2^31 elements
+  if ((int64_t)heads * (2 * dk + 2 * dv) * 4096 > (int64_t)INT32_MAX)
+    return fail(MSR_ERR_UNSUPPORTED, "heads*(2 d_k + 2 d_v) too large");
   return MSR_OK;
 }
 
@@ -82,6 +86,7 @@ msr_status check_gamma(const double* gamma, int heads) {
 msr_status check_chunk(int32_t chunk) {
   if (chunk <= 0) return fail(MSR_ERR_SHAPE, "chunk = %d must be positive", chunk);
   if (chunk % 32) return fail(MSR_ERR_UNSUPPORTED, "chunk = %d is not a multiple of 32", chunk);
+  if (chunk > 4096) return fail(MSR_ERR_UNSUPPORTED, "chunk = %d exceeds 4096", chunk);
   return MSR_OK;
 }
 

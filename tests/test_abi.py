@@ -64,6 +64,7 @@ def test_chunkwise_validation():
     assert _chunkwise(dims=(1, 64, 129, 64, 64)) == 4             # too many heads
     assert _chunkwise(chunk=0) == 2
     assert _chunkwise(chunk=48) == 4                              # not a multiple of 32
+    assert _chunkwise(chunk=8192) == 4                            # above 4096
     assert _chunkwise(gamma=False) == 1                           # gamma NULL
     assert _chunkwise(Q=None) == 1
     assert _chunkwise(ws=(None, 0)) == 5                          # workspace missing
