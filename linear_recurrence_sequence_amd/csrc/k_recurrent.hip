@@ -6,9 +6,9 @@
 //   S <- gamma S + k^T v ;   o = scale * q S
 // with q, k rotated at the absolute position (section "Retention", Eq. (3)-(4),
 // xPos).  The step reads and writes the d_k x d_v float32 state once, so it is
-// bound by HBM bandwidth: one workgroup per (batch, head) streams the state
-// row by row, each lane owning 4 contiguous d_v columns (16-byte accesses,
-// a wave covers 256 contiguous floats), with 8 rows in flight per lane.
+// bound by HBM bandwidth: workgroups stream the state row by row, each lane
+// owning 4 contiguous d_v columns (16-byte non-temporal accesses), with 8
+// rows in flight per lane.
 #include "msr_launch.h"
 
 namespace msr {
@@ -25,17 +25,22 @@ __device__ __forceinline__ void rope_cs(int64_t p, int j, int d, float base, flo
 
 template <class T> __device__ __forceinline__ float ld1(const T* p) { return (float)*p; }
 
-template <class T, int DK, int DV>
+template <class T, int DK, int DV, int CS>
 __global__ __launch_bounds__(256) void k_recurrent_step(const T* __restrict__ q, const T* __restrict__ k,
                                                         const T* __restrict__ v, float* __restrict__ S,
                                                         T* __restrict__ o, int H, float scale, int64_t pos,
                                                         float rope_base, HeadTab tab) {
+  // CS workgroups per (batch, head), each owning DV / CS columns: the sum
+  // over d_k rows of a column stays inside one workgroup, and the finer grid
+  // avoids a mostly idle last round of workgroups.  The state is touched
+  // exactly once per step, so its loads and stores are non-temporal.
   constexpr int CPT = 4;               // d_v columns per lane
-  constexpr int TPR = DV / CPT;        // lanes per state row
+  constexpr int SW = DV / CS;          // columns per workgroup
+  constexpr int TPR = SW / CPT;        // lanes per state row
   constexpr int RG = 256 / TPR;        // rows processed in parallel
   __shared__ float sq[DK], sk[DK];
   __shared__ f32x4 red[RG][TPR];
-  const int bh = blockIdx.x, h = bh % H, tid = threadIdx.x;
+  const int bh = blockIdx.x / CS, cs = blockIdx.x % CS, h = bh % H, tid = threadIdx.x;
   const T* qb = q + (size_t)bh * DK;
   const T* kb = k + (size_t)bh * DK;
   for (int j = tid; j < DK / 2; j += 256) {
@@ -52,7 +57,7 @@ __global__ __launch_bounds__(256) void k_recurrent_step(const T* __restrict__ q,
   }
   __syncthreads();
 
-  const int rg = tid / TPR, c = (tid % TPR) * CPT;
+  const int rg = tid / TPR, c = cs * SW + (tid % TPR) * CPT;
   const T* vb = v + (size_t)bh * DV + c;
   const f32x4 vv = {ld1(vb), ld1(vb + 1), ld1(vb + 2), ld1(vb + 3)};
   const float g = tab.gam[h];
@@ -61,10 +66,10 @@ __global__ __launch_bounds__(256) void k_recurrent_step(const T* __restrict__ q,
 #pragma unroll 8
   for (int i = rg; i < DK; i += RG) {
     f32x4* p = reinterpret_cast<f32x4*>(Sb + (size_t)i * DV);
-    f32x4 s = *p;
+    f32x4 s = __builtin_nontemporal_load(p);
     const float ki = sk[i], qi = sq[i];
     s = g * s + ki * vv;
-    *p = s;
+    __builtin_nontemporal_store(s, p);
     acc += qi * s;
   }
   red[rg][tid % TPR] = acc;
@@ -84,8 +89,9 @@ __global__ __launch_bounds__(256) void k_recurrent_step(const T* __restrict__ q,
 template <class T, int DK, int DV>
 static hipError_t run_step(int batch, int heads, const void* q, const void* k, const void* v, float* S, void* o,
                            float scale, int64_t pos, float base, const HeadTab& tab, hipStream_t st) {
+  constexpr int CS = DV >= 256 ? 2 : 1;
   TraceScope ts("k_recurrent_step", st);
-  hipLaunchKernelGGL((k_recurrent_step<T, DK, DV>), dim3(batch * heads), dim3(256), 0, st, (const T*)q,
+  hipLaunchKernelGGL((k_recurrent_step<T, DK, DV, CS>), dim3(batch * heads * CS), dim3(256), 0, st, (const T*)q,
                      (const T*)k, (const T*)v, S, (T*)o, heads, scale, pos, base, tab);
   return hipGetLastError();
 }

@@ -253,7 +253,7 @@ def swish(x):
 
 def msr_layer(X, WQ, WK, WV, WG, WO, gamma, heads, d_k, d_v, chunk=None,
               rope_base=10000.0, eps=1e-5, form="chunkwise", normalized=False,
-              scale=None):
+              scale=None, return_gn_var=False):
     """Gated multi-scale retention layer, [RN-zh] "門控多尺度 Retention", Eq. (8):
 
       Q^ = X W_Q, K^ = X W_K, V = X W_V (heads = contiguous column blocks)
@@ -266,6 +266,9 @@ def msr_layer(X, WQ, WK, WV, WG, WO, gamma, heads, d_k, d_v, chunk=None,
     W_O: [H*d_v, d_model].  ``form`` picks the retention form
     ("parallel", "recurrent", "chunkwise"); ``normalized=True`` uses the
     three score-normalisation factors instead (parallel form).
+    ``return_gn_var=True`` also returns the biased variance of every
+    (token, head) group entering the GroupNorm, [B, N, H] (how strongly eps
+    weighs on that group's normalisation).
     """
     X = _f64(X)
     B, N, _ = X.shape
@@ -287,7 +290,10 @@ def msr_layer(X, WQ, WK, WV, WG, WO, gamma, heads, d_k, d_v, chunk=None,
     else:
         raise ValueError(form)
     y = group_norm_heads(o, eps).reshape(B, N, heads * d_v)
-    return (swish(g) * y) @ _f64(WO)
+    out = (swish(g) * y) @ _f64(WO)
+    if return_gn_var:
+        return out, o.var(axis=-1)
+    return out
 
 
 # --------------------------------------------------------------------------

@@ -312,3 +312,13 @@ def test_error_measures():
     got[0, 0, 1, 0] += 0.05
     assert oracle.max_rel_err(got, ref) == pytest.approx(0.0005)
     assert oracle.max_rel_err_per_head(got, ref) == pytest.approx(0.05)
+
+
+def test_layer_gn_var_output_is_the_groupnorm_input_variance():
+    """return_gn_var returns the per-(token, head) variance that the
+    GroupNorm divides by: normalising by it reproduces a zero-mean, unit-
+    variance row (eps = 0)."""
+    X, W, g = _layer_case(29)
+    out, gv = oracle.msr_layer(X, *W, g, 3, 4, 4, chunk=3, eps=0.0, return_gn_var=True)
+    assert close(out, oracle.msr_layer(X, *W, g, 3, 4, 4, chunk=3, eps=0.0))
+    assert gv.shape == (1, 10, 3) and np.all(gv > 0)
