@@ -231,9 +231,24 @@ def bench_decode(steps_timed, warmup):
     return out
 
 
+def bench_copy(nbytes=1 << 30, reps=8):
+    """A plain device-to-device copy of a known size: the calibration run for
+    the FETCH_SIZE / WRITE_SIZE counters (each reads nbytes and writes nbytes
+    per launch)."""
+    import torch
+    src = torch.ones(nbytes // 4, device="cuda")
+    dst = torch.empty_like(src)
+    t = gpu_time(lambda: dst.copy_(src), reps, 2)
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"bytes_read": nbytes, "bytes_written": nbytes, "us": round(t * 1e6, 1),
+            "GB_per_s": round(2 * nbytes / t / 1e9, 1)}
+
+
 def cpu_baseline(budget_s=12.0):
     """The float64 oracle on a bounded sample of the headline workload: the
-    layer on one batch element at a time (2048 tokens) until budget_s."""
+    layer on one batch element (2048 tokens) at a time, cycling through the
+    batch, until at least budget_s seconds of CPU work are done."""
     import numpy as np
     import oracle
     import workloads
@@ -247,17 +262,18 @@ def cpu_baseline(budget_s=12.0):
     g = workloads.gammas(w.heads)
     t0 = time.perf_counter()
     done = 0
-    for b in range(w.batch):
+    while True:
+        b = done % w.batch
         oracle.msr_layer(X[b:b + 1], WQ, WK, WV, WG, WO, g, w.heads, w.d_k, w.d_v, w.chunk, rope_base=w.rope_base,
                          eps=1e-5)
         done += 1
-        if time.perf_counter() - t0 > budget_s:
+        if time.perf_counter() - t0 >= budget_s:
             break
     t = time.perf_counter() - t0
     return {"value": round(done * w.seqlen / t, 1), "unit": "tokens/s", "cores": threads,
             "host_cpus": len(os.sched_getaffinity(0)), "kind": "oracle",
-            "sample": f"{done} of {w.batch} batch elements ({done * w.seqlen} tokens) of the layer workload, "
-                      f"float64 numpy, {t:.1f} s"}
+            "sample": f"{done} batch-element passes ({done * w.seqlen} tokens, cycling over the {w.batch} "
+                      f"elements) of the layer workload, float64 numpy, {t:.1f} s"}
 
 
 def main():
@@ -328,6 +344,9 @@ def main():
         line["block"] = {"tokens_per_s": round(br["tokens_per_s"], 1), "mfma_frac": round(br["mfma_frac"], 4),
                          "ms_per_step": round(br["s_per_step"] * 1e3, 3), "tflops": round(br["tflops"], 1),
                          "kernels": br["kernels"]}
+    if "copy" in parts:
+        log("copy calibration")
+        line["copy_calibration"] = bench_copy()
     if "cpu" in parts:
         log("cpu baseline")
         line["cpu_baseline"] = cpu_baseline()

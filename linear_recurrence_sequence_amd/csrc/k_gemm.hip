@@ -18,8 +18,9 @@
 // held in the accumulation registers; a 128x128 wave tile reads 64 bytes of
 // LDS per clock at the matrix-core peak, a 128x64 one 96), 64-deep K slabs
 // double-buffered in LDS (2 x 72 KiB), the next slab's global loads in
-// flight during the current slab's matrix-core work.  f32: 128x128 tile,
-// 4 waves, 32-deep slabs.
+// flight during the current slab's matrix-core work, fragment reads one k16
+// step ahead, interleaved with the MFMAs by explicit scheduling groups.
+// f32: 128x128 tile, 4 waves, 32-deep slabs.
 #include "msr_launch.h"
 
 namespace msr {
@@ -113,14 +114,14 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm(const T* __restrict__ A, 
 #pragma unroll
     for (int u = 0; u < AU; ++u) {
       const int idx = tid + NT * u;
-      if (idx >= AUNITS) break;
+      if (AUNITS % NT != 0 && idx >= AUNITS) break;
       const int row = idx / (BK / 8), c8 = idx % (BK / 8);
       store_row8(sA + row * LDA + 8 * c8, ra[u]);
     }
 #pragma unroll
     for (int u = 0; u < BU; ++u) {
       const int idx = tid + NT * u;
-      if (idx >= BUNITS) break;
+      if (BUNITS % NT != 0 && idx >= BUNITS) break;
       const int row = idx / (BN / 8), c8 = idx % (BN / 8);
       store_row8(sB + row * LDB + 8 * c8, rb[u]);
     }
@@ -136,24 +137,83 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm(const T* __restrict__ A, 
   gload(0);
   sstore(0);
   __syncthreads();
-  for (int kt = 0; kt < KT; ++kt) {
-    if (kt + 1 < KT) gload((kt + 1) * BK);
-    const T* sA = smem[kt & 1];
+  auto lfr = [&](const T* sA, int s, Frag<T>* af, Frag<T>* bfr) {
     const T* sB = sA + BM * LDA;
 #pragma unroll
-    for (int s = 0; s < BK / 16; ++s) {
-      Frag<T> af[TM], bfr[TN];
+    for (int i = 0; i < TM; ++i) af[i] = load_frag(sA + (wm * (BM / WM) + 32 * i + lr) * LDA + 16 * s + 8 * hh);
 #pragma unroll
-      for (int i = 0; i < TM; ++i) af[i] = load_frag(sA + (wm * (BM / WM) + 32 * i + lr) * LDA + 16 * s + 8 * hh);
+    for (int j = 0; j < TN; ++j) bfr[j] = load_frag_rm<KMAP_CONTIG>(sB + 16 * s * LDB + wn * (BN / WN) + 32 * j, LDB);
+  };
+  auto mm = [&](const Frag<T>* af, const Frag<T>* bfr) {
 #pragma unroll
-      for (int j = 0; j < TN; ++j) bfr[j] = load_frag_rm<KMAP_CONTIG>(sB + 16 * s * LDB + wn * (BN / WN) + 32 * j, LDB);
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
+      for (int j = 0; j < TN; ++j) mma16(acc[i][j], af[i], bfr[j]);
+  };
+  if constexpr (sizeof(T) == 2 && BK == 64 && TM == 4 && TN == 4 && AU == 8 && BU == 8) {
+    // Software pipeline with an explicit instruction interleave.  With one
+    // wave per SIMD nothing else hides LDS or global latency, and left alone
+    // the compiler waits on every fragment read right before its matrix-core
+    // instructions.  Fragments are double-buffered in registers (set s & 1
+    // holds k16 step s); each step issues the next step's 12 LDS reads (4 A +
+    // 8 transposing B) between its 16 MFMAs, step 0 also the next slab's 16
+    // global loads, step 3 the 16 LDS writes of that slab into the other
+    // buffer.  sched_barrier fences keep each step's group in place.
+    Frag<T> af[2][TM], bfr[2][TN];
+    for (int kt = 0; kt < KT; ++kt) {
+      const T* sA = smem[kt & 1];
+      lfr(sA, 0, af[0], bfr[0]);
+      __builtin_amdgcn_sched_barrier(0);
+      gload(min(kt + 1, KT - 1) * BK);        // last slab: a harmless reload
+      lfr(sA, 1, af[1], bfr[1]);
+      mm(af[0], bfr[0]);
 #pragma unroll
-        for (int j = 0; j < TN; ++j) mma16(acc[i][j], af[i], bfr[j]);
+      for (int i = 0; i < 12; ++i) {
+        __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(SG_VMEM_READ, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(SG_VMEM_READ, 1, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int s = 1; s < 3; ++s) {
+        lfr(sA, s + 1, af[(s + 1) & 1], bfr[(s + 1) & 1]);
+        mm(af[s & 1], bfr[s & 1]);
+#pragma unroll
+        for (int i = 0; i < 12; ++i) {
+          __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(SG_MFMA, 4, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      mm(af[1], bfr[1]);
+      sstore((kt + 1) & 1);                    // last slab: the idle buffer
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(SG_DS_WRITE, 1, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();
     }
-    if (kt + 1 < KT) sstore((kt + 1) & 1);
-    __syncthreads();
+  } else {
+    for (int kt = 0; kt < KT; ++kt) {
+      if (kt + 1 < KT) gload((kt + 1) * BK);
+      const T* sA = smem[kt & 1];
+#pragma unroll
+      for (int s = 0; s < BK / 16; ++s) {
+        Frag<T> af[TM], bfr[TN];
+        lfr(sA, s, af, bfr);
+        mm(af, bfr);
+      }
+      if (kt + 1 < KT) sstore((kt + 1) & 1);
+      __syncthreads();
+    }
   }
 
   // Epilogue through LDS (free after the main loop): each wave stages 32 of

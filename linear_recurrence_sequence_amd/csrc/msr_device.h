@@ -25,6 +25,10 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kMaxHeads = 128;
 
+// Instruction classes of __builtin_amdgcn_sched_group_barrier (LLVM AMDGPU
+// scheduling-group masks).
+enum : int { SG_MFMA = 0x008, SG_VMEM_READ = 0x020, SG_DS_READ = 0x100, SG_DS_WRITE = 0x200 };
+
 // Per-head decay constants, computed on the host in double precision and
 // passed by value: log2(gamma_h) (-inf when gamma_h == 0), gamma_h^chunk,
 // gamma_h^L of the last (possibly short) chunk, and gamma_h itself.
