@@ -485,8 +485,426 @@ __global__ __launch_bounds__(64 * NW) void k_chunk_out(
 }
 
 // ---------------------------------------------------------------------------
+// k_chunk_dl: the bf16 output kernel with direct-to-LDS staging.
+// One workgroup per (batch, head, chunk, 128-row tile), 4 waves of 32 query
+// rows; each wave keeps its Q rows in registers and accumulates the full
+// d_v width of its outputs.  The stages -- d_k slabs of R_{i-1}, then
+// 32-key blocks of K and V up to the tile's last row -- stream through a
+// ring of NS LDS slots filled by direct copies with NS - 1 stages in
+// flight, so global latency overlaps the matrix-core work.
+// Key blocks are software-pipelined across stages: while a wave computes
+// S^T = K Q^T of block j it runs P_{j-1} V_{j-1} of the previous block, two
+// independent matrix-core streams; so key stage j carries K of block j and
+// V of block j - 1, and one more stage carries the last V.  Fragment reads
+// run two steps ahead.
+// LDS tiles are padded, in units of 16-byte slots, so that every fragment
+// address is one base register plus an immediate offset and reads are
+// free of bank conflicts: K and R^T rows (read row-wise, 16 rows at a time
+// at the same chunk) get an odd stride in slots; V rows (read with the
+// transposing read, 4 rows x 4 chunks per half-wave) a stride of 4 slots
+// mod 16.  A direct copy fills 64 consecutive slots, so lanes that land on
+// a pad slot copy a harmless duplicate.
+// The two tiles of a chunk are dispatched to the same XCD (block ids 8
+// apart) so the second reads K and V from that XCD's L2.
+// ---------------------------------------------------------------------------
+template <int DK, int DV>
+struct DlCfg {
+  static constexpr int NT = 256, RT = 128;
+  static constexpr int KB = 32;                                   // keys per KV stage
+  static constexpr int SK = DV <= 256 ? (DK < 64 ? DK : 64) : 32; // d_k columns per R stage
+  static constexpr int CPK = DK / 8, CPV = DV / 8, CPR = SK / 8;  // 16-byte chunks per row
+  static constexpr int SPK = CPK + 1, SPV = CPV + 4, SPR = CPR + 1; // padded strides (slots)
+  static constexpr int r64(int x) { return (x + 63) / 64 * 64; }
+  static constexpr int r4(int x) { return (x + 3) / 4 * 4; }
+  static constexpr int KSL = r64(KB * SPK), VSL = r64(KB * SPV), RSL = r64(DV * SPR);  // slots
+  static constexpr int IK = KSL / 64, IKV = r4((KSL + VSL) / 64), IR = r4(RSL / 64);    // 1 KiB copies
+  static constexpr int LPW_KV = IKV / 4, LPW_R = IR / 4;          // copies per wave per stage
+  static constexpr int STG = (IKV > IR ? IKV : IR) * 512;         // elements per ring slot
+  static constexpr int NS = (150 * 1024) / (STG * 2) >= 4 ? 4 : (150 * 1024) / (STG * 2);
+  static constexpr int AHEAD = NS - 1;
+  static_assert(NS == 4 && AHEAD == 3, "four ring slots, three stages in flight");
+  static_assert(LPW_KV == LPW_R, "equal copy counts per stage");
+};
+
+template <int DK, int DV, bool STATE, bool GN>
+__global__ __launch_bounds__(256) void k_chunk_dl(
+    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V, int64_t ldq, int64_t ldk,
+    int64_t ldv, const bf16* __restrict__ Rx, int has_sin, const bf16* __restrict__ G, int64_t ldg,
+    bf16* __restrict__ O, int64_t ldo, int BH, int N, int H, int chunk, int NC, int TPC, float scale, float eps,
+    HeadTab tab) {
+  using C = DlCfg<DK, DV>;
+  constexpr int KB = C::KB, SK = C::SK, NS = C::NS, AHEAD = C::AHEAD, RT = C::RT;
+  constexpr int CPK = C::CPK, CPV = C::CPV, CPR = C::CPR;
+  __shared__ __attribute__((aligned(1024))) bf16 smem[NS * C::STG];
+  (void)CPK; (void)CPV; (void)CPR;
+
+  const int tid = threadIdx.x, lane = tid & 63, lr = lane & 31, hh = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // block id -> (chunk unit, tile): units 8 apart in block id share an XCD;
+  // a unit's tiles are consecutive groups of 8, heaviest first.
+  const int U = NC * BH;
+  const int xg = blockIdx.x & 7, yg = blockIdx.x >> 3;
+  const int li = TPC - 1 - yg % TPC;
+  const int unit = (yg / TPC) * 8 + xg;
+  if (unit >= U) return;
+  const int ci = unit / BH, bh = unit % BH;
+  const int h = bh % H, b = bh / H;
+  const int c0 = ci * chunk;
+  const int r0 = c0 + li * RT;
+  if (r0 >= N) return;
+  const int q0 = r0 + 32 * wave;
+  const bool active = q0 < N;                      // wave-uniform
+  const float lg2 = tab.lg2[h];
+  const size_t tokb = (size_t)b * N;
+
+  // ---- stage list: nR slabs of R_{i-1}, then nKV key blocks ----
+  const bool inter = STATE && (ci > 0 || has_sin);
+  const int nR = inter ? DK / SK : 0;
+  const int kend = min(r0 + RT, N);
+  const int nKV = (kend - c0 + KB - 1) / KB;
+  const int nst = nR + nKV + 1;                    // key stage j holds K of block j and V of block j - 1
+  const bf16* Rt = STATE ? Rx + ((size_t)bh * NC + ci) * DV * DK : nullptr;
+  const bf16* Kh = K + (size_t)h * DK + tokb * ldk;
+  const bf16* Vh = V + (size_t)h * DV + tokb * ldv;
+  const int ldk32 = (int)ldk, ldv32 = (int)ldv;
+  auto slot = [&](int idx) { return smem + (idx % NS) * C::STG; };
+
+  // Copies of stage idx by this wave: instruction ii fills slots
+  // 64 ii .. 64 ii + 63 of the slot; slot u of a tile is row u / stride,
+  // chunk u % stride (pad slots and slots past the tile copy chunk 0 of row
+  // 0).  Keys past the end are clamped to the last row: they are in the
+  // future of every stored query, so they get weight 0.
+  auto kv_off = [&](int t, int lim) -> uint32_t {
+    const int ii = wave * C::LPW_KV + t;
+    if (ii < C::IK) {
+      const int u = ii * 64 + lane, row = u / C::SPK, c = u % C::SPK;
+      return row < KB && c < CPK ? (uint32_t)((min(row, lim) * ldk32 + 8 * c) * 2) : 0u;
+    }
+    const int u = (ii - C::IK) * 64 + lane, row = u / C::SPV, c = u % C::SPV;
+    return row < KB && c < CPV ? (uint32_t)((min(row, lim) * ldv32 + 8 * c) * 2) : 0u;
+  };
+  // Per-lane byte offsets of this wave's copies: they do not depend on the
+  // stage, so they are computed once (only the sequence's last, partial key
+  // block needs the clamp, computed when it comes).
+  uint32_t okv[C::LPW_KV], orr[C::LPW_R];
+#pragma unroll
+  for (int t = 0; t < C::LPW_KV; ++t) okv[t] = kv_off(t, KB);
+#pragma unroll
+  for (int t = 0; t < C::LPW_R; ++t) {
+    const int u = (wave * C::LPW_R + t) * 64 + lane, row = u / C::SPR, c = u % C::SPR;
+    orr[t] = row < DV && c < CPR ? (uint32_t)((row * DK + 8 * c) * 2) : 0u;
+  }
+  // The copies of one stage: wave-uniform source bases and LDS slot, and
+  // this lane's offsets.  Stages past the last one copy the last stage
+  // again into the free slot (unused), so that every stage issues the same
+  // number of copies and the waits are fixed.
+  struct Cp { const bf16* src[2]; bf16* dst; uint32_t off[C::LPW_KV]; };
+  auto prep = [&](int g, Cp& c) {
+    const int idx = min(g, nst - 1);
+    c.dst = slot(g) + wave * C::LPW_KV * 512;
+    if (idx < nR) {
+      c.src[0] = c.src[1] = Rt + idx * SK;
+#pragma unroll
+      for (int t = 0; t < C::LPW_KV; ++t) c.off[t] = orr[t];
+    } else {
+      // K of block j and V of block j - 1 (the first stage copies V of
+      // block 0 and the last K of block nKV - 1 again: unused)
+      const int j = idx - nR;
+      const int kbk = c0 + min(j, nKV - 1) * KB, kbv = c0 + max(j - 1, 0) * KB;
+      c.src[0] = Kh + (size_t)kbk * ldk;
+      c.src[1] = Vh + (size_t)kbv * ldv;
+      if (kbk + KB <= N) {                       // no clamp needed (V's block is never later than K's)
+#pragma unroll
+        for (int t = 0; t < C::LPW_KV; ++t) c.off[t] = okv[t];
+      } else {
+#pragma unroll
+        for (int t = 0; t < C::LPW_KV; ++t)
+          c.off[t] = kv_off(t, N - 1 - (wave * C::LPW_KV + t < C::IK ? kbk : kbv));
+      }
+    }
+  };
+  // copy t of the prepared stage (K part for the first IK copies of a key stage)
+  auto cp = [&](const Cp& c, int t) {
+    const int ii = wave * C::LPW_KV + t;         // wave-uniform
+    copy16_to_lds(ii < C::IK ? c.src[0] : c.src[1], c.off[t], lds_addr(c.dst + t * 512));
+  };
+  {
+    Cp c;
+#pragma unroll
+    for (int a = 0; a < AHEAD; ++a) {
+      prep(a, c);
+#pragma unroll
+      for (int t = 0; t < C::LPW_KV; ++t) cp(c, t);
+    }
+  }
+  // Q rows as fragments (column 16 s + 8 hh + t of query row q0 + lr; rows
+  // past the end clamped, never stored).
+  Frag<bf16> qf[DK / 16];
+  {
+    const bf16* p = Q + (tokb + min(q0 + lr, N - 1)) * ldq + (size_t)h * DK + 8 * hh;
+#pragma unroll
+    for (int s = 0; s < DK / 16; ++s) qf[s] = load_frag(p + 16 * s);
+  }
+
+  f32x16 acc[DV / 32];
+#pragma unroll
+  for (int j = 0; j < DV / 32; ++j) acc[j] = (f32x16){};
+
+  // ---- Q R_{i-1} slab: acc[j] += Q[:, slab] R^T[32 j .., slab]^T; the rows
+  // are scaled by scale * xi once all slabs are in (they come first) ----
+  constexpr int NJ = DV / 32;
+  auto compute_R = [&](const bf16* sR, const Frag<bf16>* qs, const Cp& cn) {
+    constexpr int T = (SK / 16) * NJ;
+    static_assert(T >= C::LPW_KV, "one copy per step at most");
+    const bf16* rb0 = sR + lr * (8 * C::SPR) + 8 * hh;
+    auto rd = [&](int t) {
+      const int s = t / NJ, j = t % NJ;            // row 32 j + lr, chunk 2 s + hh
+      return load_frag(rb0 + j * (32 * 8 * C::SPR) + 16 * s);
+    };
+    Frag<bf16> rb[3];
+    rb[0] = rd(0);
+    if (T > 1) rb[1] = rd(1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      if (t + 2 < T) rb[(t + 2) % 3] = rd(t + 2);
+      mma16(acc[t % NJ], qs[t / NJ], rb[t % 3]);
+      if (t < C::LPW_KV) cp(cn, t);              // next stages' copies between the MFMAs
+    }
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+      if (t + 2 < T) __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // acc rows (register r: query q0 + kk(r)) times scale * xi_t = scale * gamma^(t + 1)
+  auto scale_rows_xi = [&]() {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float x = scale * gpow(q0 - c0 + 8 * (r >> 2) + 4 * hh + (r & 3) + 1, lg2);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) acc[j][r] *= x;
+    }
+  };
+
+  // ---- key blocks ----
+  // S^T = K Q^T: lane = query q0 + lr, register r = key kb + kk(r).
+  // P V uses the accumulator as the A operand; V fragments are read in that
+  // key order (transposing read).
+  constexpr int NSS = DK / 16, NPV = DV / 16, TKV = NSS > NPV ? NSS : NPV;
+  const int g4 = lane >> 4, i4 = lane & 15, cq = g4 & 1, jj4 = i4 >> 2, q4 = i4 & 3;
+  const int kofs = lr * (8 * C::SPK) + 8 * hh;    // K: row lr, chunk 2 t + hh
+  const int vofs = (4 * hh + jj4) * (8 * C::SPV) + 8 * (2 * cq + (q4 >> 1)) + 4 * (q4 & 1);
+  auto rdK = [&](const bf16* sK, int t) { return load_frag(sK + kofs + 16 * t); };
+  // V: rows 16 s2 + 8 pp + 4 hh + jj4, chunk 4 j + 2 cq + q4 / 2 (+ 4 elements for odd q4)
+  auto rdV = [&](const bf16* sV, int t) {
+    const int j = t >> 1, s2 = t & 1;
+    Frag<bf16> f;
+#pragma unroll
+    for (int pp = 0; pp < 2; ++pp) {
+      const bf16x4 r4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+          (__attribute__((address_space(3))) bf16x4*)(const lds_char*)(sV + vofs + (16 * s2 + 8 * pp) * (8 * C::SPV) +
+                                                                        32 * j));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) f.v[4 * pp + e] = r4[e];
+    }
+    return f;
+  };
+  // One pipelined key step: S^T of the block in slot sK and P V of the
+  // pending block (P in pa, V in slot sVp), then P of the new block.  Every
+  // wave runs both matrix-core streams on every step -- P is zero for a
+  // block in the wave's future and when nothing is pending -- so there is a
+  // single code path for the accumulators; the waves meet at every stage
+  // and each has its own SIMD, so the idle ones cost no time.
+  Frag<bf16> pa[2];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) pa[0].v[e] = pa[1].v[e] = (bf16)0.0f;
+  float wm[16];                                    // gamma^(27 - m_r), m_r = 8 (r/4) + r%4 (wave-uniform)
+#pragma unroll
+  for (int r = 0; r < 16; ++r)
+    wm[r] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(gpow(27 - (8 * (r >> 2) + (r & 3)), lg2))));
+  static_assert(NSS >= 2 && NPV >= 4, "pipelined key step");
+  static_assert(NSS >= C::LPW_KV, "one copy per step at most");
+  auto kv_step = [&](const bf16* sK, const bf16* sVp, int kb, bool now, const Cp& cn) {
+    constexpr int H1 = NPV / 2;                    // P V steps in region A
+    f32x16 st = (f32x16){};
+    Frag<bf16> kq[3], vq[3];
+    kq[0] = rdK(sK, 0);
+    kq[1] = rdK(sK, 1);
+    vq[0] = rdV(sVp, 0);
+    vq[1] = rdV(sVp, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    // region A: every S^T step, the first half of P V, reads two steps ahead
+#pragma unroll
+    for (int t = 0; t < NSS; ++t) {
+      if (t + 2 < NSS) kq[(t + 2) % 3] = rdK(sK, t + 2);
+      mma16(st, kq[t % 3], qf[t]);
+      if (t < C::LPW_KV) cp(cn, t);              // next stages' copies between the MFMAs
+      if (t < H1) {
+        if (t + 2 < NPV) vq[(t + 2) % 3] = rdV(sVp, t + 2);
+        mma16(acc[t >> 1], pa[t & 1], vq[t % 3]);
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < NSS; ++t) {
+      __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+      if (t + 2 < NSS) __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
+      if (t < H1) {
+        if (t + 2 < NPV) __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // region B: the rest of P V with the decay of the new block between its
+    // MFMAs.  D[query, key] = gamma^(query - key) for key <= query, with
+    // query - key = n0 - m_r; off the diagonal block n0 >= 28 and
+    // gamma^(n0 - m_r) = u * w_r, u = gamma^(n0 - 27), w_r = gamma^(27 - m_r)
+    // (both exponents >= 0).
+    const int n0 = q0 - kb + lr - 4 * hh;
+    const float u = now ? scale * gpow(n0 - 27, lg2) : 0.0f;
+    float p[16];
+#pragma unroll
+    for (int t = H1; t < NPV; ++t) {
+      if (t + 2 < NPV) vq[(t + 2) % 3] = rdV(sVp, t + 2);
+      mma16(acc[t >> 1], pa[t & 1], vq[t % 3]);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) p[r] = st[r] * (u * wm[r]);
+#pragma unroll
+    for (int t = H1; t < NPV; ++t) {
+      __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+      if (t + 2 < NPV) __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(SG_VALU, 6, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (kb == q0) {                                // the diagonal block: key <= query only
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int n = n0 - (8 * (r >> 2) + (r & 3));
+        float e = exp2f((float)max(n, 0) * lg2);
+        e = n == 0 ? 1.0f : e;
+        p[r] = (now && n >= 0) ? st[r] * scale * e : 0.0f;
+      }
+    }
+    pa[0] = frag_from<bf16>(p);
+    pa[1] = frag_from<bf16>(p + 8);
+  };
+
+  // Make the compiler retire the Q loads here (together with the copies
+  // issued before them, which complete first): a wait for them left inside
+  // the loop would drain the copies in flight on every stage.
+#pragma unroll
+  for (int s = 0; s < DK / 16; ++s) asm volatile("" ::"v"(qf[s].v));
+  // wait for stage idx's copies, then prepare those of stage idx + AHEAD
+  // into the slot of stage idx - 1, which every wave is past; they are
+  // issued between the MFMAs of stage idx
+  // (the copies of the two stages after idx may stay in flight)
+  Cp cn;
+  auto advance = [&](int idx) {
+    copies_wait_barrier<2 * C::LPW_KV>();
+    prep(idx + AHEAD, cn);
+  };
+  // R slabs, then the rows scaled by scale * xi (outside both loops: VALU
+  // work on the accumulators inside a loop would keep them out of the
+  // accumulation registers there), then the key stages.
+  int idx = 0;
+  for (; idx < nR; ++idx) {
+    advance(idx);
+    // the slab's Q fragments, picked with static indices only (a dynamic
+    // index would move qf to scratch memory)
+    Frag<bf16> qs[SK / 16];
+#pragma unroll
+    for (int s2 = 0; s2 < SK / 16; ++s2) qs[s2] = qf[s2];
+    static_for<DK / SK>([&](auto sl) {
+      if (decltype(sl)::value > 0 && idx == decltype(sl)::value) {
+#pragma unroll
+        for (int s2 = 0; s2 < SK / 16; ++s2) qs[s2] = qf[decltype(sl)::value * (SK / 16) + s2];
+      }
+    });
+    compute_R(slot(idx), qs, cn);
+  }
+  if (nR > 0) scale_rows_xi();
+  for (; idx < nst; ++idx) {
+    advance(idx);
+    const int j = idx - nR;
+    const int kb = c0 + j * KB;
+    const bool now = j < nKV && active && kb <= q0;   // wave-uniform
+    // S of block j (discarded when not now) and P_{j-1} V_{j-1} (P = 0 on
+    // the first key stage)
+    kv_step(slot(idx), slot(idx) + C::KSL * 8, kb, now, cn);
+  }
+  copies_wait_barrier<0>();                        // no copy may land after the workgroup ends
+
+  // ---- epilogue: lane owns column 32 j + lr of rows q0 + 8 (r/4) + 4 hh + r%4 ----
+  if (!active) return;
+  if constexpr (GN) {
+    float mu[16], rs[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float sum = 0.f;
+#pragma unroll
+      for (int j = 0; j < DV / 32; ++j) sum += acc[j][r];
+      mu[r] = half_wave_sum(sum) * (1.0f / DV);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float sum = 0.f;
+#pragma unroll
+      for (int j = 0; j < DV / 32; ++j) {
+        const float dlt = acc[j][r] - mu[r];
+        sum += dlt * dlt;
+      }
+      rs[r] = rsqrtf(half_wave_sum(sum) * (1.0f / DV) + eps);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int qq = q0 + 8 * (r >> 2) + 4 * hh + (r & 3);
+      if (qq < N) {
+        const bf16* gp = G + (tokb + qq) * ldg + (size_t)h * DV + lr;
+        bf16* op = O + (tokb + qq) * ldo + (size_t)h * DV + lr;
+#pragma unroll
+        for (int j = 0; j < DV / 32; ++j) {
+          const float gv = (float)gp[32 * j];
+          const float sw = gv / (1.0f + __expf(-gv));
+          op[32 * j] = (bf16)(sw * (acc[j][r] - mu[r]) * rs[r]);
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int qq = q0 + 8 * (r >> 2) + 4 * hh + (r & 3);
+      if (qq < N) {
+        bf16* op = O + (tokb + qq) * ldo + (size_t)h * DV + lr;
+#pragma unroll
+        for (int j = 0; j < DV / 32; ++j) op[32 * j] = (bf16)acc[j][r];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Host launchers
 // ---------------------------------------------------------------------------
+template <int DK, int DV, bool STATE>
+static void launch_dl(const ChunkArgs& a, int chunk, int NC, int TPC, int has_sin, const HeadTab& tab,
+                      hipStream_t st) {
+  const int BH = a.batch * a.heads;
+  const int U = NC * BH;
+  dim3 grid(((U + 7) / 8) * 8 * TPC);
+  if (a.fuse_gn_gate)
+    hipLaunchKernelGGL((k_chunk_dl<DK, DV, STATE, true>), grid, dim3(256), 0, st, (const bf16*)a.Q,
+                       (const bf16*)a.K, (const bf16*)a.V, a.ldq, a.ldk, a.ldv, (const bf16*)a.Rx, has_sin,
+                       (const bf16*)a.G, a.ldg, (bf16*)a.O, a.ldo, BH, a.seqlen, a.heads, chunk, NC, TPC, a.scale,
+                       a.eps, tab);
+  else
+    hipLaunchKernelGGL((k_chunk_dl<DK, DV, STATE, false>), grid, dim3(256), 0, st, (const bf16*)a.Q,
+                       (const bf16*)a.K, (const bf16*)a.V, a.ldq, a.ldk, a.ldv, (const bf16*)a.Rx, has_sin,
+                       (const bf16*)nullptr, (int64_t)0, (bf16*)a.O, a.ldo, BH, a.seqlen, a.heads, chunk, NC, TPC,
+                       a.scale, a.eps, tab);
+}
+
 template <class T, int DK, int DV, int NW, bool STATE>
 static void launch_out(const ChunkArgs& a, int chunk, int NC, int TPC, int has_sin, const HeadTab& tab,
                        hipStream_t st) {
@@ -524,6 +942,12 @@ static hipError_t run_chunkwise(const ChunkArgs& a, const HeadTab& tab, hipStrea
   {
     TraceScope ts("k_chunk_out", st);
     const int has_sin = a.S_in != nullptr;
+    if constexpr (sizeof(T) == 2 && DV <= 256) {
+      if (Cn % 128 == 0) {
+        launch_dl<DK, DV, true>(a, Cn, NC, Cn / 128, has_sin, tab, st);
+        return hipGetLastError();
+      }
+    }
     if (Cn % 128 == 0)
       launch_out<T, DK, DV, 4, true>(a, Cn, NC, Cn / 128, has_sin, tab, st);
     else
@@ -536,7 +960,10 @@ template <class T, int DK, int DV>
 static hipError_t run_parallel(const ChunkArgs& a, const HeadTab& tab, hipStream_t st) {
   const int TPC = (a.seqlen + 127) / 128;
   TraceScope ts("k_chunk_out", st);
-  launch_out<T, DK, DV, 4, false>(a, TPC * 128, 1, TPC, 0, tab, st);
+  if constexpr (sizeof(T) == 2 && DV <= 256)
+    launch_dl<DK, DV, false>(a, TPC * 128, 1, TPC, 0, tab, st);
+  else
+    launch_out<T, DK, DV, 4, false>(a, TPC * 128, 1, TPC, 0, tab, st);
   return hipGetLastError();
 }
 

@@ -13,6 +13,8 @@
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <type_traits>
+#include <utility>
 
 namespace msr {
 
@@ -25,9 +27,20 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kMaxHeads = 128;
 
+// f(std::integral_constant<int, i>{}) for i = 0 .. N-1: a loop whose index
+// is a compile-time constant in the body.
+template <int N, class F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl<N>(f, std::make_integer_sequence<int, N>{});
+}
+
 // Instruction classes of __builtin_amdgcn_sched_group_barrier (LLVM AMDGPU
 // scheduling-group masks).
-enum : int { SG_MFMA = 0x008, SG_VMEM_READ = 0x020, SG_DS_READ = 0x100, SG_DS_WRITE = 0x200 };
+enum : int { SG_VALU = 0x002, SG_MFMA = 0x008, SG_VMEM_READ = 0x020, SG_DS_READ = 0x100, SG_DS_WRITE = 0x200 };
 
 // Per-head decay constants, computed on the host in double precision and
 // passed by value: log2(gamma_h) (-inf when gamma_h == 0), gamma_h^chunk,
@@ -208,6 +221,39 @@ __device__ __forceinline__ Frag<float> load_frag_rm(const float* tile, int ld) {
 // 48 banks mod 64.
 template <class T> constexpr int rm_pad() { return sizeof(T) == 2 ? 32 : 4; }
 
+// ---------------------------------------------------------------------------
+// Direct global -> LDS copies (gfx950 global_load_lds_dwordx4).  Each lane
+// copies 16 bytes from gbase + its own byte offset to LDS address
+// lds + 16 * lane, so one instruction fills 1 KiB of LDS and no register
+// holds the data while it is in flight.  gbase and lds must be wave-uniform.
+// The copy is issued from inline asm: the compiler's own wait insertion
+// does not model these LDS writes precisely and would otherwise wait for
+// every copy in flight before each LDS read.  In exchange the caller waits
+// for its copies itself (copies_wait_barrier) and, because vector-memory
+// loads complete in issue order, counts every vector load it issued after
+// the copies it waits for.  The copy asm carries no memory clobber, so the
+// compiler may move LDS reads across it: callers never copy into an LDS
+// region that is being read, and the ordering that matters -- copies into
+// a region only after every wave has left it, reads only after the copies
+// landed -- goes through copies_wait_barrier, which is a compiler memory
+// barrier.
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) char lds_char;
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const lds_char*)p;
+}
+
+__device__ __forceinline__ void copy16_to_lds(const void* gbase, uint32_t byte_off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(byte_off), "s"(gbase), "s"(lds) : "m0");
+}
+
+// Wait until at most N vector-memory loads of this wave are outstanding and
+// all its LDS operations are done, then the workgroup barrier.
+template <int N>
+__device__ __forceinline__ void copies_wait_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
 // Butterfly sum over the 32 lanes of one half-wave (xor masks < 32 stay
 // inside the half).
 __device__ __forceinline__ float half_wave_sum(float x) {
