@@ -43,6 +43,35 @@ PEAK_F32_MFMA = 157.3e12
 PEAK_HBM = 8.0e12                      # bytes/s
 
 
+# HBM bytes per launch of each kernel, from two rocprofv3 --pmc passes
+# (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) over `bench.py --only <part>`,
+# scaled by what the same counters read for a 1 GiB device-to-device copy
+# (FETCH_SIZE x 2, WRITE_SIZE x 1).  Each figure holds only for the sources
+# it was taken with: the sha256 prefix of those files is recorded, and a
+# kernel whose sources have changed since reports null.
+MEASURED_TRAFFIC = {  # (workload, kernel): (bytes per launch, sources, sha256[:16])
+    ("layer_bf16_b8_n2048", "k_gemm"): (7.059e+08, ('k_gemm.hip', 'msr_device.h'), "06911803f94c0ae9"),
+    ("layer_bf16_b8_n2048", "k_chunk_out"): (3.951e+08, ('k_chunk.hip', 'msr_device.h'), "5732c5dbbd54faac"),
+    ("layer_bf16_b8_n2048", "k_chunk_state"): (3.901e+08, ('k_chunk.hip', 'msr_device.h'), "5732c5dbbd54faac"),
+    ("layer_bf16_b8_n2048", "k_chunk_scan"): (2.032e+08, ('k_chunk.hip', 'msr_device.h'), "5732c5dbbd54faac"),
+    ("decode_fp32_b128_h16", "k_recurrent_step"): (1.086e+09, ('k_recurrent.hip', 'msr_device.h'), "74c6c3209346c23f"),
+}
+CSRC = os.path.join(ROOT, "linear_recurrence_sequence_amd", "csrc")
+
+
+def measured_traffic(workload, kernel):
+    import hashlib
+    e = MEASURED_TRAFFIC.get((workload, kernel))
+    if e is None:
+        return None
+    nbytes, files, digest = e
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return round(nbytes) if h.hexdigest()[:16] == digest else None
+
+
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
@@ -77,9 +106,10 @@ def traced(fn, steps):
     return {k: (ms * 1e-3, n) for k, (ms, n) in tot.items()}
 
 
-def roof(name, work_per_step, bound, trace, steps, launches_per_step=None):
+def roof(name, work_per_step, bound, trace, steps, launches_per_step=None, workload=None):
     """Roofline entry for one kernel: work_per_step is flops (mfma) or bytes
-    (hbm) of algorithmic work in one step."""
+    (hbm) of algorithmic work in one step; traffic = measured HBM bytes per
+    launch (see MEASURED_TRAFFIC) or None."""
     t, n = trace[name]
     per_launch_t = t / n
     lps = n / steps if launches_per_step is None else launches_per_step
@@ -88,7 +118,7 @@ def roof(name, work_per_step, bound, trace, steps, launches_per_step=None):
     scale = 1e12 if bound == "mfma" else 1e9
     ach = per_launch_work / per_launch_t
     return {"kernel": name, "bound": bound, "achieved": round(ach / scale, 2), "peak": round(peak / scale, 1),
-            "unit": unit, "frac": round(ach / peak, 4), "traffic": None,
+            "unit": unit, "frac": round(ach / peak, 4), "traffic": measured_traffic(workload, name),
             "avg_launch_us": round(per_launch_t * 1e6, 2), "launches_per_step": lps}
 
 
@@ -141,7 +171,7 @@ def bench_layer(w, steps, warmup, device_inputs=False):
         "k_chunk_scan": (B * H * nc * dk * dv * (4 + es), "hbm"),
         "k_rope_table": (N * dk // 2 * 8, "hbm"),
     }
-    kern = {n: roof(n, wk, bd, tr, steps) for n, (wk, bd) in work.items() if n in tr}
+    kern = {n: roof(n, wk, bd, tr, steps, workload=w.name) for n, (wk, bd) in work.items() if n in tr}
     del X, WQ, WK, WV, WG, WO, out, ws
     torch.cuda.empty_cache()
     res = {"s_per_step": t, "tokens_per_s": B * N / t, "flops_per_step": proj + core,
@@ -222,7 +252,7 @@ def bench_decode(steps_timed, warmup):
         if ctx == w.context:
             tr = traced(lambda: msr.msr_recurrent_step(qs[0], ks[0], vs[0], S, g, pos=ctx + n, rope_base=w.rope_base,
                                                        qk_scale=s, o=o), min(n, 128))
-            entry["roofline"] = roof("k_recurrent_step", byts, "hbm", tr, min(n, 128))
+            entry["roofline"] = roof("k_recurrent_step", byts, "hbm", tr, min(n, 128), workload=w.name)
         out[str(ctx)] = entry
         del S, qs, ks, vs, o
         torch.cuda.empty_cache()
