@@ -168,7 +168,7 @@ def bench_layer(w, steps, warmup, device_inputs=False):
         "k_gemm": (proj, "mfma"),
         "k_chunk_out": (B * N * H * (C * (dk + dv) + 2 * dk * dv), "mfma"),
         "k_chunk_state": (B * N * H * 2 * dk * dv, "mfma"),
-        "k_chunk_scan": (B * H * nc * dk * dv * (4 + es), "hbm"),
+        "k_chunk_scan": (B * H * nc * dk * dv * 2 * es, "hbm"),     # read dR_i, write R_{i-1} (element type)
         "k_rope_table": (N * dk // 2 * 8, "hbm"),
     }
     kern = {n: roof(n, wk, bd, tr, steps, workload=w.name) for n, (wk, bd) in work.items() if n in tr}
@@ -204,7 +204,7 @@ def bench_core(B, N, H, d, C, steps, warmup, parallel=False):
         res["kernels"] = {
             "k_chunk_out": roof("k_chunk_out", B * N * H * (C * 2 * d + 2 * d * d), "mfma", tr, steps),
             "k_chunk_state": roof("k_chunk_state", B * N * H * 2 * d * d, "mfma", tr, steps),
-            "k_chunk_scan": roof("k_chunk_scan", B * H * nc * d * d * 6, "hbm", tr, steps),
+            "k_chunk_scan": roof("k_chunk_scan", B * H * nc * d * d * 4, "hbm", tr, steps),
         }
     return res
 

@@ -12,9 +12,10 @@
 //
 // Three kernels per call:
 //   k_chunk_state : dR_i^T = (V_[i] (.) zeta)^T K_[i]   (matrix cores, one
-//                   workgroup per (batch, head, chunk, state tile))
-//   k_chunk_scan  : R_i = gamma^L R_{i-1} + dR_i in float32, writing the
-//                   exclusive prefix R_{i-1} per chunk (as the input type)
+//                   workgroup per (batch, head, chunk, state tile); stored
+//                   in the input type)
+//   k_chunk_scan  : R_i = gamma^L R_{i-1} + dR_i carried in float32, writing
+//                   the exclusive prefix R_{i-1} per chunk over dR_i
 //   k_chunk_out   : per row tile: Q R_{i-1} (.) xi, then the causal,
 //                   decay-weighted intra-chunk product, then either O or the
 //                   fused per-head GroupNorm + swish gate.
@@ -48,8 +49,8 @@ struct StateCfg {
 
 template <class T, int DK, int DV>
 __global__ __launch_bounds__(256) void k_chunk_state(const T* __restrict__ K, const T* __restrict__ V,
-                                                     int64_t ldk, int64_t ldv, float* __restrict__ dR,
-                                                     int N, int H, int chunk, int NC, HeadTab tab) {
+                                                     int64_t ldk, int64_t ldv, T* __restrict__ dR,
+                                                     int BH, int N, int H, int chunk, int NC, HeadTab tab) {
   using C = StateCfg<T, DK, DV>;
   constexpr int TS = C::TS, WT = C::WT, KB = C::KB, LDT = C::LDT, UNITS = C::UNITS, UPT = C::UPT;
   __shared__ __attribute__((aligned(16))) T smem[C::STAGE];
@@ -57,11 +58,16 @@ __global__ __launch_bounds__(256) void k_chunk_state(const T* __restrict__ K, co
   T* sK = smem + KB * LDT;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 31, hh = lane >> 5;
-  const int ci = blockIdx.x % NC;
-  const int bh = blockIdx.x / NC;
+  // block id -> (batch-head-chunk unit, state tile): the tiles of a unit
+  // are 8 block ids apart, so they run on one XCD and share K and V in its L2
+  constexpr int NTV = DV / TS, NTT = NTV * (DK / TS);
+  const int xg = blockIdx.x & 7, yg = blockIdx.x >> 3;
+  const int tile = yg % NTT, unit = (yg / NTT) * 8 + xg;
+  if (unit >= BH * NC) return;
+  const int ci = unit % NC;
+  const int bh = unit / NC;
   const int h = bh % H, b = bh / H;
-  constexpr int NTV = DV / TS;
-  const int tv = blockIdx.y % NTV, tk = blockIdx.y / NTV;
+  const int tv = tile % NTV, tk = tile / NTV;
   const int c0 = ci * chunk;
   const int L = min(chunk, N - c0);
   const float lg2 = tab.lg2[h];
@@ -111,7 +117,7 @@ __global__ __launch_bounds__(256) void k_chunk_state(const T* __restrict__ K, co
     __syncthreads();
   }
 
-  float* out = dR + ((size_t)bh * NC + ci) * DV * DK;
+  T* out = dR + ((size_t)bh * NC + ci) * DV * DK;
 #pragma unroll
   for (int i = 0; i < WT; ++i)
 #pragma unroll
@@ -120,14 +126,14 @@ __global__ __launch_bounds__(256) void k_chunk_state(const T* __restrict__ K, co
       for (int r = 0; r < 16; ++r) {
         const int row = tv * TS + wr + 32 * i + 8 * (r >> 2) + 4 * hh + (r & 3);
         const int col = tk * TS + wc + 32 * j + lr;
-        out[(size_t)row * DK + col] = acc[i][j][r];
+        out[(size_t)row * DK + col] = (T)acc[i][j][r];
       }
 }
 
 // ---------------------------------------------------------------------------
 // k_chunk_scan: float32 carry across chunks, 64x64 state tile per workgroup.
-// dR and Rx may alias (float32 path): each element is read before it is
-// overwritten by the same thread, so no __restrict__ on them.
+// dR and Rx alias: each element is read (two chunks ahead) before the same
+// thread overwrites it, so no __restrict__ on them.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void store16(float* p, const float* x) {
 #pragma unroll
@@ -139,6 +145,12 @@ __device__ __forceinline__ void store16(bf16* p, const float* x) {
   *reinterpret_cast<uint4*>(p) = a;
   *reinterpret_cast<uint4*>(p + 8) = b;
 }
+__device__ __forceinline__ void load16(float* x, const bf16* p) {
+  const uint4 a = *reinterpret_cast<const uint4*>(p), b = *reinterpret_cast<const uint4*>(p + 8);
+  const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) { x[2 * i] = bf16_lo(w[i]); x[2 * i + 1] = bf16_hi(w[i]); }
+}
 __device__ __forceinline__ void load16(float* x, const float* p) {
 #pragma unroll
   for (int e = 0; e < 16; e += 4) {
@@ -148,7 +160,7 @@ __device__ __forceinline__ void load16(float* x, const float* p) {
 }
 
 template <class T, int DK, int DV>
-__global__ __launch_bounds__(256) void k_chunk_scan(const float* dR, T* Rx, const float* __restrict__ S_in,
+__global__ __launch_bounds__(256) void k_chunk_scan(const T* dR, T* Rx, const float* __restrict__ S_in,
                                                     float* __restrict__ S_out, int H, int NC, HeadTab tab) {
   constexpr int NTV = DV / 64;
   constexpr int NT = NTV * (DK / 64);
@@ -177,19 +189,21 @@ __global__ __launch_bounds__(256) void k_chunk_scan(const float* dR, T* Rx, cons
 
   const size_t cstride = (size_t)DV * DK;
   const size_t off = (size_t)bh * NC * cstride + (size_t)(tv * 64 + row) * DK + tk * 64 + col;
-  const float* src = dR + off;
+  const T* src = dR + off;
   T* dst = Rx + off;
   const float gB = tab.gchunk[h], gL = tab.glast[h];
-  float d[16], dn[16];
+  // contributions of chunks ci, ci + 1, ci + 2 in flight
+  float d[16], d1[16], d2[16];
   load16(d, src);
+  if (NC > 1) load16(d1, src + cstride);
   for (int ci = 0; ci < NC; ++ci) {
-    if (ci + 1 < NC) load16(dn, src + (size_t)(ci + 1) * cstride);
+    if (ci + 2 < NC) load16(d2, src + (size_t)(ci + 2) * cstride);
     store16(dst + (size_t)ci * cstride, R);
     const float g = (ci == NC - 1) ? gL : gB;
 #pragma unroll
     for (int e = 0; e < 16; ++e) R[e] = fmaf(g, R[e], d[e]);
 #pragma unroll
-    for (int e = 0; e < 16; ++e) d[e] = dn[e];
+    for (int e = 0; e < 16; ++e) { d[e] = d1[e]; d1[e] = d2[e]; }
   }
 
   if (S_out != nullptr) {
@@ -929,14 +943,14 @@ static hipError_t run_chunkwise(const ChunkArgs& a, const HeadTab& tab, hipStrea
   constexpr int TS = StateCfg<T, DK, DV>::TS;
   {
     TraceScope ts("k_chunk_state", st);
-    dim3 grid(BH * NC, (DV / TS) * (DK / TS));
+    dim3 grid(((BH * NC + 7) / 8) * 8 * (DV / TS) * (DK / TS));
     hipLaunchKernelGGL((k_chunk_state<T, DK, DV>), grid, dim3(256), 0, st, (const T*)a.K, (const T*)a.V,
-                       a.ldk, a.ldv, a.dR, N, H, Cn, NC, tab);
+                       a.ldk, a.ldv, (T*)a.dR, BH, N, H, Cn, NC, tab);
   }
   {
     TraceScope ts("k_chunk_scan", st);
     dim3 grid(BH * (DV / 64) * (DK / 64));
-    hipLaunchKernelGGL((k_chunk_scan<T, DK, DV>), grid, dim3(256), 0, st, (const float*)a.dR, (T*)a.Rx,
+    hipLaunchKernelGGL((k_chunk_scan<T, DK, DV>), grid, dim3(256), 0, st, (const T*)a.dR, (T*)a.Rx,
                        a.S_in, a.S_out, H, NC, tab);
   }
   {

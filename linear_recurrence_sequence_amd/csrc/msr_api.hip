@@ -121,9 +121,8 @@ ChunkWs chunk_ws_layout(msr_dtype dt, const msr_dims& d, int32_t chunk, bool rop
   if (with_state) {
     const size_t nc = chunk > 0 ? ((size_t)d.seqlen + chunk - 1) / chunk : 0;
     const size_t st = (size_t)d.batch * d.heads * nc * d.d_k * d.d_v;
-    w.dr = off; off += align_up(st * sizeof(float));
-    w.rx = w.dr;
-    if (dt == MSR_BF16) { w.rx = off; off += align_up(st * 2); }
+    w.dr = off; off += align_up(st * es);
+    w.rx = w.dr;   // the scan overwrites each chunk's contribution with R_{i-1}
   }
   w.total = off;
   return w;
@@ -266,7 +265,7 @@ msr_status msr_chunkwise_fwd(msr_dtype dtype, msr_dims d, int32_t chunk, const d
   a.ldv = a.ldo = (int64_t)d.heads * d.d_v;
   a.scale = qk_scale;
   a.S_in = S_in; a.S_out = S_out;
-  a.dR = at<float>(workspace, w.dr);
+  a.dR = at<void>(workspace, w.dr);
   a.Rx = at<void>(workspace, w.rx);
   const HeadTab tab = make_tab(gamma, d.heads, chunk, d.seqlen);
   return from_hip(launch_chunkwise(a, tab, st), "msr_chunkwise_fwd");
@@ -353,7 +352,7 @@ msr_status msr_layer_fwd(msr_dtype dtype, int32_t batch, int32_t seqlen, int32_t
   a.scale = 1.0f / std::sqrt((float)d_k);
   a.eps = gn_eps;
   a.fuse_gn_gate = true;
-  a.dR = at<float>(cws, w.cw.dr);
+  a.dR = at<void>(cws, w.cw.dr);
   a.Rx = at<void>(cws, w.cw.rx);
   const HeadTab htab = make_tab(gamma, heads, chunk, seqlen);
   err = launch_chunkwise(a, htab, st);

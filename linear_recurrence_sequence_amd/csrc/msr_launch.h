@@ -39,8 +39,8 @@ struct ChunkArgs {
   float scale, eps;
   bool fuse_gn_gate;
   const float* S_in; float* S_out;
-  float* dR;                 // [B, H, NC, d_v, d_k] float32
-  void* Rx;                  // [B, H, NC, d_v, d_k] elt (may alias dR for f32)
+  void* dR;                  // [B, H, NC, d_v, d_k] elt: each chunk's own state contribution
+  void* Rx;                  // [B, H, NC, d_v, d_k] elt: R_{i-1} per chunk (aliases dR)
 };
 
 // Chunkwise retention: state contributions, fp32 scan, outputs.

@@ -117,15 +117,16 @@ def test_empty_inputs_are_no_ops():
 
 
 def test_workspace_sizes():
-    # chunkwise, bf16: dR float32 + R_excl bf16, each [B, H, NC, dk, dv]; rotation adds Q, K copies and a table
+    # chunkwise: one [B, H, NC, dk, dv] buffer of the element type (each chunk's state
+    # contribution, overwritten in place by R_{i-1}); rotation adds Q, K copies and a table
     B, N, H, dk, dv, C = 2, 1000, 3, 128, 128, 256
     nc = -(-N // C)
     st = B * H * nc * dk * dv
     up = lambda x: -(-x // 256) * 256
-    assert msr.msr_chunkwise_workspace_bytes(1, B, N, H, dk, dv, C, 0.0) == up(st * 4) + up(st * 2)
-    assert msr.msr_chunkwise_workspace_bytes(0, B, N, H, dk, dv, C, 0.0) == up(st * 4)   # f32: in place
+    assert msr.msr_chunkwise_workspace_bytes(1, B, N, H, dk, dv, C, 0.0) == up(st * 2)
+    assert msr.msr_chunkwise_workspace_bytes(0, B, N, H, dk, dv, C, 0.0) == up(st * 4)
     rot = 2 * up(B * N * H * dk * 2) + up(N * dk // 2 * 8)
-    assert msr.msr_chunkwise_workspace_bytes(1, B, N, H, dk, dv, C, 1e4) == rot + up(st * 4) + up(st * 2)
+    assert msr.msr_chunkwise_workspace_bytes(1, B, N, H, dk, dv, C, 1e4) == rot + up(st * 2)
     assert msr.msr_parallel_workspace_bytes(1, B, N, H, dk, dv, 0.0) == 0
     assert msr.msr_layer_workspace_bytes(1, 2, 64, 256, 2, 64, 64, 32) > 0
     assert msr.msr_layer_workspace_bytes(1, 2, 64, 256, 2, 64, 64, 0) == 0
