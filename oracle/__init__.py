@@ -21,6 +21,7 @@ from .retention import (  # noqa: F401
     group_norm_heads,
     swish,
     msr_layer,
+    msr_layer_decode_step,
     max_rel_err,
     max_rel_err_per_head,
 )

@@ -296,6 +296,32 @@ def msr_layer(X, WQ, WK, WV, WG, WO, gamma, heads, d_k, d_v, chunk=None,
     return out
 
 
+def msr_layer_decode_step(x, S, WQ, WK, WV, WG, WO, gamma, heads, d_k, d_v, pos,
+                          rope_base=10000.0, eps=1e-5, scale=None):
+    """One decode step of the gated MSR layer: Eq. (8) with the recurrent
+    form of retention, Eq. (6) ([RN-zh] "2) Retention 的循環表征" and
+    "門控多尺度 Retention"), for one new token per sequence:
+
+      q^, k^, v, g = x W_Q, x W_K, x W_V, x W_G         (x: [B, d_model])
+      q, k = rotary(q^), rotary(k^) at absolute position ``pos``
+      S <- gamma_h S + k^T v ;  o = scale * q S           (per head)
+      out = (swish(g) (.) GroupNorm_h(o)) W_O
+
+    S: [B, H, d_k, d_v] (the state after the tokens before ``pos``).
+    Returns (out [B, d_model], S_new).
+    """
+    x = _f64(x)
+    B = x.shape[0]
+    q = (x @ _f64(WQ)).reshape(B, heads, d_k)
+    k = (x @ _f64(WK)).reshape(B, heads, d_k)
+    v = (x @ _f64(WV)).reshape(B, heads, d_v)
+    g = x @ _f64(WG)
+    s = 1.0 / math.sqrt(d_k) if scale is None else scale
+    o, S_new = recurrent_step(S, q, k, v, gamma, s, pos=pos, base=rope_base)
+    y = group_norm_heads(o, eps).reshape(B, heads * d_v)
+    return (swish(g) * y) @ _f64(WO), S_new
+
+
 # --------------------------------------------------------------------------
 # Error measures
 # --------------------------------------------------------------------------

@@ -322,3 +322,45 @@ def test_layer_gn_var_output_is_the_groupnorm_input_variance():
     out, gv = oracle.msr_layer(X, *W, g, 3, 4, 4, chunk=3, eps=0.0, return_gn_var=True)
     assert close(out, oracle.msr_layer(X, *W, g, 3, 4, 4, chunk=3, eps=0.0))
     assert gv.shape == (1, 10, 3) and np.all(gv > 0)
+
+
+def test_layer_decode_steps_reproduce_the_layer_forward():
+    """Decoding a sequence token by token with the layer decode step from a
+    zero state (positions 0, 1, ...) gives the rows of the full-sequence
+    layer forward in the parallel form -- rotation at each absolute
+    position, the state update order of Eq. (6), GroupNorm and gate per
+    token -- and the final state equals the recurrent form's.  A second
+    batch element starts from a non-zero state: its steps equal the layer
+    forward of the same tokens with that state as the chunkwise form's
+    initial state."""
+    rng = np.random.default_rng(17)
+    B, N, dm, H, dk, dv = 2, 9, 16, 2, 4, 6
+    X = rng.standard_normal((B, N, dm))
+    WQ, WK = (rng.standard_normal((dm, H * dk)) / 4 for _ in range(2))
+    WV, WG = (rng.standard_normal((dm, H * dv)) / 4 for _ in range(2))
+    WO = rng.standard_normal((H * dv, dm)) / 4
+    g = np.array([0.9, 0.6])
+    ref = oracle.msr_layer(X, WQ, WK, WV, WG, WO, g, H, dk, dv, form="parallel", eps=1e-5)
+    S = np.zeros((B, H, dk, dv))
+    for n in range(N):
+        out, S = oracle.msr_layer_decode_step(X[:, n], S, WQ, WK, WV, WG, WO, g, H, dk, dv, pos=n, eps=1e-5)
+        assert np.max(np.abs(out - ref[:, n])) < 1e-12
+    q = oracle.rotary((X @ WQ).reshape(B, N, H, dk), 0, 1e4)
+    k = oracle.rotary((X @ WK).reshape(B, N, H, dk), 0, 1e4)
+    v = (X @ WV).reshape(B, N, H, dv)
+    _, S_rec = oracle.retention_recurrent(q, k, v, g, 1 / np.sqrt(dk))
+    assert np.max(np.abs(S - S_rec)) < 1e-12
+    # continuation from a non-zero state: 4 more tokens at positions N..N+3
+    X2 = rng.standard_normal((B, 4, dm))
+    S2 = S.copy()
+    outs = []
+    for n in range(4):
+        out, S2 = oracle.msr_layer_decode_step(X2[:, n], S2, WQ, WK, WV, WG, WO, g, H, dk, dv, pos=N + n, eps=1e-5)
+        outs.append(out)
+    q2 = oracle.rotary((X2 @ WQ).reshape(B, 4, H, dk), N, 1e4)
+    k2 = oracle.rotary((X2 @ WK).reshape(B, 4, H, dk), N, 1e4)
+    v2 = (X2 @ WV).reshape(B, 4, H, dv)
+    o2, _ = oracle.retention_chunkwise(q2, k2, v2, g, 2, 1 / np.sqrt(dk), S0=S)
+    y2 = oracle.group_norm_heads(o2, 1e-5).reshape(B, 4, H * dv)
+    ref2 = (oracle.swish(X2 @ WG) * y2) @ WO
+    assert np.max(np.abs(np.stack(outs, axis=1) - ref2)) < 1e-12
