@@ -261,6 +261,48 @@ def bench_decode(steps_timed, warmup):
     return out
 
 
+def bench_layer_decode(n_steps, warmup):
+    """Gated layer decode step at the decode workload's shape (batch 128,
+    d_model 4096, 16 heads of 256; bf16 tokens and weights, float32 state):
+    projections, rotation, state update, GroupNorm, gate, W_O per step."""
+    import torch
+    import linear_recurrence_sequence_amd as msr
+    import workloads
+    w = workloads.WORKLOADS["decode_fp32_b128_h16"]
+    B, dm, H, dk, dv = w.batch, w.d_model, w.heads, w.d_k, w.d_v
+    g = workloads.gammas(H)
+    s = dm ** -0.5
+    W = [(workloads.device_normal(shp, seed=910 + i) * s).to(torch.bfloat16)
+         for i, shp in enumerate([(dm, H * dk), (dm, H * dk), (dm, H * dv), (dm, H * dv)])]
+    WO = (workloads.device_normal((H * dv, dm), seed=920) * (H * dv) ** -0.5).to(torch.bfloat16)
+    S = workloads.device_normal((B, H, dk, dv), seed=930) * 0.5
+    xs = workloads.device_normal((n_steps, B, dm), seed=940).to(torch.bfloat16)
+    out = torch.empty((B, dm), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(msr.msr_layer_decode_workspace_bytes(1, B, dm, H, dk, dv), dtype=torch.uint8, device="cuda")
+    step = lambda t: msr.msr_layer_decode_step(xs[t % n_steps], *W, WO, S, g, H, dk, dv, w.context + t,
+                                               rope_base=w.rope_base, gn_eps=1e-5, out=out, workspace=ws)
+    for t in range(warmup):
+        step(t)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for t in range(n_steps):
+        step(t)
+    e1.record()
+    torch.cuda.synchronize()
+    ts = e0.elapsed_time(e1) * 1e-3 / n_steps
+    tr = traced(lambda: step(0), n_steps)
+    wbytes = (dm * (2 * H * dk + 2 * H * dv) + H * dv * dm) * 2
+    byts = B * H * dk * dv * 4 * 2 + wbytes + B * dm * 2 * 2
+    res = {"batch": B, "d_model": dm, "heads": H, "d_k": dk, "d_v": dv, "steps": n_steps,
+           "us_per_step": round(ts * 1e6, 2), "steps_per_s": round(1 / ts, 1), "tokens_per_s": round(B / ts, 1),
+           "GB_per_s": round(byts / ts / 1e9, 1), "hbm_frac": round(byts / ts / PEAK_HBM, 4), "bytes_per_step": byts,
+           "trace_us_per_step": {k: round(v[0] / n_steps * 1e6, 2) for k, v in tr.items()}}
+    del W, WO, S, xs, out, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def bench_copy(nbytes=1 << 30, reps=8):
     """A plain device-to-device copy of a known size: the calibration run for
     the FETCH_SIZE / WRITE_SIZE counters (each reads nbytes and writes nbytes
@@ -351,6 +393,8 @@ def main():
     if "decode" in parts:
         log("decode")
         line["decode"] = bench_decode(512, 16)
+        log("layer decode")
+        line["layer_decode"] = bench_layer_decode(64, 8)
     if "long" in parts:
         log("long")
         lw = workloads.WORKLOADS["long_bf16_b2_n16384"]

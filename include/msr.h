@@ -134,6 +134,29 @@ size_t msr_layer_workspace_bytes(msr_dtype dtype, int32_t batch, int32_t seqlen,
                                  int32_t d_model, int32_t heads, int32_t d_k,
                                  int32_t d_v, int32_t chunk);
 
+/* One decode step of the gated MSR layer: Eq. (8) of [RN-zh] with the
+ * recurrent form of retention, Eq. (6), for one new token per sequence:
+ *   q^, k^, v, g = x W_Q, x W_K, x W_V, x W_G
+ *   q, k = q^, k^ rotated at absolute position `pos` (rope_base <= 0: none)
+ *   S <- gamma_h S + k^T v ;  o = (q S) / sqrt(d_k)        (per head)
+ *   out = (swish(g) (.) GroupNorm_h(o)) W_O
+ * X: [batch, d_model] (the new token of each sequence); weights as in
+ * msr_layer_fwd; S: [batch, heads, d_k, d_v] float32, the state after the
+ * tokens before `pos`, updated in place; out: [batch, d_model].  `pos` is
+ * the number of tokens the state has absorbed (>= 0).  The retention output
+ * stays float32 up to the GroupNorm.  d_model must be a multiple of 64.
+ * Workspace: msr_layer_decode_workspace_bytes() bytes. */
+msr_status msr_layer_decode_step(msr_dtype dtype, int32_t batch, int32_t d_model,
+                                 int32_t heads, int32_t d_k, int32_t d_v,
+                                 const double* gamma, float rope_base, float gn_eps,
+                                 int64_t pos, const void* X, const void* W_Q,
+                                 const void* W_K, const void* W_V, const void* W_G,
+                                 const void* W_O, float* S, void* out,
+                                 void* workspace, size_t ws_bytes, void* stream);
+size_t msr_layer_decode_workspace_bytes(msr_dtype dtype, int32_t batch,
+                                        int32_t d_model, int32_t heads,
+                                        int32_t d_k, int32_t d_v);
+
 /* Diagnostics for benchmarks: per-kernel timing with HIP events.
  * msr_trace_enable(1) clears earlier totals and from then on brackets every
  * kernel the library launches with an event pair recorded on that launch's

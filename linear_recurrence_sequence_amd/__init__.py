@@ -19,6 +19,7 @@ __all__ = [
     "msr_parallel_fwd", "msr_parallel_workspace_bytes",
     "msr_chunkwise_fwd", "msr_chunkwise_workspace_bytes",
     "msr_recurrent_step", "msr_layer_fwd", "msr_layer_workspace_bytes",
+    "msr_layer_decode_step", "msr_layer_decode_workspace_bytes",
     "msr_status_str", "msr_last_error", "msr_trace_enable", "msr_trace_count", "msr_trace_get",
     "trace_totals",
 ]
@@ -27,8 +28,8 @@ MSR_F32, MSR_BF16 = 0, 1
 EXPORTS = (
     "msr_parallel_fwd", "msr_parallel_workspace_bytes", "msr_chunkwise_fwd",
     "msr_chunkwise_workspace_bytes", "msr_recurrent_step", "msr_layer_fwd",
-    "msr_layer_workspace_bytes", "msr_status_str", "msr_last_error",
-    "msr_trace_enable", "msr_trace_count", "msr_trace_get",
+    "msr_layer_workspace_bytes", "msr_layer_decode_step", "msr_layer_decode_workspace_bytes",
+    "msr_status_str", "msr_last_error", "msr_trace_enable", "msr_trace_count", "msr_trace_get",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -80,6 +81,9 @@ def lib():
         "msr_layer_fwd": (_I32, [_I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _DP, _F, _F, _P, _P, _P,
                                  _P, _P, _P, _P, _P, _SZ, _P]),
         "msr_layer_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32]),
+        "msr_layer_decode_step": (_I32, [_I32, _I32, _I32, _I32, _I32, _I32, _DP, _F, _F, _I64, _P, _P, _P, _P,
+                                         _P, _P, _P, _P, _P, _SZ, _P]),
+        "msr_layer_decode_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32]),
         "msr_trace_enable": (None, [_I32]),
         "msr_trace_count": (_I32, []),
         "msr_trace_get": (_I32, [_I32, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_double),
@@ -251,4 +255,28 @@ def msr_layer_fwd(X, W_Q, W_K, W_V, W_G, W_O, gamma, heads, d_k, d_v, chunk, *, 
     _check("msr_layer_fwd", lib().msr_layer_fwd(dt, B, N, dm, heads, d_k, d_v, chunk, gp, rope_base, gn_eps,
                                                 _ptr(X), _ptr(W_Q), _ptr(W_K), _ptr(W_V), _ptr(W_G), _ptr(W_O),
                                                 _ptr(out), _ptr(ws), wsb, _stream(stream)))
+    return out
+
+
+def msr_layer_decode_workspace_bytes(dtype, batch, d_model, heads, d_k, d_v):
+    return lib().msr_layer_decode_workspace_bytes(dtype, batch, d_model, heads, d_k, d_v)
+
+
+def msr_layer_decode_step(X, W_Q, W_K, W_V, W_G, W_O, S, gamma, heads, d_k, d_v, pos, *, rope_base=10000.0,
+                          gn_eps=1e-5, out=None, workspace=None, stream=None):
+    """One decode step of the gated MSR layer (Eq. 8 with Eq. 6).  X: [B, d_model] (the new token of each
+    sequence); S: [B, heads, d_k, d_v] float32, updated in place; returns out [B, d_model]."""
+    B, dm = X.shape
+    dt = _dtype_code(X)
+    if S.dtype != _torch().float32:
+        raise TypeError("S must be float32")
+    if out is None:
+        out = _torch().empty((B, dm), dtype=X.dtype, device=X.device)
+    _, gp = g = _gamma(gamma, heads)
+    nbytes = lib().msr_layer_decode_workspace_bytes(dt, B, dm, heads, d_k, d_v)
+    ws, wsb = _workspace(nbytes, workspace, X.device)
+    _check("msr_layer_decode_step",
+           lib().msr_layer_decode_step(dt, B, dm, heads, d_k, d_v, gp, rope_base, gn_eps, int(pos), _ptr(X),
+                                       _ptr(W_Q), _ptr(W_K), _ptr(W_V), _ptr(W_G), _ptr(W_O), _ptr(S), _ptr(out),
+                                       _ptr(ws), wsb, _stream(stream)))
     return out

@@ -25,11 +25,12 @@ __device__ __forceinline__ void rope_cs(int64_t p, int j, int d, float base, flo
 
 template <class T> __device__ __forceinline__ float ld1(const T* p) { return (float)*p; }
 
-template <class T, int DK, int DV, int CS>
-__global__ __launch_bounds__(256) void k_recurrent_step(const T* __restrict__ q, const T* __restrict__ k,
-                                                        const T* __restrict__ v, float* __restrict__ S,
-                                                        T* __restrict__ o, int H, float scale, int64_t pos,
-                                                        float rope_base, HeadTab tab) {
+template <class T, class OT, int DK, int DV, int CS>
+__global__ __launch_bounds__(256) void k_recurrent_step(const T* __restrict__ q, int64_t ldq, const T* __restrict__ k,
+                                                        int64_t ldk, const T* __restrict__ v, int64_t ldv,
+                                                        float* __restrict__ S, OT* __restrict__ o, int64_t ldo,
+                                                        int H, float scale, int64_t pos, float rope_base,
+                                                        HeadTab tab) {
   // CS workgroups per (batch, head), each owning DV / CS columns: the sum
   // over d_k rows of a column stays inside one workgroup, and the finer grid
   // avoids a mostly idle last round of workgroups.  The state is touched
@@ -40,9 +41,9 @@ __global__ __launch_bounds__(256) void k_recurrent_step(const T* __restrict__ q,
   constexpr int RG = 256 / TPR;        // rows processed in parallel
   __shared__ float sq[DK], sk[DK];
   __shared__ f32x4 red[RG][TPR];
-  const int bh = blockIdx.x / CS, cs = blockIdx.x % CS, h = bh % H, tid = threadIdx.x;
-  const T* qb = q + (size_t)bh * DK;
-  const T* kb = k + (size_t)bh * DK;
+  const int bh = blockIdx.x / CS, cs = blockIdx.x % CS, h = bh % H, b = bh / H, tid = threadIdx.x;
+  const T* qb = q + (size_t)b * ldq + (size_t)h * DK;
+  const T* kb = k + (size_t)b * ldk + (size_t)h * DK;
   for (int j = tid; j < DK / 2; j += 256) {
     float q0 = ld1(qb + 2 * j), q1 = ld1(qb + 2 * j + 1), k0 = ld1(kb + 2 * j), k1 = ld1(kb + 2 * j + 1);
     if (rope_base > 0.f) {
@@ -58,7 +59,7 @@ __global__ __launch_bounds__(256) void k_recurrent_step(const T* __restrict__ q,
   __syncthreads();
 
   const int rg = tid / TPR, c = cs * SW + (tid % TPR) * CPT;
-  const T* vb = v + (size_t)bh * DV + c;
+  const T* vb = v + (size_t)b * ldv + (size_t)h * DV + c;
   const f32x4 vv = {ld1(vb), ld1(vb + 1), ld1(vb + 2), ld1(vb + 3)};
   const float g = tab.gam[h];
   float* Sb = S + (size_t)bh * DK * DV + c;
@@ -78,38 +79,104 @@ __global__ __launch_bounds__(256) void k_recurrent_step(const T* __restrict__ q,
     f32x4 t = red[0][tid];
 #pragma unroll
     for (int r = 1; r < RG; ++r) t += red[r][tid];
-    T* ob = o + (size_t)bh * DV + c;
-    ob[0] = (T)(scale * t[0]);
-    ob[1] = (T)(scale * t[1]);
-    ob[2] = (T)(scale * t[2]);
-    ob[3] = (T)(scale * t[3]);
+    OT* ob = o + (size_t)b * ldo + (size_t)h * DV + c;
+    ob[0] = (OT)(scale * t[0]);
+    ob[1] = (OT)(scale * t[1]);
+    ob[2] = (OT)(scale * t[2]);
+    ob[3] = (OT)(scale * t[3]);
   }
 }
 
 template <class T, int DK, int DV>
-static hipError_t run_step(int batch, int heads, const void* q, const void* k, const void* v, float* S, void* o,
-                           float scale, int64_t pos, float base, const HeadTab& tab, hipStream_t st) {
+static hipError_t run_step(int batch, int heads, const StepIO& io, float* S, float scale, int64_t pos, float base,
+                           const HeadTab& tab, hipStream_t st) {
   constexpr int CS = DV >= 256 ? 2 : 1;
   TraceScope ts("k_recurrent_step", st);
-  hipLaunchKernelGGL((k_recurrent_step<T, DK, DV, CS>), dim3(batch * heads * CS), dim3(256), 0, st, (const T*)q,
-                     (const T*)k, (const T*)v, S, (T*)o, heads, scale, pos, base, tab);
+  const dim3 grid(batch * heads * CS);
+  if (io.o_f32)
+    hipLaunchKernelGGL((k_recurrent_step<T, float, DK, DV, CS>), grid, dim3(256), 0, st, (const T*)io.q, io.ldq,
+                       (const T*)io.k, io.ldk, (const T*)io.v, io.ldv, S, (float*)io.o, io.ldo, heads, scale, pos,
+                       base, tab);
+  else
+    hipLaunchKernelGGL((k_recurrent_step<T, T, DK, DV, CS>), grid, dim3(256), 0, st, (const T*)io.q, io.ldq,
+                       (const T*)io.k, io.ldk, (const T*)io.v, io.ldv, S, (T*)io.o, io.ldo, heads, scale, pos,
+                       base, tab);
   return hipGetLastError();
 }
 
-hipError_t launch_recurrent_step(Elt elt, int d_k, int d_v, int batch, int heads, const void* q, const void* k,
-                                 const void* v, float* S, void* o, float scale, int64_t pos, float base,
-                                 const HeadTab& tab, hipStream_t st) {
-#define MSR_STEP(T)                                                                               \
-  if (d_k == 64 && d_v == 64) return run_step<T, 64, 64>(batch, heads, q, k, v, S, o, scale, pos, base, tab, st); \
-  if (d_k == 128 && d_v == 128) return run_step<T, 128, 128>(batch, heads, q, k, v, S, o, scale, pos, base, tab, st); \
-  if (d_k == 256 && d_v == 256) return run_step<T, 256, 256>(batch, heads, q, k, v, S, o, scale, pos, base, tab, st); \
-  if (d_k == 256 && d_v == 512) return run_step<T, 256, 512>(batch, heads, q, k, v, S, o, scale, pos, base, tab, st);
+hipError_t launch_recurrent_step(Elt elt, int d_k, int d_v, int batch, int heads, const StepIO& io, float* S,
+                                 float scale, int64_t pos, float base, const HeadTab& tab, hipStream_t st) {
+#define MSR_STEP(T)                                                                                        \
+  if (d_k == 64 && d_v == 64) return run_step<T, 64, 64>(batch, heads, io, S, scale, pos, base, tab, st);     \
+  if (d_k == 128 && d_v == 128) return run_step<T, 128, 128>(batch, heads, io, S, scale, pos, base, tab, st); \
+  if (d_k == 256 && d_v == 256) return run_step<T, 256, 256>(batch, heads, io, S, scale, pos, base, tab, st); \
+  if (d_k == 256 && d_v == 512) return run_step<T, 256, 512>(batch, heads, io, S, scale, pos, base, tab, st);
   if (elt == kBF16) {
     MSR_STEP(bf16)
   } else {
     MSR_STEP(float)
   }
 #undef MSR_STEP
+  return hipErrorInvalidValue;
+}
+
+// ---------------------------------------------------------------------------
+// GroupNorm + swish gate of a decode step ([RN-zh] "門控多尺度 Retention",
+// Eq. (8)): per (batch element, head), statistics over the head's d_v
+// outputs (biased variance), z = swish(g) (.) (o - mean) / sqrt(var + eps).
+// One wave per (batch element, head); lane l holds columns l, l + 64, ...
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);
+  return x;
+}
+
+template <class T, int DV>
+__global__ __launch_bounds__(256) void k_gn_gate(const float* __restrict__ o, int64_t ldo, const T* __restrict__ g,
+                                                 int64_t ldg, T* __restrict__ z, int64_t ldz, int rows, int H,
+                                                 float eps) {
+  constexpr int PER = DV / 64;
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;                         // wave-uniform; no barrier below
+  const int b = row / H, h = row % H;
+  const float* ob = o + (size_t)b * ldo + (size_t)h * DV + lane;
+  const T* gb = g + (size_t)b * ldg + (size_t)h * DV + lane;
+  T* zb = z + (size_t)b * ldz + (size_t)h * DV + lane;
+  float x[PER];
+  float sum = 0.f;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) sum += (x[e] = ob[64 * e]);
+  const float mu = wave_sum(sum) * (1.0f / DV);
+  float sq = 0.f;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) sq += (x[e] - mu) * (x[e] - mu);
+  const float rs = rsqrtf(wave_sum(sq) * (1.0f / DV) + eps);
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const float gv = (float)gb[64 * e];
+    zb[64 * e] = (T)(gv / (1.0f + __expf(-gv)) * (x[e] - mu) * rs);
+  }
+}
+
+hipError_t launch_gn_gate(Elt elt, int d_v, int batch, int heads, const float* o, int64_t ldo, const void* g,
+                          int64_t ldg, void* z, int64_t ldz, float eps, hipStream_t st) {
+  const int rows = batch * heads;
+  const dim3 grid((rows + 3) / 4);
+  TraceScope ts("k_gn_gate", st);
+#define MSR_GN(T, D)                                                                                    \
+  if (d_v == D) {                                                                                       \
+    hipLaunchKernelGGL((k_gn_gate<T, D>), grid, dim3(256), 0, st, o, ldo, (const T*)g, ldg, (T*)z, ldz, rows, \
+                       heads, eps);                                                                     \
+    return hipGetLastError();                                                                           \
+  }
+  if (elt == kBF16) {
+    MSR_GN(bf16, 64) MSR_GN(bf16, 128) MSR_GN(bf16, 256) MSR_GN(bf16, 512)
+  } else {
+    MSR_GN(float, 64) MSR_GN(float, 128) MSR_GN(float, 256) MSR_GN(float, 512)
+  }
+#undef MSR_GN
   return hipErrorInvalidValue;
 }
 

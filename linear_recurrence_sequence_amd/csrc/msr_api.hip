@@ -154,6 +154,21 @@ template <class P> P* at(void* base, size_t off) { return reinterpret_cast<P*>(s
 
 }  // namespace
 
+struct DecodeWs {
+  size_t qkvg = 0, o = 0, z = 0, total = 0;
+};
+DecodeWs decode_ws_layout(msr_dtype dt, int32_t batch, int32_t heads, int32_t dk, int32_t dv) {
+  DecodeWs w;
+  const size_t es = elt_size(dt);
+  const size_t ntot = (size_t)heads * (2 * dk + 2 * dv);
+  size_t off = 0;
+  w.qkvg = off; off += align_up((size_t)batch * ntot * es);
+  w.o = off; off += align_up((size_t)batch * heads * dv * sizeof(float));
+  w.z = off; off += align_up((size_t)batch * heads * dv * es);
+  w.total = off;
+  return w;
+}
+
 extern "C" {
 
 const char* msr_status_str(msr_status s) {
@@ -283,9 +298,76 @@ msr_status msr_recurrent_step(msr_dtype dtype, int32_t batch, int32_t heads, int
   if (!q || !k || !v || !S || !o) return fail(MSR_ERR_NULL, "q, k, v, S and o must be non-NULL");
   if ((int64_t)batch * heads > (int64_t)INT32_MAX) return fail(MSR_ERR_UNSUPPORTED, "batch*heads too large");
   const HeadTab tab = make_tab(gamma, heads, 1, 1);
-  return from_hip(launch_recurrent_step(dtype == MSR_BF16 ? kBF16 : kF32, d_k, d_v, batch, heads, q, k, v, S, o,
-                                        qk_scale, pos, rope_base, tab, (hipStream_t)stream),
+  const StepIO io{q, (int64_t)heads * d_k, k, (int64_t)heads * d_k, v, (int64_t)heads * d_v,
+                  o, (int64_t)heads * d_v, false};
+  return from_hip(launch_recurrent_step(dtype == MSR_BF16 ? kBF16 : kF32, d_k, d_v, batch, heads, io, S, qk_scale,
+                                        pos, rope_base, tab, (hipStream_t)stream),
                   "msr_recurrent_step");
+}
+
+// ---------------------------------------------------------------------------
+// Layer decode step: Eq. (8) with the recurrent form for one token per
+// sequence.  Workspace: [Q | K | V | G] rows, float32 retention outputs, Z.
+// ---------------------------------------------------------------------------
+
+size_t msr_layer_decode_workspace_bytes(msr_dtype dtype, int32_t batch, int32_t d_model, int32_t heads, int32_t d_k,
+                                        int32_t d_v) {
+  (void)d_model;
+  if (check_dtype(dtype) || check_heads(batch, 1, heads, d_k, d_v) || batch == 0) return 0;
+  return decode_ws_layout(dtype, batch, heads, d_k, d_v).total;
+}
+
+msr_status msr_layer_decode_step(msr_dtype dtype, int32_t batch, int32_t d_model, int32_t heads, int32_t d_k,
+                                 int32_t d_v, const double* gamma, float rope_base, float gn_eps, int64_t pos,
+                                 const void* X, const void* W_Q, const void* W_K, const void* W_V, const void* W_G,
+                                 const void* W_O, float* S, void* out, void* workspace, size_t ws_bytes,
+                                 void* stream) {
+  msr_status s;
+  if ((s = check_dtype(dtype))) return s;
+  if ((s = check_heads(batch, 1, heads, d_k, d_v))) return s;
+  if ((s = check_gamma(gamma, heads))) return s;
+  if (d_model <= 0) return fail(MSR_ERR_SHAPE, "d_model = %d must be positive", d_model);
+  if (d_model % 64) return fail(MSR_ERR_UNSUPPORTED, "d_model = %d is not a multiple of 64", d_model);
+  if (!(gn_eps >= 0.f)) return fail(MSR_ERR_SHAPE, "gn_eps must be >= 0");
+  if (pos < 0) return fail(MSR_ERR_SHAPE, "pos = %lld is negative", (long long)pos);
+  if (batch == 0) return ok();
+  if (!X || !W_Q || !W_K || !W_V || !W_G || !W_O || !S || !out)
+    return fail(MSR_ERR_NULL, "X, W_Q, W_K, W_V, W_G, W_O, S and out must be non-NULL");
+  if ((int64_t)batch * heads > (int64_t)INT32_MAX) return fail(MSR_ERR_UNSUPPORTED, "batch*heads too large");
+  const DecodeWs w = decode_ws_layout(dtype, batch, heads, d_k, d_v);
+  if (!workspace || ws_bytes < w.total)
+    return fail(MSR_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", w.total, workspace ? ws_bytes : 0);
+  hipStream_t st = (hipStream_t)stream;
+  const Elt e = dtype == MSR_BF16 ? kBF16 : kF32;
+  const size_t es = elt_size(dtype);
+  const int hk = heads * d_k, hv = heads * d_v;
+  const int ntot = 2 * hk + 2 * hv;
+  char* qkvg = at<char>(workspace, w.qkvg);
+  float* o = at<float>(workspace, w.o);
+  char* z = at<char>(workspace, w.z);
+  // 1. [q | k | v | g] = x [W_Q | W_K | W_V | W_G]
+  GemmB bq{};
+  bq.ptr[0] = W_Q; bq.ptr[1] = W_K; bq.ptr[2] = W_V; bq.ptr[3] = W_G;
+  bq.ld[0] = hk; bq.ld[1] = hk; bq.ld[2] = hv; bq.ld[3] = hv;
+  bq.start[0] = 0; bq.start[1] = hk; bq.start[2] = 2 * hk; bq.start[3] = 2 * hk + hv;
+  bq.rope_segs = 0;
+  hipError_t err = launch_gemm(e, X, d_model, bq, qkvg, ntot, batch, ntot, d_model, st);
+  if (err != hipSuccess) return from_hip(err, "msr_layer_decode_step(projections)");
+  // 2. q, k rotated at pos; S <- gamma S + k^T v; o = q S / sqrt(d_k) (float32)
+  const HeadTab tab = make_tab(gamma, heads, 1, 1);
+  const StepIO io{qkvg, ntot, qkvg + (size_t)hk * es, ntot, qkvg + (size_t)2 * hk * es, ntot, o, hv, true};
+  err = launch_recurrent_step(e, d_k, d_v, batch, heads, io, S, 1.0f / std::sqrt((float)d_k), pos, rope_base, tab,
+                              st);
+  if (err != hipSuccess) return from_hip(err, "msr_layer_decode_step(recurrent step)");
+  // 3. z = swish(g) (.) GroupNorm_h(o)
+  err = launch_gn_gate(e, d_v, batch, heads, o, hv, qkvg + (size_t)(2 * hk + hv) * es, ntot, z, hv, gn_eps, st);
+  if (err != hipSuccess) return from_hip(err, "msr_layer_decode_step(group norm, gate)");
+  // 4. out = z W_O
+  GemmB bo{};
+  bo.ptr[0] = W_O; bo.ld[0] = d_model;
+  bo.start[0] = 0; bo.start[1] = bo.start[2] = bo.start[3] = INT32_MAX;
+  err = launch_gemm(e, z, hv, bo, out, d_model, batch, d_model, hv, st);
+  return from_hip(err, "msr_layer_decode_step(output projection)");
 }
 
 

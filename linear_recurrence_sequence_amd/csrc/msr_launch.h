@@ -49,10 +49,20 @@ hipError_t launch_chunkwise(const ChunkArgs& a, const HeadTab& tab, hipStream_t 
 hipError_t launch_parallel(const ChunkArgs& a, const HeadTab& tab, hipStream_t stream);
 
 // One decode step: S <- gamma S + k^T v; o = scale q S (q, k rotated at pos).
-hipError_t launch_recurrent_step(Elt elt, int d_k, int d_v, int batch, int heads,
-                                 const void* q, const void* k, const void* v, float* S,
-                                 void* o, float scale, int64_t pos, float rope_base,
-                                 const HeadTab& tab, hipStream_t stream);
+// Operands of a decode step: one row per batch element (head h at column
+// h * d of the row), row strides in elements; o is float32 when o_f32.
+struct StepIO {
+  const void* q; int64_t ldq;
+  const void* k; int64_t ldk;
+  const void* v; int64_t ldv;
+  void* o; int64_t ldo;
+  bool o_f32;
+};
+hipError_t launch_recurrent_step(Elt elt, int d_k, int d_v, int batch, int heads, const StepIO& io, float* S,
+                                 float scale, int64_t pos, float base, const HeadTab& tab, hipStream_t stream);
+// z = swish(g) (.) GroupNorm_h(o) per (batch element, head) over d_v; o float32.
+hipError_t launch_gn_gate(Elt elt, int d_v, int batch, int heads, const float* o, int64_t ldo, const void* g,
+                          int64_t ldg, void* z, int64_t ldz, float eps, hipStream_t stream);
 
 // cos/sin table: tab[n * (d/2) + j] = (cos, sin)((pos0 + n) * theta_j),
 // theta_j = base^(-2j/d), n = 0..npos-1.

@@ -98,6 +98,16 @@ def test_other_entry_points_validation():
     assert lay(256, chunk=-32) == 2
     assert lay(256, ws=10) == 5
     assert lay(256, eps=-1.0) == 2
+    dec = lambda dm=256, dk=64, pos=5, S=FAKE, ws=1 << 40, eps=1e-5, dtype=1: L.msr_layer_decode_step(
+        dtype, 2, dm, 4, dk, dk, gp, 10000.0, eps, pos, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, S, FAKE, FAKE, ws, None)
+    assert dec(dm=100) == 4                 # d_model not a multiple of 64
+    assert dec(dk=96) == 4                  # unsupported head dims
+    assert dec(pos=-1) == 2
+    assert dec(S=None) == 1
+    assert dec(ws=10) == 5
+    assert dec(eps=-1.0) == 2
+    assert dec(dtype=5) == 3
+    assert "multiple of 64" in _last(lambda: dec(dm=96))
 
 
 def test_empty_inputs_are_no_ops():
@@ -130,6 +140,11 @@ def test_workspace_sizes():
     assert msr.msr_parallel_workspace_bytes(1, B, N, H, dk, dv, 0.0) == 0
     assert msr.msr_layer_workspace_bytes(1, 2, 64, 256, 2, 64, 64, 32) > 0
     assert msr.msr_layer_workspace_bytes(1, 2, 64, 256, 2, 64, 64, 0) == 0
+    # layer decode step: [q|k|v|g] rows (element type), float32 outputs, Z (element type)
+    Bd, Hd, kd, vd = 5, 3, 256, 512
+    assert msr.msr_layer_decode_workspace_bytes(1, Bd, 256, Hd, kd, vd) == (
+        up(Bd * Hd * (2 * kd + 2 * vd) * 2) + up(Bd * Hd * vd * 4) + up(Bd * Hd * vd * 2))
+    assert msr.msr_layer_decode_workspace_bytes(1, 0, 256, Hd, kd, vd) == 0
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
