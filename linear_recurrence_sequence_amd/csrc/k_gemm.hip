@@ -60,7 +60,8 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm(const T* __restrict__ A, 
   // past N are clamped to valid addresses instead of masked: they only feed
   // output rows / columns that are never stored.
   Row8<T> ra[AU], rb[BU];
-  const T* Ab = A + (size_t)m0 * lda;
+  const int kz = blockIdx.z * K;                 // split-K: this workgroup's first K row
+  const T* Ab = A + (size_t)m0 * lda + kz;
   uint32_t aoff[AU];
 #pragma unroll
   for (int u = 0; u < AU; ++u) {
@@ -78,7 +79,8 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm(const T* __restrict__ A, 
   auto sel = [&](int sg, auto a0, auto a1, auto a2, auto a3) {
     return sg == 0 ? a0 : (sg == 1 ? a1 : (sg == 2 ? a2 : a3));
   };
-  const T* Bb = sel(seg0, s0, s1, s2, s3) + (n0 - sel(seg0, bp.start[0], bp.start[1], bp.start[2], bp.start[3]));
+  const T* Bb = sel(seg0, s0, s1, s2, s3) + (n0 - sel(seg0, bp.start[0], bp.start[1], bp.start[2], bp.start[3])) +
+                (size_t)kz * sel(seg0, bp.ld[0], bp.ld[1], bp.ld[2], bp.ld[3]);
   const int64_t ldb0 = sel(seg0, bp.ld[0], bp.ld[1], bp.ld[2], bp.ld[3]);
   uint32_t boff[BU];
   int bcol[BU];
@@ -104,7 +106,7 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm(const T* __restrict__ A, 
         const int row = idx / (BN / 8);
         const int sg = seg_of(bcol[u]);
         const T* src = sel(sg, s0, s1, s2, s3) + (bcol[u] - sel(sg, bp.start[0], bp.start[1], bp.start[2], bp.start[3]));
-        load_row8(rb[u], src + (size_t)(k0 + row) * sel(sg, bp.ld[0], bp.ld[1], bp.ld[2], bp.ld[3]), true);
+        load_row8(rb[u], src + (size_t)(kz + k0 + row) * sel(sg, bp.ld[0], bp.ld[1], bp.ld[2], bp.ld[3]), true);
       }
     }
   };
@@ -243,7 +245,7 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm(const T* __restrict__ A, 
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[e] = src[e];
       const int sg = seg_of(col);
-      if (sg < bp.rope_segs) {
+      if (sg < bp.rope_segs && !bp.part) {
         const float2* cs = bp.rope_tab + (size_t)(row % bp.seqlen) * (bp.rope_d / 2) +
                            (((col - bp.start[sg]) % bp.rope_d) >> 1);
 #pragma unroll
@@ -254,12 +256,89 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm(const T* __restrict__ A, 
           v[2 * p + 1] = x * t.y + y * t.x;
         }
       }
+      if (bp.part) {                               // split-K partial: float32, no rotation
+        Row8<float> o;
+        pack_row8(o, v);
+        store_row8(bp.part + (size_t)blockIdx.z * M * ldc + (size_t)row * ldc + col, o);
+        continue;
+      }
       Row8<T> o;
       pack_row8(o, v);
       store_row8(C + (size_t)row * ldc + col, o);
     }
     __syncthreads();
   }
+}
+
+// Sum of the split-K partials, rounded once: 8 consecutive columns per thread.
+template <class T>
+__global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__ part, int splits,
+                                                       T* __restrict__ C, int64_t ldc, int M, int N) {
+  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t row = g / (N / 8), col = (g % (N / 8)) * 8;
+  if (row >= M) return;
+  float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int z = 0; z < splits; ++z) {
+    const float* p = part + ((int64_t)z * M + row) * N + col;
+    const f32x4 a = *reinterpret_cast<const f32x4*>(p), b = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { v[e] += a[e]; v[4 + e] += b[e]; }
+  }
+  Row8<T> o;
+  pack_row8(o, v);
+  store_row8(C + row * ldc + col, o);
+}
+
+int gemm_splits(int M, int N, int K) {
+  // enough workgroups to cover the CUs, at most 8 slices, each a multiple of 64 rows of K
+  const int tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  int s = 1;
+  while (s < 8 && tiles * s < 256 && K % (64 * 2 * s) == 0) s *= 2;
+  return s;
+}
+
+hipError_t launch_gemm_splitk(Elt elt, const void* A, int64_t lda, const GemmB& b, void* C, int64_t ldc, int M,
+                              int N, int K, int splits, float* part, hipStream_t st) {
+  if (M == 0 || N == 0) return hipSuccess;
+  GemmB bs = b;
+  bs.part = part;
+  bs.rope_segs = 0;
+  const int Ks = K / splits;
+  hipError_t err;
+  {
+    TraceScope ts("k_gemm", st);
+    const int BN = elt == kBF16 ? 256 : 128;
+    bool uni = true;
+    for (int sgi = 1; sgi < 4; ++sgi)
+      if (bs.start[sgi] < N && bs.start[sgi] % BN) uni = false;
+    if (elt == kBF16) {
+      dim3 grid((N + 255) / 256, (M + 255) / 256, splits);
+      if (uni)
+        hipLaunchKernelGGL((k_gemm<bf16, 256, 256, 64, 2, 2, true>), grid, dim3(256), 0, st, (const bf16*)A, lda,
+                           bs, (bf16*)nullptr, (int64_t)N, M, N, Ks);
+      else
+        hipLaunchKernelGGL((k_gemm<bf16, 256, 256, 64, 2, 2, false>), grid, dim3(256), 0, st, (const bf16*)A, lda,
+                           bs, (bf16*)nullptr, (int64_t)N, M, N, Ks);
+    } else {
+      dim3 grid((N + 127) / 128, (M + 127) / 128, splits);
+      if (uni)
+        hipLaunchKernelGGL((k_gemm<float, 128, 128, 32, 2, 2, true>), grid, dim3(256), 0, st, (const float*)A, lda,
+                           bs, (float*)nullptr, (int64_t)N, M, N, Ks);
+      else
+        hipLaunchKernelGGL((k_gemm<float, 128, 128, 32, 2, 2, false>), grid, dim3(256), 0, st, (const float*)A,
+                           lda, bs, (float*)nullptr, (int64_t)N, M, N, Ks);
+    }
+    err = hipGetLastError();
+  }
+  if (err != hipSuccess) return err;
+  TraceScope ts("k_splitk_reduce", st);
+  const int64_t groups = (int64_t)M * (N / 8);
+  const dim3 grid((unsigned)((groups + 255) / 256));
+  if (elt == kBF16)
+    hipLaunchKernelGGL((k_splitk_reduce<bf16>), grid, dim3(256), 0, st, part, splits, (bf16*)C, ldc, M, N);
+  else
+    hipLaunchKernelGGL((k_splitk_reduce<float>), grid, dim3(256), 0, st, part, splits, (float*)C, ldc, M, N);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm(Elt elt, const void* A, int64_t lda, const GemmB& b, void* C, int64_t ldc, int M, int N,

@@ -1,5 +1,6 @@
 // libmsr C ABI: argument validation, workspace layout and dispatch.
 // The operations and their arguments are documented in include/msr.h.
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -155,16 +156,26 @@ template <class P> P* at(void* base, size_t off) { return reinterpret_cast<P*>(s
 }  // namespace
 
 struct DecodeWs {
-  size_t qkvg = 0, o = 0, z = 0, total = 0;
+  size_t qkvg = 0, o = 0, z = 0, part = 0, total = 0;
+  int split_qkvg = 1, split_o = 1;
 };
-DecodeWs decode_ws_layout(msr_dtype dt, int32_t batch, int32_t heads, int32_t dk, int32_t dv) {
+// Few rows (one per sequence): the projections split K over several
+// workgroups (float32 partials) so that the weight stream covers the CUs.
+DecodeWs decode_ws_layout(msr_dtype dt, int32_t batch, int32_t d_model, int32_t heads, int32_t dk, int32_t dv) {
   DecodeWs w;
   const size_t es = elt_size(dt);
-  const size_t ntot = (size_t)heads * (2 * dk + 2 * dv);
+  const int ntot = heads * (2 * dk + 2 * dv), hv = heads * dv;
+  if (batch <= 256) {
+    w.split_qkvg = gemm_splits(batch, ntot, d_model);
+    w.split_o = gemm_splits(batch, d_model, hv);
+  }
+  const size_t part = std::max((size_t)(w.split_qkvg > 1 ? w.split_qkvg : 0) * batch * ntot,
+                               (size_t)(w.split_o > 1 ? w.split_o : 0) * batch * d_model);
   size_t off = 0;
   w.qkvg = off; off += align_up((size_t)batch * ntot * es);
-  w.o = off; off += align_up((size_t)batch * heads * dv * sizeof(float));
-  w.z = off; off += align_up((size_t)batch * heads * dv * es);
+  w.o = off; off += align_up((size_t)batch * hv * sizeof(float));
+  w.z = off; off += align_up((size_t)batch * hv * es);
+  w.part = off; off += align_up(part * sizeof(float));
   w.total = off;
   return w;
 }
@@ -314,7 +325,8 @@ size_t msr_layer_decode_workspace_bytes(msr_dtype dtype, int32_t batch, int32_t 
                                         int32_t d_v) {
   (void)d_model;
   if (check_dtype(dtype) || check_heads(batch, 1, heads, d_k, d_v) || batch == 0) return 0;
-  return decode_ws_layout(dtype, batch, heads, d_k, d_v).total;
+  if (d_model <= 0 || d_model % 64) return 0;
+  return decode_ws_layout(dtype, batch, d_model, heads, d_k, d_v).total;
 }
 
 msr_status msr_layer_decode_step(msr_dtype dtype, int32_t batch, int32_t d_model, int32_t heads, int32_t d_k,
@@ -334,7 +346,7 @@ msr_status msr_layer_decode_step(msr_dtype dtype, int32_t batch, int32_t d_model
   if (!X || !W_Q || !W_K || !W_V || !W_G || !W_O || !S || !out)
     return fail(MSR_ERR_NULL, "X, W_Q, W_K, W_V, W_G, W_O, S and out must be non-NULL");
   if ((int64_t)batch * heads > (int64_t)INT32_MAX) return fail(MSR_ERR_UNSUPPORTED, "batch*heads too large");
-  const DecodeWs w = decode_ws_layout(dtype, batch, heads, d_k, d_v);
+  const DecodeWs w = decode_ws_layout(dtype, batch, d_model, heads, d_k, d_v);
   if (!workspace || ws_bytes < w.total)
     return fail(MSR_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", w.total, workspace ? ws_bytes : 0);
   hipStream_t st = (hipStream_t)stream;
@@ -351,7 +363,10 @@ msr_status msr_layer_decode_step(msr_dtype dtype, int32_t batch, int32_t d_model
   bq.ld[0] = hk; bq.ld[1] = hk; bq.ld[2] = hv; bq.ld[3] = hv;
   bq.start[0] = 0; bq.start[1] = hk; bq.start[2] = 2 * hk; bq.start[3] = 2 * hk + hv;
   bq.rope_segs = 0;
-  hipError_t err = launch_gemm(e, X, d_model, bq, qkvg, ntot, batch, ntot, d_model, st);
+  float* part = at<float>(workspace, w.part);
+  hipError_t err = w.split_qkvg > 1
+                       ? launch_gemm_splitk(e, X, d_model, bq, qkvg, ntot, batch, ntot, d_model, w.split_qkvg, part, st)
+                       : launch_gemm(e, X, d_model, bq, qkvg, ntot, batch, ntot, d_model, st);
   if (err != hipSuccess) return from_hip(err, "msr_layer_decode_step(projections)");
   // 2. q, k rotated at pos; S <- gamma S + k^T v; o = q S / sqrt(d_k) (float32)
   const HeadTab tab = make_tab(gamma, heads, 1, 1);
@@ -366,7 +381,8 @@ msr_status msr_layer_decode_step(msr_dtype dtype, int32_t batch, int32_t d_model
   GemmB bo{};
   bo.ptr[0] = W_O; bo.ld[0] = d_model;
   bo.start[0] = 0; bo.start[1] = bo.start[2] = bo.start[3] = INT32_MAX;
-  err = launch_gemm(e, z, hv, bo, out, d_model, batch, d_model, hv, st);
+  err = w.split_o > 1 ? launch_gemm_splitk(e, z, hv, bo, out, d_model, batch, d_model, hv, w.split_o, part, st)
+                      : launch_gemm(e, z, hv, bo, out, d_model, batch, d_model, hv, st);
   return from_hip(err, "msr_layer_decode_step(output projection)");
 }
 

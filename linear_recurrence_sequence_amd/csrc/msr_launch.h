@@ -87,11 +87,22 @@ struct GemmB {
   int start[4];
   int rope_segs, rope_d, seqlen;
   const float2* rope_tab;
+  // split-K: when set, workgroup z of the launch's z dimension sums K rows
+  // [z K_s, (z + 1) K_s) and stores float32 partials to part + z M N (no
+  // rotation); launch_gemm_splitk adds them up.
+  float* part;
 };
 
 // C[M, N] = A[M, K] * B[K, N] (row-major A and B segments), fp32
 // accumulation, C (row stride ldc) in elt.  K must be a multiple of 64.
 hipError_t launch_gemm(Elt elt, const void* A, int64_t lda, const GemmB& b, void* C, int64_t ldc, int M, int N,
                        int K, hipStream_t stream);
+// The same product for few rows (M <= 256): the K range split over
+// `splits` workgroups per output tile (K a multiple of 64 * splits), float32
+// partials in `part` ([splits, M, N]), then summed and rounded once into C.
+hipError_t launch_gemm_splitk(Elt elt, const void* A, int64_t lda, const GemmB& b, void* C, int64_t ldc, int M,
+                              int N, int K, int splits, float* part, hipStream_t stream);
+// How many K splits launch_gemm_splitk should use for an M x N x K product.
+int gemm_splits(int M, int N, int K);
 
 }  // namespace msr

@@ -140,11 +140,14 @@ def test_workspace_sizes():
     assert msr.msr_parallel_workspace_bytes(1, B, N, H, dk, dv, 0.0) == 0
     assert msr.msr_layer_workspace_bytes(1, 2, 64, 256, 2, 64, 64, 32) > 0
     assert msr.msr_layer_workspace_bytes(1, 2, 64, 256, 2, 64, 64, 0) == 0
-    # layer decode step: [q|k|v|g] rows (element type), float32 outputs, Z (element type)
-    Bd, Hd, kd, vd = 5, 3, 256, 512
-    assert msr.msr_layer_decode_workspace_bytes(1, Bd, 256, Hd, kd, vd) == (
-        up(Bd * Hd * (2 * kd + 2 * vd) * 2) + up(Bd * Hd * vd * 4) + up(Bd * Hd * vd * 2))
-    assert msr.msr_layer_decode_workspace_bytes(1, 0, 256, Hd, kd, vd) == 0
+    # layer decode step: [q|k|v|g] rows (element type), float32 outputs, Z (element type), and
+    # float32 split-K partials of the projections (at most 8 slices of the larger product)
+    Bd, Hd, kd, vd, dm = 5, 3, 256, 512, 256
+    base = up(Bd * Hd * (2 * kd + 2 * vd) * 2) + up(Bd * Hd * vd * 4) + up(Bd * Hd * vd * 2)
+    got = msr.msr_layer_decode_workspace_bytes(1, Bd, dm, Hd, kd, vd)
+    assert base <= got <= base + up(8 * Bd * max(Hd * (2 * kd + 2 * vd), dm) * 4)
+    assert msr.msr_layer_decode_workspace_bytes(1, 0, dm, Hd, kd, vd) == 0
+    assert msr.msr_layer_decode_workspace_bytes(1, Bd, 100, Hd, kd, vd) == 0
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
