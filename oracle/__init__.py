@@ -22,6 +22,9 @@ from .retention import (  # noqa: F401
     swish,
     msr_layer,
     msr_layer_decode_step,
+    layer_norm,
+    gelu,
+    retnet_block,
     max_rel_err,
     max_rel_err_per_head,
 )

@@ -323,6 +323,45 @@ def msr_layer_decode_step(x, S, WQ, WK, WV, WG, WO, gamma, heads, d_k, d_v, pos,
 
 
 # --------------------------------------------------------------------------
+# The RetNet block around the layer
+# --------------------------------------------------------------------------
+def layer_norm(X, eps: float):
+    """LayerNorm over the last axis ([RN-zh] "Retention 網路總體結構" names
+    LayerNorm [BKH16]): biased variance, identity affine (no parameters are
+    given), (x - mean) / sqrt(var + eps)."""
+    X = _f64(X)
+    mu = X.mean(axis=-1, keepdims=True)
+    var = ((X - mu) ** 2).mean(axis=-1, keepdims=True)
+    return (X - mu) / np.sqrt(var + eps)
+
+
+def gelu(x):
+    """gelu(x) = x * Phi(x), Phi the standard normal distribution function
+    (the exact, erf form)."""
+    from scipy.special import erf
+    x = _f64(x)
+    return 0.5 * x * (1.0 + erf(x / math.sqrt(2.0)))
+
+
+def retnet_block(X, WQ, WK, WV, WG, WO, W1, W2, gamma, heads, d_k, d_v, chunk=None,
+                 rope_base=10000.0, gn_eps=1e-5, ln_eps=1e-5):
+    """One RetNet block ([RN-zh] "Retention 網路總體結構"): the layer of
+    Eq. (8) and the feed-forward network FFN(X) = gelu(X W_1) W_2, each
+    behind a LayerNorm and with a residual connection:
+
+      Y   = MSR(LN(X)) + X
+      out = FFN(LN(Y)) + Y
+
+    X: [B, N, d_model]; W_1: [d_model, d_ffn]; W_2: [d_ffn, d_model]; the
+    layer's weights as in msr_layer.
+    """
+    X = _f64(X)
+    Y = msr_layer(layer_norm(X, ln_eps), WQ, WK, WV, WG, WO, gamma, heads, d_k, d_v, chunk,
+                  rope_base=rope_base, eps=gn_eps) + X
+    return gelu(layer_norm(Y, ln_eps) @ _f64(W1)) @ _f64(W2) + Y
+
+
+# --------------------------------------------------------------------------
 # Error measures
 # --------------------------------------------------------------------------
 def max_rel_err(got, ref):

@@ -364,3 +364,57 @@ def test_layer_decode_steps_reproduce_the_layer_forward():
     y2 = oracle.group_norm_heads(o2, 1e-5).reshape(B, 4, H * dv)
     ref2 = (oracle.swish(X2 @ WG) * y2) @ WO
     assert np.max(np.abs(np.stack(outs, axis=1) - ref2)) < 1e-12
+
+
+def test_layer_norm_moments_and_invariance():
+    """LayerNorm output rows have mean 0 and (at eps = 0) variance 1, and
+    LN(a x + b) = LN(x) for a > 0 and any shift b, row by row."""
+    rng = np.random.default_rng(21)
+    X = rng.standard_normal((3, 5, 12)) * 3 + 1
+    Y = oracle.layer_norm(X, 0.0)
+    assert np.max(np.abs(Y.mean(axis=-1))) < 1e-12
+    assert np.max(np.abs((Y ** 2).mean(axis=-1) - 1)) < 1e-12
+    a = rng.uniform(0.1, 10, (3, 5, 1))
+    b = rng.standard_normal((3, 5, 1))
+    assert np.max(np.abs(oracle.layer_norm(a * X + b, 0.0) - Y)) < 1e-12
+    # eps shrinks the output by sqrt(var / (var + eps))
+    var = X.var(axis=-1, keepdims=True)
+    assert np.max(np.abs(oracle.layer_norm(X, 0.5) - Y * np.sqrt(var / (var + 0.5)))) < 1e-12
+
+
+def test_gelu_closed_forms():
+    """gelu(x) = x Phi(x): gelu(0) = 0, gelu(x) - gelu(-x) = x, gelu(1) =
+    Phi(1) = 0.841344746068542948..., gelu(-1) = Phi(1) - 1, and gelu(x) ->
+    x (resp. 0) for large positive (negative) x."""
+    x = np.linspace(-6, 6, 101)
+    assert oracle.gelu(np.array([0.0]))[0] == 0.0
+    assert np.max(np.abs(oracle.gelu(x) - oracle.gelu(-x) - x)) < 1e-12
+    phi1 = 0.841344746068542948585232545632
+    assert abs(oracle.gelu(np.array([1.0]))[0] - phi1) < 1e-15
+    assert abs(oracle.gelu(np.array([-1.0]))[0] - (phi1 - 1.0)) < 1e-15
+    assert abs(oracle.gelu(np.array([12.0]))[0] - 12.0) < 1e-12
+    assert abs(oracle.gelu(np.array([-12.0]))[0]) < 1e-12
+
+
+def test_retnet_block_wiring():
+    """The block's residual wiring: with W_1 = 0 the feed-forward branch
+    vanishes and out = MSR(LN(X)) + X; with W_O = 0 the layer's branch
+    vanishes and out = X + gelu(LN(X) W_1) W_2; with both, out = X."""
+    rng = np.random.default_rng(22)
+    B, N, dm, H, dk, dv, F = 2, 7, 16, 2, 4, 4, 24
+    X = rng.standard_normal((B, N, dm))
+    WQ, WK = (rng.standard_normal((dm, H * dk)) / 4 for _ in range(2))
+    WV, WG = (rng.standard_normal((dm, H * dv)) / 4 for _ in range(2))
+    WO = rng.standard_normal((H * dv, dm)) / 4
+    W1 = rng.standard_normal((dm, F)) / 4
+    W2 = rng.standard_normal((F, dm)) / 4
+    g = np.array([0.9, 0.5])
+    Z1, ZO = np.zeros_like(W1), np.zeros_like(WO)
+    msr_x = oracle.msr_layer(oracle.layer_norm(X, 1e-5), WQ, WK, WV, WG, WO, g, H, dk, dv, form="parallel")
+    got = oracle.retnet_block(X, WQ, WK, WV, WG, WO, Z1, W2, g, H, dk, dv, chunk=3)
+    assert np.max(np.abs(got - (msr_x + X))) < 1e-12
+    got = oracle.retnet_block(X, WQ, WK, WV, WG, ZO, W1, W2, g, H, dk, dv, chunk=3)
+    ffn = oracle.gelu(oracle.layer_norm(X, 1e-5) @ W1) @ W2
+    assert np.max(np.abs(got - (X + ffn))) < 1e-12
+    got = oracle.retnet_block(X, WQ, WK, WV, WG, ZO, Z1, W2, g, H, dk, dv, chunk=3)
+    assert np.max(np.abs(got - X)) < 1e-15
