@@ -303,6 +303,37 @@ def bench_layer_decode(n_steps, warmup):
     return res
 
 
+def bench_retnet_block(steps, warmup):
+    """RetNet block (LayerNorm, the gated layer, residual, LayerNorm, gelu
+    feed-forward network of width 2 d_model, residual) at the headline
+    layer's shape, bf16."""
+    import torch
+    import linear_recurrence_sequence_amd as msr
+    import workloads
+    w = workloads.WORKLOADS["layer_bf16_b8_n2048"]
+    F = 2 * w.d_model
+    X, WQ, WK, WV, WG, WO = make_layer(w, True)
+    s = w.d_model ** -0.5
+    W1 = (workloads.device_normal((w.d_model, F), seed=950) * s).to(torch.bfloat16)
+    W2 = (workloads.device_normal((F, w.d_model), seed=951) * F ** -0.5).to(torch.bfloat16)
+    g = workloads.gammas(w.heads)
+    out = torch.empty_like(X)
+    ws = torch.empty(msr.msr_retnet_block_workspace_bytes(1, w.batch, w.seqlen, w.d_model, w.heads, w.d_k, w.d_v,
+                                                          w.chunk, F), dtype=torch.uint8, device="cuda")
+    fn = lambda: msr.msr_retnet_block_fwd(X, WQ, WK, WV, WG, WO, W1, W2, g, w.heads, w.d_k, w.d_v, w.chunk,
+                                          rope_base=w.rope_base, out=out, workspace=ws)
+    t = gpu_time(fn, steps, warmup)
+    tr = traced(fn, steps)
+    proj, core = layer_flops(w.batch, w.seqlen, w.d_model, w.heads, w.d_k, w.d_v, w.chunk)
+    ffn = w.batch * w.seqlen * 2 * 2 * w.d_model * F
+    fl = proj + core + ffn
+    del X, WQ, WK, WV, WG, WO, W1, W2, out, ws
+    torch.cuda.empty_cache()
+    return {"d_ffn": F, "tokens_per_s": round(w.batch * w.seqlen / t, 1), "ms_per_step": round(t * 1e3, 3),
+            "tflops": round(fl / t / 1e12, 1), "mfma_frac": round(fl / t / PEAK_BF16, 4),
+            "trace_ms_per_step": {k: round(v[0] / steps * 1e3, 4) for k, v in tr.items()}}
+
+
 def bench_copy(nbytes=1 << 30, reps=8):
     """A plain device-to-device copy of a known size: the calibration run for
     the FETCH_SIZE / WRITE_SIZE counters (each reads nbytes and writes nbytes
@@ -353,7 +384,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", default="layer,decode,long,block,cpu")
+    ap.add_argument("--only", default="layer,decode,long,block,retnet,cpu")
     ap.add_argument("--no-cpu", action="store_true")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -418,6 +449,9 @@ def main():
         line["block"] = {"tokens_per_s": round(br["tokens_per_s"], 1), "mfma_frac": round(br["mfma_frac"], 4),
                          "ms_per_step": round(br["s_per_step"] * 1e3, 3), "tflops": round(br["tflops"], 1),
                          "kernels": br["kernels"]}
+    if "retnet" in parts:
+        log("retnet block")
+        line["retnet_block"] = bench_retnet_block(max(3, args.steps // 2), 2)
     if "copy" in parts:
         log("copy calibration")
         line["copy_calibration"] = bench_copy()

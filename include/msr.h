@@ -30,8 +30,8 @@
  *           caller; the library allocates nothing and, apart from the
  *           opt-in msr_trace_* diagnostics, keeps no mutable global state
  *           (it is thread safe).  Outputs must not alias
- *           inputs, except S of msr_recurrent_step, which is updated in
- *           place.
+ *           inputs, except S of msr_recurrent_step and
+ *           msr_layer_decode_step, which is updated in place.
  * Streams.  `stream` is a hipStream_t (NULL = the null stream).  Every call
  *           only enqueues work and returns without synchronising.
  * Errors.   All arguments are validated on the host before anything is
@@ -133,6 +133,29 @@ msr_status msr_layer_fwd(msr_dtype dtype, int32_t batch, int32_t seqlen,
 size_t msr_layer_workspace_bytes(msr_dtype dtype, int32_t batch, int32_t seqlen,
                                  int32_t d_model, int32_t heads, int32_t d_k,
                                  int32_t d_v, int32_t chunk);
+
+/* One RetNet block around the layer, [RN-zh] section "Retention 網路總體結構":
+ * the layer of Eq. (8) and the feed-forward network FFN(X) = gelu(X W_1) W_2,
+ * each behind a LayerNorm and with a residual connection (pre-LayerNorm):
+ *   Y   = MSR(LN(X)) + X
+ *   out = FFN(LN(Y)) + Y
+ * LN: per token over d_model, biased variance, identity affine, ln_eps;
+ * gelu(x) = x Phi(x) (erf form).  X, out: [batch, seqlen, d_model]; the
+ * layer's weights as in msr_layer_fwd; W_1: [d_model, d_ffn]; W_2:
+ * [d_ffn, d_model].  Y and the hidden rows are kept in the element type.
+ * d_model (at most 8192) and d_ffn must be multiples of 64.
+ * Workspace: msr_retnet_block_workspace_bytes() bytes. */
+msr_status msr_retnet_block_fwd(msr_dtype dtype, int32_t batch, int32_t seqlen,
+                                int32_t d_model, int32_t heads, int32_t d_k, int32_t d_v,
+                                int32_t chunk, int32_t d_ffn, const double* gamma,
+                                float rope_base, float gn_eps, float ln_eps,
+                                const void* X, const void* W_Q, const void* W_K,
+                                const void* W_V, const void* W_G, const void* W_O,
+                                const void* W_1, const void* W_2, void* out,
+                                void* workspace, size_t ws_bytes, void* stream);
+size_t msr_retnet_block_workspace_bytes(msr_dtype dtype, int32_t batch, int32_t seqlen,
+                                        int32_t d_model, int32_t heads, int32_t d_k,
+                                        int32_t d_v, int32_t chunk, int32_t d_ffn);
 
 /* One decode step of the gated MSR layer: Eq. (8) of [RN-zh] with the
  * recurrent form of retention, Eq. (6), for one new token per sequence:

@@ -20,6 +20,7 @@ __all__ = [
     "msr_chunkwise_fwd", "msr_chunkwise_workspace_bytes",
     "msr_recurrent_step", "msr_layer_fwd", "msr_layer_workspace_bytes",
     "msr_layer_decode_step", "msr_layer_decode_workspace_bytes",
+    "msr_retnet_block_fwd", "msr_retnet_block_workspace_bytes",
     "msr_status_str", "msr_last_error", "msr_trace_enable", "msr_trace_count", "msr_trace_get",
     "trace_totals",
 ]
@@ -29,7 +30,7 @@ EXPORTS = (
     "msr_parallel_fwd", "msr_parallel_workspace_bytes", "msr_chunkwise_fwd",
     "msr_chunkwise_workspace_bytes", "msr_recurrent_step", "msr_layer_fwd",
     "msr_layer_workspace_bytes", "msr_layer_decode_step", "msr_layer_decode_workspace_bytes",
-    "msr_status_str", "msr_last_error", "msr_trace_enable", "msr_trace_count", "msr_trace_get",
+    "msr_retnet_block_fwd", "msr_retnet_block_workspace_bytes", "msr_status_str", "msr_last_error", "msr_trace_enable", "msr_trace_count", "msr_trace_get",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -84,6 +85,9 @@ def lib():
         "msr_layer_decode_step": (_I32, [_I32, _I32, _I32, _I32, _I32, _I32, _DP, _F, _F, _I64, _P, _P, _P, _P,
                                          _P, _P, _P, _P, _P, _SZ, _P]),
         "msr_layer_decode_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32]),
+        "msr_retnet_block_fwd": (_I32, [_I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _DP, _F, _F, _F,
+                                        _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+        "msr_retnet_block_workspace_bytes": (_SZ, [_I32] * 9),
         "msr_trace_enable": (None, [_I32]),
         "msr_trace_count": (_I32, []),
         "msr_trace_get": (_I32, [_I32, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_double),
@@ -255,6 +259,28 @@ def msr_layer_fwd(X, W_Q, W_K, W_V, W_G, W_O, gamma, heads, d_k, d_v, chunk, *, 
     _check("msr_layer_fwd", lib().msr_layer_fwd(dt, B, N, dm, heads, d_k, d_v, chunk, gp, rope_base, gn_eps,
                                                 _ptr(X), _ptr(W_Q), _ptr(W_K), _ptr(W_V), _ptr(W_G), _ptr(W_O),
                                                 _ptr(out), _ptr(ws), wsb, _stream(stream)))
+    return out
+
+
+def msr_retnet_block_workspace_bytes(dtype, batch, seqlen, d_model, heads, d_k, d_v, chunk, d_ffn):
+    return lib().msr_retnet_block_workspace_bytes(dtype, batch, seqlen, d_model, heads, d_k, d_v, chunk, d_ffn)
+
+
+def msr_retnet_block_fwd(X, W_Q, W_K, W_V, W_G, W_O, W_1, W_2, gamma, heads, d_k, d_v, chunk, *,
+                         rope_base=10000.0, gn_eps=1e-5, ln_eps=1e-5, out=None, workspace=None, stream=None):
+    """One RetNet block: Y = MSR(LN(X)) + X, out = gelu(LN(Y) W_1) W_2 + Y.  X: [B, N, d_model]."""
+    B, N, dm = X.shape
+    d_ffn = W_1.shape[1]
+    dt = _dtype_code(X)
+    if out is None:
+        out = _torch().empty((B, N, dm), dtype=X.dtype, device=X.device)
+    _, gp = g = _gamma(gamma, heads)
+    nbytes = lib().msr_retnet_block_workspace_bytes(dt, B, N, dm, heads, d_k, d_v, chunk, d_ffn)
+    ws, wsb = _workspace(nbytes, workspace, X.device)
+    _check("msr_retnet_block_fwd",
+           lib().msr_retnet_block_fwd(dt, B, N, dm, heads, d_k, d_v, chunk, d_ffn, gp, rope_base, gn_eps, ln_eps,
+                                      _ptr(X), _ptr(W_Q), _ptr(W_K), _ptr(W_V), _ptr(W_G), _ptr(W_O), _ptr(W_1),
+                                      _ptr(W_2), _ptr(out), _ptr(ws), wsb, _stream(stream)))
     return out
 
 

@@ -14,6 +14,9 @@
 // by the (cos, sin) of their row's position (row % seqlen) before the single
 // rounding to the output type.
 //
+// The epilogue optionally applies gelu and adds a residual matrix (the
+// RetNet block's feed-forward network and skip connections).
+//
 // bf16: 256x256 output tile, 4 waves of 128x128 (16 accumulator tiles each,
 // held in the accumulation registers; a 128x128 wave tile reads 64 bytes of
 // LDS per clock at the matrix-core peak, a 128x64 one 96), 64-deep K slabs
@@ -255,6 +258,18 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm(const T* __restrict__ A, 
           v[2 * p] = x * t.x - y * t.y;
           v[2 * p + 1] = x * t.y + y * t.x;
         }
+      }
+      if (bp.act == 1) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = 0.5f * v[e] * (1.0f + erff(v[e] * 0.70710678118654752f));
+      }
+      if (bp.resid) {
+        Row8<T> rr8;
+        load_row8(rr8, reinterpret_cast<const T*>(bp.resid) + (size_t)row * bp.ldr + col, true);
+        float rv[8];
+        unpack_row8(rv, rr8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] += rv[e];
       }
       if (bp.part) {                               // split-K partial: float32, no rotation
         Row8<float> o;

@@ -180,6 +180,86 @@ DecodeWs decode_ws_layout(msr_dtype dt, int32_t batch, int32_t d_model, int32_t 
   return w;
 }
 
+// RetNet block: the layer's workspace, then LN output, Y, and the
+// feed-forward hidden rows.
+struct BlockWs {
+  LayerWs lw;
+  size_t layer = 0, h = 0, y = 0, f = 0, total = 0;
+};
+BlockWs block_ws_layout(msr_dtype dt, int32_t batch, int32_t seqlen, int32_t d_model, int32_t heads, int32_t dk,
+                        int32_t dv, int32_t chunk, int32_t d_ffn) {
+  BlockWs w;
+  const size_t es = elt_size(dt);
+  const size_t M = (size_t)batch * seqlen;
+  w.lw = layer_ws_layout(dt, batch, seqlen, d_model, heads, dk, dv, chunk);
+  size_t off = 0;
+  w.layer = off; off += align_up(w.lw.total);
+  w.h = off; off += align_up(M * d_model * es);
+  w.y = off; off += align_up(M * d_model * es);
+  w.f = off; off += align_up(M * (size_t)d_ffn * es);
+  w.total = off;
+  return w;
+}
+
+// The layer's launches on validated arguments; the output projection adds
+// `resid` ([M, d_model], nullable) in its epilogue.
+static msr_status layer_launch(msr_dtype dtype, int32_t batch, int32_t seqlen, int32_t d_model, int32_t heads,
+                               int32_t d_k, int32_t d_v, int32_t chunk, const double* gamma, float rope_base,
+                               float gn_eps, const void* X, const void* W_Q, const void* W_K, const void* W_V,
+                               const void* W_G, const void* W_O, void* out, const void* resid, const LayerWs& w,
+                               void* workspace, void* stream) {
+  const int64_t M = (int64_t)batch * seqlen;
+  hipStream_t st = (hipStream_t)stream;
+  const Elt e = dtype == MSR_BF16 ? kBF16 : kF32;
+  const size_t es = elt_size(dtype);
+  const int hk = heads * d_k, hv = heads * d_v;
+  const int ntot = 2 * hk + 2 * hv;
+  char* qkvg = at<char>(workspace, w.qkvg);
+  char* z = at<char>(workspace, w.z);
+  float2* tab = at<float2>(workspace, w.tab);
+  void* cws = at<void>(workspace, w.chunk);
+  const bool rope = rope_base > 0.f;
+
+  // 1. (cos, sin) table of the positions 0..seqlen-1
+  hipError_t err = rope ? launch_rope_table(tab, seqlen, d_k, 0, rope_base, st) : hipSuccess;
+  // 2. [Q | K | V | G] = X [W_Q | W_K | W_V | W_G], Q and K rotated in the epilogue
+  GemmB bq{};
+  bq.ptr[0] = W_Q; bq.ptr[1] = W_K; bq.ptr[2] = W_V; bq.ptr[3] = W_G;
+  bq.ld[0] = hk; bq.ld[1] = hk; bq.ld[2] = hv; bq.ld[3] = hv;
+  bq.start[0] = 0; bq.start[1] = hk; bq.start[2] = 2 * hk; bq.start[3] = 2 * hk + hv;
+  bq.rope_segs = rope ? 2 : 0;
+  bq.rope_d = d_k;
+  bq.seqlen = seqlen;
+  bq.rope_tab = tab;
+  if (err == hipSuccess) err = launch_gemm(e, X, d_model, bq, qkvg, ntot, (int)M, ntot, d_model, st);
+  if (err != hipSuccess) return from_hip(err, "msr_layer_fwd(projections)");
+  // 3. chunkwise retention + per-head GroupNorm + swish gate -> Z
+  ChunkArgs a{};
+  a.elt = e;
+  a.d_k = d_k; a.d_v = d_v; a.batch = batch; a.seqlen = seqlen; a.heads = heads;
+  a.chunk = chunk;
+  a.Q = qkvg; a.ldq = ntot;
+  a.K = qkvg + (size_t)hk * es; a.ldk = ntot;
+  a.V = qkvg + (size_t)2 * hk * es; a.ldv = ntot;
+  a.G = qkvg + (size_t)(2 * hk + hv) * es; a.ldg = ntot;
+  a.O = z; a.ldo = hv;
+  a.scale = 1.0f / std::sqrt((float)d_k);
+  a.eps = gn_eps;
+  a.fuse_gn_gate = true;
+  a.dR = at<void>(cws, w.cw.dr);
+  a.Rx = at<void>(cws, w.cw.rx);
+  const HeadTab htab = make_tab(gamma, heads, chunk, seqlen);
+  err = launch_chunkwise(a, htab, st);
+  if (err != hipSuccess) return from_hip(err, "msr_layer_fwd(retention)");
+  // 4. out = Z W_O
+  GemmB bo{};
+  bo.ptr[0] = W_O; bo.ld[0] = d_model;
+  bo.start[0] = 0; bo.start[1] = bo.start[2] = bo.start[3] = INT32_MAX;
+  bo.resid = resid; bo.ldr = d_model;
+  err = launch_gemm(e, z, hv, bo, out, d_model, (int)M, d_model, hv, st);
+  return from_hip(err, "msr_layer_fwd(output projection)");
+}
+
 extern "C" {
 
 const char* msr_status_str(msr_status s) {
@@ -413,54 +493,68 @@ msr_status msr_layer_fwd(msr_dtype dtype, int32_t batch, int32_t seqlen, int32_t
   const LayerWs w = layer_ws_layout(dtype, batch, seqlen, d_model, heads, d_k, d_v, chunk);
   if (!workspace || ws_bytes < w.total)
     return fail(MSR_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", w.total, workspace ? ws_bytes : 0);
+  return layer_launch(dtype, batch, seqlen, d_model, heads, d_k, d_v, chunk, gamma, rope_base, gn_eps, X, W_Q, W_K,
+                      W_V, W_G, W_O, out, nullptr, w, workspace, stream);
+}
+
+size_t msr_retnet_block_workspace_bytes(msr_dtype dtype, int32_t batch, int32_t seqlen, int32_t d_model,
+                                        int32_t heads, int32_t d_k, int32_t d_v, int32_t chunk, int32_t d_ffn) {
+  if (check_dtype(dtype) || check_heads(batch, seqlen, heads, d_k, d_v) || check_chunk(chunk)) return 0;
+  if ((int64_t)batch * seqlen == 0 || d_model <= 0 || d_ffn <= 0) return 0;
+  return block_ws_layout(dtype, batch, seqlen, d_model, heads, d_k, d_v, chunk, d_ffn).total;
+}
+
+msr_status msr_retnet_block_fwd(msr_dtype dtype, int32_t batch, int32_t seqlen, int32_t d_model, int32_t heads,
+                                int32_t d_k, int32_t d_v, int32_t chunk, int32_t d_ffn, const double* gamma,
+                                float rope_base, float gn_eps, float ln_eps, const void* X, const void* W_Q,
+                                const void* W_K, const void* W_V, const void* W_G, const void* W_O,
+                                const void* W_1, const void* W_2, void* out, void* workspace, size_t ws_bytes,
+                                void* stream) {
+  msr_status s;
+  if ((s = check_dtype(dtype))) return s;
+  if ((s = check_heads(batch, seqlen, heads, d_k, d_v))) return s;
+  if ((s = check_matrix_dims(dtype, d_v))) return s;
+  if ((s = check_chunk(chunk))) return s;
+  if ((s = check_gamma(gamma, heads))) return s;
+  if (d_model <= 0 || d_ffn <= 0) return fail(MSR_ERR_SHAPE, "d_model = %d and d_ffn = %d must be positive", d_model, d_ffn);
+  if (d_model % 64 || d_ffn % 64)
+    return fail(MSR_ERR_UNSUPPORTED, "d_model = %d and d_ffn = %d must be multiples of 64", d_model, d_ffn);
+  if (d_model > 8192) return fail(MSR_ERR_UNSUPPORTED, "d_model = %d is above 8192", d_model);
+  if (!(gn_eps >= 0.f) || !(ln_eps >= 0.f)) return fail(MSR_ERR_SHAPE, "gn_eps and ln_eps must be >= 0");
+  const int64_t M = (int64_t)batch * seqlen;
+  if (M == 0) return ok();
+  if (!X || !W_Q || !W_K || !W_V || !W_G || !W_O || !W_1 || !W_2 || !out)
+    return fail(MSR_ERR_NULL, "X, the seven weights and out must be non-NULL");
+  if (M * (int64_t)d_ffn > (int64_t)INT32_MAX * 8) return fail(MSR_ERR_UNSUPPORTED, "batch*seqlen*d_ffn too large");
+  const BlockWs w = block_ws_layout(dtype, batch, seqlen, d_model, heads, d_k, d_v, chunk, d_ffn);
+  if (!workspace || ws_bytes < w.total)
+    return fail(MSR_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", w.total, workspace ? ws_bytes : 0);
   hipStream_t st = (hipStream_t)stream;
   const Elt e = dtype == MSR_BF16 ? kBF16 : kF32;
-  const size_t es = elt_size(dtype);
-  const int hk = heads * d_k, hv = heads * d_v;
-  const int ntot = 2 * hk + 2 * hv;
-  char* qkvg = at<char>(workspace, w.qkvg);
-  char* z = at<char>(workspace, w.z);
-  float2* tab = at<float2>(workspace, w.tab);
-  void* cws = at<void>(workspace, w.chunk);
-  const bool rope = rope_base > 0.f;
-
-  // 1. (cos, sin) table of the positions 0..seqlen-1
-  hipError_t err = rope ? launch_rope_table(tab, seqlen, d_k, 0, rope_base, st) : hipSuccess;
-  // 2. [Q | K | V | G] = X [W_Q | W_K | W_V | W_G], Q and K rotated in the epilogue
-  GemmB bq{};
-  bq.ptr[0] = W_Q; bq.ptr[1] = W_K; bq.ptr[2] = W_V; bq.ptr[3] = W_G;
-  bq.ld[0] = hk; bq.ld[1] = hk; bq.ld[2] = hv; bq.ld[3] = hv;
-  bq.start[0] = 0; bq.start[1] = hk; bq.start[2] = 2 * hk; bq.start[3] = 2 * hk + hv;
-  bq.rope_segs = rope ? 2 : 0;
-  bq.rope_d = d_k;
-  bq.seqlen = seqlen;
-  bq.rope_tab = tab;
-  if (err == hipSuccess) err = launch_gemm(e, X, d_model, bq, qkvg, ntot, (int)M, ntot, d_model, st);
-  if (err != hipSuccess) return from_hip(err, "msr_layer_fwd(projections)");
-  // 3. chunkwise retention + per-head GroupNorm + swish gate -> Z
-  ChunkArgs a{};
-  a.elt = e;
-  a.d_k = d_k; a.d_v = d_v; a.batch = batch; a.seqlen = seqlen; a.heads = heads;
-  a.chunk = chunk;
-  a.Q = qkvg; a.ldq = ntot;
-  a.K = qkvg + (size_t)hk * es; a.ldk = ntot;
-  a.V = qkvg + (size_t)2 * hk * es; a.ldv = ntot;
-  a.G = qkvg + (size_t)(2 * hk + hv) * es; a.ldg = ntot;
-  a.O = z; a.ldo = hv;
-  a.scale = 1.0f / std::sqrt((float)d_k);
-  a.eps = gn_eps;
-  a.fuse_gn_gate = true;
-  a.dR = at<void>(cws, w.cw.dr);
-  a.Rx = at<void>(cws, w.cw.rx);
-  const HeadTab htab = make_tab(gamma, heads, chunk, seqlen);
-  err = launch_chunkwise(a, htab, st);
-  if (err != hipSuccess) return from_hip(err, "msr_layer_fwd(retention)");
-  // 4. out = Z W_O
-  GemmB bo{};
-  bo.ptr[0] = W_O; bo.ld[0] = d_model;
-  bo.start[0] = 0; bo.start[1] = bo.start[2] = bo.start[3] = INT32_MAX;
-  err = launch_gemm(e, z, hv, bo, out, d_model, (int)M, d_model, hv, st);
-  return from_hip(err, "msr_layer_fwd(output projection)");
+  void* H = at<void>(workspace, w.h);
+  void* Y = at<void>(workspace, w.y);
+  void* F = at<void>(workspace, w.f);
+  // Y = MSR(LN(X)) + X
+  hipError_t err = launch_layer_norm(e, X, d_model, H, d_model, (int)M, d_model, ln_eps, st);
+  if (err != hipSuccess) return from_hip(err, "msr_retnet_block_fwd(layer norm)");
+  s = layer_launch(dtype, batch, seqlen, d_model, heads, d_k, d_v, chunk, gamma, rope_base, gn_eps, H, W_Q, W_K, W_V,
+                   W_G, W_O, Y, X, w.lw, at<void>(workspace, w.layer), stream);
+  if (s != MSR_OK) return s;
+  // out = gelu(LN(Y) W_1) W_2 + Y
+  err = launch_layer_norm(e, Y, d_model, H, d_model, (int)M, d_model, ln_eps, st);
+  if (err != hipSuccess) return from_hip(err, "msr_retnet_block_fwd(layer norm)");
+  GemmB b1{};
+  b1.ptr[0] = W_1; b1.ld[0] = d_ffn;
+  b1.start[0] = 0; b1.start[1] = b1.start[2] = b1.start[3] = INT32_MAX;
+  b1.act = 1;
+  err = launch_gemm(e, H, d_model, b1, F, d_ffn, (int)M, d_ffn, d_model, st);
+  if (err != hipSuccess) return from_hip(err, "msr_retnet_block_fwd(W_1)");
+  GemmB b2{};
+  b2.ptr[0] = W_2; b2.ld[0] = d_model;
+  b2.start[0] = 0; b2.start[1] = b2.start[2] = b2.start[3] = INT32_MAX;
+  b2.resid = Y; b2.ldr = d_model;
+  err = launch_gemm(e, F, d_ffn, b2, out, d_model, (int)M, d_model, d_ffn, st);
+  return from_hip(err, "msr_retnet_block_fwd(W_2)");
 }
 
 }  // extern "C"

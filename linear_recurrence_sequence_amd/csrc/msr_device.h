@@ -153,6 +153,17 @@ __device__ __forceinline__ void pack_row8(Row8<float>& r, const float* v) {
   r.hi = make_uint4(__float_as_uint(v[4]), __float_as_uint(v[5]), __float_as_uint(v[6]), __float_as_uint(v[7]));
 }
 
+__device__ __forceinline__ void unpack_row8(float* v, const Row8<bf16>& r) {
+  const uint32_t w[4] = {r.u.x, r.u.y, r.u.z, r.u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { v[2 * i] = bf16_lo(w[i]); v[2 * i + 1] = bf16_hi(w[i]); }
+}
+__device__ __forceinline__ void unpack_row8(float* v, const Row8<float>& r) {
+  const uint32_t w[8] = {r.lo.x, r.lo.y, r.lo.z, r.lo.w, r.hi.x, r.hi.y, r.hi.z, r.hi.w};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = __uint_as_float(w[i]);
+}
+
 // Multiply the 8 elements of a row by s (rounding back to the storage type).
 __device__ __forceinline__ void scale_row8(Row8<bf16>& r, float s) {
   uint32_t w[4] = {r.u.x, r.u.y, r.u.z, r.u.w};

@@ -91,6 +91,11 @@ struct GemmB {
   // [z K_s, (z + 1) K_s) and stores float32 partials to part + z M N (no
   // rotation); launch_gemm_splitk adds them up.
   float* part;
+  // epilogue: C = act(A B) + resid, act = gelu when act == 1 (after any
+  // rotation), resid an [M, N] matrix with row stride ldr (nullable)
+  int act;
+  const void* resid;
+  int64_t ldr;
 };
 
 // C[M, N] = A[M, K] * B[K, N] (row-major A and B segments), fp32
@@ -104,5 +109,9 @@ hipError_t launch_gemm_splitk(Elt elt, const void* A, int64_t lda, const GemmB& 
                               int N, int K, int splits, float* part, hipStream_t stream);
 // How many K splits launch_gemm_splitk should use for an M x N x K product.
 int gemm_splits(int M, int N, int K);
+// Row-wise LayerNorm over d columns (biased variance, identity affine):
+// Y = (X - mean) / sqrt(var + eps); d a multiple of 8, at most 8192.
+hipError_t launch_layer_norm(Elt elt, const void* X, int64_t ldx, void* Y, int64_t ldy, int rows, int d, float eps,
+                             hipStream_t stream);
 
 }  // namespace msr

@@ -108,6 +108,15 @@ def test_other_entry_points_validation():
     assert dec(eps=-1.0) == 2
     assert dec(dtype=5) == 3
     assert "multiple of 64" in _last(lambda: dec(dm=96))
+    blk = lambda dm=256, F=512, W1=FAKE, ws=1 << 40, ln=1e-5: L.msr_retnet_block_fwd(
+        1, 1, 128, dm, 4, 64, 64, 64, F, gp, 10000.0, 1e-5, ln, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, W1, FAKE, FAKE,
+        FAKE, ws, None)
+    assert blk(F=100) == 4                  # d_ffn not a multiple of 64
+    assert blk(dm=16384) == 4               # d_model above 8192
+    assert blk(W1=None) == 1
+    assert blk(ln=-1.0) == 2
+    assert blk(ws=10) == 5
+    assert blk(F=0) == 2
 
 
 def test_empty_inputs_are_no_ops():
@@ -148,6 +157,11 @@ def test_workspace_sizes():
     assert base <= got <= base + up(8 * Bd * max(Hd * (2 * kd + 2 * vd), dm) * 4)
     assert msr.msr_layer_decode_workspace_bytes(1, 0, dm, Hd, kd, vd) == 0
     assert msr.msr_layer_decode_workspace_bytes(1, Bd, 100, Hd, kd, vd) == 0
+    # RetNet block: the layer's workspace, then LN(X) / LN(Y), Y and the hidden rows
+    Bb, Nb, dmb, Hb, db, Cb, Fb = 2, 64, 256, 2, 64, 32, 512
+    lay = msr.msr_layer_workspace_bytes(1, Bb, Nb, dmb, Hb, db, db, Cb)
+    assert msr.msr_retnet_block_workspace_bytes(1, Bb, Nb, dmb, Hb, db, db, Cb, Fb) == (
+        up(lay) + 2 * up(Bb * Nb * dmb * 2) + up(Bb * Nb * Fb * 2))
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

@@ -1,0 +1,72 @@
+"""Parity of the RetNet block (msr_retnet_block_fwd: LayerNorm, the gated
+layer, residual, LayerNorm, gelu feed-forward network, residual) against the
+float64 oracle: small shapes in both precisions with a ragged sequence, and
+the b8 x 2048 layer shape with a 4096-wide feed-forward network on a sampled
+batch element.  Rows whose layer-internal GroupNorm is ill-conditioned (the
+same criterion as the layer tests) are excluded and counted."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from gpu_util import TOL, dev, host, layer_err, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _msr():
+    import linear_recurrence_sequence_amd as msr
+    return msr
+
+
+def _weights(rng, dm, H, dk, dv, F, dtype):
+    n = lambda shape, std: workloads.normal(rng, shape, std, dtype)
+    return (n((dm, H * dk), dm ** -0.5), n((dm, H * dk), dm ** -0.5), n((dm, H * dv), dm ** -0.5),
+            n((dm, H * dv), dm ** -0.5), n((H * dv, dm), (H * dv) ** -0.5), n((dm, F), dm ** -0.5),
+            n((F, dm), F ** -0.5))
+
+
+def _check(X, Ws, g, H, dk, dv, C, got, dtype, limit):
+    WQ, WK, WV, WG, WO, W1, W2 = Ws
+    ref = oracle.retnet_block(X, WQ, WK, WV, WG, WO, W1, W2, g, H, dk, dv, C, gn_eps=1e-5, ln_eps=1e-5)
+    _, gv = oracle.msr_layer(oracle.layer_norm(X, 1e-5), WQ, WK, WV, WG, WO, g, H, dk, dv, C, eps=1e-5,
+                             return_gn_var=True)
+    err, excluded = layer_err(got, ref, gv, 1e-5)
+    print(f"block err {err:.2e} (excluded rows {excluded:.2e})", flush=True)
+    assert err < TOL[dtype] and excluded < limit
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_block_small(dtype):
+    msr = _msr()
+    B, N, dm, H, d, C, F = 2, 130, 256, 2, 64, 64, 512
+    rng = np.random.default_rng(61)
+    X = workloads.normal(rng, (B, N, dm), 1.0, dtype)
+    Ws = _weights(rng, dm, H, d, d, F, dtype)
+    g = workloads.gammas(H)
+    say("retnet block", dtype, B, N, dm, F)
+    out = msr.msr_retnet_block_fwd(dev(X, dtype), *(dev(w, dtype) for w in Ws), g, H, d, d, C, rope_base=1e4,
+                                   gn_eps=1e-5, ln_eps=1e-5)
+    _check(X, Ws, g, H, d, d, C, host(out), dtype, 1e-2)
+
+
+@pytest.mark.slow
+def test_block_b8_n2048_sampled():
+    """bf16, batch 8 x 2048 tokens, d_model 2048, 8 heads of 256, chunk 256,
+    d_ffn 4096: batch element 5 against the oracle."""
+    import torch
+    msr = _msr()
+    w = workloads.WORKLOADS["layer_bf16_b8_n2048"]
+    F = 2 * w.d_model
+    X, WQ, WK, WV, WG, WO = workloads.layer_inputs(w)
+    rng = np.random.default_rng(62)
+    W1 = workloads.normal(rng, (w.d_model, F), w.d_model ** -0.5, "bf16")
+    W2 = workloads.normal(rng, (F, w.d_model), F ** -0.5, "bf16")
+    g = workloads.gammas(w.heads)
+    say("retnet block full shape")
+    out = msr.msr_retnet_block_fwd(*(dev(a, "bf16") for a in (X, WQ, WK, WV, WG, WO, W1, W2)), g, w.heads, w.d_k,
+                                   w.d_v, w.chunk, rope_base=w.rope_base, gn_eps=1e-5, ln_eps=1e-5)
+    torch.cuda.synchronize()
+    b = 5
+    _check(X[b:b + 1], (WQ, WK, WV, WG, WO, W1, W2), g, w.heads, w.d_k, w.d_v, w.chunk, host(out)[b:b + 1], "bf16",
+           1e-3)
