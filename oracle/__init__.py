@@ -25,6 +25,8 @@ from .retention import (  # noqa: F401
     layer_norm,
     gelu,
     retnet_block,
+    rotary_adjoint,
+    retention_grad,
     max_rel_err,
     max_rel_err_per_head,
 )

@@ -362,6 +362,73 @@ def retnet_block(X, WQ, WK, WV, WG, WO, W1, W2, gamma, heads, d_k, d_v, chunk=No
 
 
 # --------------------------------------------------------------------------
+# Gradients of retention (training)
+# --------------------------------------------------------------------------
+def rotary_adjoint(x, pos0: int = 0, base: float = 10000.0):
+    """Adjoint (= inverse) of ``rotary``: every interleaved pair is
+    multiplied by e^{-i p theta_j} instead of e^{+i p theta_j}, so a
+    gradient with respect to the rotated Q or K becomes the gradient with
+    respect to the unrotated one.  ``base <= 0`` means no rotation."""
+    x = _f64(x)
+    if base is None or base <= 0:
+        return x.copy()
+    B, N, H, d = x.shape
+    j = np.arange(d // 2, dtype=F64)
+    theta = base ** (-2.0 * j / d)
+    ang = (pos0 + np.arange(N, dtype=F64))[:, None] * theta[None, :]
+    c = np.cos(ang)[None, :, None, :]
+    s = np.sin(ang)[None, :, None, :]
+    xe, xo = x[..., 0::2], x[..., 1::2]
+    out = np.empty_like(x)
+    out[..., 0::2] = xe * c + xo * s
+    out[..., 1::2] = -xe * s + xo * c
+    return out
+
+
+def retention_grad(q, k, v, dO, gamma, scale: float = 1.0, S0=None, dS=None):
+    """Gradients of retention for training.  [RN-zh] "Retention 網路總體結構"
+    trains with the parallel (Eq. 5) and chunkwise (Eq. 7) forms, which both
+    compute, per (batch, head) with initial state S0 (zeros if None):
+
+      S_n = gamma^(n+1) S0 + sum_{m <= n} gamma^(n-m) k_m^T v_m   (Eq. 6 unrolled)
+      o_n = scale * q_n S_n,     S_last = S_{N-1}
+
+    For the loss L = <dO, O> + <dS, S_last> (dS: gradient arriving at the
+    last state, zeros if None) the gradients, written with the decay mask D
+    of Eq. (5), xi_n = gamma^(n+1), zeta_m = gamma^(N-1-m) and A = (dO V^T) (.) D:
+
+      dQ  = scale * A K + scale * xi (.) (dO S0^T)
+      dK  = scale * A^T Q + zeta (.) (V dS^T)
+      dV  = scale * ((Q K^T) (.) D)^T dO + zeta (.) (K dS)
+      dS0 = scale * (Q (.) xi)^T dO + gamma^N dS
+
+    q, k: [B, N, H, dk]; v, dO: [B, N, H, dv]; S0, dS: [B, H, dk, dv].
+    Returns (dq, dk, dv, dS0).
+    """
+    q, k, v, dO = _f64(q), _f64(k), _f64(v), _f64(dO)
+    B, N, H, dk = q.shape
+    dv = v.shape[-1]
+    S0 = np.zeros((B, H, dk, dv), dtype=F64) if S0 is None else _f64(S0)
+    dS = np.zeros((B, H, dk, dv), dtype=F64) if dS is None else _f64(dS)
+    dq, dkk, dvv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    dS0 = np.zeros((B, H, dk, dv), dtype=F64)
+    t = np.arange(N, dtype=F64)
+    for h in range(H):
+        gam = F64(gamma[h])
+        D = decay_mask(N, gam)
+        xi = np.power(gam, t + 1.0)[:, None]
+        zeta = np.power(gam, N - 1.0 - t)[:, None]
+        for b in range(B):
+            Q, K, V, G = q[b, :, h], k[b, :, h], v[b, :, h], dO[b, :, h]
+            A = (G @ V.T) * D
+            dq[b, :, h] = scale * (A @ K) + scale * xi * (G @ S0[b, h].T)
+            dkk[b, :, h] = scale * (A.T @ Q) + zeta * (V @ dS[b, h].T)
+            dvv[b, :, h] = scale * (((Q @ K.T) * D).T @ G) + zeta * (K @ dS[b, h])
+            dS0[b, h] = scale * ((Q * xi).T @ G) + np.power(gam, N) * dS[b, h]
+    return dq, dkk, dvv, dS0
+
+
+# --------------------------------------------------------------------------
 # Error measures
 # --------------------------------------------------------------------------
 def max_rel_err(got, ref):

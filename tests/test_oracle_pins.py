@@ -418,3 +418,89 @@ def test_retnet_block_wiring():
     assert np.max(np.abs(got - (X + ffn))) < 1e-12
     got = oracle.retnet_block(X, WQ, WK, WV, WG, ZO, Z1, W2, g, H, dk, dv, chunk=3)
     assert np.max(np.abs(got - X)) < 1e-15
+
+
+# --------------------------------------------------------------------------
+# Gradients (training with the parallel and chunkwise forms)
+# --------------------------------------------------------------------------
+def _loss(q, k, v, S0, dO, dS, gamma, scale):
+    O, S = oracle.retention_recurrent(q, k, v, gamma, scale, S0=S0)
+    return float(np.sum(dO * O) + np.sum(dS * S))
+
+
+def test_retention_grad_matches_finite_differences():
+    """Every entry of dQ, dK, dV, dS0 against a central difference of the
+    recurrent form's loss <dO, O> + <dS, S_last>.  The loss is linear in
+    each single entry, so the difference is exact up to rounding; gamma = 0
+    and gamma = 1 heads are included."""
+    rng = np.random.default_rng(41)
+    B, N, H, dk, dv = 2, 5, 3, 3, 2
+    gamma = np.array([0.9, 0.0, 1.0])
+    scale = 0.7
+    q, k = rng.standard_normal((B, N, H, dk)), rng.standard_normal((B, N, H, dk))
+    v, dO = rng.standard_normal((B, N, H, dv)), rng.standard_normal((B, N, H, dv))
+    S0, dS = rng.standard_normal((B, H, dk, dv)), rng.standard_normal((B, H, dk, dv))
+    grads = oracle.retention_grad(q, k, v, dO, gamma, scale, S0=S0, dS=dS)
+    args = [q, k, v, S0]
+    eps = 1e-3
+    for which, g in enumerate(grads):
+        x = args[which]
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(*x.shape):
+            old = x[idx]
+            x[idx] = old + eps
+            lp = _loss(*args, dO, dS, gamma, scale)
+            x[idx] = old - eps
+            lm = _loss(*args, dO, dS, gamma, scale)
+            x[idx] = old
+            fd[idx] = (lp - lm) / (2 * eps)
+        np.testing.assert_allclose(g, fd, rtol=1e-9, atol=1e-9, err_msg=f"gradient {which}")
+
+
+def test_retention_grad_without_state_terms():
+    """S0 = None and dS = None are zeros: the gradients equal those with
+    explicit zero states, and dS0 is then scale * (Q (.) xi)^T dO alone, a
+    sum that the recurrent form's loss also yields by differences in S0."""
+    rng = np.random.default_rng(42)
+    B, N, H, dk, dv = 1, 4, 2, 2, 3
+    gamma = np.array([0.5, 0.8])
+    q, k = rng.standard_normal((B, N, H, dk)), rng.standard_normal((B, N, H, dk))
+    v, dO = rng.standard_normal((B, N, H, dv)), rng.standard_normal((B, N, H, dv))
+    z = np.zeros((B, H, dk, dv))
+    a = oracle.retention_grad(q, k, v, dO, gamma, 1.3)
+    b = oracle.retention_grad(q, k, v, dO, gamma, 1.3, S0=z, dS=z)
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
+    # entry (0, 1, 1, 2) of dS0 by difference
+    e = np.zeros_like(z)
+    e[0, 1, 1, 2] = 1.0
+    fd = (_loss(q, k, v, e, dO, z, gamma, 1.3) - _loss(q, k, v, -e, dO, z, gamma, 1.3)) / 2
+    assert abs(a[3][0, 1, 1, 2] - fd) < 1e-12
+
+
+def test_retention_grad_sequence_split():
+    """Carried-state semantics: the gradients of a sequence equal those of
+    its two halves, the second half started from the first half's last
+    state, and the first half receiving the second half's dS0 as dS."""
+    rng = np.random.default_rng(43)
+    B, N, H, dk, dv, n1 = 2, 9, 2, 3, 4, 4
+    gamma = np.array([0.95, 0.6])
+    q, k = rng.standard_normal((B, N, H, dk)), rng.standard_normal((B, N, H, dk))
+    v, dO = rng.standard_normal((B, N, H, dv)), rng.standard_normal((B, N, H, dv))
+    S0, dS = rng.standard_normal((B, H, dk, dv)), rng.standard_normal((B, H, dk, dv))
+    full = oracle.retention_grad(q, k, v, dO, gamma, 0.5, S0=S0, dS=dS)
+    _, S_mid = oracle.retention_recurrent(q[:, :n1], k[:, :n1], v[:, :n1], gamma, 0.5, S0=S0)
+    second = oracle.retention_grad(q[:, n1:], k[:, n1:], v[:, n1:], dO[:, n1:], gamma, 0.5, S0=S_mid, dS=dS)
+    first = oracle.retention_grad(q[:, :n1], k[:, :n1], v[:, :n1], dO[:, :n1], gamma, 0.5, S0=S0, dS=second[3])
+    for i in range(3):
+        np.testing.assert_allclose(np.concatenate([first[i], second[i]], axis=1), full[i], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(first[3], full[3], rtol=1e-12, atol=1e-12)
+
+
+def test_rotary_adjoint_is_the_inverse_rotation():
+    rng = np.random.default_rng(44)
+    x, y = rng.standard_normal((2, 7, 3, 8)), rng.standard_normal((2, 7, 3, 8))
+    for base, pos0 in ((10000.0, 0), (10000.0, 4000), (50.0, 3), (0.0, 9)):
+        rx = oracle.rotary(x, pos0, base)
+        assert abs(np.sum(rx * y) - np.sum(x * oracle.rotary_adjoint(y, pos0, base))) < 1e-10
+        np.testing.assert_allclose(oracle.rotary_adjoint(rx, pos0, base), x, rtol=0, atol=1e-12)
