@@ -209,6 +209,33 @@ def bench_core(B, N, H, d, C, steps, warmup, parallel=False):
     return res
 
 
+def bench_backward(B, N, H, d, C, steps, warmup):
+    """Chunkwise backward (dQ, dK, dV, dS_in) at a core shape, bf16, no
+    rotation; algorithmic flops = three chunkwise passes."""
+    import torch
+    import linear_recurrence_sequence_amd as msr
+    import workloads
+    Q, K, V, dO = (workloads.device_normal((B, N, H, d), seed=70 + i, dtype=torch.bfloat16) for i in range(4))
+    dQ, dK, dV = torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V)
+    dS_in = torch.empty((B, H, d, d), device="cuda")
+    g = workloads.gammas(H)
+    s = 1 / math.sqrt(d)
+    ws = torch.empty(msr.msr_chunkwise_bwd_workspace_bytes(1, B, N, H, d, d, C, 0.0), dtype=torch.uint8,
+                     device="cuda")
+    fn = lambda: msr.msr_chunkwise_bwd(Q, K, V, dO, g, C, qk_scale=s, dS_in=dS_in, dQ=dQ, dK=dK, dV=dV,
+                                       workspace=ws)
+    flops = 3 * B * N * H * (C * 2 * d + 4 * d * d)
+    t = gpu_time(fn, steps, warmup)
+    tr = traced(fn, steps)
+    res = {"batch": B, "seqlen": N, "heads": H, "d": d, "chunk": C, "ms_per_step": round(t * 1e3, 4),
+           "tokens_per_s": round(B * N / t, 1), "tflops": round(flops / t / 1e12, 1),
+           "mfma_frac": round(flops / t / PEAK_BF16, 4),
+           "trace_ms_per_step": {k: round(v[0] / steps * 1e3, 4) for k, v in tr.items()}}
+    del Q, K, V, dO, dQ, dK, dV, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def bench_decode(steps_timed, warmup):
     import torch
     import linear_recurrence_sequence_amd as msr
@@ -384,7 +411,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", default="layer,decode,long,block,retnet,cpu")
+    ap.add_argument("--only", default="layer,decode,long,block,retnet,backward,cpu")
     ap.add_argument("--no-cpu", action="store_true")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -452,6 +479,12 @@ def main():
     if "retnet" in parts:
         log("retnet block")
         line["retnet_block"] = bench_retnet_block(max(3, args.steps // 2), 2)
+    if "backward" in parts:
+        log("backward")
+        lw = workloads.WORKLOADS["long_bf16_b2_n16384"]
+        line["backward"] = {
+            "headline_core": bench_backward(w.batch, w.seqlen, w.heads, w.d_k, w.chunk, args.steps, args.warmup),
+            "long_core": bench_backward(lw.batch, lw.seqlen, lw.heads, lw.d_k, lw.chunk, max(3, args.steps // 2), 2)}
     if "copy" in parts:
         log("copy calibration")
         line["copy_calibration"] = bench_copy()

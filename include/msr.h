@@ -101,6 +101,35 @@ msr_status msr_chunkwise_fwd(msr_dtype dtype, msr_dims dims, int32_t chunk,
 size_t msr_chunkwise_workspace_bytes(msr_dtype dtype, msr_dims dims, int32_t chunk,
                                      float rope_base);
 
+/* Backward of the chunkwise (equivalently parallel) form, for training
+ * ([RN-zh] section "Retention 網路總體結構": training runs the parallel
+ * form, Eq. (5), and the chunkwise form, Eq. (7)).  With Q, K rotated as in
+ * msr_chunkwise_fwd, S_n = gamma^(n+1) S_in + sum_{m<=n} gamma^(n-m) k_m^T v_m
+ * and o_n = qk_scale q_n S_n, it returns the gradients of
+ * L = <dO, O> + <dS_out, S_last>, per (batch, head), D as in Eq. (5),
+ * xi_n = gamma^(n+1), zeta_m = gamma^(seqlen-1-m), A = (dO V^T) (.) D:
+ *   dQ    = qk_scale A K + qk_scale xi (.) (dO S_in^T)   (then rotated back)
+ *   dK    = qk_scale A^T Q + zeta (.) (V dS_out^T)       (then rotated back)
+ *   dV    = qk_scale ((Q K^T) (.) D)^T dO + zeta (.) (K dS_out)
+ *   dS_in = qk_scale (Q (.) xi)^T dO + gamma^seqlen dS_out
+ * Q, K, dQ, dK: [batch, seqlen, heads, d_k]; V, dO, dV: [.., d_v] (dtype);
+ * S_in, dS_out (nullable: zeros) and dS_in (nullable: not computed):
+ * [batch, heads, d_k, d_v] float32.  Q, K are the unrotated inputs when
+ * rope_base > 0 and dQ, dK the gradients with respect to them.  Needs
+ * d_k == d_v; with dS_out, |qk_scale| * gamma_h >= 2^-60 for every head
+ * (else MSR_ERR_UNSUPPORTED).  dS_in may alias dS_out but not S_in.  The
+ * gradient state runs backwards through the sequence in float32 chunk by
+ * chunk.  Workspace: msr_chunkwise_bwd_workspace_bytes() bytes. */
+msr_status msr_chunkwise_bwd(msr_dtype dtype, msr_dims dims, int32_t chunk,
+                             const double* gamma, float rope_base, int64_t pos0,
+                             float qk_scale, const void* Q, const void* K,
+                             const void* V, const void* dO, const float* S_in,
+                             const float* dS_out, void* dQ, void* dK, void* dV,
+                             float* dS_in, void* workspace, size_t ws_bytes,
+                             void* stream);
+size_t msr_chunkwise_bwd_workspace_bytes(msr_dtype dtype, msr_dims dims, int32_t chunk,
+                                         float rope_base);
+
 /* Recurrent form, one decode step, [RN-zh] Eq. (6), for every (batch, head):
  *   S <- gamma_h S + k^T v ;  o = qk_scale * q S   (S updated in place)
  * q, k: [batch, heads, d_k]; v, o: [batch, heads, d_v] (dtype); S:

@@ -18,6 +18,7 @@ __all__ = [
     "MSR_F32", "MSR_BF16", "MsrError", "MsrLibraryMissing", "library_path", "lib",
     "msr_parallel_fwd", "msr_parallel_workspace_bytes",
     "msr_chunkwise_fwd", "msr_chunkwise_workspace_bytes",
+    "msr_chunkwise_bwd", "msr_chunkwise_bwd_workspace_bytes",
     "msr_recurrent_step", "msr_layer_fwd", "msr_layer_workspace_bytes",
     "msr_layer_decode_step", "msr_layer_decode_workspace_bytes",
     "msr_retnet_block_fwd", "msr_retnet_block_workspace_bytes",
@@ -28,7 +29,8 @@ __all__ = [
 MSR_F32, MSR_BF16 = 0, 1
 EXPORTS = (
     "msr_parallel_fwd", "msr_parallel_workspace_bytes", "msr_chunkwise_fwd",
-    "msr_chunkwise_workspace_bytes", "msr_recurrent_step", "msr_layer_fwd",
+    "msr_chunkwise_workspace_bytes", "msr_chunkwise_bwd", "msr_chunkwise_bwd_workspace_bytes",
+    "msr_recurrent_step", "msr_layer_fwd",
     "msr_layer_workspace_bytes", "msr_layer_decode_step", "msr_layer_decode_workspace_bytes",
     "msr_retnet_block_fwd", "msr_retnet_block_workspace_bytes", "msr_status_str", "msr_last_error", "msr_trace_enable", "msr_trace_count", "msr_trace_get",
 )
@@ -77,6 +79,9 @@ def lib():
         "msr_chunkwise_fwd": (_I32, [_I32, MsrDims, _I32, _DP, _F, _I64, _F, _P, _P, _P, _P, _P, _P, _P,
                                      _SZ, _P]),
         "msr_chunkwise_workspace_bytes": (_SZ, [_I32, MsrDims, _I32, _F]),
+        "msr_chunkwise_bwd": (_I32, [_I32, MsrDims, _I32, _DP, _F, _I64, _F, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                     _P, _P, _SZ, _P]),
+        "msr_chunkwise_bwd_workspace_bytes": (_SZ, [_I32, MsrDims, _I32, _F]),
         "msr_recurrent_step": (_I32, [_I32, _I32, _I32, _I32, _I32, _DP, _F, _I64, _F, _P, _P, _P, _P, _P,
                                       _P]),
         "msr_layer_fwd": (_I32, [_I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _DP, _F, _F, _P, _P, _P,
@@ -229,6 +234,33 @@ def msr_chunkwise_fwd(Q, K, V, gamma, chunk, *, rope_base=0.0, pos0=0, qk_scale=
                                                         _ptr(K), _ptr(V), _ptr(S_in), _ptr(S_out), _ptr(O),
                                                         _ptr(ws), wsb, _stream(stream)))
     return O
+
+
+def msr_chunkwise_bwd_workspace_bytes(dtype: int, batch, seqlen, heads, d_k, d_v, chunk, rope_base) -> int:
+    return lib().msr_chunkwise_bwd_workspace_bytes(dtype, MsrDims(batch, seqlen, heads, d_k, d_v), chunk,
+                                                   rope_base)
+
+
+def msr_chunkwise_bwd(Q, K, V, dO, gamma, chunk, *, rope_base=0.0, pos0=0, qk_scale=1.0, S_in=None,
+                      dS_out=None, dS_in=None, dQ=None, dK=None, dV=None, workspace=None, stream=None):
+    """Backward of the chunkwise form.  Returns (dQ, dK, dV); dS_in (if
+    given, [B, H, d_k, d_v] float32) receives the gradient of the initial
+    state."""
+    B, N, H, dk = Q.shape
+    dv = V.shape[-1]
+    dt = _dtype_code(Q)
+    t = _torch()
+    dQ = t.empty_like(Q) if dQ is None else dQ
+    dK = t.empty_like(K) if dK is None else dK
+    dV = t.empty_like(V) if dV is None else dV
+    _, gp = g = _gamma(gamma, H)
+    dims = MsrDims(B, N, H, dk, dv)
+    ws, wsb = _workspace(lib().msr_chunkwise_bwd_workspace_bytes(dt, dims, chunk, rope_base), workspace, Q.device)
+    _check("msr_chunkwise_bwd", lib().msr_chunkwise_bwd(dt, dims, chunk, gp, rope_base, pos0, qk_scale, _ptr(Q),
+                                                        _ptr(K), _ptr(V), _ptr(dO), _ptr(S_in), _ptr(dS_out),
+                                                        _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(dS_in), _ptr(ws), wsb,
+                                                        _stream(stream)))
+    return dQ, dK, dV
 
 
 def msr_recurrent_step(q, k, v, S, gamma, *, pos, rope_base=0.0, qk_scale=1.0, o=None, stream=None):

@@ -1,0 +1,117 @@
+// Pieces of the chunkwise backward that are not retention passes: time
+// reversal of token rows, and per-head scaled copies or transposes of
+// float32 states.
+//
+// The gradients of retention ([RN-zh] "Retention 網路總體結構": training runs
+// the parallel and chunkwise forms) are retentions themselves: dQ is the
+// causal retention of (dO, V, K), and dK, dV are anti-causal retentions,
+// which become causal ones on the time-reversed sequence.  The passes run on
+// the chunkwise kernels (k_chunk.hip); this file supplies the reversals and
+// the state seeds.
+#include "msr_launch.h"
+
+namespace msr {
+
+// Row (b, t) of each job's source goes to row (b, seqlen-1-t) of its
+// destination; blockIdx.y picks the job; each thread moves 16 bytes.
+__global__ void k_reverse_rows(RevJobs j, int batch, int seqlen, int row_bytes) {
+  const int job = blockIdx.y;
+  const int vec = row_bytes / 16;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)batch * seqlen * vec) return;
+  const int64_t row = i / vec;
+  const int c = (int)(i % vec);
+  const int64_t b = row / seqlen;
+  const int t = (int)(row % seqlen);
+  const int64_t out_row = b * seqlen + (seqlen - 1 - t);
+  const uint4 x = *reinterpret_cast<const uint4*>(j.src[job] + row * j.lds[job] + 16 * c);
+  *reinterpret_cast<uint4*>(j.dst[job] + out_row * j.ldd[job] + 16 * c) = x;
+}
+
+// In place: rows t and seqlen-1-t (t < seqlen/2) of each job's destination
+// swap; every thread owns one 16-byte column of one pair, so no two threads
+// touch the same bytes.
+__global__ void k_reverse_rows_inplace(RevJobs j, int batch, int seqlen, int row_bytes) {
+  const int job = blockIdx.y;
+  const int vec = row_bytes / 16;
+  const int half = seqlen / 2;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)batch * half * vec) return;
+  const int64_t pair = i / vec;
+  const int c = (int)(i % vec);
+  const int64_t b = pair / half;
+  const int t = (int)(pair % half);
+  char* lo = j.dst[job] + (b * seqlen + t) * j.ldd[job] + 16 * c;
+  char* hi = j.dst[job] + (b * seqlen + (seqlen - 1 - t)) * j.ldd[job] + 16 * c;
+  const uint4 x = *reinterpret_cast<const uint4*>(lo);
+  const uint4 y = *reinterpret_cast<const uint4*>(hi);
+  *reinterpret_cast<uint4*>(lo) = y;
+  *reinterpret_cast<uint4*>(hi) = x;
+}
+
+hipError_t launch_reverse_rows(const RevJobs& jobs, int njobs, int batch, int seqlen, int row_bytes, bool in_place,
+                               hipStream_t st) {
+  if (njobs < 1 || njobs > 4 || row_bytes % 16) return hipErrorInvalidValue;
+  for (int q = 0; q < njobs; ++q)
+    if (jobs.ldd[q] % 16 || (!in_place && jobs.lds[q] % 16)) return hipErrorInvalidValue;
+  const int64_t rows = in_place ? (int64_t)batch * (seqlen / 2) : (int64_t)batch * seqlen;
+  const int64_t n = rows * (row_bytes / 16);
+  if (n == 0) return hipSuccess;
+  const dim3 grid((unsigned)((n + 255) / 256), njobs);
+  if (in_place) {
+    TraceScope ts("k_reverse_rows_inplace", st);
+    hipLaunchKernelGGL(k_reverse_rows_inplace, grid, dim3(256), 0, st, jobs, batch, seqlen, row_bytes);
+  } else {
+    TraceScope ts("k_reverse_rows", st);
+    hipLaunchKernelGGL(k_reverse_rows, grid, dim3(256), 0, st, jobs, batch, seqlen, row_bytes);
+  }
+  return hipGetLastError();
+}
+
+// dst[bh] (rows x cols) = c_h * src[bh] or c_h * src[bh]^T (src cols x rows),
+// h = bh % heads; src == nullptr writes zeros.  32 x 32 tiles through LDS
+// so that both the reads and the writes of a transpose are row-contiguous.
+__global__ __launch_bounds__(256) void k_state_xform(const float* __restrict__ src, float* dst, int heads, int rows,
+                                                     int cols, int transpose, HeadScale hs) {
+  __shared__ float tile[32][33];
+  const int tc = cols / 32, tiles = (rows / 32) * tc;
+  const int bh = blockIdx.x / tiles, tile_id = blockIdx.x % tiles;
+  const int r0 = (tile_id / tc) * 32, c0 = (tile_id % tc) * 32;
+  const float c = hs.c[bh % heads];
+  const size_t base = (size_t)bh * rows * cols;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;   // 32 x 8
+  if (!src) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) dst[base + (size_t)(r0 + ty + 8 * k) * cols + c0 + tx] = 0.f;
+    return;
+  }
+  if (!transpose) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const size_t o = base + (size_t)(r0 + ty + 8 * k) * cols + c0 + tx;
+      dst[o] = c * src[o];
+    }
+    return;
+  }
+  // src is [cols][rows]: read the (c0, r0) tile row-contiguously, write transposed
+#pragma unroll
+  for (int k = 0; k < 4; ++k) tile[ty + 8 * k][tx] = src[base + (size_t)(c0 + ty + 8 * k) * rows + r0 + tx];
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 4; ++k) dst[base + (size_t)(r0 + ty + 8 * k) * cols + c0 + tx] = c * tile[tx][ty + 8 * k];
+}
+
+hipError_t launch_state_xform(const float* src, float* dst, int bh, int heads, int rows, int cols, bool transpose,
+                              const HeadScale& hs, hipStream_t st) {
+  if (rows % 32 || cols % 32 || heads < 1 || heads > kMaxHeads) return hipErrorInvalidValue;
+  if (transpose && src == dst) return hipErrorInvalidValue;
+  const int64_t blocks = (int64_t)bh * (rows / 32) * (cols / 32);
+  if (blocks == 0) return hipSuccess;
+  if (blocks > INT32_MAX) return hipErrorInvalidValue;
+  TraceScope ts("k_state_xform", st);
+  hipLaunchKernelGGL(k_state_xform, dim3((unsigned)blocks), dim3(256), 0, st, src, dst, heads, rows, cols,
+                     transpose ? 1 : 0, hs);
+  return hipGetLastError();
+}
+
+}  // namespace msr

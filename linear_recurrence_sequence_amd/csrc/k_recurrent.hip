@@ -204,7 +204,7 @@ hipError_t launch_rope_table(float2* tab, int npos, int d, int64_t pos0, float b
 // One lane rotates 4 pairs (8 contiguous elements) of one (token, head).
 template <class T>
 __global__ void k_rope_apply(const T* src, int64_t lds, T* dst, int64_t ldd, int rows, int seqlen, int heads, int d,
-                             const float2* __restrict__ tab) {
+                             const float2* __restrict__ tab, float sgn) {
   const int groups = d / 8;
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t per_row = (int64_t)heads * groups;
@@ -222,26 +222,28 @@ __global__ void k_rope_apply(const T* src, int64_t lds, T* dst, int64_t ldd, int
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
     const float2 t = cs[p];
+    const float sn = sgn * t.y;
     const float a = x[2 * p], b = x[2 * p + 1];
-    x[2 * p] = a * t.x - b * t.y;
-    x[2 * p + 1] = a * t.y + b * t.x;
+    x[2 * p] = a * t.x - b * sn;
+    x[2 * p + 1] = a * sn + b * t.x;
   }
 #pragma unroll
   for (int e = 0; e < 8; ++e) o[e] = (T)x[e];
 }
 
 hipError_t launch_rope_apply(Elt elt, const void* src, int64_t lds, void* dst, int64_t ldd, int rows, int seqlen,
-                             int heads, int d, const float2* tab, hipStream_t st) {
+                             int heads, int d, const float2* tab, hipStream_t st, bool inverse) {
   const int64_t n = (int64_t)rows * heads * (d / 8);
+  const float sgn = inverse ? -1.f : 1.f;
   if (n == 0) return hipSuccess;
   const dim3 grid((unsigned)((n + 255) / 256));
   TraceScope ts("k_rope_apply", st);
   if (elt == kBF16)
     hipLaunchKernelGGL(k_rope_apply<bf16>, grid, dim3(256), 0, st, (const bf16*)src, lds, (bf16*)dst, ldd, rows,
-                       seqlen, heads, d, tab);
+                       seqlen, heads, d, tab, sgn);
   else
     hipLaunchKernelGGL(k_rope_apply<float>, grid, dim3(256), 0, st, (const float*)src, lds, (float*)dst, ldd, rows,
-                       seqlen, heads, d, tab);
+                       seqlen, heads, d, tab, sgn);
   return hipGetLastError();
 }
 

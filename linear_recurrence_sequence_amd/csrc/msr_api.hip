@@ -129,6 +129,32 @@ ChunkWs chunk_ws_layout(msr_dtype dt, const msr_dims& d, int32_t chunk, bool rop
   return w;
 }
 
+// Chunkwise backward: the retention passes' chunk workspace (shared, the
+// passes run one after another), the rotated Q and K, the four reversed
+// inputs and the three state seeds.
+struct BwdWs {
+  ChunkWs cw;
+  size_t chunk = 0, rq = 0, rk = 0, rv = 0, rdo = 0, sin_t = 0, dso = 0, dso_t = 0, total = 0;
+};
+BwdWs bwd_ws_layout(msr_dtype dt, const msr_dims& d, int32_t chunk, bool rope) {
+  BwdWs w;
+  const size_t es = elt_size(dt);
+  const size_t rows = (size_t)d.batch * d.seqlen * d.heads * d.d_k * es;
+  const size_t state = (size_t)d.batch * d.heads * d.d_k * d.d_v * sizeof(float);
+  w.cw = chunk_ws_layout(dt, d, chunk, rope, true);
+  size_t off = 0;
+  w.chunk = off; off += align_up(w.cw.total);
+  w.rq = off; off += align_up(rows);
+  w.rk = off; off += align_up(rows);
+  w.rv = off; off += align_up(rows);
+  w.rdo = off; off += align_up(rows);
+  w.sin_t = off; off += align_up(state);
+  w.dso = off; off += align_up(state);
+  w.dso_t = off; off += align_up(state);
+  w.total = off;
+  return w;
+}
+
 struct LayerWs {
   size_t qkvg = 0, z = 0, tab = 0, chunk = 0, total = 0;
   ChunkWs cw;
@@ -347,13 +373,13 @@ msr_status msr_chunkwise_fwd(msr_dtype dtype, msr_dims d, int32_t chunk, const d
   if (S_out && S_out == S_in) return fail(MSR_ERR_SHAPE, "S_out may not alias S_in");
   hipStream_t st = (hipStream_t)stream;
   const size_t tok = (size_t)d.batch * d.seqlen;
-  const size_t state_bytes = (size_t)d.batch * d.heads * d.d_k * d.d_v * sizeof(float);
   if (d.batch == 0) return ok();
   if (d.seqlen == 0) {  // no tokens: the state passes through unchanged
     if (!S_out) return ok();
-    hipError_t e = S_in ? hipMemcpyAsync(S_out, S_in, state_bytes, hipMemcpyDeviceToDevice, st)
-                        : hipMemsetAsync(S_out, 0, state_bytes, st);
-    return from_hip(e, "msr_chunkwise_fwd(seqlen=0)");
+    HeadScale one;
+    std::fill(one.c, one.c + kMaxHeads, 1.0f);
+    return from_hip(launch_state_xform(S_in, S_out, d.batch * d.heads, d.heads, d.d_k, d.d_v, false, one, st),
+                    "msr_chunkwise_fwd(seqlen=0)");
   }
   if (!Q || !K || !V || !O) return fail(MSR_ERR_NULL, "Q, K, V and O must be non-NULL");
   const bool rope = rope_base > 0.f;
@@ -375,6 +401,130 @@ msr_status msr_chunkwise_fwd(msr_dtype dtype, msr_dims d, int32_t chunk, const d
   a.Rx = at<void>(workspace, w.rx);
   const HeadTab tab = make_tab(gamma, d.heads, chunk, d.seqlen);
   return from_hip(launch_chunkwise(a, tab, st), "msr_chunkwise_fwd");
+}
+
+size_t msr_chunkwise_bwd_workspace_bytes(msr_dtype dtype, msr_dims dims, int32_t chunk, float rope_base) {
+  if (dims.batch < 0 || dims.seqlen < 0 || dims.heads <= 0 || dims.d_k <= 0 || dims.d_v <= 0 || chunk <= 0) return 0;
+  return bwd_ws_layout(dtype, dims, chunk, rope_base > 0.f).total;
+}
+
+// dQ is the causal retention of (dO, V, K) seeded with S_in^T; dV and dK are
+// the causal retentions of (rev K, rev Q, rev dO) and (rev V, rev dO, rev Q)
+// on the time-reversed sequence, seeded with dS_out / (scale gamma) (and its
+// transpose), whose outputs are reversed back; dS_in = scale gamma times the
+// last state of the dV pass.
+msr_status msr_chunkwise_bwd(msr_dtype dtype, msr_dims d, int32_t chunk, const double* gamma, float rope_base,
+                             int64_t pos0, float qk_scale, const void* Q, const void* K, const void* V,
+                             const void* dO, const float* S_in, const float* dS_out, void* dQ, void* dK, void* dV,
+                             float* dS_in, void* workspace, size_t ws_bytes, void* stream) {
+  msr_status s;
+  if ((s = check_dtype(dtype))) return s;
+  if ((s = check_heads(d.batch, d.seqlen, d.heads, d.d_k, d.d_v))) return s;
+  if (d.d_k != d.d_v)
+    return fail(MSR_ERR_UNSUPPORTED, "the backward needs d_k == d_v (got %d, %d): its dQ and dK passes swap them",
+                d.d_k, d.d_v);
+  if ((s = check_matrix_dims(dtype, d.d_v))) return s;
+  if ((s = check_chunk(chunk))) return s;
+  if ((s = check_gamma(gamma, d.heads))) return s;
+  if (pos0 < 0) return fail(MSR_ERR_SHAPE, "pos0 = %lld is negative", (long long)pos0);
+  if (dS_in && dS_in == S_in) return fail(MSR_ERR_SHAPE, "dS_in may not alias S_in");
+  if (dS_out && d.batch > 0 && d.seqlen > 0)
+    for (int h = 0; h < d.heads; ++h)
+      if (!(std::fabs((double)qk_scale) * gamma[h] >= 0x1p-60))
+        return fail(MSR_ERR_UNSUPPORTED,
+                    "dS_out needs |qk_scale| * gamma_h >= 2^-60 (head %d: gamma %g, scale %g): it seeds the "
+                    "reversed passes divided by qk_scale * gamma_h", h, gamma[h], (double)qk_scale);
+  if (d.batch == 0) return ok();
+  hipStream_t st = (hipStream_t)stream;
+  const int nbh = d.batch * d.heads;
+  HeadScale hs;
+  if (d.seqlen == 0) {  // no tokens: dS_in = dS_out
+    if (!dS_in) return ok();
+    std::fill(hs.c, hs.c + kMaxHeads, 1.0f);
+    return from_hip(launch_state_xform(dS_out, dS_in, nbh, d.heads, d.d_k, d.d_v, false, hs, st),
+                    "msr_chunkwise_bwd(seqlen=0)");
+  }
+  if (!Q || !K || !V || !dO || !dQ || !dK || !dV)
+    return fail(MSR_ERR_NULL, "Q, K, V, dO, dQ, dK and dV must be non-NULL");
+  const bool rope = rope_base > 0.f;
+  const BwdWs w = bwd_ws_layout(dtype, d, chunk, rope);
+  if (!workspace || ws_bytes < w.total)
+    return fail(MSR_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", w.total, workspace ? ws_bytes : 0);
+  void* cws = at<void>(workspace, w.chunk);
+  if (rope && (s = rotate_qk(dtype, d, rope_base, pos0, Q, K, cws, w.cw, st, &Q, &K))) return s;
+  const Elt e = dtype == MSR_BF16 ? kBF16 : kF32;
+  const size_t es = elt_size(dtype);
+  const int64_t ld = (int64_t)d.heads * d.d_k;   // d_k == d_v: one token stride for every tensor
+  const HeadTab tab = make_tab(gamma, d.heads, chunk, d.seqlen);
+  float* sin_t = at<float>(workspace, w.sin_t);
+  float* dso = at<float>(workspace, w.dso);
+  float* dso_t = at<float>(workspace, w.dso_t);
+  hipError_t err = hipSuccess;
+  // state seeds
+  std::fill(hs.c, hs.c + kMaxHeads, 1.0f);
+  if (S_in) err = launch_state_xform(S_in, sin_t, nbh, d.heads, d.d_v, d.d_k, true, hs, st);
+  if (dS_out && err == hipSuccess) {
+    for (int h = 0; h < d.heads; ++h) hs.c[h] = (float)(1.0 / ((double)qk_scale * gamma[h]));
+    err = launch_state_xform(dS_out, dso, nbh, d.heads, d.d_k, d.d_v, false, hs, st);
+    if (err == hipSuccess) err = launch_state_xform(dS_out, dso_t, nbh, d.heads, d.d_v, d.d_k, true, hs, st);
+  }
+  if (err != hipSuccess) return from_hip(err, "msr_chunkwise_bwd(state seeds)");
+  auto pass = [&](const void* q, const void* k, const void* v, void* o, const float* sin, float* sout) {
+    ChunkArgs a{};
+    a.elt = e;
+    a.d_k = d.d_k; a.d_v = d.d_v; a.batch = d.batch; a.seqlen = d.seqlen; a.heads = d.heads;
+    a.chunk = chunk;
+    a.Q = q; a.K = k; a.V = v; a.O = o;
+    a.ldq = a.ldk = a.ldv = a.ldo = ld;
+    a.scale = qk_scale;
+    a.S_in = sin; a.S_out = sout;
+    a.dR = at<void>(cws, w.cw.dr);
+    a.Rx = at<void>(cws, w.cw.rx);
+    return launch_chunkwise(a, tab, st);
+  };
+  // dQ = causal retention of (dO, V, K) from S_in^T
+  err = pass(dO, V, K, dQ, S_in ? sin_t : nullptr, nullptr);
+  if (err != hipSuccess) return from_hip(err, "msr_chunkwise_bwd(dQ)");
+  // reversed K, Q, V, dO
+  RevJobs rj{};
+  const void* srcs[4] = {K, Q, V, dO};
+  const size_t offs[4] = {w.rk, w.rq, w.rv, w.rdo};
+  for (int j = 0; j < 4; ++j) {
+    rj.src[j] = static_cast<const char*>(srcs[j]);
+    rj.dst[j] = at<char>(workspace, offs[j]);
+    rj.lds[j] = rj.ldd[j] = ld * (int64_t)es;
+  }
+  const int row_bytes = (int)(ld * (int64_t)es);
+  err = launch_reverse_rows(rj, 4, d.batch, d.seqlen, row_bytes, false, st);
+  if (err != hipSuccess) return from_hip(err, "msr_chunkwise_bwd(reverse)");
+  const void* rk = at<void>(workspace, w.rk);
+  const void* rq = at<void>(workspace, w.rq);
+  const void* rv = at<void>(workspace, w.rv);
+  const void* rdo = at<void>(workspace, w.rdo);
+  // reversed dV = causal retention of (rev K, rev Q, rev dO); its last state gives dS_in
+  err = pass(rk, rq, rdo, dV, dS_out ? dso : nullptr, dS_in);
+  if (err != hipSuccess) return from_hip(err, "msr_chunkwise_bwd(dV)");
+  // reversed dK = causal retention of (rev V, rev dO, rev Q)
+  err = pass(rv, rdo, rq, dK, dS_out ? dso_t : nullptr, nullptr);
+  if (err != hipSuccess) return from_hip(err, "msr_chunkwise_bwd(dK)");
+  RevJobs back{};
+  back.dst[0] = static_cast<char*>(dV);
+  back.dst[1] = static_cast<char*>(dK);
+  back.ldd[0] = back.ldd[1] = ld * (int64_t)es;
+  err = launch_reverse_rows(back, 2, d.batch, d.seqlen, row_bytes, true, st);
+  if (err != hipSuccess) return from_hip(err, "msr_chunkwise_bwd(reverse back)");
+  if (rope) {  // gradients with respect to the unrotated Q and K
+    const float2* rtab = at<float2>(cws, w.cw.tab);
+    const int rows = d.batch * d.seqlen;
+    err = launch_rope_apply(e, dQ, ld, dQ, ld, rows, d.seqlen, d.heads, d.d_k, rtab, st, true);
+    if (err == hipSuccess) err = launch_rope_apply(e, dK, ld, dK, ld, rows, d.seqlen, d.heads, d.d_k, rtab, st, true);
+    if (err != hipSuccess) return from_hip(err, "msr_chunkwise_bwd(rotation)");
+  }
+  if (dS_in) {
+    for (int h = 0; h < d.heads; ++h) hs.c[h] = (float)((double)qk_scale * gamma[h]);
+    err = launch_state_xform(dS_in, dS_in, nbh, d.heads, d.d_k, d.d_v, false, hs, st);
+  }
+  return from_hip(err, "msr_chunkwise_bwd(dS_in)");
 }
 
 msr_status msr_recurrent_step(msr_dtype dtype, int32_t batch, int32_t heads, int32_t d_k, int32_t d_v,

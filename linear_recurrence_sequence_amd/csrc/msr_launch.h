@@ -64,6 +64,27 @@ hipError_t launch_recurrent_step(Elt elt, int d_k, int d_v, int batch, int heads
 hipError_t launch_gn_gate(Elt elt, int d_v, int batch, int heads, const float* o, int64_t ldo, const void* g,
                           int64_t ldg, void* z, int64_t ldz, float eps, hipStream_t stream);
 
+// Time reversal of token rows for the backward's anti-causal passes: up to
+// four jobs, byte row strides (multiples of 16), rows of row_bytes bytes
+// (a multiple of 16).  in_place: each job's dst is reversed in place (src
+// unused); otherwise dst row (b, seqlen-1-t) = src row (b, t).
+struct RevJobs {
+  const char* src[4];
+  char* dst[4];
+  int64_t lds[4], ldd[4];
+};
+hipError_t launch_reverse_rows(const RevJobs& jobs, int njobs, int batch, int seqlen, int row_bytes, bool in_place,
+                               hipStream_t stream);
+// Per-head factors of launch_state_xform.
+struct HeadScale {
+  float c[kMaxHeads];
+};
+// dst[bh] (rows x cols float32) = c[bh % heads] * (transpose ? src[bh]^T :
+// src[bh]) for bh < nbh; src == nullptr writes zeros; dst may equal src
+// only without transpose.  rows and cols multiples of 32.
+hipError_t launch_state_xform(const float* src, float* dst, int nbh, int heads, int rows, int cols, bool transpose,
+                              const HeadScale& hs, hipStream_t stream);
+
 // cos/sin table: tab[n * (d/2) + j] = (cos, sin)((pos0 + n) * theta_j),
 // theta_j = base^(-2j/d), n = 0..npos-1.
 hipError_t launch_rope_table(float2* tab, int npos, int d, int64_t pos0, float base,
@@ -71,9 +92,10 @@ hipError_t launch_rope_table(float2* tab, int npos, int d, int64_t pos0, float b
 // Rotate the first d columns of every head of a [rows, heads * d] block
 // (rows = batch * seqlen tokens, token n = row % seqlen) from src to dst
 // (dst may equal src).  Strides in elements.
+// inverse: rotate by the negative angle (the adjoint, for gradients).
 hipError_t launch_rope_apply(Elt elt, const void* src, int64_t lds, void* dst, int64_t ldd,
                              int rows, int seqlen, int heads, int d, const float2* tab,
-                             hipStream_t stream);
+                             hipStream_t stream, bool inverse = false);
 
 // B operand of launch_gemm: up to four column segments, segment s covering
 // output columns [start[s], start[s+1]) (start[0] = 0, unused entries set to

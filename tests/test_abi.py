@@ -119,6 +119,28 @@ def test_other_entry_points_validation():
     assert blk(F=0) == 2
 
 
+def test_backward_validation():
+    L = msr.lib()
+    g, gp = _gamma(2)
+    bwd = lambda dims=(1, 64, 2, 64, 64), chunk=32, gam=gp, scale=1.0, dQ=FAKE, S_in=None, dS_out=None, dS_in=None, \
+        ws=1 << 40, dtype=1: L.msr_chunkwise_bwd(dtype, msr.MsrDims(*dims), chunk, gam, 0.0, 0, scale, FAKE, FAKE,
+                                                FAKE, FAKE, S_in, dS_out, dQ, FAKE, FAKE, dS_in, FAKE, ws, None)
+    assert bwd(dims=(1, 64, 2, 256, 512)) == 4                   # d_k != d_v
+    assert "d_k == d_v" in msr.msr_last_error()
+    assert bwd(dims=(1, 64, 2, 48, 48)) == 4
+    assert bwd(chunk=40) == 4
+    assert bwd(dtype=3) == 3
+    assert bwd(dQ=None) == 1
+    assert bwd(ws=16) == 5
+    assert bwd(S_in=FAKE, dS_in=FAKE) == 2                      # dS_in aliases S_in
+    z = np.array([0.9, 0.0])
+    zp = z.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+    assert bwd(gam=zp, dS_out=FAKE) == 4                         # dS_out seeds divide by gamma
+    assert bwd(scale=0.0, dS_out=FAKE) == 4
+    assert bwd(dims=(0, 64, 2, 64, 64), gam=zp, dS_out=FAKE) == 0   # nothing to do
+    assert bwd(dims=(2, 64, 2, 64, 64), gam=zp, ws=16) == 5     # gamma = 0 is fine without dS_out
+
+
 def test_empty_inputs_are_no_ops():
     """batch = 0 or seqlen = 0 (parallel / layer) returns OK without touching memory."""
     L = msr.lib()
@@ -157,6 +179,10 @@ def test_workspace_sizes():
     assert base <= got <= base + up(8 * Bd * max(Hd * (2 * kd + 2 * vd), dm) * 4)
     assert msr.msr_layer_decode_workspace_bytes(1, 0, dm, Hd, kd, vd) == 0
     assert msr.msr_layer_decode_workspace_bytes(1, Bd, 100, Hd, kd, vd) == 0
+    # backward: the chunk workspace (with the rotated copies), four reversed inputs, three state seeds
+    cw = msr.msr_chunkwise_workspace_bytes(1, B, N, H, dk, dv, C, 1e4)
+    assert msr.msr_chunkwise_bwd_workspace_bytes(1, B, N, H, dk, dv, C, 1e4) == (
+        up(cw) + 4 * up(B * N * H * dk * 2) + 3 * up(B * H * dk * dv * 4))
     # RetNet block: the layer's workspace, then LN(X) / LN(Y), Y and the hidden rows
     Bb, Nb, dmb, Hb, db, Cb, Fb = 2, 64, 256, 2, 64, 32, 512
     lay = msr.msr_layer_workspace_bytes(1, Bb, Nb, dmb, Hb, db, db, Cb)

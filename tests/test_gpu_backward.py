@@ -1,0 +1,134 @@
+"""Parity of the chunkwise backward (msr_chunkwise_bwd) against the float64
+oracle's retention gradients (themselves pinned to finite differences of the
+recurrent form): every supported head dim, ragged tails over several chunks,
+initial state, final-state gradient and rotation, the degenerate decays, the
+empty cases, and the headline core shape (batch 8, 2048 tokens, 8 heads of
+256, bf16) on sampled (batch, head) slices."""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from gpu_util import TOL, dev, host, say
+
+pytestmark = pytest.mark.gpu
+
+STATE_TOL = {"f32": 1e-4, "bf16": 1e-2}
+
+
+def _msr():
+    import linear_recurrence_sequence_amd as msr
+    return msr
+
+
+def _state_err(got, ref):
+    """max over (batch, head) of the slice's max-abs-relative error."""
+    return max(oracle.max_rel_err(got[b, h], ref[b, h]) for b in range(ref.shape[0]) for h in range(ref.shape[1]))
+
+
+def _check(name, got, ref, tol):
+    err = oracle.max_rel_err_per_head(got, ref)
+    print(f"{name}: {err:.2e}", flush=True)
+    assert np.all(np.isfinite(got)), name
+    assert err < tol, (name, err)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("d,N,chunk", [(64, 200, 64), (64, 31, 32), (128, 300, 128), (256, 257, 128),
+                                       (256, 520, 256)])
+def test_backward(dtype, d, N, chunk):
+    import torch
+    msr = _msr()
+    B, H = 2, 3
+    q, k, v = workloads.core_inputs(21 + d, B, N, H, d, d, dtype)
+    rng = np.random.default_rng(22 + d)
+    dO = workloads.normal(rng, (B, N, H, d), 1.0, dtype)
+    S0 = rng.standard_normal((B, H, d, d)).astype(np.float32)
+    dS = rng.standard_normal((B, H, d, d)).astype(np.float32)
+    g = np.array([0.9, 1 - 2.0 ** -5, 1 - 2.0 ** -12])
+    scale, pos0, base = 1 / math.sqrt(d), 5, 10000.0
+    dS_in = torch.empty((B, H, d, d), device="cuda")
+    say("backward", dtype, d, N, chunk)
+    dQ, dK, dV = msr.msr_chunkwise_bwd(dev(q, dtype), dev(k, dtype), dev(v, dtype), dev(dO, dtype), g, chunk,
+                                       rope_base=base, pos0=pos0, qk_scale=scale, S_in=torch.from_numpy(S0).cuda(),
+                                       dS_out=torch.from_numpy(dS).cuda(), dS_in=dS_in)
+    torch.cuda.synchronize()
+    qr, kr = oracle.rotary(q, pos0, base), oracle.rotary(k, pos0, base)
+    rq, rk, rv, rS = oracle.retention_grad(qr, kr, v, dO, g, scale, S0=S0, dS=dS)
+    _check("dQ", host(dQ), oracle.rotary_adjoint(rq, pos0, base), TOL[dtype])
+    _check("dK", host(dK), oracle.rotary_adjoint(rk, pos0, base), TOL[dtype])
+    _check("dV", host(dV), rv, TOL[dtype])
+    err = _state_err(host(dS_in), rS)
+    print(f"dS_in: {err:.2e}", flush=True)
+    assert err < STATE_TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_backward_degenerate_decays_without_states(dtype):
+    """gamma = 0, 0.5 and 1, no S_in, no dS_out, no rotation, scale 1,
+    ragged sequence; dS_in still returned."""
+    import torch
+    msr = _msr()
+    B, N, H, d = 2, 161, 3, 64
+    q, k, v = workloads.core_inputs(31, B, N, H, d, d, dtype)
+    dO = workloads.normal(np.random.default_rng(32), (B, N, H, d), 1.0, dtype)
+    g = np.array([0.0, 0.5, 1.0])
+    dS_in = torch.empty((B, H, d, d), device="cuda")
+    say("backward degenerate", dtype)
+    dQ, dK, dV = msr.msr_chunkwise_bwd(dev(q, dtype), dev(k, dtype), dev(v, dtype), dev(dO, dtype), g, 64,
+                                       dS_in=dS_in)
+    torch.cuda.synchronize()
+    rq, rk, rv, rS = oracle.retention_grad(q, k, v, dO, g, 1.0)
+    for name, got, ref in (("dQ", dQ, rq), ("dK", dK, rk), ("dV", dV, rv)):
+        _check(name, host(got), ref, TOL[dtype])
+    got = host(dS_in)
+    assert np.all(got[:, 0] == 0.0)                      # gamma = 0: no gradient reaches the initial state
+    assert _state_err(got[:, 1:], rS[:, 1:]) < STATE_TOL[dtype]
+
+
+def test_backward_empty_sequences():
+    """seqlen = 0: dS_in = dS_out exactly (and zeros without dS_out); batch = 0
+    is a no-op."""
+    import torch
+    msr = _msr()
+    B, H, d = 3, 2, 64
+    g = np.array([0.9, 0.99])
+    dS = torch.randn((B, H, d, d), device="cuda")
+    dS_in = torch.full((B, H, d, d), 7.0, device="cuda")
+    e = torch.empty((B, 0, H, d), device="cuda")
+    say("backward empty")
+    msr.msr_chunkwise_bwd(e, e, e, e, g, 64, dS_out=dS, dS_in=dS_in)
+    torch.cuda.synchronize()
+    assert torch.equal(dS_in, dS)
+    msr.msr_chunkwise_bwd(e, e, e, e, g, 64, dS_in=dS_in)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(dS_in).item() == 0
+    z = torch.empty((0, 5, H, d), device="cuda")
+    msr.msr_chunkwise_bwd(z, z, z, z, g, 64)
+
+
+@pytest.mark.slow
+def test_backward_headline_core_shape_sampled():
+    """Batch 8, 2048 tokens, 8 heads of 256, bf16, chunk 256, rotation, the
+    heads' gammas 1 - 2^(-5-h), scale 1/16: (batch, head) slices (0, 0),
+    (3, 5) and (7, 7) of dQ, dK, dV and dS_in against the oracle."""
+    import torch
+    msr = _msr()
+    B, N, H, d, C = 8, 2048, 8, 256, 256
+    g = workloads.gammas(H)
+    say("backward headline core shape")
+    q, k, v, dO = (workloads.device_normal((B, N, H, d), seed=900 + i).to(torch.bfloat16) for i in range(4))
+    dS_in = torch.empty((B, H, d, d), device="cuda")
+    dQ, dK, dV = msr.msr_chunkwise_bwd(q, k, v, dO, g, C, rope_base=1e4, qk_scale=1 / 16, dS_in=dS_in)
+    torch.cuda.synchronize()
+    for b, h in ((0, 0), (3, 5), (7, 7)):
+        sl = lambda t: host(t[b:b + 1, :, h:h + 1])
+        qs, ks = oracle.rotary(sl(q), 0, 1e4), oracle.rotary(sl(k), 0, 1e4)
+        rq, rk, rv, rS = oracle.retention_grad(qs, ks, sl(v), sl(dO), g[h:h + 1], 1 / 16)
+        _check(f"dQ[{b},{h}]", sl(dQ), oracle.rotary_adjoint(rq, 0, 1e4), TOL["bf16"])
+        _check(f"dK[{b},{h}]", sl(dK), oracle.rotary_adjoint(rk, 0, 1e4), TOL["bf16"])
+        _check(f"dV[{b},{h}]", sl(dV), rv, TOL["bf16"])
+        assert oracle.max_rel_err(host(dS_in[b, h]), rS[0, 0]) < STATE_TOL["bf16"]
