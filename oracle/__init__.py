@@ -27,6 +27,8 @@ from .retention import (  # noqa: F401
     retnet_block,
     rotary_adjoint,
     retention_grad,
+    log_sigmoid,
+    rglru,
     max_rel_err,
     max_rel_err_per_head,
 )

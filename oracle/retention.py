@@ -13,6 +13,8 @@ Pages cited (titles as printed on them):
   Large Language Models" -- abstract and method bullets.
 * [RN-ru]  "Retentive Network: архитектурный прорыв или временный успех?" --
   decay-masked causal mask, per-head gamma, chunkwise recursion.
+* [GR-zh]  "Griffin ：將門控線性循環與局部注意力混合以實現高效的語言模型" --
+  section "實門線性循環單元 (RG-LRU)": the gated diagonal recurrence.
 
 Tensor layout everywhere: [batch, seqlen, heads, head_dim] (token-major, the
 natural output of X @ W).  gamma is a float64 array with one value per head.
@@ -426,6 +428,45 @@ def retention_grad(q, k, v, dO, gamma, scale: float = 1.0, S0=None, dS=None):
             dvv[b, :, h] = scale * (((Q @ K.T) * D).T @ G) + zeta * (K @ dS[b, h])
             dS0[b, h] = scale * ((Q * xi).T @ G) + np.power(gam, N) * dS[b, h]
     return dq, dkk, dvv, dS0
+
+
+# --------------------------------------------------------------------------
+# RG-LRU: the gated diagonal linear recurrence of Griffin
+# --------------------------------------------------------------------------
+def log_sigmoid(z):
+    """log(sigma(z)) = -log(1 + e^(-z)), evaluated without overflow."""
+    z = _f64(z)
+    return -(np.maximum(-z, 0.0) + np.log1p(np.exp(-np.abs(z))))
+
+
+def rglru(x, Wa, ba, Wx, bx, Lam, c: float = 8.0, h0=None):
+    """Real-gated linear recurrent unit, [GR-zh] section "實門線性循環單元
+    (RG-LRU)" (page "Griffin"):
+
+      r_t = sigma(x_t W_a + b_a)            recurrence gate
+      i_t = sigma(x_t W_x + b_x)            input gate
+      a_t = a^(c r_t),  a = sigma(Lambda)   (diagonal, per channel)
+      h_t = a_t (.) h_{t-1} + sqrt(1 - a_t^2) (.) (i_t (.) x_t)
+      y_t = h_t
+
+    a^(c r_t) is formed in log space, log a_t = c r_t log sigma(Lambda), and
+    1 - a_t^2 = -expm1(2 log a_t), so neither loses precision as a_t -> 1.
+    x: [B, T, D]; W_a, W_x: [D, D] (applied as x @ W); b_a, b_x, Lambda: [D];
+    h0: [B, D] (zeros if None).  Returns (y [B, T, D], h_T [B, D]).
+    """
+    x = _f64(x)
+    B, T, D = x.shape
+    r = 1.0 / (1.0 + np.exp(-(x @ _f64(Wa) + _f64(ba))))
+    i = 1.0 / (1.0 + np.exp(-(x @ _f64(Wx) + _f64(bx))))
+    log_a = c * r * log_sigmoid(Lam)                       # [B, T, D]
+    a = np.exp(log_a)
+    gain = np.sqrt(-np.expm1(2.0 * log_a))
+    h = np.zeros((B, D), dtype=F64) if h0 is None else _f64(h0).copy()
+    y = np.empty((B, T, D), dtype=F64)
+    for t in range(T):
+        h = a[:, t] * h + gain[:, t] * (i[:, t] * x[:, t])
+        y[:, t] = h
+    return y, h
 
 
 # --------------------------------------------------------------------------

@@ -504,3 +504,98 @@ def test_rotary_adjoint_is_the_inverse_rotation():
         rx = oracle.rotary(x, pos0, base)
         assert abs(np.sum(rx * y) - np.sum(x * oracle.rotary_adjoint(y, pos0, base))) < 1e-10
         np.testing.assert_allclose(oracle.rotary_adjoint(rx, pos0, base), x, rtol=0, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# RG-LRU ([GR-zh] section "實門線性循環單元 (RG-LRU)")
+# --------------------------------------------------------------------------
+def _zero_gates(D):
+    z = np.zeros((D, D))
+    return z, np.zeros(D), z.copy(), np.zeros(D)
+
+
+def test_log_sigmoid():
+    z = np.array([-3.0, -0.5, 0.0, 0.7, 4.0])
+    np.testing.assert_allclose(oracle.log_sigmoid(z), np.log(1.0 / (1.0 + np.exp(-z))), rtol=1e-14)
+    assert oracle.log_sigmoid(np.array([-800.0]))[0] == -800.0
+    big = oracle.log_sigmoid(np.array([800.0]))[0]
+    assert big <= 0.0 and big > -1e-300
+
+
+def test_rglru_geometric_closed_form():
+    """W = 0, b = 0 give r = i = 1/2; Lambda = 0 gives a = 1/2, so with c = 8
+    a_t = (1/2)^4 = 1/16 and the gain is sqrt(1 - 1/256).  A constant input
+    u then gives h_t = a^(t+1) h0 + gain (u/2) (1 - a^(t+1)) / (1 - a)."""
+    rng = np.random.default_rng(51)
+    B, T, D = 2, 40, 8
+    u = rng.standard_normal((B, D))
+    x = np.repeat(u[:, None, :], T, axis=1)
+    h0 = rng.standard_normal((B, D))
+    y, hT = oracle.rglru(x, *_zero_gates(D), np.zeros(D), 8.0, h0=h0)
+    a, gain = 1.0 / 16.0, math.sqrt(1.0 - 1.0 / 256.0)
+    t = np.arange(T)[None, :, None]
+    ref = a ** (t + 1) * h0[:, None, :] + gain * (u[:, None, :] / 2) * (1 - a ** (t + 1)) / (1 - a)
+    np.testing.assert_allclose(y, ref, rtol=1e-13, atol=1e-15)
+    np.testing.assert_array_equal(hT, y[:, -1])
+
+
+def test_rglru_gate_orientation_exact_values():
+    """One weight W_a[j, k] = ln 3 and x_j = 1 make r_k = sigma(ln 3) = 3/4
+    (applied as x @ W_a; the transposed product would gate channel j
+    instead); with Lambda = 0, a_k = (1/2)^(8 * 3/4) = 1/64, i = 1/2, and
+    one step from h0 = 0 gives y_k = sqrt(1 - 1/4096) * x_k / 2, while the
+    other channels keep a = 1/16."""
+    D, j, k = 6, 1, 4
+    Wa, ba, Wx, bx = _zero_gates(D)
+    Wa[j, k] = math.log(3.0)
+    x = np.zeros((1, 1, D))
+    x[0, 0, j], x[0, 0, k], x[0, 0, 0] = 1.0, 2.0, -3.0
+    y, _ = oracle.rglru(x, Wa, ba, Wx, bx, np.zeros(D), 8.0)
+    assert abs(y[0, 0, k] - math.sqrt(4095.0) / 64.0) < 1e-14
+    g16 = math.sqrt(1.0 - 1.0 / 256.0)
+    assert abs(y[0, 0, j] - g16 * 0.5) < 1e-14
+    assert abs(y[0, 0, 0] - g16 * -1.5) < 1e-14
+    assert np.all(y[0, 0, [2, 3, 5]] == 0.0)
+
+
+def test_rglru_limits_and_log_space():
+    """a -> 0 (Lambda very negative): no memory, y = i x.  a -> 1 (Lambda
+    very positive): the state is kept, y = h0.  Lambda = 45: a_t rounds to
+    1 in float64, but the log-space gain is sqrt(8 e^-45) (since
+    log sigma(45) = -e^-45 to 20 digits and 1 - a^2 = -2 * 4 * log sigma(45)
+    to first order)."""
+    rng = np.random.default_rng(52)
+    B, T, D = 2, 9, 5
+    x = rng.standard_normal((B, T, D))
+    h0 = rng.standard_normal((B, D))
+    y, _ = oracle.rglru(x, *_zero_gates(D), np.full(D, -60.0), 8.0, h0=h0)
+    np.testing.assert_allclose(y, 0.5 * x, rtol=1e-13, atol=1e-15)
+    y, hT = oracle.rglru(x, *_zero_gates(D), np.full(D, 40.0), 8.0, h0=h0)
+    np.testing.assert_allclose(y, np.repeat(h0[:, None], T, axis=1), rtol=0, atol=1e-7)
+    y, _ = oracle.rglru(np.ones((1, 1, 1)), *_zero_gates(1), np.array([45.0]), 8.0)
+    assert abs(y[0, 0, 0] / (0.5 * math.sqrt(8.0) * math.exp(-22.5)) - 1.0) < 1e-12
+
+
+def test_rglru_split_continuation():
+    """Running the second half from the first half's last state gives the
+    full sequence's outputs and last state."""
+    rng = np.random.default_rng(53)
+    B, T, D, t1 = 2, 17, 6, 7
+    x = rng.standard_normal((B, T, D))
+    Wa, Wx = rng.standard_normal((D, D)) / math.sqrt(D), rng.standard_normal((D, D)) / math.sqrt(D)
+    ba, bx, lam = rng.standard_normal(D), rng.standard_normal(D), rng.standard_normal(D) * 3
+    h0 = rng.standard_normal((B, D))
+    y, hT = oracle.rglru(x, Wa, ba, Wx, bx, lam, 8.0, h0=h0)
+    y1, h1 = oracle.rglru(x[:, :t1], Wa, ba, Wx, bx, lam, 8.0, h0=h0)
+    y2, h2 = oracle.rglru(x[:, t1:], Wa, ba, Wx, bx, lam, 8.0, h0=h1)
+    np.testing.assert_allclose(np.concatenate([y1, y2], axis=1), y, rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(h2, hT, rtol=1e-14, atol=1e-15)
+
+
+def test_rglru_input_recipe():
+    """The generated Lambda puts sigma(Lambda)^8 on [0.9, 0.999]."""
+    import workloads
+    *_, lam = workloads.rglru_inputs(5, 1, 2, 512)
+    ac = np.exp(8.0 * oracle.log_sigmoid(lam.astype(np.float64)))
+    assert ac.min() >= 0.9 - 1e-6 and ac.max() <= 0.999 + 1e-6
+    assert 0.93 < ac.mean() < 0.97

@@ -19,6 +19,11 @@ Workloads (sizes as named; all inputs Gaussian, weights with variance
 * ``block_bf16_b4_n8192`` -- gated MSR block, bf16, batch 4, 8192 tokens,
   d_model 4096, 16 heads, q/k head dim 256, v head dim 512, chunk 512.
 
+RG-LRU inputs (``rglru_inputs``): x ~ N(0, 1); W_a, W_x ~ N(0, 1/width)
+(LeCun normal, the Griffin page's initialisation); b_a, b_x ~ N(0, 1/4);
+Lambda drawn so that a^c = sigma(Lambda)^c is uniform on [0.9, 0.999] (the
+same page's initialisation of the recurrent weight), c = 8.
+
 The per-head decay is gamma_h = 1 - 2**(-5-h); the pages give a different
 fixed gamma to every head (RetNet page "Transformer取代者登場！微軟、清華剛推出
 RetNet", section "門控多尺度 Retention") but their formula is stripped, so the
@@ -33,7 +38,7 @@ import numpy as np
 
 __all__ = [
     "Workload", "WORKLOADS", "gammas", "round_bf16", "bf16_bits",
-    "normal", "layer_inputs", "core_inputs", "device_normal",
+    "normal", "layer_inputs", "core_inputs", "device_normal", "rglru_inputs",
 ]
 
 
@@ -145,3 +150,20 @@ def device_normal(shape, seed: int, device="cuda", dtype=None):
     g.manual_seed(int(seed))
     t = torch.randn(tuple(shape), generator=g, device=device, dtype=torch.float32)
     return t if dtype is None else t.to(dtype)
+
+
+def rglru_inputs(seed, batch, seqlen, width, dtype="f32", c=8.0):
+    """x [batch, seqlen, width], W_a, W_x [width, width] (dtype-rounded),
+    b_a, b_x, Lambda [width] (float32), drawn from ``default_rng(seed)`` in
+    that order (x, W_a, b_a, W_x, b_x, then the uniform draw for Lambda).
+    Lambda = logit(u^(1/c)) with u ~ U[0.9, 0.999], so sigma(Lambda)^c = u."""
+    rng = np.random.default_rng(seed)
+    x = normal(rng, (batch, seqlen, width), 1.0, dtype)
+    Wa = normal(rng, (width, width), width ** -0.5, dtype)
+    ba = normal(rng, (width,), 0.5, "f32")
+    Wx = normal(rng, (width, width), width ** -0.5, dtype)
+    bx = normal(rng, (width,), 0.5, "f32")
+    u = rng.uniform(0.9, 0.999, size=width)
+    p = u ** (1.0 / c)
+    lam = np.log(p / (1.0 - p)).astype(np.float32)
+    return x, Wa, ba, Wx, bx, lam
