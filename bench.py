@@ -236,6 +236,33 @@ def bench_backward(B, N, H, d, C, steps, warmup):
     return res
 
 
+def bench_rglru(B, T, D, steps, warmup):
+    """RG-LRU over a sequence (gate GEMM with sigmoid epilogue + float32
+    scan), bf16, inputs of the seeded recipe drawn on the host once."""
+    import torch
+    import linear_recurrence_sequence_amd as msr
+    import workloads
+    x, Wa, ba, Wx, bx, lam = workloads.rglru_inputs(80, B, T, D, "bf16")
+    cu = lambda a, dt=torch.bfloat16: torch.from_numpy(a).cuda().to(dt)
+    X, WA, WX = cu(x), cu(Wa), cu(Wx)
+    BA, BX, LAM = cu(ba, torch.float32), cu(bx, torch.float32), cu(lam, torch.float32)
+    Y = torch.empty_like(X)
+    hT = torch.empty((B, D), device="cuda")
+    ws = torch.empty(msr.msr_rglru_workspace_bytes(1, B, T, D), dtype=torch.uint8, device="cuda")
+    fn = lambda: msr.msr_rglru_fwd(X, WA, BA, WX, BX, LAM, h_last=hT, Y=Y, workspace=ws)
+    t = gpu_time(fn, steps, warmup)
+    tr = traced(fn, steps)
+    M = B * T
+    scan_bytes = M * D * 4 * 2            # x, r, i read once, y written once (bf16)
+    res = {"workload": f"rglru_bf16_b{B}_n{T}_d{D}", "ms_per_step": round(t * 1e3, 4),
+           "tokens_per_s": round(M / t, 1),
+           "kernels": {"k_gemm": roof("k_gemm", 2 * M * 2 * D * D, "mfma", tr, steps),
+                       "k_rglru_scan": roof("k_rglru_scan", scan_bytes, "hbm", tr, steps)}}
+    del X, WA, WX, Y, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def bench_decode(steps_timed, warmup):
     import torch
     import linear_recurrence_sequence_amd as msr
@@ -411,7 +438,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", default="layer,decode,long,block,retnet,backward,cpu")
+    ap.add_argument("--only", default="layer,decode,long,block,retnet,backward,rglru,cpu")
     ap.add_argument("--no-cpu", action="store_true")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -485,6 +512,9 @@ def main():
         line["backward"] = {
             "headline_core": bench_backward(w.batch, w.seqlen, w.heads, w.d_k, w.chunk, args.steps, args.warmup),
             "long_core": bench_backward(lw.batch, lw.seqlen, lw.heads, lw.d_k, lw.chunk, max(3, args.steps // 2), 2)}
+    if "rglru" in parts:
+        log("rglru")
+        line["rglru"] = bench_rglru(8, 2048, 2048, args.steps, args.warmup)
     if "copy" in parts:
         log("copy calibration")
         line["copy_calibration"] = bench_copy()

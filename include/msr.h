@@ -130,6 +130,27 @@ msr_status msr_chunkwise_bwd(msr_dtype dtype, msr_dims dims, int32_t chunk,
 size_t msr_chunkwise_bwd_workspace_bytes(msr_dtype dtype, msr_dims dims, int32_t chunk,
                                          float rope_base);
 
+/* RG-LRU, the gated diagonal linear recurrence of the page "Griffin ：將門控
+ * 線性循環與局部注意力混合以實現高效的語言模型", section "實門線性循環單元
+ * (RG-LRU)", per batch element and channel:
+ *   r_t = sigmoid(x_t W_a + b_a),  i_t = sigmoid(x_t W_x + b_x)
+ *   a_t = a^(c r_t), a = sigmoid(Lambda), formed in log space:
+ *         log a_t = c r_t log sigmoid(Lambda), 1 - a_t^2 = -expm1(2 log a_t)
+ *   h_t = a_t h_{t-1} + sqrt(1 - a_t^2) (i_t x_t),  y_t = h_t
+ * X, Y: [batch, seqlen, width] (dtype); W_a, W_x: [width, width] (dtype,
+ * applied as x @ W); b_a, b_x, Lambda: [width] float32; h0 (nullable:
+ * zeros) and h_last (nullable) [batch, width] float32, h_last may not
+ * alias h0.  The gates are stored in the workspace in dtype; the recurrence
+ * runs in float32.  width must be a multiple of 64; c > 0 (the page uses 8).
+ * Workspace: msr_rglru_workspace_bytes() bytes. */
+msr_status msr_rglru_fwd(msr_dtype dtype, int32_t batch, int32_t seqlen,
+                         int32_t width, float c, const void* X, const void* W_a,
+                         const float* b_a, const void* W_x, const float* b_x,
+                         const float* Lambda, const float* h0, float* h_last,
+                         void* Y, void* workspace, size_t ws_bytes, void* stream);
+size_t msr_rglru_workspace_bytes(msr_dtype dtype, int32_t batch, int32_t seqlen,
+                                 int32_t width);
+
 /* Recurrent form, one decode step, [RN-zh] Eq. (6), for every (batch, head):
  *   S <- gamma_h S + k^T v ;  o = qk_scale * q S   (S updated in place)
  * q, k: [batch, heads, d_k]; v, o: [batch, heads, d_v] (dtype); S:

@@ -18,7 +18,7 @@ __all__ = [
     "MSR_F32", "MSR_BF16", "MsrError", "MsrLibraryMissing", "library_path", "lib",
     "msr_parallel_fwd", "msr_parallel_workspace_bytes",
     "msr_chunkwise_fwd", "msr_chunkwise_workspace_bytes",
-    "msr_chunkwise_bwd", "msr_chunkwise_bwd_workspace_bytes",
+    "msr_chunkwise_bwd", "msr_chunkwise_bwd_workspace_bytes", "msr_rglru_fwd", "msr_rglru_workspace_bytes",
     "msr_recurrent_step", "msr_layer_fwd", "msr_layer_workspace_bytes",
     "msr_layer_decode_step", "msr_layer_decode_workspace_bytes",
     "msr_retnet_block_fwd", "msr_retnet_block_workspace_bytes",
@@ -30,7 +30,7 @@ MSR_F32, MSR_BF16 = 0, 1
 EXPORTS = (
     "msr_parallel_fwd", "msr_parallel_workspace_bytes", "msr_chunkwise_fwd",
     "msr_chunkwise_workspace_bytes", "msr_chunkwise_bwd", "msr_chunkwise_bwd_workspace_bytes",
-    "msr_recurrent_step", "msr_layer_fwd",
+    "msr_rglru_fwd", "msr_rglru_workspace_bytes", "msr_recurrent_step", "msr_layer_fwd",
     "msr_layer_workspace_bytes", "msr_layer_decode_step", "msr_layer_decode_workspace_bytes",
     "msr_retnet_block_fwd", "msr_retnet_block_workspace_bytes", "msr_status_str", "msr_last_error", "msr_trace_enable", "msr_trace_count", "msr_trace_get",
 )
@@ -82,6 +82,8 @@ def lib():
         "msr_chunkwise_bwd": (_I32, [_I32, MsrDims, _I32, _DP, _F, _I64, _F, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                      _P, _P, _SZ, _P]),
         "msr_chunkwise_bwd_workspace_bytes": (_SZ, [_I32, MsrDims, _I32, _F]),
+        "msr_rglru_fwd": (_I32, [_I32, _I32, _I32, _I32, _F, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+        "msr_rglru_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32]),
         "msr_recurrent_step": (_I32, [_I32, _I32, _I32, _I32, _I32, _DP, _F, _I64, _F, _P, _P, _P, _P, _P,
                                       _P]),
         "msr_layer_fwd": (_I32, [_I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _DP, _F, _F, _P, _P, _P,
@@ -261,6 +263,25 @@ def msr_chunkwise_bwd(Q, K, V, dO, gamma, chunk, *, rope_base=0.0, pos0=0, qk_sc
                                                         _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(dS_in), _ptr(ws), wsb,
                                                         _stream(stream)))
     return dQ, dK, dV
+
+
+def msr_rglru_workspace_bytes(dtype: int, batch, seqlen, width) -> int:
+    return lib().msr_rglru_workspace_bytes(dtype, batch, seqlen, width)
+
+
+def msr_rglru_fwd(X, W_a, b_a, W_x, b_x, Lambda, *, c=8.0, h0=None, h_last=None, Y=None, workspace=None,
+                  stream=None):
+    """RG-LRU over a sequence.  X: [B, T, width]; W_a, W_x: [width, width];
+    b_a, b_x, Lambda: [width] float32; h0, h_last: [B, width] float32.
+    Returns Y [B, T, width]."""
+    B, T, D = X.shape
+    dt = _dtype_code(X)
+    Y = _torch().empty_like(X) if Y is None else Y
+    ws, wsb = _workspace(lib().msr_rglru_workspace_bytes(dt, B, T, D), workspace, X.device)
+    _check("msr_rglru_fwd", lib().msr_rglru_fwd(dt, B, T, D, c, _ptr(X), _ptr(W_a), _ptr(b_a), _ptr(W_x), _ptr(b_x),
+                                                _ptr(Lambda), _ptr(h0), _ptr(h_last), _ptr(Y), _ptr(ws), wsb,
+                                                _stream(stream)))
+    return Y
 
 
 def msr_recurrent_step(q, k, v, S, gamma, *, pos, rope_base=0.0, qk_scale=1.0, o=None, stream=None):

@@ -259,9 +259,17 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm(const T* __restrict__ A, 
           v[2 * p + 1] = x * t.y + y * t.x;
         }
       }
+      if (const float* bias = sel(sg, bp.bias[0], bp.bias[1], bp.bias[2], bp.bias[3])) {
+        const float* bs = bias + (col - sel(sg, bp.start[0], bp.start[1], bp.start[2], bp.start[3]));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] += bs[e];
+      }
       if (bp.act == 1) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = 0.5f * v[e] * (1.0f + erff(v[e] * 0.70710678118654752f));
+      } else if (bp.act == 2) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = 1.0f / (1.0f + expf(-v[e]));
       }
       if (bp.resid) {
         Row8<T> rr8;
@@ -315,6 +323,7 @@ int gemm_splits(int M, int N, int K) {
 hipError_t launch_gemm_splitk(Elt elt, const void* A, int64_t lda, const GemmB& b, void* C, int64_t ldc, int M,
                               int N, int K, int splits, float* part, hipStream_t st) {
   if (M == 0 || N == 0) return hipSuccess;
+  if (b.act || b.resid || b.bias[0] || b.bias[1] || b.bias[2] || b.bias[3]) return hipErrorInvalidValue;
   GemmB bs = b;
   bs.part = part;
   bs.rope_segs = 0;

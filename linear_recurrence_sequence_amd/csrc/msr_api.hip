@@ -527,6 +527,50 @@ msr_status msr_chunkwise_bwd(msr_dtype dtype, msr_dims d, int32_t chunk, const d
   return from_hip(err, "msr_chunkwise_bwd(dS_in)");
 }
 
+size_t msr_rglru_workspace_bytes(msr_dtype dtype, int32_t batch, int32_t seqlen, int32_t width) {
+  if (check_dtype(dtype) || batch < 0 || seqlen < 0 || width <= 0) return 0;
+  return align_up((size_t)batch * seqlen * 2 * width * elt_size(dtype));
+}
+
+msr_status msr_rglru_fwd(msr_dtype dtype, int32_t batch, int32_t seqlen, int32_t width, float c, const void* X,
+                         const void* W_a, const float* b_a, const void* W_x, const float* b_x, const float* Lambda,
+                         const float* h0, float* h_last, void* Y, void* workspace, size_t ws_bytes, void* stream) {
+  msr_status s;
+  if ((s = check_dtype(dtype))) return s;
+  if (batch < 0 || seqlen < 0 || width <= 0)
+    return fail(MSR_ERR_SHAPE, "invalid sizes batch=%d seqlen=%d width=%d", batch, seqlen, width);
+  if (width % 64) return fail(MSR_ERR_UNSUPPORTED, "width = %d is not a multiple of 64", width);
+  if (!(c > 0.f) || !std::isfinite(c)) return fail(MSR_ERR_SHAPE, "c = %g must be positive and finite", (double)c);
+  const int64_t M = (int64_t)batch * seqlen;
+  if (M > (int64_t)INT32_MAX) return fail(MSR_ERR_UNSUPPORTED, "batch*seqlen exceeds 2^31-1");
+  if ((int64_t)2 * width * 4096 > (int64_t)INT32_MAX) return fail(MSR_ERR_UNSUPPORTED, "width too large");
+  if (h_last && h_last == h0) return fail(MSR_ERR_SHAPE, "h_last may not alias h0");
+  if (batch == 0) return ok();
+  if (!Lambda) return fail(MSR_ERR_NULL, "Lambda must be non-NULL");
+  hipStream_t st = (hipStream_t)stream;
+  const Elt e = dtype == MSR_BF16 ? kBF16 : kF32;
+  if (M > 0) {
+    if (!X || !W_a || !b_a || !W_x || !b_x || !Y)
+      return fail(MSR_ERR_NULL, "X, W_a, b_a, W_x, b_x and Y must be non-NULL");
+    const size_t need = msr_rglru_workspace_bytes(dtype, batch, seqlen, width);
+    if (!workspace || ws_bytes < need)
+      return fail(MSR_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need, workspace ? ws_bytes : 0);
+    // [r | i] = sigmoid(X [W_a | W_x] + [b_a | b_x])
+    GemmB bg{};
+    bg.ptr[0] = W_a; bg.ptr[1] = W_x;
+    bg.ld[0] = bg.ld[1] = width;
+    bg.start[0] = 0; bg.start[1] = width; bg.start[2] = bg.start[3] = INT32_MAX;
+    bg.bias[0] = b_a; bg.bias[1] = b_x;
+    bg.act = 2;
+    hipError_t err = launch_gemm(e, X, width, bg, workspace, 2 * width, (int)M, 2 * width, width, st);
+    if (err != hipSuccess) return from_hip(err, "msr_rglru_fwd(gates)");
+  }
+  // seqlen == 0 runs the scan too: it copies h0 (or zeros) to h_last
+  return from_hip(launch_rglru_scan(e, X, width, workspace, 2 * width, Lambda, c, h0, h_last, Y, width, batch, seqlen,
+                                    width, st),
+                  "msr_rglru_fwd(scan)");
+}
+
 msr_status msr_recurrent_step(msr_dtype dtype, int32_t batch, int32_t heads, int32_t d_k, int32_t d_v,
                               const double* gamma, float rope_base, int64_t pos, float qk_scale, const void* q,
                               const void* k, const void* v, float* S, void* o, void* stream) {

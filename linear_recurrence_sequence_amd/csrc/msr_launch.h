@@ -64,6 +64,14 @@ hipError_t launch_recurrent_step(Elt elt, int d_k, int d_v, int batch, int heads
 hipError_t launch_gn_gate(Elt elt, int d_v, int batch, int heads, const float* o, int64_t ldo, const void* g,
                           int64_t ldg, void* z, int64_t ldz, float eps, hipStream_t stream);
 
+// RG-LRU scan over gates already formed: G = [r | i], [batch*seqlen, 2*width]
+// (row stride ldg), X and Y [batch*seqlen, width] (row strides ldx, ldy),
+// lam [width] float32, h0 / hT [batch, width] float32 (nullable).  width a
+// multiple of 64.
+hipError_t launch_rglru_scan(Elt elt, const void* X, int64_t ldx, const void* G, int64_t ldg, const float* lam,
+                             float c, const float* h0, float* hT, void* Y, int64_t ldy, int batch, int seqlen,
+                             int width, hipStream_t stream);
+
 // Time reversal of token rows for the backward's anti-causal passes: up to
 // four jobs, byte row strides (multiples of 16), rows of row_bytes bytes
 // (a multiple of 16).  in_place: each job's dst is reversed in place (src
@@ -113,8 +121,11 @@ struct GemmB {
   // [z K_s, (z + 1) K_s) and stores float32 partials to part + z M N (no
   // rotation); launch_gemm_splitk adds them up.
   float* part;
-  // epilogue: C = act(A B) + resid, act = gelu when act == 1 (after any
-  // rotation), resid an [M, N] matrix with row stride ldr (nullable)
+  // epilogue: C = act(A B + bias) + resid, act = gelu when act == 1 and
+  // sigmoid when act == 2 (after any rotation), bias[s] a float32 vector
+  // over segment s's columns (nullable), resid an [M, N] matrix with row
+  // stride ldr (nullable).  Not with split-K.
+  const float* bias[4];
   int act;
   const void* resid;
   int64_t ldr;

@@ -141,6 +141,25 @@ def test_backward_validation():
     assert bwd(dims=(2, 64, 2, 64, 64), gam=zp, ws=16) == 5     # gamma = 0 is fine without dS_out
 
 
+def test_rglru_validation():
+    L = msr.lib()
+    rg = lambda B=2, T=16, D=128, c=8.0, X=FAKE, lam=FAKE, h0=None, hT=None, ws=1 << 40, dtype=1: L.msr_rglru_fwd(
+        dtype, B, T, D, c, X, FAKE, FAKE, FAKE, FAKE, lam, h0, hT, FAKE, FAKE, ws, None)
+    assert rg(D=100) == 4                   # width not a multiple of 64
+    assert rg(D=0) == 2
+    assert rg(T=-1) == 2
+    assert rg(c=0.0) == 2
+    assert rg(c=float("inf")) == 2
+    assert rg(X=None) == 1
+    assert rg(lam=None) == 1
+    assert rg(ws=10) == 5
+    assert rg(h0=FAKE, hT=FAKE) == 2        # h_last aliases h0
+    assert rg(dtype=9) == 3
+    assert rg(B=0) == 0
+    assert msr.msr_rglru_workspace_bytes(1, 2, 16, 128) == 2 * 16 * 256 * 2
+    assert msr.msr_rglru_workspace_bytes(0, 3, 5, 64) == -(-3 * 5 * 128 * 4 // 256) * 256
+
+
 def test_empty_inputs_are_no_ops():
     """batch = 0 or seqlen = 0 (parallel / layer) returns OK without touching memory."""
     L = msr.lib()
