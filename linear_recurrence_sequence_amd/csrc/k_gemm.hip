@@ -269,7 +269,8 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm(const T* __restrict__ A, 
         for (int e = 0; e < 8; ++e) v[e] = 0.5f * v[e] * (1.0f + erff(v[e] * 0.70710678118654752f));
       } else if (bp.act == 2) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = 1.0f / (1.0f + expf(-v[e]));
+        for (int e = 0; e < 8; ++e)   // sigmoid from the hardware exp2 and reciprocal (about 2 ulp)
+          v[e] = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(v[e] * -1.4426950408889634f));
       }
       if (bp.resid) {
         Row8<T> rr8;

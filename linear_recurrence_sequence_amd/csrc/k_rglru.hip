@@ -24,10 +24,40 @@ namespace msr {
 
 namespace {
 
-__device__ __forceinline__ float ld_f(const bf16* p) { return (float)*p; }
-__device__ __forceinline__ float ld_f(const float* p) { return *p; }
+// Raw loaded values: a bf16 stays zero-extended in its own 32-bit register
+// until it is used (packing two per register would force the load to
+// complete right away).
+template <class T> struct Raw;
+template <> struct Raw<bf16> {
+  using type = uint32_t;
+  static __device__ __forceinline__ uint32_t load(const bf16* p) { return *reinterpret_cast<const uint16_t*>(p); }
+  static __device__ __forceinline__ float value(uint32_t r) { return __uint_as_float(r << 16); }
+};
+template <> struct Raw<float> {
+  using type = float;
+  static __device__ __forceinline__ float load(const float* p) { return *p; }
+  static __device__ __forceinline__ float value(float r) { return r; }
+};
+
 __device__ __forceinline__ void st_f(bf16* p, float v) { *p = (bf16)v; }
 __device__ __forceinline__ void st_f(float* p, float v) { *p = v; }
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// 1 - 2^(2 l2) for l2 <= 0, i.e. -expm1(z) with z = 2 l2 ln 2, without the
+// cancellation of 1 - a^2 as a -> 1: the Taylor series of -expm1 through z^6
+// for |z| < 1/4 (truncation below 1e-7 relative), else 1 - a^2 directly
+// (there a^2 <= e^(-1/4), so no digits cancel).
+__device__ __forceinline__ float one_minus_a2(float l2, float a) {
+  const float z = l2 * (2.f * kLn2);
+  float p = fmaf(z, 1.f / 720.f, 1.f / 120.f);
+  p = fmaf(z, p, 1.f / 24.f);
+  p = fmaf(z, p, 1.f / 6.f);
+  p = fmaf(z, p, 0.5f);
+  p = fmaf(z, p, 1.f);
+  return z > -0.25f ? -z * p : fmaf(-a, a, 1.f);
+}
 
 }  // namespace
 
@@ -38,45 +68,52 @@ __global__ __launch_bounds__(64 * NW) void k_rglru_scan(const T* __restrict__ X,
                                                         T* __restrict__ Y, int64_t ldy, int seqlen, int width) {
   __shared__ float segA[2][NW][64], segB[2][NW][64];
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nblk = width / 64;
   const int b = blockIdx.x / nblk;
-  const int ch = (blockIdx.x % nblk) * 64 + lane;
-  // log a^c = c log sigma(Lambda), log sigma(z) = -(max(-z, 0) + log1p(e^-|z|))
+  const int c0 = (blockIdx.x % nblk) * 64;
+  const int ch = c0 + lane;
+  // log2 a^c = c log2 sigma(Lambda), log sigma(z) = -(max(-z, 0) + log1p(e^-|z|))
   const float L = lam[ch];
-  const float la_c = -c * (fmaxf(-L, 0.f) + log1pf(expf(-fabsf(L))));
+  const float l2ac = -c * (fmaxf(-L, 0.f) + log1pf(expf(-fabsf(L)))) * kLog2e;
   float carry = h0 ? h0[(size_t)b * width + ch] : 0.f;
+  // wave-uniform row bases: the per-step row offset is scalar arithmetic and
+  // each access adds only the lane's channel
   const size_t row0 = (size_t)b * seqlen;
-  const T* xp = X + ch;
-  const T* rp = G + ch;
-  const T* ip = G + width + ch;
-  T* yp = Y + ch;
+  const T* xb = X + row0 * ldx + c0;
+  const T* rb = G + row0 * ldg + c0;
+  const T* ib = rb + width;
+  T* yb = Y + row0 * ldy + c0;
 
-  float nx[S], nr[S], ni[S];
-  auto load_tile = [&](int t0) {
+  // raw inputs of the current and the next tile, converted where used so
+  // that no load has to complete before the next one is issued; rows past
+  // the end re-read the last row (its steps are masked to the identity)
+  using R = Raw<T>;
+  typename R::type cx[S], cr[S], ci[S], nx[S], nr[S], ni[S];
+  auto load = [&](int t0, typename R::type* vx, typename R::type* vr, typename R::type* vi) {
 #pragma unroll
     for (int s = 0; s < S; ++s) {
-      const int t = t0 + wave * S + s;
-      const bool ok = t < seqlen;
-      const size_t row = row0 + (ok ? t : 0);
-      nx[s] = ok ? ld_f(xp + row * ldx) : 0.f;
-      nr[s] = ok ? ld_f(rp + row * ldg) : 0.f;
-      ni[s] = ok ? ld_f(ip + row * ldg) : 0.f;
+      const int t = min(t0 + wave * S + s, seqlen - 1);   // uniform
+      vx[s] = R::load(xb + (int64_t)t * ldx + lane);
+      vr[s] = R::load(rb + (int64_t)t * ldg + lane);
+      vi[s] = R::load(ib + (int64_t)t * ldg + lane);
     }
   };
-  load_tile(0);
+  if (seqlen > 0) load(0, cx, cr, ci);
   int it = 0;
   for (int t0 = 0; t0 < seqlen; t0 += NW * S, ++it) {
+    const bool more = t0 + NW * S < seqlen;
+    if (more) load(t0 + NW * S, nx, nr, ni);
     float a[S], bb[S];
 #pragma unroll
     for (int s = 0; s < S; ++s) {
       const bool ok = t0 + wave * S + s < seqlen;
-      const float la = nr[s] * la_c;                  // log a_t
-      const float gain = sqrtf(-expm1f(2.f * la));    // sqrt(1 - a_t^2)
-      a[s] = ok ? expf(la) : 1.f;                     // steps past the end are the identity
-      bb[s] = ok ? gain * (ni[s] * nx[s]) : 0.f;
+      const float l2 = R::value(cr[s]) * l2ac;        // log2 a_t
+      const float at = __builtin_amdgcn_exp2f(l2);
+      const float gain = __builtin_amdgcn_sqrtf(one_minus_a2(l2, at));
+      a[s] = ok ? at : 1.f;                           // steps past the end are the identity
+      bb[s] = ok ? gain * (R::value(ci[s]) * R::value(cx[s])) : 0.f;
     }
-    if (t0 + NW * S < seqlen) load_tile(t0 + NW * S);
     float A = 1.f, B = 0.f;
 #pragma unroll
     for (int s = 0; s < S; ++s) {
@@ -98,9 +135,17 @@ __global__ __launch_bounds__(64 * NW) void k_rglru_scan(const T* __restrict__ X,
     for (int s = 0; s < S; ++s) {
       const int t = t0 + wave * S + s;
       h = fmaf(a[s], h, bb[s]);
-      if (t < seqlen) st_f(yp + (row0 + t) * ldy, h);
+      if (t < seqlen) st_f(yb + (int64_t)t * ldy + lane, h);
     }
     carry = next;
+    if (more) {
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        cx[s] = nx[s];
+        cr[s] = nr[s];
+        ci[s] = ni[s];
+      }
+    }
   }
   if (hT && wave == 0) hT[(size_t)b * width + ch] = carry;
 }
@@ -112,7 +157,7 @@ hipError_t launch_rglru_scan(Elt elt, const void* X, int64_t ldx, const void* G,
   const int64_t blocks = (int64_t)batch * (width / 64);
   if (blocks == 0) return hipSuccess;
   if (blocks > INT32_MAX) return hipErrorInvalidValue;
-  constexpr int NW = 8, S = 8;
+  constexpr int NW = 16, S = 8;   // 16 waves x 8 steps: the fastest of a sweep at batch 8 x 2048 x 2048
   TraceScope ts("k_rglru_scan", st);
   if (elt == kBF16)
     hipLaunchKernelGGL((k_rglru_scan<bf16, NW, S>), dim3((unsigned)blocks), dim3(64 * NW), 0, st, (const bf16*)X,
