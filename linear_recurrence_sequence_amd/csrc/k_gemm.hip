@@ -313,12 +313,40 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__
   store_row8(C + row * ldc + col, o);
 }
 
-int gemm_splits(int M, int N, int K) {
+// bf16 products of at most 128 rows (one token per sequence in decode) use
+// 128 x 64 tiles: the weight stream is split over many more workgroups, and
+// no matrix-core work is spent on empty rows.
+static bool skinny(Elt elt, int M) { return elt == kBF16 && M <= 128; }
+
+int gemm_splits(Elt elt, int M, int N, int K) {
+  if (skinny(elt, M)) {
+    // at least two workgroups per CU, at most 4 slices (more only adds partials traffic)
+    const int tiles = (N + 63) / 64;
+    int s = 1;
+    while (s < 4 && tiles * s < 512 && K % (64 * 2 * s) == 0) s *= 2;
+    return s;
+  }
   // enough workgroups to cover the CUs, at most 8 slices, each a multiple of 64 rows of K
   const int tiles = ((M + 255) / 256) * ((N + 255) / 256);
   int s = 1;
   while (s < 8 && tiles * s < 256 && K % (64 * 2 * s) == 0) s *= 2;
   return s;
+}
+
+// Segment boundaries all on multiples of the tile width: the uniform B path.
+static bool uniform_segments(const GemmB& b, int N, int BN) {
+  for (int sgi = 1; sgi < 4; ++sgi)
+    if (b.start[sgi] < N && b.start[sgi] % BN) return false;
+  return true;
+}
+
+static void launch_skinny(const bf16* A, int64_t lda, const GemmB& b, bf16* C, int64_t ldc, int M, int N, int K,
+                          int splits, hipStream_t st) {
+  dim3 grid((N + 63) / 64, 1, splits);
+  if (uniform_segments(b, N, 64))
+    hipLaunchKernelGGL((k_gemm<bf16, 128, 64, 64, 2, 2, true>), grid, dim3(256), 0, st, A, lda, b, C, ldc, M, N, K);
+  else
+    hipLaunchKernelGGL((k_gemm<bf16, 128, 64, 64, 2, 2, false>), grid, dim3(256), 0, st, A, lda, b, C, ldc, M, N, K);
 }
 
 hipError_t launch_gemm_splitk(Elt elt, const void* A, int64_t lda, const GemmB& b, void* C, int64_t ldc, int M,
@@ -333,10 +361,10 @@ hipError_t launch_gemm_splitk(Elt elt, const void* A, int64_t lda, const GemmB& 
   {
     TraceScope ts("k_gemm", st);
     const int BN = elt == kBF16 ? 256 : 128;
-    bool uni = true;
-    for (int sgi = 1; sgi < 4; ++sgi)
-      if (bs.start[sgi] < N && bs.start[sgi] % BN) uni = false;
-    if (elt == kBF16) {
+    const bool uni = uniform_segments(bs, N, BN);
+    if (skinny(elt, M)) {
+      launch_skinny((const bf16*)A, lda, bs, nullptr, (int64_t)N, M, N, Ks, splits, st);
+    } else if (elt == kBF16) {
       dim3 grid((N + 255) / 256, (M + 255) / 256, splits);
       if (uni)
         hipLaunchKernelGGL((k_gemm<bf16, 256, 256, 64, 2, 2, true>), grid, dim3(256), 0, st, (const bf16*)A, lda,
@@ -370,11 +398,11 @@ hipError_t launch_gemm(Elt elt, const void* A, int64_t lda, const GemmB& b, void
                        int K, hipStream_t st) {
   if (M == 0 || N == 0) return hipSuccess;
   const int BN = elt == kBF16 ? 256 : 128;
-  bool uni = true;  // every segment boundary on a tile boundary
-  for (int sgi = 1; sgi < 4; ++sgi)
-    if (b.start[sgi] < N && b.start[sgi] % BN) uni = false;
+  const bool uni = uniform_segments(b, N, BN);  // every segment boundary on a tile boundary
   TraceScope ts("k_gemm", st);
-  if (elt == kBF16) {
+  if (skinny(elt, M)) {
+    launch_skinny((const bf16*)A, lda, b, (bf16*)C, ldc, M, N, K, 1, st);
+  } else if (elt == kBF16) {
     dim3 grid((N + 255) / 256, (M + 255) / 256);
     if (uni)
       hipLaunchKernelGGL((k_gemm<bf16, 256, 256, 64, 2, 2, true>), grid, dim3(256), 0, st, (const bf16*)A, lda, b,

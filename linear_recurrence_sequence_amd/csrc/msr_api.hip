@@ -192,8 +192,9 @@ DecodeWs decode_ws_layout(msr_dtype dt, int32_t batch, int32_t d_model, int32_t 
   const size_t es = elt_size(dt);
   const int ntot = heads * (2 * dk + 2 * dv), hv = heads * dv;
   if (batch <= 256) {
-    w.split_qkvg = gemm_splits(batch, ntot, d_model);
-    w.split_o = gemm_splits(batch, d_model, hv);
+    const Elt e = dt == MSR_BF16 ? kBF16 : kF32;
+    w.split_qkvg = gemm_splits(e, batch, ntot, d_model);
+    w.split_o = gemm_splits(e, batch, d_model, hv);
   }
   const size_t part = std::max((size_t)(w.split_qkvg > 1 ? w.split_qkvg : 0) * batch * ntot,
                                (size_t)(w.split_o > 1 ? w.split_o : 0) * batch * d_model);

@@ -141,7 +141,7 @@ hipError_t launch_gemm(Elt elt, const void* A, int64_t lda, const GemmB& b, void
 hipError_t launch_gemm_splitk(Elt elt, const void* A, int64_t lda, const GemmB& b, void* C, int64_t ldc, int M,
                               int N, int K, int splits, float* part, hipStream_t stream);
 // How many K splits launch_gemm_splitk should use for an M x N x K product.
-int gemm_splits(int M, int N, int K);
+int gemm_splits(Elt elt, int M, int N, int K);
 // Row-wise LayerNorm over d columns (biased variance, identity affine):
 // Y = (X - mean) / sqrt(var + eps); d a multiple of 8, at most 8192.
 hipError_t launch_layer_norm(Elt elt, const void* X, int64_t ldx, void* Y, int64_t ldy, int rows, int d, float eps,
