@@ -28,7 +28,14 @@
 
 namespace msr {
 
-template <class T, int BM, int BN, int BK, int WM, int WN, bool UNI>
+// Epilogue option sets (a compile-time parameter, so that a launch carries
+// only the code of the options it uses; kEpiAny checks every option at run
+// time and serves any combination).
+enum : int {
+  kEpiRope = 1, kEpiGelu = 2, kEpiSigmoid = 4, kEpiBias = 8, kEpiResid = 16, kEpiPart = 32, kEpiAny = 63
+};
+
+template <class T, int BM, int BN, int BK, int WM, int WN, bool UNI, int EPI>
 __global__ __launch_bounds__(64 * WM * WN) void k_gemm(const T* __restrict__ A, int64_t lda, GemmB bp,
                                                        T* __restrict__ C, int64_t ldc, int M, int N, int K) {
   constexpr int NT = 64 * WM * WN;
@@ -238,7 +245,7 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm(const T* __restrict__ A, 
       for (int r = 0; r < 16; ++r) stg[(8 * (r >> 2) + 4 * hh + (r & 3)) * SLD + 32 * j + lr] = acc[i][j][r];
     __syncthreads();
     const int rbase = m0 + wm * (BM / WM) + 32 * i;
-#pragma unroll 1
+#pragma unroll
     for (int g = lane; g < 32 * (WCOLS / 8); g += 64) {
       const int rr = g / (WCOLS / 8), c8 = g % (WCOLS / 8);
       const int row = rbase + rr, col = cw0 + 8 * c8;
@@ -248,7 +255,7 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm(const T* __restrict__ A, 
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[e] = src[e];
       const int sg = seg_of(col);
-      if (sg < bp.rope_segs && !bp.part) {
+      if ((EPI & kEpiRope) && sg < bp.rope_segs && !bp.part) {
         const float2* cs = bp.rope_tab + (size_t)(row % bp.seqlen) * (bp.rope_d / 2) +
                            (((col - bp.start[sg]) % bp.rope_d) >> 1);
 #pragma unroll
@@ -259,20 +266,20 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm(const T* __restrict__ A, 
           v[2 * p + 1] = x * t.y + y * t.x;
         }
       }
-      if (const float* bias = sel(sg, bp.bias[0], bp.bias[1], bp.bias[2], bp.bias[3])) {
+      if (const float* bias = (EPI & kEpiBias) ? sel(sg, bp.bias[0], bp.bias[1], bp.bias[2], bp.bias[3]) : nullptr) {
         const float* bs = bias + (col - sel(sg, bp.start[0], bp.start[1], bp.start[2], bp.start[3]));
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] += bs[e];
       }
-      if (bp.act == 1) {
+      if ((EPI & kEpiGelu) && bp.act == 1) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = 0.5f * v[e] * (1.0f + erff(v[e] * 0.70710678118654752f));
-      } else if (bp.act == 2) {
+      } else if ((EPI & kEpiSigmoid) && bp.act == 2) {
 #pragma unroll
         for (int e = 0; e < 8; ++e)   // sigmoid from the hardware exp2 and reciprocal (about 2 ulp)
           v[e] = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(v[e] * -1.4426950408889634f));
       }
-      if (bp.resid) {
+      if ((EPI & kEpiResid) && bp.resid) {
         Row8<T> rr8;
         load_row8(rr8, reinterpret_cast<const T*>(bp.resid) + (size_t)row * bp.ldr + col, true);
         float rv[8];
@@ -280,7 +287,7 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm(const T* __restrict__ A, 
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] += rv[e];
       }
-      if (bp.part) {                               // split-K partial: float32, no rotation
+      if ((EPI & kEpiPart) && bp.part) {           // split-K partial: float32, no rotation
         Row8<float> o;
         pack_row8(o, v);
         store_row8(bp.part + (size_t)blockIdx.z * M * ldc + (size_t)row * ldc + col, o);
@@ -340,13 +347,57 @@ static bool uniform_segments(const GemmB& b, int N, int BN) {
   return true;
 }
 
-static void launch_skinny(const bf16* A, int64_t lda, const GemmB& b, bf16* C, int64_t ldc, int M, int N, int K,
-                          int splits, hipStream_t st) {
-  dim3 grid((N + 63) / 64, 1, splits);
-  if (uniform_segments(b, N, 64))
-    hipLaunchKernelGGL((k_gemm<bf16, 128, 64, 64, 2, 2, true>), grid, dim3(256), 0, st, A, lda, b, C, ldc, M, N, K);
-  else
-    hipLaunchKernelGGL((k_gemm<bf16, 128, 64, 64, 2, 2, false>), grid, dim3(256), 0, st, A, lda, b, C, ldc, M, N, K);
+// The epilogue option set of a launch.
+static int epilogue_set(const GemmB& b) {
+  int m = 0;
+  if (b.rope_segs > 0) m |= kEpiRope;
+  if (b.act == 1) m |= kEpiGelu;
+  if (b.act == 2) m |= kEpiSigmoid;
+  if (b.bias[0] || b.bias[1] || b.bias[2] || b.bias[3]) m |= kEpiBias;
+  if (b.resid) m |= kEpiResid;
+  if (b.part) m |= kEpiPart;
+  return m;
+}
+
+// One tile configuration: picks the uniform-B variant and the instantiation
+// for the epilogue option set (the sets the library launches have their
+// own; any other combination runs the all-options instantiation).
+template <class T, int BM, int BN, int BK, int WM, int WN>
+static void launch_tiles(dim3 grid, const T* A, int64_t lda, const GemmB& b, T* C, int64_t ldc, int M, int N, int K,
+                         hipStream_t st) {
+  const bool uni = uniform_segments(b, N, BN);
+  const dim3 block(64 * WM * WN);
+#define MSR_GEMM_EPI(E)                                                                                             \
+  if (uni)                                                                                                         \
+    hipLaunchKernelGGL((k_gemm<T, BM, BN, BK, WM, WN, true, E>), grid, block, 0, st, A, lda, b, C, ldc, M, N, K); \
+  else                                                                                                             \
+    hipLaunchKernelGGL((k_gemm<T, BM, BN, BK, WM, WN, false, E>), grid, block, 0, st, A, lda, b, C, ldc, M, N, K); \
+  return;
+  switch (epilogue_set(b)) {
+    case 0: MSR_GEMM_EPI(0)
+    case kEpiRope: MSR_GEMM_EPI(kEpiRope)
+    case kEpiResid: MSR_GEMM_EPI(kEpiResid)
+    case kEpiGelu: MSR_GEMM_EPI(kEpiGelu)
+    case kEpiBias | kEpiSigmoid: MSR_GEMM_EPI(kEpiBias | kEpiSigmoid)
+    case kEpiPart: MSR_GEMM_EPI(kEpiPart)
+    default: MSR_GEMM_EPI(kEpiAny)
+  }
+#undef MSR_GEMM_EPI
+}
+
+// bf16 and f32 products on their usual tiles, or on the skinny tiles.
+static void launch_any(Elt elt, const void* A, int64_t lda, const GemmB& b, void* C, int64_t ldc, int M, int N,
+                       int K, int splits, hipStream_t st) {
+  if (skinny(elt, M)) {
+    launch_tiles<bf16, 128, 64, 64, 2, 2>(dim3((N + 63) / 64, 1, splits), (const bf16*)A, lda, b, (bf16*)C, ldc, M,
+                                          N, K, st);
+  } else if (elt == kBF16) {
+    launch_tiles<bf16, 256, 256, 64, 2, 2>(dim3((N + 255) / 256, (M + 255) / 256, splits), (const bf16*)A, lda, b,
+                                           (bf16*)C, ldc, M, N, K, st);
+  } else {
+    launch_tiles<float, 128, 128, 32, 2, 2>(dim3((N + 127) / 128, (M + 127) / 128, splits), (const float*)A, lda, b,
+                                            (float*)C, ldc, M, N, K, st);
+  }
 }
 
 hipError_t launch_gemm_splitk(Elt elt, const void* A, int64_t lda, const GemmB& b, void* C, int64_t ldc, int M,
@@ -356,31 +407,10 @@ hipError_t launch_gemm_splitk(Elt elt, const void* A, int64_t lda, const GemmB& 
   GemmB bs = b;
   bs.part = part;
   bs.rope_segs = 0;
-  const int Ks = K / splits;
   hipError_t err;
   {
     TraceScope ts("k_gemm", st);
-    const int BN = elt == kBF16 ? 256 : 128;
-    const bool uni = uniform_segments(bs, N, BN);
-    if (skinny(elt, M)) {
-      launch_skinny((const bf16*)A, lda, bs, nullptr, (int64_t)N, M, N, Ks, splits, st);
-    } else if (elt == kBF16) {
-      dim3 grid((N + 255) / 256, (M + 255) / 256, splits);
-      if (uni)
-        hipLaunchKernelGGL((k_gemm<bf16, 256, 256, 64, 2, 2, true>), grid, dim3(256), 0, st, (const bf16*)A, lda,
-                           bs, (bf16*)nullptr, (int64_t)N, M, N, Ks);
-      else
-        hipLaunchKernelGGL((k_gemm<bf16, 256, 256, 64, 2, 2, false>), grid, dim3(256), 0, st, (const bf16*)A, lda,
-                           bs, (bf16*)nullptr, (int64_t)N, M, N, Ks);
-    } else {
-      dim3 grid((N + 127) / 128, (M + 127) / 128, splits);
-      if (uni)
-        hipLaunchKernelGGL((k_gemm<float, 128, 128, 32, 2, 2, true>), grid, dim3(256), 0, st, (const float*)A, lda,
-                           bs, (float*)nullptr, (int64_t)N, M, N, Ks);
-      else
-        hipLaunchKernelGGL((k_gemm<float, 128, 128, 32, 2, 2, false>), grid, dim3(256), 0, st, (const float*)A,
-                           lda, bs, (float*)nullptr, (int64_t)N, M, N, Ks);
-    }
+    launch_any(elt, A, lda, bs, nullptr, (int64_t)N, M, N, K / splits, splits, st);
     err = hipGetLastError();
   }
   if (err != hipSuccess) return err;
@@ -397,28 +427,8 @@ hipError_t launch_gemm_splitk(Elt elt, const void* A, int64_t lda, const GemmB& 
 hipError_t launch_gemm(Elt elt, const void* A, int64_t lda, const GemmB& b, void* C, int64_t ldc, int M, int N,
                        int K, hipStream_t st) {
   if (M == 0 || N == 0) return hipSuccess;
-  const int BN = elt == kBF16 ? 256 : 128;
-  const bool uni = uniform_segments(b, N, BN);  // every segment boundary on a tile boundary
   TraceScope ts("k_gemm", st);
-  if (skinny(elt, M)) {
-    launch_skinny((const bf16*)A, lda, b, (bf16*)C, ldc, M, N, K, 1, st);
-  } else if (elt == kBF16) {
-    dim3 grid((N + 255) / 256, (M + 255) / 256);
-    if (uni)
-      hipLaunchKernelGGL((k_gemm<bf16, 256, 256, 64, 2, 2, true>), grid, dim3(256), 0, st, (const bf16*)A, lda, b,
-                         (bf16*)C, ldc, M, N, K);
-    else
-      hipLaunchKernelGGL((k_gemm<bf16, 256, 256, 64, 2, 2, false>), grid, dim3(256), 0, st, (const bf16*)A, lda, b,
-                         (bf16*)C, ldc, M, N, K);
-  } else {
-    dim3 grid((N + 127) / 128, (M + 127) / 128);
-    if (uni)
-      hipLaunchKernelGGL((k_gemm<float, 128, 128, 32, 2, 2, true>), grid, dim3(256), 0, st, (const float*)A, lda, b,
-                         (float*)C, ldc, M, N, K);
-    else
-      hipLaunchKernelGGL((k_gemm<float, 128, 128, 32, 2, 2, false>), grid, dim3(256), 0, st, (const float*)A, lda, b,
-                         (float*)C, ldc, M, N, K);
-  }
+  launch_any(elt, A, lda, b, C, ldc, M, N, K, 1, st);
   return hipGetLastError();
 }
 
