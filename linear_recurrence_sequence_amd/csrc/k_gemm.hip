@@ -295,7 +295,7 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm(const T* __restrict__ A, 
       }
       Row8<T> o;
       pack_row8(o, v);
-      store_row8(C + (size_t)row * ldc + col, o);
+      store_row8_nt(C + (size_t)row * ldc + col, o);
     }
     __syncthreads();
   }

@@ -137,6 +137,19 @@ __device__ __forceinline__ void store_row8(float* p, const Row8<float>& r) {
   *reinterpret_cast<uint4*>(p) = r.lo;
   *reinterpret_cast<uint4*>(p + 4) = r.hi;
 }
+// Non-temporal variants for the GEMM's output tiles (the stores of a whole
+// tile leave at once; marked streaming they stall the next tile's loads
+// less -- measured faster for the projection GEMM and for the kernels that
+// read its output; slower where the next kernel re-reads a smaller output).
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x4_t as_u32x4(uint4 u) { return u32x4_t{u.x, u.y, u.z, u.w}; }
+__device__ __forceinline__ void store_row8_nt(bf16* p, const Row8<bf16>& r) {
+  __builtin_nontemporal_store(as_u32x4(r.u), reinterpret_cast<u32x4_t*>(p));
+}
+__device__ __forceinline__ void store_row8_nt(float* p, const Row8<float>& r) {
+  __builtin_nontemporal_store(as_u32x4(r.lo), reinterpret_cast<u32x4_t*>(p));
+  __builtin_nontemporal_store(as_u32x4(r.hi), reinterpret_cast<u32x4_t*>(p + 4));
+}
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
