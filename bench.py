@@ -50,11 +50,13 @@ PEAK_HBM = 8.0e12                      # bytes/s
 # it was taken with: the sha256 prefix of those files is recorded, and a
 # kernel whose sources have changed since reports null.
 MEASURED_TRAFFIC = {  # (workload, kernel): (bytes per launch, sources, sha256[:16])
-    ("layer_bf16_b8_n2048", "k_gemm"): (7.059e+08, ('k_gemm.hip', 'msr_device.h'), "06911803f94c0ae9"),
-    ("layer_bf16_b8_n2048", "k_chunk_out"): (3.951e+08, ('k_chunk.hip', 'msr_device.h'), "5732c5dbbd54faac"),
-    ("layer_bf16_b8_n2048", "k_chunk_state"): (3.901e+08, ('k_chunk.hip', 'msr_device.h'), "5732c5dbbd54faac"),
-    ("layer_bf16_b8_n2048", "k_chunk_scan"): (2.032e+08, ('k_chunk.hip', 'msr_device.h'), "5732c5dbbd54faac"),
-    ("decode_fp32_b128_h16", "k_recurrent_step"): (1.086e+09, ('k_recurrent.hip', 'msr_device.h'), "74c6c3209346c23f"),
+    ("layer_bf16_b8_n2048", "k_gemm"): (7.055e+08, ('k_gemm.hip', 'msr_device.h'), "ef06f0eb46ac019e"),
+    ("layer_bf16_b8_n2048", "k_chunk_out"): (3.951e+08, ('k_chunk.hip', 'msr_device.h'), "f5c5a51a05780d53"),
+    ("layer_bf16_b8_n2048", "k_chunk_state"): (2.03e+08, ('k_chunk.hip', 'msr_device.h'), "f5c5a51a05780d53"),
+    ("layer_bf16_b8_n2048", "k_chunk_scan"): (1.344e+08, ('k_chunk.hip', 'msr_device.h'), "f5c5a51a05780d53"),
+    ("decode_fp32_b128_h16", "k_recurrent_step"): (1.086e+09, ('k_recurrent.hip', 'msr_device.h'), "0d48a9428dc9ba19"),
+    ("rglru_bf16_b8_n2048_d2048", "k_gemm"): (5.377e+08, ('k_gemm.hip', 'msr_device.h'), "ef06f0eb46ac019e"),
+    ("rglru_bf16_b8_n2048_d2048", "k_rglru_scan"): (2.686e+08, ('k_rglru.hip', 'msr_device.h'), "3fbf3c4a1fcbb785"),
 }
 CSRC = os.path.join(ROOT, "linear_recurrence_sequence_amd", "csrc")
 
@@ -256,8 +258,9 @@ def bench_rglru(B, T, D, steps, warmup):
     scan_bytes = M * D * 4 * 2            # x, r, i read once, y written once (bf16)
     res = {"workload": f"rglru_bf16_b{B}_n{T}_d{D}", "ms_per_step": round(t * 1e3, 4),
            "tokens_per_s": round(M / t, 1),
-           "kernels": {"k_gemm": roof("k_gemm", 2 * M * 2 * D * D, "mfma", tr, steps),
-                       "k_rglru_scan": roof("k_rglru_scan", scan_bytes, "hbm", tr, steps)}}
+           "kernels": {"k_gemm": roof("k_gemm", 2 * M * 2 * D * D, "mfma", tr, steps, workload=f"rglru_bf16_b{B}_n{T}_d{D}"),
+                       "k_rglru_scan": roof("k_rglru_scan", scan_bytes, "hbm", tr, steps,
+                                            workload=f"rglru_bf16_b{B}_n{T}_d{D}")}}
     del X, WA, WX, Y, ws
     torch.cuda.empty_cache()
     return res
