@@ -1,13 +1,14 @@
 // Pieces of the chunkwise backward that are not retention passes: time
-// reversal of token rows, and per-head scaled copies or transposes of
-// float32 states.
+// reversal of the token rows of its inputs, and per-head scaled copies or
+// transposes of float32 states.
 //
 // The gradients of retention ([RN-zh] "Retention 網路總體結構": training runs
 // the parallel and chunkwise forms) are retentions themselves: dQ is the
 // causal retention of (dO, V, K), and dK, dV are anti-causal retentions,
 // which become causal ones on the time-reversed sequence.  The passes run on
-// the chunkwise kernels (k_chunk.hip); this file supplies the reversals and
-// the state seeds.
+// the chunkwise kernels (k_chunk.hip, whose output kernels can write rows
+// back in forward order); this file supplies the input reversals and the
+// state seeds.
 #include "msr_launch.h"
 
 namespace msr {
@@ -28,43 +29,15 @@ __global__ void k_reverse_rows(RevJobs j, int batch, int seqlen, int row_bytes) 
   *reinterpret_cast<uint4*>(j.dst[job] + out_row * j.ldd[job] + 16 * c) = x;
 }
 
-// In place: rows t and seqlen-1-t (t < seqlen/2) of each job's destination
-// swap; every thread owns one 16-byte column of one pair, so no two threads
-// touch the same bytes.
-__global__ void k_reverse_rows_inplace(RevJobs j, int batch, int seqlen, int row_bytes) {
-  const int job = blockIdx.y;
-  const int vec = row_bytes / 16;
-  const int half = seqlen / 2;
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= (int64_t)batch * half * vec) return;
-  const int64_t pair = i / vec;
-  const int c = (int)(i % vec);
-  const int64_t b = pair / half;
-  const int t = (int)(pair % half);
-  char* lo = j.dst[job] + (b * seqlen + t) * j.ldd[job] + 16 * c;
-  char* hi = j.dst[job] + (b * seqlen + (seqlen - 1 - t)) * j.ldd[job] + 16 * c;
-  const uint4 x = *reinterpret_cast<const uint4*>(lo);
-  const uint4 y = *reinterpret_cast<const uint4*>(hi);
-  *reinterpret_cast<uint4*>(lo) = y;
-  *reinterpret_cast<uint4*>(hi) = x;
-}
-
-hipError_t launch_reverse_rows(const RevJobs& jobs, int njobs, int batch, int seqlen, int row_bytes, bool in_place,
-                               hipStream_t st) {
+hipError_t launch_reverse_rows(const RevJobs& jobs, int njobs, int batch, int seqlen, int row_bytes, hipStream_t st) {
   if (njobs < 1 || njobs > 4 || row_bytes % 16) return hipErrorInvalidValue;
   for (int q = 0; q < njobs; ++q)
-    if (jobs.ldd[q] % 16 || (!in_place && jobs.lds[q] % 16)) return hipErrorInvalidValue;
-  const int64_t rows = in_place ? (int64_t)batch * (seqlen / 2) : (int64_t)batch * seqlen;
-  const int64_t n = rows * (row_bytes / 16);
+    if (jobs.ldd[q] % 16 || jobs.lds[q] % 16) return hipErrorInvalidValue;
+  const int64_t n = (int64_t)batch * seqlen * (row_bytes / 16);
   if (n == 0) return hipSuccess;
   const dim3 grid((unsigned)((n + 255) / 256), njobs);
-  if (in_place) {
-    TraceScope ts("k_reverse_rows_inplace", st);
-    hipLaunchKernelGGL(k_reverse_rows_inplace, grid, dim3(256), 0, st, jobs, batch, seqlen, row_bytes);
-  } else {
-    TraceScope ts("k_reverse_rows", st);
-    hipLaunchKernelGGL(k_reverse_rows, grid, dim3(256), 0, st, jobs, batch, seqlen, row_bytes);
-  }
+  TraceScope ts("k_reverse_rows", st);
+  hipLaunchKernelGGL(k_reverse_rows, grid, dim3(256), 0, st, jobs, batch, seqlen, row_bytes);
   return hipGetLastError();
 }
 

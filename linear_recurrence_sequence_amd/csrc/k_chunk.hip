@@ -253,7 +253,7 @@ template <class T, int DK, int DV, int NW, bool STATE, bool GN>
 __global__ __launch_bounds__(64 * NW) void k_chunk_out(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, int64_t ldq, int64_t ldk,
     int64_t ldv, const T* __restrict__ Rx, int has_sin, const T* __restrict__ G, int64_t ldg, T* __restrict__ O,
-    int64_t ldo, int BH, int N, int H, int chunk, int NC, int TPC, float scale, float eps, HeadTab tab) {
+    int64_t ldo, int BH, int N, int H, int chunk, int NC, int TPC, float scale, float eps, HeadTab tab, int rev) {
   using C = OutCfg<T, DK, DV, NW>;
   constexpr int NT = C::NT, KB = C::KB, SK = C::SK, LDK = C::LDK, LDV = C::LDV, LDR = C::LDR;
   constexpr int RT = 32 * NW;
@@ -476,7 +476,7 @@ __global__ __launch_bounds__(64 * NW) void k_chunk_out(
       const int q = q0 + 8 * (r >> 2) + 4 * hh + (r & 3);
       if (q < N) {
         const T* gp = G + (tokb + q) * ldg + (size_t)h * DV + lr;
-        T* op = O + (tokb + q) * ldo + (size_t)h * DV + lr;
+        T* op = O + (tokb + (rev ? N - 1 - q : q)) * ldo + (size_t)h * DV + lr;
 #pragma unroll
         for (int j = 0; j < DV / 32; ++j) {
           const float g = (float)gp[32 * j];
@@ -490,7 +490,7 @@ __global__ __launch_bounds__(64 * NW) void k_chunk_out(
     for (int r = 0; r < 16; ++r) {
       const int q = q0 + 8 * (r >> 2) + 4 * hh + (r & 3);
       if (q < N) {
-        T* op = O + (tokb + q) * ldo + (size_t)h * DV + lr;
+        T* op = O + (tokb + (rev ? N - 1 - q : q)) * ldo + (size_t)h * DV + lr;
 #pragma unroll
         for (int j = 0; j < DV / 32; ++j) op[32 * j] = (T)acc[j][r];
       }
@@ -545,7 +545,7 @@ __global__ __launch_bounds__(256) void k_chunk_dl(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V, int64_t ldq, int64_t ldk,
     int64_t ldv, const bf16* __restrict__ Rx, int has_sin, const bf16* __restrict__ G, int64_t ldg,
     bf16* __restrict__ O, int64_t ldo, int BH, int N, int H, int chunk, int NC, int TPC, float scale, float eps,
-    HeadTab tab) {
+    HeadTab tab, int rev) {
   using C = DlCfg<DK, DV>;
   constexpr int KB = C::KB, SK = C::SK, NS = C::NS, AHEAD = C::AHEAD, RT = C::RT;
   constexpr int CPK = C::CPK, CPV = C::CPV, CPR = C::CPR;
@@ -876,7 +876,7 @@ __global__ __launch_bounds__(256) void k_chunk_dl(
       const int qq = q0 + 8 * (r >> 2) + 4 * hh + (r & 3);
       if (qq < N) {
         const bf16* gp = G + (tokb + qq) * ldg + (size_t)h * DV + lr;
-        bf16* op = O + (tokb + qq) * ldo + (size_t)h * DV + lr;
+        bf16* op = O + (tokb + (rev ? N - 1 - qq : qq)) * ldo + (size_t)h * DV + lr;
 #pragma unroll
         for (int j = 0; j < DV / 32; ++j) {
           const float gv = (float)gp[32 * j];
@@ -890,7 +890,7 @@ __global__ __launch_bounds__(256) void k_chunk_dl(
     for (int r = 0; r < 16; ++r) {
       const int qq = q0 + 8 * (r >> 2) + 4 * hh + (r & 3);
       if (qq < N) {
-        bf16* op = O + (tokb + qq) * ldo + (size_t)h * DV + lr;
+        bf16* op = O + (tokb + (rev ? N - 1 - qq : qq)) * ldo + (size_t)h * DV + lr;
 #pragma unroll
         for (int j = 0; j < DV / 32; ++j) op[32 * j] = (bf16)acc[j][r];
       }
@@ -911,12 +911,12 @@ static void launch_dl(const ChunkArgs& a, int chunk, int NC, int TPC, int has_si
     hipLaunchKernelGGL((k_chunk_dl<DK, DV, STATE, true>), grid, dim3(256), 0, st, (const bf16*)a.Q,
                        (const bf16*)a.K, (const bf16*)a.V, a.ldq, a.ldk, a.ldv, (const bf16*)a.Rx, has_sin,
                        (const bf16*)a.G, a.ldg, (bf16*)a.O, a.ldo, BH, a.seqlen, a.heads, chunk, NC, TPC, a.scale,
-                       a.eps, tab);
+                       a.eps, tab, a.rev_out ? 1 : 0);
   else
     hipLaunchKernelGGL((k_chunk_dl<DK, DV, STATE, false>), grid, dim3(256), 0, st, (const bf16*)a.Q,
                        (const bf16*)a.K, (const bf16*)a.V, a.ldq, a.ldk, a.ldv, (const bf16*)a.Rx, has_sin,
                        (const bf16*)nullptr, (int64_t)0, (bf16*)a.O, a.ldo, BH, a.seqlen, a.heads, chunk, NC, TPC,
-                       a.scale, a.eps, tab);
+                       a.scale, a.eps, tab, a.rev_out ? 1 : 0);
 }
 
 template <class T, int DK, int DV, int NW, bool STATE>
@@ -927,12 +927,13 @@ static void launch_out(const ChunkArgs& a, int chunk, int NC, int TPC, int has_s
   if (a.fuse_gn_gate)
     hipLaunchKernelGGL((k_chunk_out<T, DK, DV, NW, STATE, true>), grid, dim3(64 * NW), 0, st, (const T*)a.Q,
                        (const T*)a.K, (const T*)a.V, a.ldq, a.ldk, a.ldv, (const T*)a.Rx, has_sin, (const T*)a.G,
-                       a.ldg, (T*)a.O, a.ldo, BH, a.seqlen, a.heads, chunk, NC, TPC, a.scale, a.eps, tab);
+                       a.ldg, (T*)a.O, a.ldo, BH, a.seqlen, a.heads, chunk, NC, TPC, a.scale, a.eps, tab,
+                       a.rev_out ? 1 : 0);
   else
     hipLaunchKernelGGL((k_chunk_out<T, DK, DV, NW, STATE, false>), grid, dim3(64 * NW), 0, st, (const T*)a.Q,
                        (const T*)a.K, (const T*)a.V, a.ldq, a.ldk, a.ldv, (const T*)a.Rx, has_sin,
                        (const T*)nullptr, (int64_t)0, (T*)a.O, a.ldo, BH, a.seqlen, a.heads, chunk, NC, TPC,
-                       a.scale, a.eps, tab);
+                       a.scale, a.eps, tab, a.rev_out ? 1 : 0);
 }
 
 template <class T, int DK, int DV>

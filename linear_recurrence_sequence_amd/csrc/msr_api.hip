@@ -412,8 +412,8 @@ size_t msr_chunkwise_bwd_workspace_bytes(msr_dtype dtype, msr_dims dims, int32_t
 // dQ is the causal retention of (dO, V, K) seeded with S_in^T; dV and dK are
 // the causal retentions of (rev K, rev Q, rev dO) and (rev V, rev dO, rev Q)
 // on the time-reversed sequence, seeded with dS_out / (scale gamma) (and its
-// transpose), whose outputs are reversed back; dS_in = scale gamma times the
-// last state of the dV pass.
+// transpose), whose output kernels write their rows back in forward time
+// order; dS_in = scale gamma times the last state of the dV pass.
 msr_status msr_chunkwise_bwd(msr_dtype dtype, msr_dims d, int32_t chunk, const double* gamma, float rope_base,
                              int64_t pos0, float qk_scale, const void* Q, const void* K, const void* V,
                              const void* dO, const float* S_in, const float* dS_out, void* dQ, void* dK, void* dV,
@@ -470,7 +470,7 @@ msr_status msr_chunkwise_bwd(msr_dtype dtype, msr_dims d, int32_t chunk, const d
     if (err == hipSuccess) err = launch_state_xform(dS_out, dso_t, nbh, d.heads, d.d_v, d.d_k, true, hs, st);
   }
   if (err != hipSuccess) return from_hip(err, "msr_chunkwise_bwd(state seeds)");
-  auto pass = [&](const void* q, const void* k, const void* v, void* o, const float* sin, float* sout) {
+  auto pass = [&](const void* q, const void* k, const void* v, void* o, const float* sin, float* sout, bool rev) {
     ChunkArgs a{};
     a.elt = e;
     a.d_k = d.d_k; a.d_v = d.d_v; a.batch = d.batch; a.seqlen = d.seqlen; a.heads = d.heads;
@@ -481,10 +481,11 @@ msr_status msr_chunkwise_bwd(msr_dtype dtype, msr_dims d, int32_t chunk, const d
     a.S_in = sin; a.S_out = sout;
     a.dR = at<void>(cws, w.cw.dr);
     a.Rx = at<void>(cws, w.cw.rx);
+    a.rev_out = rev;
     return launch_chunkwise(a, tab, st);
   };
   // dQ = causal retention of (dO, V, K) from S_in^T
-  err = pass(dO, V, K, dQ, S_in ? sin_t : nullptr, nullptr);
+  err = pass(dO, V, K, dQ, S_in ? sin_t : nullptr, nullptr, false);
   if (err != hipSuccess) return from_hip(err, "msr_chunkwise_bwd(dQ)");
   // reversed K, Q, V, dO
   RevJobs rj{};
@@ -496,24 +497,19 @@ msr_status msr_chunkwise_bwd(msr_dtype dtype, msr_dims d, int32_t chunk, const d
     rj.lds[j] = rj.ldd[j] = ld * (int64_t)es;
   }
   const int row_bytes = (int)(ld * (int64_t)es);
-  err = launch_reverse_rows(rj, 4, d.batch, d.seqlen, row_bytes, false, st);
+  err = launch_reverse_rows(rj, 4, d.batch, d.seqlen, row_bytes, st);
   if (err != hipSuccess) return from_hip(err, "msr_chunkwise_bwd(reverse)");
   const void* rk = at<void>(workspace, w.rk);
   const void* rq = at<void>(workspace, w.rq);
   const void* rv = at<void>(workspace, w.rv);
   const void* rdo = at<void>(workspace, w.rdo);
-  // reversed dV = causal retention of (rev K, rev Q, rev dO); its last state gives dS_in
-  err = pass(rk, rq, rdo, dV, dS_out ? dso : nullptr, dS_in);
+  // dV = causal retention of (rev K, rev Q, rev dO), its rows written back in
+  // forward time order; its last state gives dS_in
+  err = pass(rk, rq, rdo, dV, dS_out ? dso : nullptr, dS_in, true);
   if (err != hipSuccess) return from_hip(err, "msr_chunkwise_bwd(dV)");
-  // reversed dK = causal retention of (rev V, rev dO, rev Q)
-  err = pass(rv, rdo, rq, dK, dS_out ? dso_t : nullptr, nullptr);
+  // dK = causal retention of (rev V, rev dO, rev Q), rows in forward order
+  err = pass(rv, rdo, rq, dK, dS_out ? dso_t : nullptr, nullptr, true);
   if (err != hipSuccess) return from_hip(err, "msr_chunkwise_bwd(dK)");
-  RevJobs back{};
-  back.dst[0] = static_cast<char*>(dV);
-  back.dst[1] = static_cast<char*>(dK);
-  back.ldd[0] = back.ldd[1] = ld * (int64_t)es;
-  err = launch_reverse_rows(back, 2, d.batch, d.seqlen, row_bytes, true, st);
-  if (err != hipSuccess) return from_hip(err, "msr_chunkwise_bwd(reverse back)");
   if (rope) {  // gradients with respect to the unrotated Q and K
     const float2* rtab = at<float2>(cws, w.cw.tab);
     const int rows = d.batch * d.seqlen;

@@ -41,6 +41,7 @@ struct ChunkArgs {
   const float* S_in; float* S_out;
   void* dR;                  // [B, H, NC, d_v, d_k] elt: each chunk's own state contribution
   void* Rx;                  // [B, H, NC, d_v, d_k] elt: R_{i-1} per chunk (aliases dR)
+  bool rev_out;              // write output row t of each sequence to row seqlen-1-t
 };
 
 // Chunkwise retention: state contributions, fp32 scan, outputs.
@@ -74,14 +75,13 @@ hipError_t launch_rglru_scan(Elt elt, const void* X, int64_t ldx, const void* G,
 
 // Time reversal of token rows for the backward's anti-causal passes: up to
 // four jobs, byte row strides (multiples of 16), rows of row_bytes bytes
-// (a multiple of 16).  in_place: each job's dst is reversed in place (src
-// unused); otherwise dst row (b, seqlen-1-t) = src row (b, t).
+// (a multiple of 16); dst row (b, seqlen-1-t) = src row (b, t).
 struct RevJobs {
   const char* src[4];
   char* dst[4];
   int64_t lds[4], ldd[4];
 };
-hipError_t launch_reverse_rows(const RevJobs& jobs, int njobs, int batch, int seqlen, int row_bytes, bool in_place,
+hipError_t launch_reverse_rows(const RevJobs& jobs, int njobs, int batch, int seqlen, int row_bytes,
                                hipStream_t stream);
 // Per-head factors of launch_state_xform.
 struct HeadScale {
