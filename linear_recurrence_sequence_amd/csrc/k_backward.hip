@@ -1,6 +1,7 @@
 // Pieces of the chunkwise backward that are not retention passes: time
-// reversal of the token rows of its inputs, and per-head scaled copies or
-// transposes of float32 states.
+// reversal of the token rows of its inputs, in-place transposes of the
+// per-chunk states, and per-head scaled copies or transposes of float32
+// states.
 //
 // The gradients of retention ([RN-zh] "Retention 網路總體結構": training runs
 // the parallel and chunkwise forms) are retentions themselves: dQ is the
@@ -38,6 +39,52 @@ hipError_t launch_reverse_rows(const RevJobs& jobs, int njobs, int batch, int se
   const dim3 grid((unsigned)((n + 255) / 256), njobs);
   TraceScope ts("k_reverse_rows", st);
   hipLaunchKernelGGL(k_reverse_rows, grid, dim3(256), 0, st, jobs, batch, seqlen, row_bytes);
+  return hipGetLastError();
+}
+
+// In-place transpose of nblocks contiguous d x d blocks (d a multiple of 32):
+// workgroup (block, tile pair I <= J) reads tiles (I, J) and (J, I) through
+// LDS and writes each one transposed into the other's place.  Workgroups
+// touch disjoint tile pairs, and each reads both tiles before writing.
+template <class T>
+__global__ __launch_bounds__(256) void k_transpose_blocks(T* base, int d, int npairs) {
+  __shared__ float ta[32][33], tb[32][33];
+  const int nt = d / 32;
+  const int64_t blk = blockIdx.x / npairs;
+  int pr = blockIdx.x % npairs, I = 0;
+  while (pr >= nt - I) {   // row-major upper triangle of the tile grid
+    pr -= nt - I;
+    ++I;
+  }
+  const int J = I + pr;
+  T* m = base + blk * d * d;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int r = ty + 8 * k;
+    ta[r][tx] = (float)m[(size_t)(32 * I + r) * d + 32 * J + tx];
+    tb[r][tx] = (float)m[(size_t)(32 * J + r) * d + 32 * I + tx];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int r = ty + 8 * k;
+    m[(size_t)(32 * J + r) * d + 32 * I + tx] = (T)ta[tx][r];
+    if (I != J) m[(size_t)(32 * I + r) * d + 32 * J + tx] = (T)tb[tx][r];
+  }
+}
+
+hipError_t launch_transpose_blocks(Elt elt, void* base, int d, int64_t nblocks, hipStream_t st) {
+  if (d % 32 || d <= 0) return hipErrorInvalidValue;
+  const int nt = d / 32, npairs = nt * (nt + 1) / 2;
+  const int64_t wgs = nblocks * npairs;
+  if (wgs == 0) return hipSuccess;
+  if (wgs > INT32_MAX) return hipErrorInvalidValue;
+  TraceScope ts("k_transpose_blocks", st);
+  if (elt == kBF16)
+    hipLaunchKernelGGL(k_transpose_blocks<bf16>, dim3((unsigned)wgs), dim3(256), 0, st, (bf16*)base, d, npairs);
+  else
+    hipLaunchKernelGGL(k_transpose_blocks<float>, dim3((unsigned)wgs), dim3(256), 0, st, (float*)base, d, npairs);
   return hipGetLastError();
 }
 

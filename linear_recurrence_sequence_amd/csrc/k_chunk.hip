@@ -942,6 +942,7 @@ static hipError_t run_chunkwise(const ChunkArgs& a, const HeadTab& tab, hipStrea
   const int NC = (N + Cn - 1) / Cn;
   const int BH = B * H;
   constexpr int TS = StateCfg<T, DK, DV>::TS;
+  if (!a.reuse_rx) {
   {
     TraceScope ts("k_chunk_state", st);
     dim3 grid(((BH * NC + 7) / 8) * 8 * (DV / TS) * (DK / TS));
@@ -954,9 +955,10 @@ static hipError_t run_chunkwise(const ChunkArgs& a, const HeadTab& tab, hipStrea
     hipLaunchKernelGGL((k_chunk_scan<T, DK, DV>), grid, dim3(256), 0, st, (const T*)a.dR, (T*)a.Rx,
                        a.S_in, a.S_out, H, NC, tab);
   }
+  }
   {
     TraceScope ts("k_chunk_out", st);
-    const int has_sin = a.S_in != nullptr;
+    const int has_sin = a.reuse_rx ? (int)a.reuse_seeded : (int)(a.S_in != nullptr);
     if constexpr (sizeof(T) == 2 && DV <= 256) {
       if (Cn % 128 == 0) {
         launch_dl<DK, DV, true>(a, Cn, NC, Cn / 128, has_sin, tab, st);

@@ -131,10 +131,10 @@ ChunkWs chunk_ws_layout(msr_dtype dt, const msr_dims& d, int32_t chunk, bool rop
 
 // Chunkwise backward: the retention passes' chunk workspace (shared, the
 // passes run one after another), the rotated Q and K, the four reversed
-// inputs and the three state seeds.
+// inputs and the two state seeds.
 struct BwdWs {
   ChunkWs cw;
-  size_t chunk = 0, rq = 0, rk = 0, rv = 0, rdo = 0, sin_t = 0, dso = 0, dso_t = 0, total = 0;
+  size_t chunk = 0, rq = 0, rk = 0, rv = 0, rdo = 0, sin_t = 0, dso = 0, total = 0;
 };
 BwdWs bwd_ws_layout(msr_dtype dt, const msr_dims& d, int32_t chunk, bool rope) {
   BwdWs w;
@@ -150,7 +150,6 @@ BwdWs bwd_ws_layout(msr_dtype dt, const msr_dims& d, int32_t chunk, bool rope) {
   w.rdo = off; off += align_up(rows);
   w.sin_t = off; off += align_up(state);
   w.dso = off; off += align_up(state);
-  w.dso_t = off; off += align_up(state);
   w.total = off;
   return w;
 }
@@ -411,9 +410,10 @@ size_t msr_chunkwise_bwd_workspace_bytes(msr_dtype dtype, msr_dims dims, int32_t
 
 // dQ is the causal retention of (dO, V, K) seeded with S_in^T; dV and dK are
 // the causal retentions of (rev K, rev Q, rev dO) and (rev V, rev dO, rev Q)
-// on the time-reversed sequence, seeded with dS_out / (scale gamma) (and its
-// transpose), whose output kernels write their rows back in forward time
-// order; dS_in = scale gamma times the last state of the dV pass.
+// on the time-reversed sequence, seeded with dS_out / (scale gamma) and its
+// transpose (the dK pass's per-chunk states are the dV pass's transposed),
+// whose output kernels write their rows back in forward time order;
+// dS_in = scale gamma times the last state of the dV pass.
 msr_status msr_chunkwise_bwd(msr_dtype dtype, msr_dims d, int32_t chunk, const double* gamma, float rope_base,
                              int64_t pos0, float qk_scale, const void* Q, const void* K, const void* V,
                              const void* dO, const float* S_in, const float* dS_out, void* dQ, void* dK, void* dV,
@@ -459,7 +459,6 @@ msr_status msr_chunkwise_bwd(msr_dtype dtype, msr_dims d, int32_t chunk, const d
   const HeadTab tab = make_tab(gamma, d.heads, chunk, d.seqlen);
   float* sin_t = at<float>(workspace, w.sin_t);
   float* dso = at<float>(workspace, w.dso);
-  float* dso_t = at<float>(workspace, w.dso_t);
   hipError_t err = hipSuccess;
   // state seeds
   std::fill(hs.c, hs.c + kMaxHeads, 1.0f);
@@ -467,10 +466,10 @@ msr_status msr_chunkwise_bwd(msr_dtype dtype, msr_dims d, int32_t chunk, const d
   if (dS_out && err == hipSuccess) {
     for (int h = 0; h < d.heads; ++h) hs.c[h] = (float)(1.0 / ((double)qk_scale * gamma[h]));
     err = launch_state_xform(dS_out, dso, nbh, d.heads, d.d_k, d.d_v, false, hs, st);
-    if (err == hipSuccess) err = launch_state_xform(dS_out, dso_t, nbh, d.heads, d.d_v, d.d_k, true, hs, st);
   }
   if (err != hipSuccess) return from_hip(err, "msr_chunkwise_bwd(state seeds)");
-  auto pass = [&](const void* q, const void* k, const void* v, void* o, const float* sin, float* sout, bool rev) {
+  auto pass = [&](const void* q, const void* k, const void* v, void* o, const float* sin, float* sout, bool rev,
+                  bool reuse = false, bool seeded = false) {
     ChunkArgs a{};
     a.elt = e;
     a.d_k = d.d_k; a.d_v = d.d_v; a.batch = d.batch; a.seqlen = d.seqlen; a.heads = d.heads;
@@ -482,6 +481,8 @@ msr_status msr_chunkwise_bwd(msr_dtype dtype, msr_dims d, int32_t chunk, const d
     a.dR = at<void>(cws, w.cw.dr);
     a.Rx = at<void>(cws, w.cw.rx);
     a.rev_out = rev;
+    a.reuse_rx = reuse;
+    a.reuse_seeded = seeded;
     return launch_chunkwise(a, tab, st);
   };
   // dQ = causal retention of (dO, V, K) from S_in^T
@@ -507,8 +508,14 @@ msr_status msr_chunkwise_bwd(msr_dtype dtype, msr_dims d, int32_t chunk, const d
   // forward time order; its last state gives dS_in
   err = pass(rk, rq, rdo, dV, dS_out ? dso : nullptr, dS_in, true);
   if (err != hipSuccess) return from_hip(err, "msr_chunkwise_bwd(dV)");
-  // dK = causal retention of (rev V, rev dO, rev Q), rows in forward order
-  err = pass(rv, rdo, rq, dK, dS_out ? dso_t : nullptr, nullptr, true);
+  // dK = causal retention of (rev V, rev dO, rev Q), rows in forward order.
+  // Its state is the transpose of the dV pass's, chunk by chunk (the sum of
+  // rev dO^T rev Q against rev Q^T rev dO, seeded with dS_out^T against
+  // dS_out), so it reuses those per-chunk states transposed in place.
+  const int NC = (d.seqlen + chunk - 1) / chunk;
+  err = launch_transpose_blocks(e, at<void>(cws, w.cw.rx), d.d_k, (int64_t)nbh * NC, st);
+  if (err != hipSuccess) return from_hip(err, "msr_chunkwise_bwd(state transpose)");
+  err = pass(rv, rdo, rq, dK, nullptr, nullptr, true, true, dS_out != nullptr);
   if (err != hipSuccess) return from_hip(err, "msr_chunkwise_bwd(dK)");
   if (rope) {  // gradients with respect to the unrotated Q and K
     const float2* rtab = at<float2>(cws, w.cw.tab);

@@ -42,6 +42,9 @@ struct ChunkArgs {
   void* dR;                  // [B, H, NC, d_v, d_k] elt: each chunk's own state contribution
   void* Rx;                  // [B, H, NC, d_v, d_k] elt: R_{i-1} per chunk (aliases dR)
   bool rev_out;              // write output row t of each sequence to row seqlen-1-t
+  // Rx already holds every chunk's R_{i-1} (state and scan kernels skipped);
+  // reuse_seeded: chunk 0's R_{-1} is a seed (else zero)
+  bool reuse_rx, reuse_seeded;
 };
 
 // Chunkwise retention: state contributions, fp32 scan, outputs.
@@ -83,6 +86,8 @@ struct RevJobs {
 };
 hipError_t launch_reverse_rows(const RevJobs& jobs, int njobs, int batch, int seqlen, int row_bytes,
                                hipStream_t stream);
+// In-place transpose of nblocks contiguous d x d blocks of elt (d % 32 == 0).
+hipError_t launch_transpose_blocks(Elt elt, void* base, int d, int64_t nblocks, hipStream_t stream);
 // Per-head factors of launch_state_xform.
 struct HeadScale {
   float c[kMaxHeads];
