@@ -42,6 +42,24 @@ hipError_t launch_reverse_rows(const RevJobs& jobs, int njobs, int batch, int se
   return hipGetLastError();
 }
 
+namespace {
+// Four consecutive elements as floats (8-byte bf16 or 16-byte f32 accesses).
+__device__ __forceinline__ void load4(float* v, const bf16* p) {
+  const uint2 w = *reinterpret_cast<const uint2*>(p);
+  v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x); v[2] = bf16_lo(w.y); v[3] = bf16_hi(w.y);
+}
+__device__ __forceinline__ void load4(float* v, const float* p) {
+  const float4 w = *reinterpret_cast<const float4*>(p);
+  v[0] = w.x; v[1] = w.y; v[2] = w.z; v[3] = w.w;
+}
+__device__ __forceinline__ void store4(bf16* p, const float* v) {
+  *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]));
+}
+__device__ __forceinline__ void store4(float* p, const float* v) {
+  *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+}
+}  // namespace
+
 // In-place transpose of nblocks contiguous d x d blocks (d a multiple of 32):
 // workgroup (block, tile pair I <= J) reads tiles (I, J) and (J, I) through
 // LDS and writes each one transposed into the other's place.  Workgroups
@@ -58,20 +76,25 @@ __global__ __launch_bounds__(256) void k_transpose_blocks(T* base, int d, int np
   }
   const int J = I + pr;
   T* m = base + blk * d * d;
-  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+  // each thread moves 4 consecutive elements of one tile row: 8 threads per
+  // row, 32 rows per pass
+  const int r = threadIdx.x >> 3, c4 = (threadIdx.x & 7) * 4;
+  float x[4], y[4];
+  load4(x, m + (size_t)(32 * I + r) * d + 32 * J + c4);
+  load4(y, m + (size_t)(32 * J + r) * d + 32 * I + c4);
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int r = ty + 8 * k;
-    ta[r][tx] = (float)m[(size_t)(32 * I + r) * d + 32 * J + tx];
-    tb[r][tx] = (float)m[(size_t)(32 * J + r) * d + 32 * I + tx];
+  for (int e = 0; e < 4; ++e) {
+    ta[r][c4 + e] = x[e];
+    tb[r][c4 + e] = y[e];
   }
   __syncthreads();
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int r = ty + 8 * k;
-    m[(size_t)(32 * J + r) * d + 32 * I + tx] = (T)ta[tx][r];
-    if (I != J) m[(size_t)(32 * I + r) * d + 32 * J + tx] = (T)tb[tx][r];
+  for (int e = 0; e < 4; ++e) {
+    x[e] = ta[c4 + e][r];
+    y[e] = tb[c4 + e][r];
   }
+  store4(m + (size_t)(32 * J + r) * d + 32 * I + c4, x);   // tile (I, J) transposed into (J, I)
+  if (I != J) store4(m + (size_t)(32 * I + r) * d + 32 * J + c4, y);
 }
 
 hipError_t launch_transpose_blocks(Elt elt, void* base, int d, int64_t nblocks, hipStream_t st) {
