@@ -94,6 +94,21 @@ def gpu_time(fn, steps, warmup):
     return s.elapsed_time(e) * 1e-3 / steps
 
 
+def step_stats(fn, steps):
+    """Median and minimum seconds of single calls of fn (an event pair around
+    each call), from a pass after the timed region."""
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for a, b in evs:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    ts = sorted(a.elapsed_time(b) * 1e-3 for a, b in evs)
+    return ts[len(ts) // 2], ts[0]
+
+
 def traced(fn, steps):
     """Per-kernel (total s, launches) over `steps` calls, from HIP events the
     library records around each launch on its stream."""
@@ -108,10 +123,12 @@ def traced(fn, steps):
     return {k: (ms * 1e-3, n) for k, (ms, n) in tot.items()}
 
 
-def roof(name, work_per_step, bound, trace, steps, launches_per_step=None, workload=None):
+def roof(name, work_per_step, bound, trace, steps, launches_per_step=None, workload=None, bytes_per_step=None):
     """Roofline entry for one kernel: work_per_step is flops (mfma) or bytes
     (hbm) of algorithmic work in one step; traffic = measured HBM bytes per
-    launch (see MEASURED_TRAFFIC) or None."""
+    launch (see MEASURED_TRAFFIC) or None.  For a matrix-core kernel with
+    its algorithmic bytes given, also the attainable rate min(peak, I x HBM
+    peak), I = flops / bytes, and the fraction of it achieved."""
     t, n = trace[name]
     per_launch_t = t / n
     lps = n / steps if launches_per_step is None else launches_per_step
@@ -119,9 +136,15 @@ def roof(name, work_per_step, bound, trace, steps, launches_per_step=None, workl
     peak, unit = (PEAK_BF16, "TFLOP/s") if bound == "mfma" else (PEAK_HBM, "GB/s")
     scale = 1e12 if bound == "mfma" else 1e9
     ach = per_launch_work / per_launch_t
-    return {"kernel": name, "bound": bound, "achieved": round(ach / scale, 2), "peak": round(peak / scale, 1),
-            "unit": unit, "frac": round(ach / peak, 4), "traffic": measured_traffic(workload, name),
-            "avg_launch_us": round(per_launch_t * 1e6, 2), "launches_per_step": lps}
+    r = {"kernel": name, "bound": bound, "achieved": round(ach / scale, 2), "peak": round(peak / scale, 1),
+         "unit": unit, "frac": round(ach / peak, 4), "traffic": measured_traffic(workload, name),
+         "avg_launch_us": round(per_launch_t * 1e6, 2), "launches_per_step": lps}
+    if bound == "mfma" and bytes_per_step:
+        inten = work_per_step / bytes_per_step
+        att = min(peak, inten * PEAK_HBM)
+        r.update({"intensity_flop_per_byte": round(inten, 1), "attainable": round(att / scale, 1),
+                  "frac_of_attainable": round(ach / att, 4)})
+    return r
 
 
 def layer_flops(B, N, dm, H, dk, dv, C):
@@ -161,22 +184,28 @@ def bench_layer(w, steps, warmup, device_inputs=False):
     fn = lambda: msr.msr_layer_fwd(X, WQ, WK, WV, WG, WO, g, w.heads, w.d_k, w.d_v, w.chunk, rope_base=w.rope_base,
                                    gn_eps=1e-5, out=out, workspace=ws)
     t = gpu_time(fn, steps, warmup)
+    med, mn = step_stats(fn, steps)
     tr = traced(fn, steps)
     proj, core = layer_flops(w.batch, w.seqlen, w.d_model, w.heads, w.d_k, w.d_v, w.chunk)
     B, N, H, dk, dv, C = w.batch, w.seqlen, w.heads, w.d_k, w.d_v, w.chunk
     nc = -(-N // C)
     es = 2
-    work = {  # algorithmic work per step: flops (mfma) or bytes (hbm)
-        "k_gemm": (proj, "mfma"),
-        "k_chunk_out": (B * N * H * (C * (dk + dv) + 2 * dk * dv), "mfma"),
-        "k_chunk_state": (B * N * H * 2 * dk * dv, "mfma"),
-        "k_chunk_scan": (B * H * nc * dk * dv * 2 * es, "hbm"),     # read dR_i, write R_{i-1} (element type)
-        "k_rope_table": (N * dk // 2 * 8, "hbm"),
+    M, dm, hk, hv = B * N, w.d_model, H * dk, H * dv
+    ntot = 2 * hk + 2 * hv
+    states = B * H * nc * dk * dv * es
+    work = {  # algorithmic work per step: flops (mfma) or bytes (hbm); algorithmic bytes of the mfma kernels
+        "k_gemm": (proj, "mfma", (M * dm + dm * ntot + M * ntot + M * hv + hv * dm + M * dm) * es),
+        "k_chunk_out": (B * N * H * (C * (dk + dv) + 2 * dk * dv), "mfma", M * (ntot + hv) * es + states),
+        "k_chunk_state": (B * N * H * 2 * dk * dv, "mfma", M * (hk + hv) * es + states),
+        "k_chunk_scan": (2 * states, "hbm", None),     # read dR_i, write R_{i-1} (element type)
+        "k_rope_table": (N * dk // 2 * 8, "hbm", None),
     }
-    kern = {n: roof(n, wk, bd, tr, steps, workload=w.name) for n, (wk, bd) in work.items() if n in tr}
+    kern = {n: roof(n, wk, bd, tr, steps, workload=w.name, bytes_per_step=by) for n, (wk, bd, by) in work.items()
+            if n in tr}
     del X, WQ, WK, WV, WG, WO, out, ws
     torch.cuda.empty_cache()
-    res = {"s_per_step": t, "tokens_per_s": B * N / t, "flops_per_step": proj + core,
+    res = {"s_per_step": t, "s_per_step_median": med, "s_per_step_min": mn, "tokens_per_s": B * N / t,
+           "flops_per_step": proj + core,
            "tflops": (proj + core) / t / 1e12, "mfma_frac": (proj + core) / t / PEAK_BF16, "kernels": kern,
            "trace_s_per_step": {k: v[0] / steps for k, v in tr.items()}}
     return res
@@ -203,10 +232,13 @@ def bench_core(B, N, H, d, C, steps, warmup, parallel=False):
     if not parallel:
         tr = traced(fn, steps)
         nc = -(-N // C)
+        states = B * H * nc * d * d * 2
         res["kernels"] = {
-            "k_chunk_out": roof("k_chunk_out", B * N * H * (C * 2 * d + 2 * d * d), "mfma", tr, steps),
-            "k_chunk_state": roof("k_chunk_state", B * N * H * 2 * d * d, "mfma", tr, steps),
-            "k_chunk_scan": roof("k_chunk_scan", B * H * nc * d * d * 4, "hbm", tr, steps),
+            "k_chunk_out": roof("k_chunk_out", B * N * H * (C * 2 * d + 2 * d * d), "mfma", tr, steps,
+                                bytes_per_step=B * N * H * 4 * d * 2 + states),   # Q, K, V read, O written, R_{i-1}
+            "k_chunk_state": roof("k_chunk_state", B * N * H * 2 * d * d, "mfma", tr, steps,
+                                  bytes_per_step=B * N * H * 2 * d * 2 + states),
+            "k_chunk_scan": roof("k_chunk_scan", 2 * states, "hbm", tr, steps),
         }
     return res
 
@@ -439,8 +471,8 @@ def cpu_baseline(budget_s=12.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--only", default="layer,decode,long,block,retnet,backward,rglru,cpu")
     ap.add_argument("--no-cpu", action="store_true")
     args = ap.parse_args()
@@ -470,6 +502,8 @@ def main():
         r = bench_layer(w, args.steps, args.warmup)
         line["value"] = round(r["tokens_per_s"], 1)
         line["ms_per_step"] = round(r["s_per_step"] * 1e3, 4)
+        line["ms_per_step_median"] = round(r["s_per_step_median"] * 1e3, 4)   # single-call events, a pass after
+        line["ms_per_step_min"] = round(r["s_per_step_min"] * 1e3, 4)
         line["mfma_frac"] = round(r["mfma_frac"], 4)
         line["tflops"] = round(r["tflops"], 1)
         k = r["kernels"]

@@ -159,6 +159,31 @@ __device__ __forceinline__ void load16(float* x, const float* p) {
   }
 }
 
+// 16 consecutive elements as loaded (not yet converted to float).
+template <class T> struct Raw16;
+template <> struct Raw16<bf16> { uint4 a, b; };
+template <> struct Raw16<float> { f32x4 x[4]; };
+__device__ __forceinline__ Raw16<bf16> load_raw16(const bf16* p) {
+  return {*reinterpret_cast<const uint4*>(p), *reinterpret_cast<const uint4*>(p + 8)};
+}
+__device__ __forceinline__ Raw16<float> load_raw16(const float* p) {
+  Raw16<float> r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r.x[i] = *reinterpret_cast<const f32x4*>(p + 4 * i);
+  return r;
+}
+__device__ __forceinline__ void unpack_raw16(float* x, const Raw16<bf16>& r) {
+  const uint32_t w[8] = {r.a.x, r.a.y, r.a.z, r.a.w, r.b.x, r.b.y, r.b.z, r.b.w};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) { x[2 * i] = bf16_lo(w[i]); x[2 * i + 1] = bf16_hi(w[i]); }
+}
+__device__ __forceinline__ void unpack_raw16(float* x, const Raw16<float>& r) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[4 * i + e] = r.x[i][e];
+}
+
 template <class T, int DK, int DV>
 __global__ __launch_bounds__(256) void k_chunk_scan(const T* dR, T* Rx, const float* __restrict__ S_in,
                                                     float* __restrict__ S_out, int H, int NC, HeadTab tab) {
@@ -192,18 +217,35 @@ __global__ __launch_bounds__(256) void k_chunk_scan(const T* dR, T* Rx, const fl
   const T* src = dR + off;
   T* dst = Rx + off;
   const float gB = tab.gchunk[h], gL = tab.glast[h];
-  // contributions of chunks ci, ci + 1, ci + 2 in flight
-  float d[16], d1[16], d2[16];
-  load16(d, src);
-  if (NC > 1) load16(d1, src + cstride);
-  for (int ci = 0; ci < NC; ++ci) {
-    if (ci + 2 < NC) load16(d2, src + (size_t)(ci + 2) * cstride);
-    store16(dst + (size_t)ci * cstride, R);
-    const float g = (ci == NC - 1) ? gL : gB;
+  // Contributions of the next PF chunks in flight, kept raw (unconverted) in a
+  // statically indexed ring: converting right after the load would make the
+  // load complete at once.  Chunk ci's slot is reloaded with chunk ci + PF
+  // right after it has been read.  The reloads are unconditional, clamped to
+  // the last chunk (a re-read whose value is never used), so no slot has to
+  // be kept across a branch; chunk NC - 1 is loaded before it is written.
+  constexpr int PF = 4;
+  Raw16<T> ring[PF];
+  // (issued in slot order, as in the loop, so that the wait counts at the
+  // loop head are the steady-state ones)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) R[e] = fmaf(g, R[e], d[e]);
+  for (int u = 0; u < PF; ++u) {
+    ring[u] = load_raw16(src + (size_t)min(u, NC - 1) * cstride);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  for (int c0 = 0; c0 < NC; c0 += PF) {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) { d[e] = d1[e]; d1[e] = d2[e]; }
+    for (int u = 0; u < PF; ++u) {
+      const int ci = c0 + u;
+      float d[16];
+      unpack_raw16(d, ring[u]);
+      ring[u] = load_raw16(src + (size_t)min(ci + PF, NC - 1) * cstride);
+      if (ci < NC) {
+        store16(dst + (size_t)ci * cstride, R);
+        const float g = (ci == NC - 1) ? gL : gB;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) R[e] = fmaf(g, R[e], d[e]);
+      }
+    }
   }
 
   if (S_out != nullptr) {
