@@ -131,89 +131,97 @@ __global__ __launch_bounds__(256) void k_chunk_state(const T* __restrict__ K, co
 }
 
 // ---------------------------------------------------------------------------
-// k_chunk_scan: float32 carry across chunks, 64x64 state tile per workgroup.
-// dR and Rx alias: each element is read (two chunks ahead) before the same
+// k_chunk_scan: float32 carry across chunks, one state tile per workgroup.
+// dR and Rx alias: each element is read (chunks ahead) before the same
 // thread overwrites it, so no __restrict__ on them.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void store16(float* p, const float* x) {
-#pragma unroll
-  for (int e = 0; e < 16; e += 4) *reinterpret_cast<f32x4*>(p + e) = (f32x4){x[e], x[e + 1], x[e + 2], x[e + 3]};
-}
-__device__ __forceinline__ void store16(bf16* p, const float* x) {
-  uint4 a = make_uint4(pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]), pack_bf16(x[4], x[5]), pack_bf16(x[6], x[7]));
-  uint4 b = make_uint4(pack_bf16(x[8], x[9]), pack_bf16(x[10], x[11]), pack_bf16(x[12], x[13]), pack_bf16(x[14], x[15]));
-  *reinterpret_cast<uint4*>(p) = a;
-  *reinterpret_cast<uint4*>(p + 8) = b;
-}
-__device__ __forceinline__ void load16(float* x, const bf16* p) {
-  const uint4 a = *reinterpret_cast<const uint4*>(p), b = *reinterpret_cast<const uint4*>(p + 8);
-  const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-  for (int i = 0; i < 8; ++i) { x[2 * i] = bf16_lo(w[i]); x[2 * i + 1] = bf16_hi(w[i]); }
-}
-__device__ __forceinline__ void load16(float* x, const float* p) {
-#pragma unroll
-  for (int e = 0; e < 16; e += 4) {
-    f32x4 v = *reinterpret_cast<const f32x4*>(p + e);
-    x[e] = v[0]; x[e + 1] = v[1]; x[e + 2] = v[2]; x[e + 3] = v[3];
+// E consecutive elements (E = 4 or 16) as loaded, not yet converted to float.
+template <class T, int E> struct RawN;
+template <int E> struct RawN<bf16, E> { uint32_t w[E / 2]; };
+template <int E> struct RawN<float, E> { f32x4 x[E / 4]; };
+template <int E>
+__device__ __forceinline__ RawN<bf16, E> load_raw(const bf16* p) {
+  RawN<bf16, E> r;
+  if constexpr (E == 16) {
+    const uint4 a = *reinterpret_cast<const uint4*>(p), b = *reinterpret_cast<const uint4*>(p + 8);
+    r.w[0] = a.x; r.w[1] = a.y; r.w[2] = a.z; r.w[3] = a.w; r.w[4] = b.x; r.w[5] = b.y; r.w[6] = b.z; r.w[7] = b.w;
+  } else {
+    const uint2 a = *reinterpret_cast<const uint2*>(p);
+    r.w[0] = a.x; r.w[1] = a.y;
   }
-}
-
-// 16 consecutive elements as loaded (not yet converted to float).
-template <class T> struct Raw16;
-template <> struct Raw16<bf16> { uint4 a, b; };
-template <> struct Raw16<float> { f32x4 x[4]; };
-__device__ __forceinline__ Raw16<bf16> load_raw16(const bf16* p) {
-  return {*reinterpret_cast<const uint4*>(p), *reinterpret_cast<const uint4*>(p + 8)};
-}
-__device__ __forceinline__ Raw16<float> load_raw16(const float* p) {
-  Raw16<float> r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) r.x[i] = *reinterpret_cast<const f32x4*>(p + 4 * i);
   return r;
 }
-__device__ __forceinline__ void unpack_raw16(float* x, const Raw16<bf16>& r) {
-  const uint32_t w[8] = {r.a.x, r.a.y, r.a.z, r.a.w, r.b.x, r.b.y, r.b.z, r.b.w};
+template <int E>
+__device__ __forceinline__ RawN<float, E> load_raw(const float* p) {
+  RawN<float, E> r;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) { x[2 * i] = bf16_lo(w[i]); x[2 * i + 1] = bf16_hi(w[i]); }
+  for (int i = 0; i < E / 4; ++i) r.x[i] = *reinterpret_cast<const f32x4*>(p + 4 * i);
+  return r;
 }
-__device__ __forceinline__ void unpack_raw16(float* x, const Raw16<float>& r) {
+template <int E>
+__device__ __forceinline__ void unpack_raw(float* x, const RawN<bf16, E>& r) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < E / 2; ++i) { x[2 * i] = bf16_lo(r.w[i]); x[2 * i + 1] = bf16_hi(r.w[i]); }
+}
+template <int E>
+__device__ __forceinline__ void unpack_raw(float* x, const RawN<float, E>& r) {
+#pragma unroll
+  for (int i = 0; i < E / 4; ++i)
 #pragma unroll
     for (int e = 0; e < 4; ++e) x[4 * i + e] = r.x[i][e];
 }
+template <int E>
+__device__ __forceinline__ void store_n(float* p, const float* x) {
+#pragma unroll
+  for (int e = 0; e < E; e += 4) *reinterpret_cast<f32x4*>(p + e) = (f32x4){x[e], x[e + 1], x[e + 2], x[e + 3]};
+}
+template <int E>
+__device__ __forceinline__ void store_n(bf16* p, const float* x) {
+  uint32_t w[E / 2];
+#pragma unroll
+  for (int i = 0; i < E / 2; ++i) w[i] = pack_bf16(x[2 * i], x[2 * i + 1]);
+  if constexpr (E == 16) {
+    *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+    *reinterpret_cast<uint4*>(p + 8) = make_uint4(w[4], w[5], w[6], w[7]);
+  } else {
+    *reinterpret_cast<uint2*>(p) = make_uint2(w[0], w[1]);
+  }
+}
 
-template <class T, int DK, int DV>
+// TS x TS state tile per workgroup (TS = 64: 16 elements per thread; TS =
+// 32 for shapes with few (batch, head) pairs: four times the workgroups,
+// 4 elements per thread).
+template <class T, int DK, int DV, int TS>
 __global__ __launch_bounds__(256) void k_chunk_scan(const T* dR, T* Rx, const float* __restrict__ S_in,
                                                     float* __restrict__ S_out, int H, int NC, HeadTab tab) {
-  constexpr int NTV = DV / 64;
-  constexpr int NT = NTV * (DK / 64);
+  constexpr int E = TS * TS / 256;   // elements per thread
+  constexpr int NTV = DV / TS;
+  constexpr int NT = NTV * (DK / TS);
   const int bh = blockIdx.x / NT, tile = blockIdx.x % NT;
   const int h = bh % H;
   const int tv = tile % NTV, tk = tile / NTV;
   const int tid = threadIdx.x;
-  const int row = tid >> 2;         // d_v index inside the tile
-  const int col = (tid & 3) * 16;   // first of 16 d_k indices inside the tile
-  __shared__ float sT[64][65];
+  const int row = tid / (TS / E);       // d_v index inside the tile
+  const int col = (tid % (TS / E)) * E; // first of E d_k indices inside the tile
+  __shared__ float sT[TS][TS + 1];
 
-  float R[16];
+  float R[E];
   if (S_in != nullptr) {
-    // S_in is [dk][dv]; stage the 64x64 tile and read it transposed.
-    const float* src = S_in + (size_t)bh * DK * DV + (size_t)(tk * 64 + row) * DV + tv * 64 + col;
+    // S_in is [dk][dv]; stage the tile and read it transposed.
+    const float* src = S_in + (size_t)bh * DK * DV + (size_t)(tk * TS + row) * DV + tv * TS + col;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) sT[row][col + e] = src[e];
+    for (int e = 0; e < E; ++e) sT[row][col + e] = src[e];
     __syncthreads();
 #pragma unroll
-    for (int e = 0; e < 16; ++e) R[e] = sT[col + e][row];
+    for (int e = 0; e < E; ++e) R[e] = sT[col + e][row];
     __syncthreads();
   } else {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) R[e] = 0.f;
+    for (int e = 0; e < E; ++e) R[e] = 0.f;
   }
 
   const size_t cstride = (size_t)DV * DK;
-  const size_t off = (size_t)bh * NC * cstride + (size_t)(tv * 64 + row) * DK + tk * 64 + col;
+  const size_t off = (size_t)bh * NC * cstride + (size_t)(tv * TS + row) * DK + tk * TS + col;
   const T* src = dR + off;
   T* dst = Rx + off;
   const float gB = tab.gchunk[h], gL = tab.glast[h];
@@ -224,37 +232,37 @@ __global__ __launch_bounds__(256) void k_chunk_scan(const T* dR, T* Rx, const fl
   // the last chunk (a re-read whose value is never used), so no slot has to
   // be kept across a branch; chunk NC - 1 is loaded before it is written.
   constexpr int PF = 4;
-  Raw16<T> ring[PF];
+  RawN<T, E> ring[PF];
   // (issued in slot order, as in the loop, so that the wait counts at the
   // loop head are the steady-state ones)
 #pragma unroll
   for (int u = 0; u < PF; ++u) {
-    ring[u] = load_raw16(src + (size_t)min(u, NC - 1) * cstride);
+    ring[u] = load_raw<E>(src + (size_t)min(u, NC - 1) * cstride);
     __builtin_amdgcn_sched_barrier(0);
   }
   for (int c0 = 0; c0 < NC; c0 += PF) {
 #pragma unroll
     for (int u = 0; u < PF; ++u) {
       const int ci = c0 + u;
-      float d[16];
-      unpack_raw16(d, ring[u]);
-      ring[u] = load_raw16(src + (size_t)min(ci + PF, NC - 1) * cstride);
+      float d[E];
+      unpack_raw<E>(d, ring[u]);
+      ring[u] = load_raw<E>(src + (size_t)min(ci + PF, NC - 1) * cstride);
       if (ci < NC) {
-        store16(dst + (size_t)ci * cstride, R);
+        store_n<E>(dst + (size_t)ci * cstride, R);
         const float g = (ci == NC - 1) ? gL : gB;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) R[e] = fmaf(g, R[e], d[e]);
+        for (int e = 0; e < E; ++e) R[e] = fmaf(g, R[e], d[e]);
       }
     }
   }
 
   if (S_out != nullptr) {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) sT[col + e][row] = R[e];
+    for (int e = 0; e < E; ++e) sT[col + e][row] = R[e];
     __syncthreads();
-    float* o = S_out + (size_t)bh * DK * DV + (size_t)(tk * 64 + row) * DV + tv * 64 + col;
+    float* o = S_out + (size_t)bh * DK * DV + (size_t)(tk * TS + row) * DV + tv * TS + col;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) o[e] = sT[row][col + e];
+    for (int e = 0; e < E; ++e) o[e] = sT[row][col + e];
   }
 }
 
@@ -993,9 +1001,17 @@ static hipError_t run_chunkwise(const ChunkArgs& a, const HeadTab& tab, hipStrea
   }
   {
     TraceScope ts("k_chunk_scan", st);
-    dim3 grid(BH * (DV / 64) * (DK / 64));
-    hipLaunchKernelGGL((k_chunk_scan<T, DK, DV>), grid, dim3(256), 0, st, (const T*)a.dR, (T*)a.Rx,
-                       a.S_in, a.S_out, H, NC, tab);
+    // few (batch, head) pairs (one long sequence per head): 32 x 32 tiles, so
+    // that enough workgroups walk the chunks
+    if (DK >= 64 && DV >= 64 && BH * (DV / 64) * (DK / 64) >= 1024) {
+      dim3 grid(BH * (DV / 64) * (DK / 64));
+      hipLaunchKernelGGL((k_chunk_scan<T, DK, DV, 64>), grid, dim3(256), 0, st, (const T*)a.dR, (T*)a.Rx,
+                         a.S_in, a.S_out, H, NC, tab);
+    } else {
+      dim3 grid(BH * (DV / 32) * (DK / 32));
+      hipLaunchKernelGGL((k_chunk_scan<T, DK, DV, 32>), grid, dim3(256), 0, st, (const T*)a.dR, (T*)a.Rx,
+                         a.S_in, a.S_out, H, NC, tab);
+    }
   }
   }
   {
