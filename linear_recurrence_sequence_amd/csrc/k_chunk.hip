@@ -521,17 +521,31 @@ __global__ __launch_bounds__(64 * NW) void k_chunk_out(
       }
       rs[r] = rsqrtf(half_wave_sum(s) * (1.0f / DV) + eps);
     }
+    // gate values RB rows at a time (raw, rows past the end clamped and never
+    // stored): one round trip per RB rows instead of one per row
+    constexpr int RB = DV <= 256 ? 16 : 4;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int q = q0 + 8 * (r >> 2) + 4 * hh + (r & 3);
-      if (q < N) {
+    for (int r0 = 0; r0 < 16; r0 += RB) {
+      typename RawElt<T>::type graw[RB][DV / 32];
+#pragma unroll
+      for (int rr = 0; rr < RB; ++rr) {
+        const int r = r0 + rr;
+        const int q = min(q0 + 8 * (r >> 2) + 4 * hh + (r & 3), N - 1);
         const T* gp = G + (tokb + q) * ldg + (size_t)h * DV + lr;
-        T* op = O + (tokb + (rev ? N - 1 - q : q)) * ldo + (size_t)h * DV + lr;
 #pragma unroll
-        for (int j = 0; j < DV / 32; ++j) {
-          const float g = (float)gp[32 * j];
-          const float sw = g / (1.0f + __expf(-g));
-          op[32 * j] = (T)(sw * (acc[j][r] - mu[r]) * rs[r]);
+        for (int j = 0; j < DV / 32; ++j) graw[rr][j] = RawElt<T>::load(gp + 32 * j);
+      }
+#pragma unroll
+      for (int rr = 0; rr < RB; ++rr) {
+        const int r = r0 + rr;
+        const int q = q0 + 8 * (r >> 2) + 4 * hh + (r & 3);
+        if (q < N) {
+          T* op = O + (tokb + (rev ? N - 1 - q : q)) * ldo + (size_t)h * DV + lr;
+#pragma unroll
+          for (int j = 0; j < DV / 32; ++j) {
+            const float sw = swish_fast(RawElt<T>::value(graw[rr][j]));
+            op[32 * j] = (T)(sw * (acc[j][r] - mu[r]) * rs[r]);
+          }
         }
       }
     }
@@ -903,6 +917,17 @@ __global__ __launch_bounds__(256) void k_chunk_dl(
   // ---- epilogue: lane owns column 32 j + lr of rows q0 + 8 (r/4) + 4 hh + r%4 ----
   if (!active) return;
   if constexpr (GN) {
+    // the gate values of all 16 rows first (raw, rows past the end clamped
+    // to the last row and never stored): one round trip, overlapped with the
+    // row statistics, instead of one per row
+    typename RawElt<bf16>::type graw[16][DV / 32];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int qq = min(q0 + 8 * (r >> 2) + 4 * hh + (r & 3), N - 1);
+      const bf16* gp = G + (tokb + qq) * ldg + (size_t)h * DV + lr;
+#pragma unroll
+      for (int j = 0; j < DV / 32; ++j) graw[r][j] = RawElt<bf16>::load(gp + 32 * j);
+    }
     float mu[16], rs[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -925,12 +950,10 @@ __global__ __launch_bounds__(256) void k_chunk_dl(
     for (int r = 0; r < 16; ++r) {
       const int qq = q0 + 8 * (r >> 2) + 4 * hh + (r & 3);
       if (qq < N) {
-        const bf16* gp = G + (tokb + qq) * ldg + (size_t)h * DV + lr;
         bf16* op = O + (tokb + (rev ? N - 1 - qq : qq)) * ldo + (size_t)h * DV + lr;
 #pragma unroll
         for (int j = 0; j < DV / 32; ++j) {
-          const float gv = (float)gp[32 * j];
-          const float sw = gv / (1.0f + __expf(-gv));
+          const float sw = swish_fast(RawElt<bf16>::value(graw[r][j]));
           op[32 * j] = (bf16)(sw * (acc[j][r] - mu[r]) * rs[r]);
         }
       }

@@ -24,21 +24,6 @@ namespace msr {
 
 namespace {
 
-// Raw loaded values: a bf16 stays zero-extended in its own 32-bit register
-// until it is used (packing two per register would force the load to
-// complete right away).
-template <class T> struct Raw;
-template <> struct Raw<bf16> {
-  using type = uint32_t;
-  static __device__ __forceinline__ uint32_t load(const bf16* p) { return *reinterpret_cast<const uint16_t*>(p); }
-  static __device__ __forceinline__ float value(uint32_t r) { return __uint_as_float(r << 16); }
-};
-template <> struct Raw<float> {
-  using type = float;
-  static __device__ __forceinline__ float load(const float* p) { return *p; }
-  static __device__ __forceinline__ float value(float r) { return r; }
-};
-
 __device__ __forceinline__ void st_f(bf16* p, float v) { *p = (bf16)v; }
 __device__ __forceinline__ void st_f(float* p, float v) { *p = v; }
 
@@ -88,7 +73,7 @@ __global__ __launch_bounds__(64 * NW) void k_rglru_scan(const T* __restrict__ X,
   // raw inputs of the current and the next tile, converted where used so
   // that no load has to complete before the next one is issued; rows past
   // the end re-read the last row (its steps are masked to the identity)
-  using R = Raw<T>;
+  using R = RawElt<T>;
   typename R::type cx[S], cr[S], ci[S], nx[S], nr[S], ni[S];
   auto load = [&](int t0, typename R::type* vx, typename R::type* vr, typename R::type* vi) {
 #pragma unroll

@@ -137,6 +137,26 @@ __device__ __forceinline__ void store_row8(float* p, const Row8<float>& r) {
   *reinterpret_cast<uint4*>(p) = r.lo;
   *reinterpret_cast<uint4*>(p + 4) = r.hi;
 }
+// One element as loaded, not yet converted: a bf16 stays zero-extended in its
+// own 32-bit register until used (converting -- or packing two per register
+// -- right after the load would make the load complete at once).
+template <class T> struct RawElt;
+template <> struct RawElt<bf16> {
+  using type = uint32_t;
+  static __device__ __forceinline__ uint32_t load(const bf16* p) { return *reinterpret_cast<const uint16_t*>(p); }
+  static __device__ __forceinline__ float value(uint32_t r) { return __uint_as_float(r << 16); }
+};
+template <> struct RawElt<float> {
+  using type = float;
+  static __device__ __forceinline__ float load(const float* p) { return *p; }
+  static __device__ __forceinline__ float value(float r) { return r; }
+};
+
+// swish(x) = x sigmoid(x) from the hardware exp2 and reciprocal (about 2 ulp).
+__device__ __forceinline__ float swish_fast(float x) {
+  return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x * -1.4426950408889634f));
+}
+
 // Non-temporal variants for the GEMM's output tiles (the stores of a whole
 // tile leave at once; marked streaming they stall the next tile's loads
 // less -- measured faster for the projection GEMM and for the kernels that
