@@ -300,10 +300,25 @@ __device__ __forceinline__ void copies_wait_barrier() {
 }
 // Butterfly sum over the 32 lanes of one half-wave (xor masks < 32 stay
 // inside the half).
+// Sum over the 32 lanes of each half of the wave, returned to all of them,
+// with lane moves (DPP) instead of LDS round trips: quad exchanges, then the
+// half-row and row mirrors give every lane its 16-lane row sum; a row
+// broadcast adds row 0 into row 1 and row 2 into row 3, whose last lanes
+// (31 and 63) then hold the two half sums.
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float x) {
+  return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
 __device__ __forceinline__ float half_wave_sum(float x) {
-#pragma unroll
-  for (int m = 16; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);
-  return x;
+  x = dpp_add<0xB1>(x);    // quad_perm [1, 0, 3, 2]
+  x = dpp_add<0x4E>(x);    // quad_perm [2, 3, 0, 1]
+  x = dpp_add<0x141>(x);   // row_half_mirror
+  x = dpp_add<0x140>(x);   // row_mirror
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x142, 0xA, 0xF, false));   // row_bcast:15, rows 1 and 3
+  // (readlane is integer-typed: move the bits, not a converted value)
+  const float s0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 31));
+  const float s1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+  return (__lane_id() & 32) ? s1 : s0;
 }
 
 }  // namespace msr
