@@ -35,6 +35,89 @@ enum : int {
   kEpiRope = 1, kEpiGelu = 2, kEpiSigmoid = 4, kEpiBias = 8, kEpiResid = 16, kEpiPart = 32, kEpiAny = 63
 };
 
+// Epilogue through LDS: each wave stages 32 of its rows at a time in
+// float32, then every lane takes 8 consecutive columns of one row -- a
+// rotation pair lives in one lane -- applies the rotation if the columns
+// belong to a rotated segment, then bias, activation and residual, rounds
+// once and writes 16 contiguous bytes.  stg0: at least
+// WM WN 32 (BN / WN + 4) floats of LDS that no wave reads any more.
+template <class T, int BM, int BN, int WM, int WN, int EPI, int TM = BM / WM / 32, int TN = BN / WN / 32>
+__device__ __forceinline__ void gemm_epilogue(f32x16 (&acc)[TM][TN], float* stg0, const GemmB& bp, T* __restrict__ C,
+                                              int64_t ldc, int M, int N, int m0, int n0, int wave, int lane) {
+  const int lr = lane & 31, hh = lane >> 5;
+  const int wm = wave / WN, wn = wave % WN;
+  auto seg_of = [&](int n) { return (n >= bp.start[1]) + (n >= bp.start[2]) + (n >= bp.start[3]); };
+  auto sel = [&](int sg, auto a0, auto a1, auto a2, auto a3) {
+    return sg == 0 ? a0 : (sg == 1 ? a1 : (sg == 2 ? a2 : a3));
+  };
+  constexpr int WCOLS = BN / WN;                 // columns per wave
+  constexpr int SLD = WCOLS + 4;                 // staged row stride (floats)
+  float* stg = stg0 + wave * 32 * SLD;
+  const int cw0 = n0 + wn * WCOLS;               // first column of this wave
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) stg[(8 * (r >> 2) + 4 * hh + (r & 3)) * SLD + 32 * j + lr] = acc[i][j][r];
+    __syncthreads();
+    const int rbase = m0 + wm * (BM / WM) + 32 * i;
+#pragma unroll
+    for (int g = lane; g < 32 * (WCOLS / 8); g += 64) {
+      const int rr = g / (WCOLS / 8), c8 = g % (WCOLS / 8);
+      const int row = rbase + rr, col = cw0 + 8 * c8;
+      if (row >= M || col >= N) continue;
+      const float* src = stg + rr * SLD + 8 * c8;
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = src[e];
+      const int sg = seg_of(col);
+      if ((EPI & kEpiRope) && sg < bp.rope_segs && !bp.part) {
+        const float2* cs = bp.rope_tab + (size_t)(row % bp.seqlen) * (bp.rope_d / 2) +
+                           (((col - bp.start[sg]) % bp.rope_d) >> 1);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const float2 t = cs[p];
+          const float x = v[2 * p], y = v[2 * p + 1];
+          v[2 * p] = x * t.x - y * t.y;
+          v[2 * p + 1] = x * t.y + y * t.x;
+        }
+      }
+      if (const float* bias = (EPI & kEpiBias) ? sel(sg, bp.bias[0], bp.bias[1], bp.bias[2], bp.bias[3]) : nullptr) {
+        const float* bs = bias + (col - sel(sg, bp.start[0], bp.start[1], bp.start[2], bp.start[3]));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] += bs[e];
+      }
+      if ((EPI & kEpiGelu) && bp.act == 1) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = 0.5f * v[e] * (1.0f + erff(v[e] * 0.70710678118654752f));
+      } else if ((EPI & kEpiSigmoid) && bp.act == 2) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)   // sigmoid from the hardware exp2 and reciprocal (about 2 ulp)
+          v[e] = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(v[e] * -1.4426950408889634f));
+      }
+      if ((EPI & kEpiResid) && bp.resid) {
+        Row8<T> rr8;
+        load_row8(rr8, reinterpret_cast<const T*>(bp.resid) + (size_t)row * bp.ldr + col, true);
+        float rv[8];
+        unpack_row8(rv, rr8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] += rv[e];
+      }
+      if ((EPI & kEpiPart) && bp.part) {           // split-K partial: float32, no rotation
+        Row8<float> o;
+        pack_row8(o, v);
+        store_row8(bp.part + (size_t)blockIdx.z * M * ldc + (size_t)row * ldc + col, o);
+        continue;
+      }
+      Row8<T> o;
+      pack_row8(o, v);
+      store_row8_nt(C + (size_t)row * ldc + col, o);
+    }
+    __syncthreads();
+  }
+}
+
 template <class T, int BM, int BN, int BK, int WM, int WN, bool UNI, int EPI>
 __global__ __launch_bounds__(64 * WM * WN) void k_gemm(const T* __restrict__ A, int64_t lda, GemmB bp,
                                                        T* __restrict__ C, int64_t ldc, int M, int N, int K) {
@@ -171,6 +254,7 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm(const T* __restrict__ A, 
     // 8 transposing B) between its 16 MFMAs, step 0 also the next slab's 16
     // global loads, step 3 the 16 LDS writes of that slab into the other
     // buffer.  sched_barrier fences keep each step's group in place.
+    constexpr int NRD = TM + 2 * TN;                  // LDS fragment reads per k16 step (4 A + 8 transposing B)
     Frag<T> af[2][TM], bfr[2][TN];
     for (int kt = 0; kt < KT; ++kt) {
       const T* sA = smem[kt & 1];
@@ -180,13 +264,13 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm(const T* __restrict__ A, 
       lfr(sA, 1, af[1], bfr[1]);
       mm(af[0], bfr[0]);
 #pragma unroll
-      for (int i = 0; i < 12; ++i) {
+      for (int i = 0; i < NRD; ++i) {
         __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
         __builtin_amdgcn_sched_group_barrier(SG_VMEM_READ, 1, 0);
         __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = NRD; i < 16; ++i) {
         __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
         __builtin_amdgcn_sched_group_barrier(SG_VMEM_READ, 1, 0);
       }
@@ -196,11 +280,11 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm(const T* __restrict__ A, 
         lfr(sA, s + 1, af[(s + 1) & 1], bfr[(s + 1) & 1]);
         mm(af[s & 1], bfr[s & 1]);
 #pragma unroll
-        for (int i = 0; i < 12; ++i) {
+        for (int i = 0; i < NRD; ++i) {
           __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
           __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(SG_MFMA, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(SG_MFMA, 16 - NRD, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
       mm(af[1], bfr[1]);
@@ -228,77 +312,141 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm(const T* __restrict__ A, 
     }
   }
 
-  // Epilogue through LDS (free after the main loop): each wave stages 32 of
-  // its rows at a time in float32, then every lane takes 8 consecutive
-  // columns of one row -- a rotation pair lives in one lane -- applies the
-  // rotation if the columns belong to a rotated segment, rounds once and
-  // writes 16 contiguous bytes.
-  constexpr int WCOLS = BN / WN;                 // columns per wave
-  constexpr int SLD = WCOLS + 4;                 // staged row stride (floats)
-  float* stg = reinterpret_cast<float*>(&smem[0][0]) + wave * 32 * SLD;
-  const int cw0 = n0 + wn * WCOLS;               // first column of this wave
+  // epilogue through LDS (free after the main loop)
+  gemm_epilogue<T, BM, BN, WM, WN, EPI>(acc, reinterpret_cast<float*>(&smem[0][0]), bp, C, ldc, M, N, m0, n0, wave,
+                                        lane);
+}
+
+// ---------------------------------------------------------------------------
+// k_gemm_bt: bf16 C = A B with B given transposed (B^T [N, K], k contiguous,
+// as for A), 256 x 256 output tiles, 4 waves of 128 x 128.  Both operand
+// tiles stream into LDS by direct 16-byte copies (no staging registers, no
+// LDS write instructions) through a ring of NS slots of 32-deep K slabs,
+// NS - 2 slabs in flight ahead of the one being read.  A slab holds the 256
+// rows of A and of B^T, 4 16-byte chunks (32 k) per row, row r's chunk c in
+// slot c ^ ((r / 4) % 4) of the row: the 16 lanes that one LDS read pass
+// serves (rows r0 .. r0 + 15, one chunk) then fall on 16 different 16-byte
+// bank groups, and a copy still fills 64 consecutive slots.
+// Per slab, two k16 steps of 16 MFMAs per wave; the fragments of the next
+// step are read during the current one, and the wait + barrier for the next
+// slab sits between the two steps, so the first fragments of a slab are
+// read before its first MFMA is due.
+// ---------------------------------------------------------------------------
+template <int EPI, int NS, int NW>
+__global__ __launch_bounds__(64 * NW) void k_gemm_bt(const bf16* __restrict__ A, int64_t lda, GemmB bp,
+                                                     bf16* __restrict__ C, int64_t ldc, int M, int N, int K) {
+  constexpr int BM = 256, BN = 256, BK = 32, WM = 2, WN = NW / 2, TM = 4, TN = 4 / (NW / 4);
+  constexpr int SLOTS = (BM + BN) * (BK / 8);        // 16-byte slots per slab
+  constexpr int CPW = SLOTS / 64 / NW;               // copies per wave per slab
+  static_assert((NW == 4 || NW == 8) && NS >= 3, "slab layout");
+  __shared__ __attribute__((aligned(1024))) bf16 smem[NS * SLOTS * 8];
+  static_assert(NS * SLOTS * 8 * 2 >= NW * 32 * (BN / WN + 4) * 4, "epilogue staging fits in the ring");
+
+  const int tid = threadIdx.x, lane = tid & 63, lr = lane & 31, hh = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  const int KT = K / BK;
+  // tile order: as k_gemm (contiguous tile ranges per XCD, 8 tile-rows at a time)
+  const int Mt = gridDim.y, Nt = gridDim.x, total = Mt * Nt;
+  const int bid = blockIdx.y * Nt + blockIdx.x;
+  const int xcd = bid % 8, q8 = total / 8, r8 = total % 8;
+  const int t8 = xcd * q8 + min(xcd, r8) + bid / 8;
+  constexpr int GM = 8;
+  const int grp = t8 / (GM * Nt), first = grp * GM, gm = min(GM, Mt - first);
+  const int w8 = t8 % (GM * Nt);
+  const int m0 = (first + w8 % gm) * BM, n0 = (w8 / gm) * BN;
+
+  // Copies: this wave fills slots [64 (CPW wave + t), +64) of a slab; waves
+  // 0-1 the A rows, 2-3 the B^T rows.  Rows past M (N) are clamped: they
+  // feed outputs that are never stored.
+  const int kz = blockIdx.z * K;                     // split-K: first K row of this workgroup
+  const bool isA = wave < NW / 2;                    // wave-uniform
+  const bf16* src = isA ? A + (size_t)m0 * lda + kz : reinterpret_cast<const bf16*>(bp.ptr[0]) + (size_t)n0 * bp.ld[0] + kz;
+  const int64_t lds_ = isA ? lda : bp.ld[0];
+  const int rlim = isA ? M - 1 - m0 : N - 1 - n0;
+  uint32_t off[CPW];
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) stg[(8 * (r >> 2) + 4 * hh + (r & 3)) * SLD + 32 * j + lr] = acc[i][j][r];
-    __syncthreads();
-    const int rbase = m0 + wm * (BM / WM) + 32 * i;
-#pragma unroll
-    for (int g = lane; g < 32 * (WCOLS / 8); g += 64) {
-      const int rr = g / (WCOLS / 8), c8 = g % (WCOLS / 8);
-      const int row = rbase + rr, col = cw0 + 8 * c8;
-      if (row >= M || col >= N) continue;
-      const float* src = stg + rr * SLD + 8 * c8;
-      float v[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = src[e];
-      const int sg = seg_of(col);
-      if ((EPI & kEpiRope) && sg < bp.rope_segs && !bp.part) {
-        const float2* cs = bp.rope_tab + (size_t)(row % bp.seqlen) * (bp.rope_d / 2) +
-                           (((col - bp.start[sg]) % bp.rope_d) >> 1);
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const float2 t = cs[p];
-          const float x = v[2 * p], y = v[2 * p + 1];
-          v[2 * p] = x * t.x - y * t.y;
-          v[2 * p + 1] = x * t.y + y * t.x;
-        }
-      }
-      if (const float* bias = (EPI & kEpiBias) ? sel(sg, bp.bias[0], bp.bias[1], bp.bias[2], bp.bias[3]) : nullptr) {
-        const float* bs = bias + (col - sel(sg, bp.start[0], bp.start[1], bp.start[2], bp.start[3]));
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] += bs[e];
-      }
-      if ((EPI & kEpiGelu) && bp.act == 1) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = 0.5f * v[e] * (1.0f + erff(v[e] * 0.70710678118654752f));
-      } else if ((EPI & kEpiSigmoid) && bp.act == 2) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e)   // sigmoid from the hardware exp2 and reciprocal (about 2 ulp)
-          v[e] = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(v[e] * -1.4426950408889634f));
-      }
-      if ((EPI & kEpiResid) && bp.resid) {
-        Row8<T> rr8;
-        load_row8(rr8, reinterpret_cast<const T*>(bp.resid) + (size_t)row * bp.ldr + col, true);
-        float rv[8];
-        unpack_row8(rv, rr8);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] += rv[e];
-      }
-      if ((EPI & kEpiPart) && bp.part) {           // split-K partial: float32, no rotation
-        Row8<float> o;
-        pack_row8(o, v);
-        store_row8(bp.part + (size_t)blockIdx.z * M * ldc + (size_t)row * ldc + col, o);
-        continue;
-      }
-      Row8<T> o;
-      pack_row8(o, v);
-      store_row8_nt(C + (size_t)row * ldc + col, o);
-    }
-    __syncthreads();
+  for (int t = 0; t < CPW; ++t) {
+    const int u = ((wave % (NW / 2)) * CPW + t) * 64 + lane;  // slot within this operand's 1024
+    const int row = u >> 2, c = (u & 3) ^ ((row >> 2) & 3);
+    off[t] = (uint32_t)((min(row, rlim) * lds_ + 8 * c) * 2);
   }
+  const uint32_t lbase = lds_addr(smem) + (uint32_t)(wave * CPW * 64 * 16);
+  // copy t of slab kt into its ring slot; slabs past the end copy the last
+  // slab again (into a slot no slab still needs), so that every step issues
+  // the same copies and the waits are fixed
+  auto issue = [&](int kt, int t) {
+    copy16_to_lds(src + min(kt, KT - 1) * BK, off[t], lbase + (uint32_t)((kt % NS) * SLOTS * 16 + t * 1024));
+  };
+
+  // Fragments: lane lr reads row lr of a 32-row block, chunk 2 s + hh of
+  // k16 step s, i.e. slot (2 s + hh) ^ ((lr / 4) % 4) (block rows are
+  // multiples of 16, so the swizzle depends on the lane only).
+  const int sw = (lr >> 2) & 3;
+  const int fo0 = lr * 32 + 8 * ((0 + hh) ^ sw), fo1 = lr * 32 + 8 * ((2 + hh) ^ sw);   // elements
+  auto rd = [&](const bf16* slab, int s, Frag<bf16>* af, Frag<bf16>* bfr) {
+    const int fo = s ? fo1 : fo0;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) af[i] = load_frag(slab + (wm * 128 + 32 * i) * 32 + fo);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) bfr[j] = load_frag(slab + BM * 32 + (wn * (BN / WN) + 32 * j) * 32 + fo);
+  };
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = (f32x16){};
+
+  // prologue: slabs 0 .. NS - 2 in flight, wait for slab 0
+#pragma unroll
+  for (int a = 0; a < NS - 1; ++a)
+#pragma unroll
+    for (int t = 0; t < CPW; ++t) issue(a, t);
+  copies_wait_barrier<CPW * (NS - 2)>();
+  Frag<bf16> af[2][TM], bfr[2][TN];
+  rd(smem, 0, af[0], bfr[0]);
+  for (int kt = 0; kt < KT; ++kt) {
+    const bf16* slab = smem + (kt % NS) * SLOTS * 8;
+    // step 0: read step 1's fragments, MFMAs of step 0
+    rd(slab, 1, af[1], bfr[1]);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) mma16(acc[i][j], af[0][i], bfr[0][j]);
+#pragma unroll
+    for (int i = 0; i < TM + TN; ++i) {
+      __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(SG_MFMA, TM * TN - TM - TN, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    // slab kt + 1 landed (this wave's copies, then everyone's), every wave
+    // is past slab kt - 1: its slot takes slab kt + NS - 1
+    copies_wait_barrier<CPW * (NS - 3)>();
+    // step 1: the next slab's step-0 fragments (after the last slab: a
+    // harmless read of a slot nobody writes) and the refill copies between
+    // the MFMAs of step 1
+    rd(smem + ((kt + 1) % NS) * SLOTS * 8, 0, af[0], bfr[0]);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        mma16(acc[i][j], af[1][i], bfr[1][j]);
+        constexpr int EVERY = TM * TN / CPW;         // one copy per EVERY MFMAs
+        if ((i * TN + j) % EVERY == EVERY - 1) issue(kt + NS - 1, (i * TN + j) / EVERY);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < TM + TN; ++i) {
+      __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(SG_MFMA, TM * TN - TM - TN, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  copies_wait_barrier<0>();                          // the trailing copies landed, every wave is done with the ring
+  gemm_epilogue<bf16, BM, BN, WM, WN, EPI>(acc, reinterpret_cast<float*>(smem), bp, C, ldc, M, N, m0, n0, wave, lane);
 }
 
 // Sum of the split-K partials, rounded once: 8 consecutive columns per thread.
@@ -324,6 +472,72 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__
 // 128 x 64 tiles: the weight stream is split over many more workgroups, and
 // no matrix-core work is spent on empty rows.
 static bool skinny(Elt elt, int M) { return elt == kBF16 && M <= 128; }
+
+bool gemm_transposed_b(Elt elt, int64_t M) { return elt == kBF16 && M > 128; }
+
+// dst[c][r] = src[r][c] for up to kMaxTransposeJobs bf16 matrices in one
+// launch (the weights of one call): 64 x 64 tiles through LDS, 16-byte
+// loads and stores (rows and cols multiples of 8).  Workgroup g takes tile
+// g - first[j] of the job j whose tile range holds g.
+struct TransposeJobs {
+  TransposeJob job[kMaxTransposeJobs];
+  int first[kMaxTransposeJobs + 1];   // prefix sums of the jobs' tile counts
+  int njobs;
+};
+__global__ __launch_bounds__(256) void k_transpose_bf16(TransposeJobs tj) {
+  __shared__ __attribute__((aligned(16))) bf16 t[64][64 + 8];
+  int j = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxTransposeJobs; ++i) j += (i < tj.njobs && (int)blockIdx.x >= tj.first[i]);
+  const TransposeJob& jb = tj.job[j];
+  const int tile = blockIdx.x - tj.first[j], tcols = (jb.cols + 63) / 64;
+  const int r0 = (tile / tcols) * 64, c0 = (tile % tcols) * 64;
+  const bf16* src = reinterpret_cast<const bf16*>(jb.src);
+  bf16* dst = reinterpret_cast<bf16*>(jb.dst);
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int idx = threadIdx.x + 256 * u, r = idx >> 3, c8 = idx & 7;
+    if (r0 + r < jb.rows && c0 + 8 * c8 < jb.cols) {
+      Row8<bf16> v;
+      load_row8(v, src + (size_t)(r0 + r) * jb.lds + c0 + 8 * c8, true);
+      store_row8(&t[r][8 * c8], v);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int idx = threadIdx.x + 256 * u, c = idx >> 3, r8 = idx & 7;
+    if (c0 + c < jb.cols && r0 + 8 * r8 < jb.rows) {
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = (float)t[8 * r8 + e][c];
+      Row8<bf16> o;
+      pack_row8(o, v);
+      store_row8(dst + (size_t)(c0 + c) * jb.ldd + r0 + 8 * r8, o);
+    }
+  }
+}
+
+hipError_t launch_transpose(Elt elt, const TransposeJob* jobs, int njobs, hipStream_t st) {
+  if (elt != kBF16 || njobs < 0 || njobs > kMaxTransposeJobs) return hipErrorInvalidValue;
+  TransposeJobs tj{};
+  tj.njobs = njobs;
+  int64_t tiles = 0;
+  for (int i = 0; i < njobs; ++i) {
+    const TransposeJob& jb = jobs[i];
+    if (jb.rows < 0 || jb.cols < 0 || jb.rows % 8 || jb.cols % 8) return hipErrorInvalidValue;
+    tj.job[i] = jb;
+    tj.first[i] = (int)tiles;
+    tiles += (int64_t)((jb.rows + 63) / 64) * ((jb.cols + 63) / 64);
+    if (tiles > INT32_MAX) return hipErrorInvalidValue;
+  }
+  for (int i = njobs; i <= kMaxTransposeJobs; ++i) tj.first[i] = (int)tiles;
+  if (tiles == 0) return hipSuccess;
+  TraceScope ts("k_transpose_bf16", st);
+  hipLaunchKernelGGL(k_transpose_bf16, dim3((unsigned)tiles), dim3(256), 0, st, tj);
+  return hipGetLastError();
+}
+
 
 int gemm_splits(Elt elt, int M, int N, int K) {
   if (skinny(elt, M)) {
@@ -385,12 +599,37 @@ static void launch_tiles(dim3 grid, const T* A, int64_t lda, const GemmB& b, T* 
 #undef MSR_GEMM_EPI
 }
 
+// The transposed-B bf16 product on 256 x 256 tiles, instantiated for the
+// epilogue option set as launch_tiles does.  8 waves (two per SIMD: one
+// wave's matrix-core work covers the other's waits at the slab barriers)
+// and four ring slots (the fastest of 4 / 8 waves x 4 / 5 slots on the
+// layer's projection shapes).
+static void launch_bt(dim3 grid, const bf16* A, int64_t lda, const GemmB& b, bf16* C, int64_t ldc, int M, int N, int K,
+                      hipStream_t st) {
+  constexpr int NS = 4, NW = 8;
+#define MSR_GEMM_BT(E)                                                                                         \
+  hipLaunchKernelGGL((k_gemm_bt<E, NS, NW>), grid, dim3(64 * NW), 0, st, A, lda, b, C, ldc, M, N, K);         \
+  return;
+  switch (epilogue_set(b)) {
+    case 0: MSR_GEMM_BT(0)
+    case kEpiRope: MSR_GEMM_BT(kEpiRope)
+    case kEpiResid: MSR_GEMM_BT(kEpiResid)
+    case kEpiGelu: MSR_GEMM_BT(kEpiGelu)
+    case kEpiBias | kEpiSigmoid: MSR_GEMM_BT(kEpiBias | kEpiSigmoid)
+    case kEpiPart: MSR_GEMM_BT(kEpiPart)
+    default: MSR_GEMM_BT(kEpiAny)
+  }
+#undef MSR_GEMM_BT
+}
+
 // bf16 and f32 products on their usual tiles, or on the skinny tiles.
 static void launch_any(Elt elt, const void* A, int64_t lda, const GemmB& b, void* C, int64_t ldc, int M, int N,
                        int K, int splits, hipStream_t st) {
   if (skinny(elt, M)) {
     launch_tiles<bf16, 128, 64, 64, 2, 2>(dim3((N + 63) / 64, 1, splits), (const bf16*)A, lda, b, (bf16*)C, ldc, M,
                                           N, K, st);
+  } else if (b.bt) {
+    launch_bt(dim3((N + 255) / 256, (M + 255) / 256, splits), (const bf16*)A, lda, b, (bf16*)C, ldc, M, N, K, st);
   } else if (elt == kBF16) {
     launch_tiles<bf16, 256, 256, 64, 2, 2>(dim3((N + 255) / 256, (M + 255) / 256, splits), (const bf16*)A, lda, b,
                                            (bf16*)C, ldc, M, N, K, st);
@@ -404,6 +643,7 @@ hipError_t launch_gemm_splitk(Elt elt, const void* A, int64_t lda, const GemmB& 
                               int N, int K, int splits, float* part, hipStream_t st) {
   if (M == 0 || N == 0) return hipSuccess;
   if (b.act || b.resid || b.bias[0] || b.bias[1] || b.bias[2] || b.bias[3]) return hipErrorInvalidValue;
+  if (b.bt && !gemm_transposed_b(elt, M)) return hipErrorInvalidValue;
   GemmB bs = b;
   bs.part = part;
   bs.rope_segs = 0;
@@ -427,6 +667,7 @@ hipError_t launch_gemm_splitk(Elt elt, const void* A, int64_t lda, const GemmB& 
 hipError_t launch_gemm(Elt elt, const void* A, int64_t lda, const GemmB& b, void* C, int64_t ldc, int M, int N,
                        int K, hipStream_t st) {
   if (M == 0 || N == 0) return hipSuccess;
+  if (b.bt && !gemm_transposed_b(elt, M)) return hipErrorInvalidValue;
   TraceScope ts("k_gemm", st);
   launch_any(elt, A, lda, b, C, ldc, M, N, K, 1, st);
   return hipGetLastError();
