@@ -54,33 +54,73 @@ __device__ __forceinline__ void gemm_epilogue(f32x16 (&acc)[TM][TN], float* stg0
   constexpr int SLD = WCOLS + 4;                 // staged row stride (floats)
   float* stg = stg0 + wave * 32 * SLD;
   const int cw0 = n0 + wn * WCOLS;               // first column of this wave
+  constexpr int ITER = 32 * (WCOLS / 8) / 64;    // 8-column groups per lane per 32 rows
+  static_assert(32 * (WCOLS / 8) % 64 == 0, "whole iterations");
+  // rows and columns past the end are clamped for the loads (table, bias,
+  // residual) and only the stores are predicated: the iterations stay
+  // branch-free, so their loads can all be in flight together
+  auto where = [&](int i, int it, int& row, int& col, bool& ok) {
+    const int g = lane + 64 * it, rr = g / (WCOLS / 8), c8 = g % (WCOLS / 8);
+    const int row0 = m0 + wm * (BM / WM) + 32 * i + rr, col0 = cw0 + 8 * c8;
+    ok = row0 < M && col0 < N;
+    row = min(row0, M - 1);
+    col = min(col0, N - 8);
+  };
+  // (cos, sin) of the 4 column pairs of an 8-column group at its row's position
+  auto rope_cs = [&](int row, int col, int sg) {
+    return reinterpret_cast<const float4*>(bp.rope_tab + (size_t)(row % bp.seqlen) * (bp.rope_d / 2) +
+                                           (((col - bp.start[sg]) % bp.rope_d) >> 1));
+  };
+  constexpr bool PRE = (EPI & kEpiRope) && ITER <= 4;   // table values loaded before the staging
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
+    float4 csv[PRE ? ITER : 1][2];
+    if constexpr (PRE) {
+#pragma unroll
+      for (int it = 0; it < ITER; ++it) {
+        int row, col;
+        bool ok;
+        where(i, it, row, col, ok);
+        const int sg = seg_of(col);
+        if (sg < bp.rope_segs && !bp.part) {
+          const float4* cs = rope_cs(row, col, sg);
+          csv[it][0] = cs[0];
+          csv[it][1] = cs[1];
+        }
+      }
+    }
 #pragma unroll
     for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) stg[(8 * (r >> 2) + 4 * hh + (r & 3)) * SLD + 32 * j + lr] = acc[i][j][r];
     __syncthreads();
-    const int rbase = m0 + wm * (BM / WM) + 32 * i;
 #pragma unroll
-    for (int g = lane; g < 32 * (WCOLS / 8); g += 64) {
-      const int rr = g / (WCOLS / 8), c8 = g % (WCOLS / 8);
-      const int row = rbase + rr, col = cw0 + 8 * c8;
-      if (row >= M || col >= N) continue;
+    for (int it = 0; it < ITER; ++it) {
+      const int g = lane + 64 * it, rr = g / (WCOLS / 8), c8 = g % (WCOLS / 8);
+      int row, col;
+      bool ok;
+      where(i, it, row, col, ok);
       const float* src = stg + rr * SLD + 8 * c8;
       float v[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[e] = src[e];
       const int sg = seg_of(col);
       if ((EPI & kEpiRope) && sg < bp.rope_segs && !bp.part) {
-        const float2* cs = bp.rope_tab + (size_t)(row % bp.seqlen) * (bp.rope_d / 2) +
-                           (((col - bp.start[sg]) % bp.rope_d) >> 1);
+        float4 c0, c1;
+        if constexpr (PRE) {
+          c0 = csv[PRE ? it : 0][0];
+          c1 = csv[PRE ? it : 0][1];
+        } else {
+          const float4* cs = rope_cs(row, col, sg);
+          c0 = cs[0];
+          c1 = cs[1];
+        }
+        const float t[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-          const float2 t = cs[p];
           const float x = v[2 * p], y = v[2 * p + 1];
-          v[2 * p] = x * t.x - y * t.y;
-          v[2 * p + 1] = x * t.y + y * t.x;
+          v[2 * p] = x * t[2 * p] - y * t[2 * p + 1];
+          v[2 * p + 1] = x * t[2 * p + 1] + y * t[2 * p];
         }
       }
       if (const float* bias = (EPI & kEpiBias) ? sel(sg, bp.bias[0], bp.bias[1], bp.bias[2], bp.bias[3]) : nullptr) {
@@ -107,12 +147,12 @@ __device__ __forceinline__ void gemm_epilogue(f32x16 (&acc)[TM][TN], float* stg0
       if ((EPI & kEpiPart) && bp.part) {           // split-K partial: float32, no rotation
         Row8<float> o;
         pack_row8(o, v);
-        store_row8(bp.part + (size_t)blockIdx.z * M * ldc + (size_t)row * ldc + col, o);
+        if (ok) store_row8(bp.part + (size_t)blockIdx.z * M * ldc + (size_t)row * ldc + col, o);
         continue;
       }
       Row8<T> o;
       pack_row8(o, v);
-      store_row8_nt(C + (size_t)row * ldc + col, o);
+      if (ok) store_row8_nt(C + (size_t)row * ldc + col, o);
     }
     __syncthreads();
   }
@@ -346,12 +386,13 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_bt(const bf16* __restrict__ A,
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
   const int KT = K / BK;
-  // tile order: as k_gemm (contiguous tile ranges per XCD, 8 tile-rows at a time)
+  // tile order: as k_gemm (contiguous tile ranges per XCD), 4 tile-rows at
+  // a time (4, 2, 1, 8 and 16 measured on the projection shapes: 4 fastest)
   const int Mt = gridDim.y, Nt = gridDim.x, total = Mt * Nt;
   const int bid = blockIdx.y * Nt + blockIdx.x;
   const int xcd = bid % 8, q8 = total / 8, r8 = total % 8;
   const int t8 = xcd * q8 + min(xcd, r8) + bid / 8;
-  constexpr int GM = 8;
+  constexpr int GM = 4;
   const int grp = t8 / (GM * Nt), first = grp * GM, gm = min(GM, Mt - first);
   const int w8 = t8 % (GM * Nt);
   const int m0 = (first + w8 % gm) * BM, n0 = (w8 / gm) * BN;
