@@ -40,7 +40,8 @@ enum : int {
 // rotation pair lives in one lane -- applies the rotation if the columns
 // belong to a rotated segment, then bias, activation and residual, rounds
 // once and writes 16 contiguous bytes.  stg0: at least
-// WM WN 32 (BN / WN + 4) floats of LDS that no wave reads any more.
+// WM WN 32 (BN / WN + 4) floats of LDS that no wave reads or writes any
+// more (the caller's barrier); each wave then uses its own part of it.
 template <class T, int BM, int BN, int WM, int WN, int EPI, int TM = BM / WM / 32, int TN = BN / WN / 32>
 __device__ __forceinline__ void gemm_epilogue(f32x16 (&acc)[TM][TN], float* stg0, const GemmB& bp, T* __restrict__ C,
                                               int64_t ldc, int M, int N, int m0, int n0, int wave, int lane) {
@@ -93,7 +94,9 @@ __device__ __forceinline__ void gemm_epilogue(f32x16 (&acc)[TM][TN], float* stg0
     for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) stg[(8 * (r >> 2) + 4 * hh + (r & 3)) * SLD + 32 * j + lr] = acc[i][j][r];
-    __syncthreads();
+    // the staging rows are this wave's own and a wave's LDS operations are
+    // performed in order: no workgroup barrier, only a compiler fence
+    asm volatile("" ::: "memory");
 #pragma unroll
     for (int it = 0; it < ITER; ++it) {
       const int g = lane + 64 * it, rr = g / (WCOLS / 8), c8 = g % (WCOLS / 8);
@@ -154,7 +157,7 @@ __device__ __forceinline__ void gemm_epilogue(f32x16 (&acc)[TM][TN], float* stg0
       pack_row8(o, v);
       if (ok) store_row8_nt(C + (size_t)row * ldc + col, o);
     }
-    __syncthreads();
+    asm volatile("" ::: "memory");
   }
 }
 
