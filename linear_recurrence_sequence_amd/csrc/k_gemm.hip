@@ -14,16 +14,19 @@
 // by the (cos, sin) of their row's position (row % seqlen) before the single
 // rounding to the output type.
 //
-// The epilogue optionally applies gelu and adds a residual matrix (the
-// RetNet block's feed-forward network and skip connections).
+// The epilogue optionally applies gelu or a sigmoid, adds a per-segment
+// bias and a residual matrix (the RetNet block's feed-forward network and
+// skip connections, the RG-LRU gates).
 //
-// bf16: 256x256 output tile, 4 waves of 128x128 (16 accumulator tiles each,
-// held in the accumulation registers; a 128x128 wave tile reads 64 bytes of
-// LDS per clock at the matrix-core peak, a 128x64 one 96), 64-deep K slabs
-// double-buffered in LDS (2 x 72 KiB), the next slab's global loads in
-// flight during the current slab's matrix-core work, fragment reads one k16
-// step ahead, interleaved with the MFMAs by explicit scheduling groups.
-// f32: 128x128 tile, 4 waves, 32-deep slabs.
+// Two kernels:
+//   k_gemm_dc: bf16 with more than 128 rows whose weight segments start on
+//     256-column boundaries (every projection of the layer, block and
+//     RG-LRU at the benchmark shapes): 256x256 tiles, 8 waves, operand slabs
+//     streamed into LDS by direct copies through a 4-slot ring.
+//   k_gemm: everything else -- f32 (128x128 tiles, 32-deep slabs), bf16
+//     with at most 128 rows (128x64 tiles, split-K, the decode step) and
+//     bf16 with other segment boundaries (256x256 tiles, 4 waves of 128x128,
+//     64-deep slabs double-buffered through registers).
 #include "msr_launch.h"
 
 namespace msr {
@@ -361,22 +364,27 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm(const T* __restrict__ A, 
 }
 
 // ---------------------------------------------------------------------------
-// k_gemm_bt: bf16 C = A B with B given transposed (B^T [N, K], k contiguous,
-// as for A), 256 x 256 output tiles, 4 waves of 128 x 128.  Both operand
-// tiles stream into LDS by direct 16-byte copies (no staging registers, no
-// LDS write instructions) through a ring of NS slots of 32-deep K slabs,
-// NS - 2 slabs in flight ahead of the one being read.  A slab holds the 256
-// rows of A and of B^T, 4 16-byte chunks (32 k) per row, row r's chunk c in
-// slot c ^ ((r / 4) % 4) of the row: the 16 lanes that one LDS read pass
-// serves (rows r0 .. r0 + 15, one chunk) then fall on 16 different 16-byte
-// bank groups, and a copy still fills 64 consecutive slots.
-// Per slab, two k16 steps of 16 MFMAs per wave; the fragments of the next
-// step are read during the current one, and the wait + barrier for the next
-// slab sits between the two steps, so the first fragments of a slab are
-// read before its first MFMA is due.
+// k_gemm_dc: bf16 C = A B (B row-major, in up to four column segments whose
+// boundaries fall on 256-column tile edges), 256 x 256 output tiles, NW
+// waves: 8 waves of 128 x 64 (two per SIMD, so that one wave's matrix-core
+// work covers the other's waits) or 4 of 128 x 128.  Both operand tiles
+// stream into LDS by direct 16-byte copies (no staging registers, no LDS
+// write instructions) through a ring of NS slots of 32-deep K slabs, NS - 2
+// slabs in flight ahead of the one being read.
+//   A slab: the 256 rows of A, 4 16-byte chunks (32 k) per row, row r's
+//   chunk c in slot c ^ ((r / 4) % 4) of the row -- the 16 lanes that one
+//   LDS read pass serves (rows r0 .. r0 + 15, one chunk) fall on 16
+//   different 16-byte bank groups; and the 32 k-rows of B, 512 bytes each,
+//   64-byte group g of k-row r in group g ^ (r % 4) -- the four k-rows that
+//   one pass of the transposing read serves fall on four different 64-byte
+//   bank groups.  A copy still fills 64 consecutive slots.
+// Per slab, two k16 steps per wave; the fragments of the next step are read
+// during the current one, and the wait + barrier for the next slab sits
+// between the two steps, so the first fragments of a slab are read before
+// its first MFMA is due.
 // ---------------------------------------------------------------------------
 template <int EPI, int NS, int NW>
-__global__ __launch_bounds__(64 * NW) void k_gemm_bt(const bf16* __restrict__ A, int64_t lda, GemmB bp,
+__global__ __launch_bounds__(64 * NW) void k_gemm_dc(const bf16* __restrict__ A, int64_t lda, GemmB bp,
                                                      bf16* __restrict__ C, int64_t ldc, int M, int N, int K) {
   constexpr int BM = 256, BN = 256, BK = 32, WM = 2, WN = NW / 2, TM = 4, TN = 4 / (NW / 4);
   constexpr int SLOTS = (BM + BN) * (BK / 8);        // 16-byte slots per slab
@@ -400,27 +408,38 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_bt(const bf16* __restrict__ A,
   const int w8 = t8 % (GM * Nt);
   const int m0 = (first + w8 % gm) * BM, n0 = (w8 / gm) * BN;
 
-  // Copies: this wave fills slots [64 (CPW wave + t), +64) of a slab; waves
-  // 0-1 the A rows, 2-3 the B^T rows.  Rows past M (N) are clamped: they
-  // feed outputs that are never stored.
+  // Copies: this wave fills slots [64 (CPW wave + t), +64) of a slab; the
+  // first half of the waves the A rows, the second half the B k-rows (of
+  // the weight segment that holds the tile).  Rows past M and columns past
+  // N are clamped: they feed outputs that are never stored.
   const int kz = blockIdx.z * K;                     // split-K: first K row of this workgroup
   const bool isA = wave < NW / 2;                    // wave-uniform
-  const bf16* src = isA ? A + (size_t)m0 * lda + kz : reinterpret_cast<const bf16*>(bp.ptr[0]) + (size_t)n0 * bp.ld[0] + kz;
-  const int64_t lds_ = isA ? lda : bp.ld[0];
-  const int rlim = isA ? M - 1 - m0 : N - 1 - n0;
+  const int sg0 = (n0 >= bp.start[1]) + (n0 >= bp.start[2]) + (n0 >= bp.start[3]);
+  const bf16* bseg = reinterpret_cast<const bf16*>(sg0 == 0 ? bp.ptr[0] : sg0 == 1 ? bp.ptr[1] : sg0 == 2 ? bp.ptr[2]
+                                                                                                          : bp.ptr[3]);
+  const int64_t ldb = sg0 == 0 ? bp.ld[0] : sg0 == 1 ? bp.ld[1] : sg0 == 2 ? bp.ld[2] : bp.ld[3];
+  const int nb0 = n0 - (sg0 == 0 ? bp.start[0] : sg0 == 1 ? bp.start[1] : sg0 == 2 ? bp.start[2] : bp.start[3]);
+  const bf16* src = isA ? A + (size_t)m0 * lda + kz : bseg + nb0 + (size_t)kz * ldb;
+  const int64_t kstep = isA ? BK : BK * ldb;         // elements from one slab to the next
   uint32_t off[CPW];
 #pragma unroll
   for (int t = 0; t < CPW; ++t) {
     const int u = ((wave % (NW / 2)) * CPW + t) * 64 + lane;  // slot within this operand's 1024
-    const int row = u >> 2, c = (u & 3) ^ ((row >> 2) & 3);
-    off[t] = (uint32_t)((min(row, rlim) * lds_ + 8 * c) * 2);
+    if (isA) {
+      const int row = u >> 2, c = (u & 3) ^ ((row >> 2) & 3);
+      off[t] = (uint32_t)((min(row, M - 1 - m0) * lda + 8 * c) * 2);
+    } else {
+      const int kr = u >> 5, pc = u & 31;
+      const int lc = 4 * ((pc >> 2) ^ (kr & 3)) + (pc & 3);           // logical 16-byte chunk of the row
+      off[t] = (uint32_t)((kr * ldb + (min(n0 + 8 * lc, N - 8) - n0)) * 2);
+    }
   }
   const uint32_t lbase = lds_addr(smem) + (uint32_t)(wave * CPW * 64 * 16);
   // copy t of slab kt into its ring slot; slabs past the end copy the last
   // slab again (into a slot no slab still needs), so that every step issues
   // the same copies and the waits are fixed
   auto issue = [&](int kt, int t) {
-    copy16_to_lds(src + min(kt, KT - 1) * BK, off[t], lbase + (uint32_t)((kt % NS) * SLOTS * 16 + t * 1024));
+    copy16_to_lds(src + min(kt, KT - 1) * kstep, off[t], lbase + (uint32_t)((kt % NS) * SLOTS * 16 + t * 1024));
   };
 
   // Fragments: lane lr reads row lr of a 32-row block, chunk 2 s + hh of
@@ -428,12 +447,25 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_bt(const bf16* __restrict__ A,
   // multiples of 16, so the swizzle depends on the lane only).
   const int sw = (lr >> 2) & 3;
   const int fo0 = lr * 32 + 8 * ((0 + hh) ^ sw), fo1 = lr * 32 + 8 * ((2 + hh) ^ sw);   // elements
+  // B: the transposing read of lane (hh, c, j, q) (lane = 32 hh + 16 c +
+  // 4 j + q) takes k-row 16 s + 8 hh + 4 p + j, columns 16 c + 4 q of the
+  // fragment's 32-column group
+  const int tc = (lane >> 4) & 1, tj = (lane >> 2) & 3, tq = lane & 3;
   auto rd = [&](const bf16* slab, int s, Frag<bf16>* af, Frag<bf16>* bfr) {
     const int fo = s ? fo1 : fo0;
 #pragma unroll
     for (int i = 0; i < TM; ++i) af[i] = load_frag(slab + (wm * 128 + 32 * i) * 32 + fo);
 #pragma unroll
-    for (int j = 0; j < TN; ++j) bfr[j] = load_frag(slab + BM * 32 + (wn * (BN / WN) + 32 * j) * 32 + fo);
+    for (int j = 0; j < TN; ++j) {
+      const int grp = (wn * (BN / WN) + 32 * j) >> 5;
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const bf16* a = slab + BM * 32 + (16 * s + 8 * hh + 4 * p + tj) * BN + 32 * (grp ^ tj) + 16 * tc + 4 * tq;
+        const bf16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)a);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bfr[j].v[4 * p + e] = r[e];
+      }
+    }
   };
 
   f32x16 acc[TM][TN];
@@ -458,12 +490,14 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_bt(const bf16* __restrict__ A,
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j) mma16(acc[i][j], af[0][i], bfr[0][j]);
+    constexpr int NRD = TM + 2 * TN;                  // LDS reads per k16 step (A, then two per B fragment)
+    static_assert(NRD <= TM * TN, "one read per MFMA at most");
 #pragma unroll
-    for (int i = 0; i < TM + TN; ++i) {
+    for (int i = 0; i < NRD; ++i) {
       __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
       __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(SG_MFMA, TM * TN - TM - TN, 0);
+    __builtin_amdgcn_sched_group_barrier(SG_MFMA, TM * TN - NRD, 0);
     __builtin_amdgcn_sched_barrier(0);
     // slab kt + 1 landed (this wave's copies, then everyone's), every wave
     // is past slab kt - 1: its slot takes slab kt + NS - 1
@@ -482,11 +516,11 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_bt(const bf16* __restrict__ A,
       }
     }
 #pragma unroll
-    for (int i = 0; i < TM + TN; ++i) {
+    for (int i = 0; i < NRD; ++i) {
       __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
       __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(SG_MFMA, TM * TN - TM - TN, 0);
+    __builtin_amdgcn_sched_group_barrier(SG_MFMA, TM * TN - NRD, 0);
     __builtin_amdgcn_sched_barrier(0);
   }
   copies_wait_barrier<0>();                          // the trailing copies landed, every wave is done with the ring
@@ -517,70 +551,6 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__
 // no matrix-core work is spent on empty rows.
 static bool skinny(Elt elt, int M) { return elt == kBF16 && M <= 128; }
 
-bool gemm_transposed_b(Elt elt, int64_t M) { return elt == kBF16 && M > 128; }
-
-// dst[c][r] = src[r][c] for up to kMaxTransposeJobs bf16 matrices in one
-// launch (the weights of one call): 64 x 64 tiles through LDS, 16-byte
-// loads and stores (rows and cols multiples of 8).  Workgroup g takes tile
-// g - first[j] of the job j whose tile range holds g.
-struct TransposeJobs {
-  TransposeJob job[kMaxTransposeJobs];
-  int first[kMaxTransposeJobs + 1];   // prefix sums of the jobs' tile counts
-  int njobs;
-};
-__global__ __launch_bounds__(256) void k_transpose_bf16(TransposeJobs tj) {
-  __shared__ __attribute__((aligned(16))) bf16 t[64][64 + 8];
-  int j = 0;
-#pragma unroll
-  for (int i = 1; i < kMaxTransposeJobs; ++i) j += (i < tj.njobs && (int)blockIdx.x >= tj.first[i]);
-  const TransposeJob& jb = tj.job[j];
-  const int tile = blockIdx.x - tj.first[j], tcols = (jb.cols + 63) / 64;
-  const int r0 = (tile / tcols) * 64, c0 = (tile % tcols) * 64;
-  const bf16* src = reinterpret_cast<const bf16*>(jb.src);
-  bf16* dst = reinterpret_cast<bf16*>(jb.dst);
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int idx = threadIdx.x + 256 * u, r = idx >> 3, c8 = idx & 7;
-    if (r0 + r < jb.rows && c0 + 8 * c8 < jb.cols) {
-      Row8<bf16> v;
-      load_row8(v, src + (size_t)(r0 + r) * jb.lds + c0 + 8 * c8, true);
-      store_row8(&t[r][8 * c8], v);
-    }
-  }
-  __syncthreads();
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int idx = threadIdx.x + 256 * u, c = idx >> 3, r8 = idx & 7;
-    if (c0 + c < jb.cols && r0 + 8 * r8 < jb.rows) {
-      float v[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = (float)t[8 * r8 + e][c];
-      Row8<bf16> o;
-      pack_row8(o, v);
-      store_row8(dst + (size_t)(c0 + c) * jb.ldd + r0 + 8 * r8, o);
-    }
-  }
-}
-
-hipError_t launch_transpose(Elt elt, const TransposeJob* jobs, int njobs, hipStream_t st) {
-  if (elt != kBF16 || njobs < 0 || njobs > kMaxTransposeJobs) return hipErrorInvalidValue;
-  TransposeJobs tj{};
-  tj.njobs = njobs;
-  int64_t tiles = 0;
-  for (int i = 0; i < njobs; ++i) {
-    const TransposeJob& jb = jobs[i];
-    if (jb.rows < 0 || jb.cols < 0 || jb.rows % 8 || jb.cols % 8) return hipErrorInvalidValue;
-    tj.job[i] = jb;
-    tj.first[i] = (int)tiles;
-    tiles += (int64_t)((jb.rows + 63) / 64) * ((jb.cols + 63) / 64);
-    if (tiles > INT32_MAX) return hipErrorInvalidValue;
-  }
-  for (int i = njobs; i <= kMaxTransposeJobs; ++i) tj.first[i] = (int)tiles;
-  if (tiles == 0) return hipSuccess;
-  TraceScope ts("k_transpose_bf16", st);
-  hipLaunchKernelGGL(k_transpose_bf16, dim3((unsigned)tiles), dim3(256), 0, st, tj);
-  return hipGetLastError();
-}
 
 
 int gemm_splits(Elt elt, int M, int N, int K) {
@@ -643,16 +613,15 @@ static void launch_tiles(dim3 grid, const T* A, int64_t lda, const GemmB& b, T* 
 #undef MSR_GEMM_EPI
 }
 
-// The transposed-B bf16 product on 256 x 256 tiles, instantiated for the
-// epilogue option set as launch_tiles does.  8 waves (two per SIMD: one
-// wave's matrix-core work covers the other's waits at the slab barriers)
-// and four ring slots (the fastest of 4 / 8 waves x 4 / 5 slots on the
-// layer's projection shapes).
-static void launch_bt(dim3 grid, const bf16* A, int64_t lda, const GemmB& b, bf16* C, int64_t ldc, int M, int N, int K,
+// The direct-copy bf16 product on 256 x 256 tiles, instantiated for the
+// epilogue option set as launch_tiles does.  8 waves and four ring slots:
+// the fastest of 4 / 8 waves x 3 / 4 / 5 slots on the layer's projection
+// shapes.
+static void launch_dc(dim3 grid, const bf16* A, int64_t lda, const GemmB& b, bf16* C, int64_t ldc, int M, int N, int K,
                       hipStream_t st) {
   constexpr int NS = 4, NW = 8;
 #define MSR_GEMM_BT(E)                                                                                         \
-  hipLaunchKernelGGL((k_gemm_bt<E, NS, NW>), grid, dim3(64 * NW), 0, st, A, lda, b, C, ldc, M, N, K);         \
+  hipLaunchKernelGGL((k_gemm_dc<E, NS, NW>), grid, dim3(64 * NW), 0, st, A, lda, b, C, ldc, M, N, K);         \
   return;
   switch (epilogue_set(b)) {
     case 0: MSR_GEMM_BT(0)
@@ -672,8 +641,8 @@ static void launch_any(Elt elt, const void* A, int64_t lda, const GemmB& b, void
   if (skinny(elt, M)) {
     launch_tiles<bf16, 128, 64, 64, 2, 2>(dim3((N + 63) / 64, 1, splits), (const bf16*)A, lda, b, (bf16*)C, ldc, M,
                                           N, K, st);
-  } else if (b.bt) {
-    launch_bt(dim3((N + 255) / 256, (M + 255) / 256, splits), (const bf16*)A, lda, b, (bf16*)C, ldc, M, N, K, st);
+  } else if (elt == kBF16 && uniform_segments(b, N, 256)) {
+    launch_dc(dim3((N + 255) / 256, (M + 255) / 256, splits), (const bf16*)A, lda, b, (bf16*)C, ldc, M, N, K, st);
   } else if (elt == kBF16) {
     launch_tiles<bf16, 256, 256, 64, 2, 2>(dim3((N + 255) / 256, (M + 255) / 256, splits), (const bf16*)A, lda, b,
                                            (bf16*)C, ldc, M, N, K, st);
@@ -687,7 +656,6 @@ hipError_t launch_gemm_splitk(Elt elt, const void* A, int64_t lda, const GemmB& 
                               int N, int K, int splits, float* part, hipStream_t st) {
   if (M == 0 || N == 0) return hipSuccess;
   if (b.act || b.resid || b.bias[0] || b.bias[1] || b.bias[2] || b.bias[3]) return hipErrorInvalidValue;
-  if (b.bt && !gemm_transposed_b(elt, M)) return hipErrorInvalidValue;
   GemmB bs = b;
   bs.part = part;
   bs.rope_segs = 0;
@@ -711,7 +679,6 @@ hipError_t launch_gemm_splitk(Elt elt, const void* A, int64_t lda, const GemmB& 
 hipError_t launch_gemm(Elt elt, const void* A, int64_t lda, const GemmB& b, void* C, int64_t ldc, int M, int N,
                        int K, hipStream_t st) {
   if (M == 0 || N == 0) return hipSuccess;
-  if (b.bt && !gemm_transposed_b(elt, M)) return hipErrorInvalidValue;
   TraceScope ts("k_gemm", st);
   launch_any(elt, A, lda, b, C, ldc, M, N, K, 1, st);
   return hipGetLastError();

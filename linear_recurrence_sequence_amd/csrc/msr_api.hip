@@ -154,17 +154,13 @@ BwdWs bwd_ws_layout(msr_dtype dt, const msr_dims& d, int32_t chunk, bool rope) {
   return w;
 }
 
-// Layer: [Q | K | V | G] rows, Z, the rotation table, the chunk workspace,
-// and for the transposed-B projections (bf16, more than 128 rows) the
-// weights transposed: [W_Q | W_K | W_V | W_G]^T ([ntot, d_model]) and W_O^T
-// ([d_model, H d_v]).
 struct LayerWs {
-  size_t qkvg = 0, z = 0, tab = 0, chunk = 0, wt = 0, wto = 0, total = 0;
-  bool bt = false;
+  size_t qkvg = 0, z = 0, tab = 0, chunk = 0, total = 0;
   ChunkWs cw;
 };
 LayerWs layer_ws_layout(msr_dtype dt, int32_t batch, int32_t seqlen, int32_t d_model, int32_t heads, int32_t dk,
                         int32_t dv, int32_t chunk) {
+  (void)d_model;
   LayerWs w;
   const size_t es = elt_size(dt);
   const size_t M = (size_t)batch * seqlen;
@@ -176,11 +172,6 @@ LayerWs layer_ws_layout(msr_dtype dt, int32_t batch, int32_t seqlen, int32_t d_m
   msr_dims d{batch, seqlen, heads, dk, dv};
   w.cw = chunk_ws_layout(dt, d, chunk, false, true);
   w.chunk = off; off += w.cw.total;
-  w.bt = gemm_transposed_b(dt == MSR_BF16 ? kBF16 : kF32, (int64_t)M);
-  if (w.bt) {
-    w.wt = off; off += align_up(ntot * d_model * es);
-    w.wto = off; off += align_up((size_t)d_model * heads * dv * es);
-  }
   w.total = off;
   return w;
 }
@@ -216,11 +207,10 @@ DecodeWs decode_ws_layout(msr_dtype dt, int32_t batch, int32_t d_model, int32_t 
 }
 
 // RetNet block: the layer's workspace, then LN output, Y, and the
-// feed-forward hidden rows; with the transposed-B products also W_1^T
-// ([d_ffn, d_model]) and W_2^T ([d_model, d_ffn]).
+// feed-forward hidden rows.
 struct BlockWs {
   LayerWs lw;
-  size_t layer = 0, h = 0, y = 0, f = 0, w1t = 0, w2t = 0, total = 0;
+  size_t layer = 0, h = 0, y = 0, f = 0, total = 0;
 };
 BlockWs block_ws_layout(msr_dtype dt, int32_t batch, int32_t seqlen, int32_t d_model, int32_t heads, int32_t dk,
                         int32_t dv, int32_t chunk, int32_t d_ffn) {
@@ -233,10 +223,6 @@ BlockWs block_ws_layout(msr_dtype dt, int32_t batch, int32_t seqlen, int32_t d_m
   w.h = off; off += align_up(M * d_model * es);
   w.y = off; off += align_up(M * d_model * es);
   w.f = off; off += align_up(M * (size_t)d_ffn * es);
-  if (w.lw.bt) {
-    w.w1t = off; off += align_up((size_t)d_ffn * d_model * es);
-    w.w2t = off; off += align_up((size_t)d_model * d_ffn * es);
-  }
   w.total = off;
   return w;
 }
@@ -267,16 +253,6 @@ static msr_status layer_launch(msr_dtype dtype, int32_t batch, int32_t seqlen, i
   bq.ptr[0] = W_Q; bq.ptr[1] = W_K; bq.ptr[2] = W_V; bq.ptr[3] = W_G;
   bq.ld[0] = hk; bq.ld[1] = hk; bq.ld[2] = hv; bq.ld[3] = hv;
   bq.start[0] = 0; bq.start[1] = hk; bq.start[2] = 2 * hk; bq.start[3] = 2 * hk + hv;
-  if (w.bt) {   // the four weights into one [ntot, d_model] operand, W_O into [d_model, H d_v]
-    char* wt = at<char>(workspace, w.wt);
-    TransposeJob jobs[5];
-    for (int sg = 0; sg < 4; ++sg)
-      jobs[sg] = {bq.ptr[sg], bq.ld[sg], wt + (size_t)bq.start[sg] * d_model * es, d_model, d_model, sg < 2 ? hk : hv};
-    jobs[4] = {W_O, d_model, at<void>(workspace, w.wto), hv, hv, d_model};
-    if (err == hipSuccess) err = launch_transpose(e, jobs, 5, st);
-    bq.ptr[0] = wt; bq.ld[0] = d_model;
-    bq.bt = 1;
-  }
   bq.rope_segs = rope ? 2 : 0;
   bq.rope_d = d_k;
   bq.seqlen = seqlen;
@@ -306,10 +282,6 @@ static msr_status layer_launch(msr_dtype dtype, int32_t batch, int32_t seqlen, i
   bo.ptr[0] = W_O; bo.ld[0] = d_model;
   bo.start[0] = 0; bo.start[1] = bo.start[2] = bo.start[3] = INT32_MAX;
   bo.resid = resid; bo.ldr = d_model;
-  if (w.bt) {   // transposed with the projection weights above
-    bo.ptr[0] = at<void>(workspace, w.wto); bo.ld[0] = hv;
-    bo.bt = 1;
-  }
   err = launch_gemm(e, z, hv, bo, out, d_model, (int)M, d_model, hv, st);
   return from_hip(err, "msr_layer_fwd(output projection)");
 }
@@ -559,14 +531,9 @@ msr_status msr_chunkwise_bwd(msr_dtype dtype, msr_dims d, int32_t chunk, const d
   return from_hip(err, "msr_chunkwise_bwd(dS_in)");
 }
 
-// RG-LRU: the gate rows [r | i]; with the transposed-B product (bf16, more
-// than 128 rows) then [W_a | W_x]^T ([2 width, width]).
 size_t msr_rglru_workspace_bytes(msr_dtype dtype, int32_t batch, int32_t seqlen, int32_t width) {
   if (check_dtype(dtype) || batch < 0 || seqlen < 0 || width <= 0) return 0;
-  const int64_t M = (int64_t)batch * seqlen;
-  const size_t gates = align_up((size_t)M * 2 * width * elt_size(dtype));
-  if (!gemm_transposed_b(dtype == MSR_BF16 ? kBF16 : kF32, M)) return gates;
-  return gates + align_up((size_t)2 * width * width * elt_size(dtype));
+  return align_up((size_t)batch * seqlen * 2 * width * elt_size(dtype));
 }
 
 msr_status msr_rglru_fwd(msr_dtype dtype, int32_t batch, int32_t seqlen, int32_t width, float c, const void* X,
@@ -599,16 +566,7 @@ msr_status msr_rglru_fwd(msr_dtype dtype, int32_t batch, int32_t seqlen, int32_t
     bg.start[0] = 0; bg.start[1] = width; bg.start[2] = bg.start[3] = INT32_MAX;
     bg.bias[0] = b_a; bg.bias[1] = b_x;
     bg.act = 2;
-    hipError_t err = hipSuccess;
-    if (gemm_transposed_b(e, M)) {   // [W_a | W_x]^T after the gate rows
-      char* wt = static_cast<char*>(workspace) + align_up((size_t)M * 2 * width * elt_size(dtype));
-      const TransposeJob jobs[2] = {{W_a, width, wt, width, width, width},
-                                    {W_x, width, wt + (size_t)width * width * elt_size(dtype), width, width, width}};
-      err = launch_transpose(e, jobs, 2, st);
-      bg.ptr[0] = wt; bg.ld[0] = width;
-      bg.bt = 1;
-    }
-    if (err == hipSuccess) err = launch_gemm(e, X, width, bg, workspace, 2 * width, (int)M, 2 * width, width, st);
+    hipError_t err = launch_gemm(e, X, width, bg, workspace, 2 * width, (int)M, 2 * width, width, st);
     if (err != hipSuccess) return from_hip(err, "msr_rglru_fwd(gates)");
   }
   // seqlen == 0 runs the scan too: it copies h0 (or zeros) to h_last
@@ -787,20 +745,12 @@ msr_status msr_retnet_block_fwd(msr_dtype dtype, int32_t batch, int32_t seqlen, 
   b1.ptr[0] = W_1; b1.ld[0] = d_ffn;
   b1.start[0] = 0; b1.start[1] = b1.start[2] = b1.start[3] = INT32_MAX;
   b1.act = 1;
+  err = launch_gemm(e, H, d_model, b1, F, d_ffn, (int)M, d_ffn, d_model, st);
+  if (err != hipSuccess) return from_hip(err, "msr_retnet_block_fwd(W_1)");
   GemmB b2{};
   b2.ptr[0] = W_2; b2.ld[0] = d_model;
   b2.start[0] = 0; b2.start[1] = b2.start[2] = b2.start[3] = INT32_MAX;
   b2.resid = Y; b2.ldr = d_model;
-  if (w.lw.bt) {
-    const TransposeJob jobs[2] = {{W_1, d_ffn, at<void>(workspace, w.w1t), d_model, d_model, d_ffn},
-                                  {W_2, d_model, at<void>(workspace, w.w2t), d_ffn, d_ffn, d_model}};
-    err = launch_transpose(e, jobs, 2, st);
-    if (err != hipSuccess) return from_hip(err, "msr_retnet_block_fwd(weight layout)");
-    b1.ptr[0] = at<void>(workspace, w.w1t); b1.ld[0] = d_model; b1.bt = 1;
-    b2.ptr[0] = at<void>(workspace, w.w2t); b2.ld[0] = d_ffn; b2.bt = 1;
-  }
-  err = launch_gemm(e, H, d_model, b1, F, d_ffn, (int)M, d_ffn, d_model, st);
-  if (err != hipSuccess) return from_hip(err, "msr_retnet_block_fwd(W_1)");
   err = launch_gemm(e, F, d_ffn, b2, out, d_model, (int)M, d_model, d_ffn, st);
   return from_hip(err, "msr_retnet_block_fwd(W_2)");
 }

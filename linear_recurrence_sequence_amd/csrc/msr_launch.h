@@ -134,9 +134,6 @@ struct GemmB {
   int act;
   const void* resid;
   int64_t ldr;
-  // bt: B is given transposed, one [N, K] matrix (k contiguous) at ptr[0]
-  // with row stride ld[0]; start[] still marks the epilogue's segments.
-  int bt;
 };
 
 // C[M, N] = A[M, K] * B[K, N] (row-major A and B segments), fp32
@@ -150,21 +147,6 @@ hipError_t launch_gemm_splitk(Elt elt, const void* A, int64_t lda, const GemmB& 
                               int N, int K, int splits, float* part, hipStream_t stream);
 // How many K splits launch_gemm_splitk should use for an M x N x K product.
 int gemm_splits(Elt elt, int M, int N, int K);
-// Whether an M-row product runs on the transposed-B kernel (GemmB::bt):
-// bf16 with more than 128 rows; launch_gemm rejects bt otherwise.
-bool gemm_transposed_b(Elt elt, int64_t M);
-// dst[c][r] = src[r][c] (bf16, rows and cols multiples of 8; strides in
-// elements): the weights' [in, out] layout to the transposed-B operand.
-// One launch transposes up to kMaxTransposeJobs matrices.
-constexpr int kMaxTransposeJobs = 5;
-struct TransposeJob {
-  const void* src;
-  int64_t lds;
-  void* dst;
-  int64_t ldd;
-  int rows, cols;
-};
-hipError_t launch_transpose(Elt elt, const TransposeJob* jobs, int njobs, hipStream_t stream);
 // Row-wise LayerNorm over d columns (biased variance, identity affine):
 // Y = (X - mean) / sqrt(var + eps); d a multiple of 8, at most 8192.
 hipError_t launch_layer_norm(Elt elt, const void* X, int64_t ldx, void* Y, int64_t ldy, int rows, int d, float eps,

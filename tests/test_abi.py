@@ -209,26 +209,6 @@ def test_workspace_sizes():
         up(lay) + 2 * up(Bb * Nb * dmb * 2) + up(Bb * Nb * Fb * 2))
 
 
-def test_workspace_sizes_with_transposed_weights():
-    """bf16 products of more than 128 rows take the weights transposed in the
-    workspace: the layer adds [W_Q | W_K | W_V | W_G]^T and W_O^T, the block
-    W_1^T and W_2^T, the RG-LRU [W_a | W_x]^T; float32 and 128 rows do not."""
-    up = lambda x: -(-x // 256) * 256
-    B, N, dm, H, dk, dv, C, F = 2, 65, 256, 2, 128, 128, 32, 512
-    ntot, hv = H * (2 * dk + 2 * dv), H * dv
-    lay = msr.msr_layer_workspace_bytes(1, B, N, dm, H, dk, dv, C)
-    lay_short = msr.msr_layer_workspace_bytes(1, 2, 64, dm, H, dk, dv, C)     # 128 rows
-    nc = -(-N // C)
-    base = (up(B * N * ntot * 2) + up(B * N * hv * 2) + up(N * dk // 2 * 8) + up(B * H * nc * dk * dv * 2))
-    assert lay == base + up(ntot * dm * 2) + up(dm * hv * 2)
-    assert lay_short == (up(2 * 64 * ntot * 2) + up(2 * 64 * hv * 2) + up(64 * dk // 2 * 8) +
-                         up(2 * H * 2 * dk * dv * 2))
-    assert msr.msr_retnet_block_workspace_bytes(1, B, N, dm, H, dk, dv, C, F) == (
-        up(lay) + 2 * up(B * N * dm * 2) + up(B * N * F * 2) + 2 * up(F * dm * 2))
-    assert msr.msr_rglru_workspace_bytes(1, 3, 50, 128) == up(150 * 256 * 2) + up(2 * 128 * 128 * 2)
-    assert msr.msr_rglru_workspace_bytes(0, 3, 50, 128) == up(150 * 256 * 4)
-
-
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(msr, "_lib", None)
     monkeypatch.setattr(msr, "library_path", lambda: str(tmp_path / "missing.so"))
