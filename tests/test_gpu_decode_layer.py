@@ -31,7 +31,10 @@ def _inputs(seed, B, dm, H, dk, dv, dtype, s_std=0.5):
     return x, WQ, WK, WV, WG, WO, S
 
 
-CASES = [(3, 128, 2, 64, 64), (2, 256, 2, 128, 128), (4, 512, 2, 256, 256), (2, 256, 2, 256, 512)]
+# the last case has more than 128 rows: its bf16 projections take the
+# 256 x 256 direct-copy tiles with split-K instead of the 128 x 64 ones
+CASES = [(3, 128, 2, 64, 64), (2, 256, 2, 128, 128), (4, 512, 2, 256, 256), (2, 256, 2, 256, 512),
+         (200, 512, 2, 256, 256)]
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
