@@ -365,9 +365,9 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm(const T* __restrict__ A, 
 
 // ---------------------------------------------------------------------------
 // k_gemm_dc: bf16 C = A B (B row-major, in up to four column segments whose
-// boundaries fall on 256-column tile edges), 256 x 256 output tiles, NW
-// waves: 8 waves of 128 x 64 (two per SIMD, so that one wave's matrix-core
-// work covers the other's waits) or 4 of 128 x 128.  Both operand tiles
+// boundaries fall on 256-column tile edges), 256 x 256 output tiles, 8
+// waves of 128 x 64 (two per SIMD, so that one wave's matrix-core work
+// covers the other's waits; 4 waves of 128 x 128 measured slower).  Both operand tiles
 // stream into LDS by direct 16-byte copies (no staging registers, no LDS
 // write instructions) through a ring of NS slots of 32-deep K slabs, NS - 2
 // slabs in flight ahead of the one being read.
@@ -389,7 +389,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_dc(const bf16* __restrict__ A,
   constexpr int BM = 256, BN = 256, BK = 32, WM = 2, WN = NW / 2, TM = 4, TN = 4 / (NW / 4);
   constexpr int SLOTS = (BM + BN) * (BK / 8);        // 16-byte slots per slab
   constexpr int CPW = SLOTS / 64 / NW;               // copies per wave per slab
-  static_assert((NW == 4 || NW == 8) && NS >= 3, "slab layout");
+  static_assert(NW == 8 && NS >= 3, "slab layout");
   __shared__ __attribute__((aligned(1024))) bf16 smem[NS * SLOTS * 8];
   static_assert(NS * SLOTS * 8 * 2 >= NW * 32 * (BN / WN + 4) * 4, "epilogue staging fits in the ring");
 
