@@ -211,33 +211,40 @@ def bench_layer(w, steps, warmup, device_inputs=False):
     return res
 
 
-def bench_core(B, N, H, d, C, steps, warmup, parallel=False):
+def bench_core(B, N, H, d, C, steps, warmup, parallel=False, dv=None):
+    """Chunkwise (or parallel) retention core on projected bf16 Q, K, V of
+    [B, N, H, d] (V and O [B, N, H, dv]); algorithmic flops count the causal
+    half of the intra-chunk products: per token and head C (d_k + d_v) +
+    4 d_k d_v (chunkwise), N (d_k + d_v) on average (parallel)."""
     import torch
     import linear_recurrence_sequence_amd as msr
     import workloads
-    Q, K, V = (workloads.device_normal((B, N, H, d), seed=7 + i, dtype=torch.bfloat16) for i in range(3))
-    O = torch.empty_like(Q)
+    dk, dv = d, dv or d
+    Q, K = (workloads.device_normal((B, N, H, dk), seed=7 + i, dtype=torch.bfloat16) for i in range(2))
+    V = workloads.device_normal((B, N, H, dv), seed=9, dtype=torch.bfloat16)
+    O = torch.empty_like(V)
     g = workloads.gammas(H)
-    s = 1 / math.sqrt(d)
+    s = 1 / math.sqrt(dk)
     if parallel:
         fn = lambda: msr.msr_parallel_fwd(Q, K, V, g, qk_scale=s, O=O)
-        flops = B * N * H * N * 2 * d       # causal: N(dk + dv) per token on average
+        flops = B * N * H * N * (dk + dv)
     else:
-        ws = torch.empty(msr.msr_chunkwise_workspace_bytes(1, B, N, H, d, d, C, 0.0), dtype=torch.uint8,
+        ws = torch.empty(msr.msr_chunkwise_workspace_bytes(1, B, N, H, dk, dv, C, 0.0), dtype=torch.uint8,
                          device="cuda")
         fn = lambda: msr.msr_chunkwise_fwd(Q, K, V, g, C, qk_scale=s, O=O, workspace=ws)
-        flops = B * N * H * (C * 2 * d + 4 * d * d)
+        flops = B * N * H * (C * (dk + dv) + 4 * dk * dv)
     t = gpu_time(fn, steps, warmup)
     res = {"N": N, "s": t, "tokens_per_s": B * N / t, "tflops": flops / t / 1e12, "mfma_frac": flops / t / PEAK_BF16}
     if not parallel:
         tr = traced(fn, steps)
         nc = -(-N // C)
-        states = B * H * nc * d * d * 2
+        states = B * H * nc * dk * dv * 2
         res["kernels"] = {
-            "k_chunk_out": roof("k_chunk_out", B * N * H * (C * 2 * d + 2 * d * d), "mfma", tr, steps,
-                                bytes_per_step=B * N * H * 4 * d * 2 + states),   # Q, K, V read, O written, R_{i-1}
-            "k_chunk_state": roof("k_chunk_state", B * N * H * 2 * d * d, "mfma", tr, steps,
-                                  bytes_per_step=B * N * H * 2 * d * 2 + states),
+            # Q, K read, V read, O written, R_{i-1} read
+            "k_chunk_out": roof("k_chunk_out", B * N * H * (C * (dk + dv) + 2 * dk * dv), "mfma", tr, steps,
+                                bytes_per_step=B * N * H * (2 * dk + 2 * dv) * 2 + states),
+            "k_chunk_state": roof("k_chunk_state", B * N * H * 2 * dk * dv, "mfma", tr, steps,
+                                  bytes_per_step=B * N * H * (dk + dv) * 2 + states),
             "k_chunk_scan": roof("k_chunk_scan", 2 * states, "hbm", tr, steps),
         }
     return res
@@ -540,6 +547,11 @@ def main():
         line["block"] = {"tokens_per_s": round(br["tokens_per_s"], 1), "mfma_frac": round(br["mfma_frac"], 4),
                          "ms_per_step": round(br["s_per_step"] * 1e3, 3), "tflops": round(br["tflops"], 1),
                          "kernels": br["kernels"]}
+        # the chunkwise core alone at the block workload's shape (d_v = 512)
+        bc = bench_core(bw.batch, bw.seqlen, bw.heads, bw.d_k, bw.chunk, max(3, args.steps // 4), 2, dv=bw.d_v)
+        line["block"]["core_chunkwise"] = {
+            "tokens_per_s": round(bc["tokens_per_s"], 1), "us_per_step": round(bc["s"] * 1e6, 1),
+            "tflops": round(bc["tflops"], 1), "mfma_frac": round(bc["mfma_frac"], 4), "kernels": bc["kernels"]}
     if "retnet" in parts:
         log("retnet block")
         line["retnet_block"] = bench_retnet_block(max(3, args.steps // 2), 2)

@@ -502,7 +502,76 @@ __global__ __launch_bounds__(64 * NW) void k_chunk_out(
   }
 
   // ---- epilogue: lane owns column 32 j + lr of rows q0 + 8 (r/4) + 4 hh + r%4 ----
-  if constexpr (GN) {
+  if constexpr (GN && DV > 256) {
+    // d_v = 512 (every register in use): the normalised rows go through
+    // LDS, 8 rows of this wave per pass (accumulator registers 4 p .. 4 p + 3),
+    // so that each lane then takes one 8-column chunk of each row -- 16-byte
+    // gate loads, the next pass's in flight during the current one, and
+    // 16-byte stores.  The staging rows are the wave's own (in-order LDS
+    // operations, a compiler fence between the phases).
+    float mu[16], rs[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float s = 0.f;
+#pragma unroll
+      for (int j = 0; j < DV / 32; ++j) s += acc[j][r];
+      mu[r] = half_wave_sum(s) * (1.0f / DV);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float s = 0.f;
+#pragma unroll
+      for (int j = 0; j < DV / 32; ++j) {
+        const float dlt = acc[j][r] - mu[r];
+        s += dlt * dlt;
+      }
+      rs[r] = rsqrtf(half_wave_sum(s) * (1.0f / DV) + eps);
+    }
+    constexpr int SLD = DV + 4;                    // staged row stride (floats)
+    constexpr int CH = 8 * (DV / 8) / 64;          // 8-column chunks per lane per pass
+    static_assert(NW * 8 * SLD * 4 <= C::NBUF * C::STAGE * (int)sizeof(T), "staging fits in the stage buffers");
+    __syncthreads();                               // every wave is done with the stage buffers
+    float* stg = reinterpret_cast<float*>(smem) + wave * 8 * SLD;
+    Row8<T> gv[2][CH];
+    auto gload = [&](int p, int buf) {
+#pragma unroll
+      for (int k = 0; k < CH; ++k) {
+        const int c = lane + 64 * k, rr = c / (DV / 8), c8 = c % (DV / 8);
+        const int q = min(q0 + 8 * p + rr, N - 1);
+        load_row8(gv[buf][k], G + (tokb + q) * ldg + (size_t)h * DV + 8 * c8, true);
+      }
+    };
+    gload(0, 0);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      if (p + 1 < 4) gload(p + 1, (p + 1) & 1);
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        const int r = 4 * p + rq;
+#pragma unroll
+        for (int j = 0; j < DV / 32; ++j) stg[(4 * hh + rq) * SLD + 32 * j + lr] = (acc[j][r] - mu[r]) * rs[r];
+      }
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int k = 0; k < CH; ++k) {
+        const int c = lane + 64 * k, rr = c / (DV / 8), c8 = c % (DV / 8);
+        const int q = q0 + 8 * p + rr;
+        const f32x4 y0 = *reinterpret_cast<const f32x4*>(stg + rr * SLD + 8 * c8);
+        const f32x4 y1 = *reinterpret_cast<const f32x4*>(stg + rr * SLD + 8 * c8 + 4);
+        float g[8], z[8];
+        unpack_row8(g, gv[p & 1][k]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          z[e] = swish_fast(g[e]) * y0[e];
+          z[4 + e] = swish_fast(g[4 + e]) * y1[e];
+        }
+        Row8<T> o;
+        pack_row8(o, z);
+        if (q < N) store_row8(O + (tokb + (rev ? N - 1 - q : q)) * ldo + (size_t)h * DV + 8 * c8, o);
+      }
+      asm volatile("" ::: "memory");
+    }
+  } else if constexpr (GN) {
     float mu[16], rs[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
