@@ -1,46 +1,17 @@
-// Pieces of the chunkwise backward that are not retention passes: time
-// reversal of the token rows of its inputs, in-place transposes of the
-// per-chunk states, and per-head scaled copies or transposes of float32
-// states.
+// Pieces of the chunkwise backward that are not retention passes: in-place
+// transposes of the per-chunk states, and per-head scaled copies or
+// transposes of float32 states.
 //
 // The gradients of retention ([RN-zh] "Retention 網路總體結構": training runs
 // the parallel and chunkwise forms) are retentions themselves: dQ is the
 // causal retention of (dO, V, K), and dK, dV are anti-causal retentions,
 // which become causal ones on the time-reversed sequence.  The passes run on
-// the chunkwise kernels (k_chunk.hip, whose output kernels can write rows
-// back in forward order); this file supplies the input reversals and the
-// state seeds.
+// the chunkwise kernels (k_chunk.hip, which can read their input rows
+// backwards and write their output rows back in forward order); this file
+// supplies the state seeds and transposes.
 #include "msr_launch.h"
 
 namespace msr {
-
-// Row (b, t) of each job's source goes to row (b, seqlen-1-t) of its
-// destination; blockIdx.y picks the job; each thread moves 16 bytes.
-__global__ void k_reverse_rows(RevJobs j, int batch, int seqlen, int row_bytes) {
-  const int job = blockIdx.y;
-  const int vec = row_bytes / 16;
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= (int64_t)batch * seqlen * vec) return;
-  const int64_t row = i / vec;
-  const int c = (int)(i % vec);
-  const int64_t b = row / seqlen;
-  const int t = (int)(row % seqlen);
-  const int64_t out_row = b * seqlen + (seqlen - 1 - t);
-  const uint4 x = *reinterpret_cast<const uint4*>(j.src[job] + row * j.lds[job] + 16 * c);
-  *reinterpret_cast<uint4*>(j.dst[job] + out_row * j.ldd[job] + 16 * c) = x;
-}
-
-hipError_t launch_reverse_rows(const RevJobs& jobs, int njobs, int batch, int seqlen, int row_bytes, hipStream_t st) {
-  if (njobs < 1 || njobs > 4 || row_bytes % 16) return hipErrorInvalidValue;
-  for (int q = 0; q < njobs; ++q)
-    if (jobs.ldd[q] % 16 || jobs.lds[q] % 16) return hipErrorInvalidValue;
-  const int64_t n = (int64_t)batch * seqlen * (row_bytes / 16);
-  if (n == 0) return hipSuccess;
-  const dim3 grid((unsigned)((n + 255) / 256), njobs);
-  TraceScope ts("k_reverse_rows", st);
-  hipLaunchKernelGGL(k_reverse_rows, grid, dim3(256), 0, st, jobs, batch, seqlen, row_bytes);
-  return hipGetLastError();
-}
 
 namespace {
 // Four consecutive elements as floats (8-byte bf16 or 16-byte f32 accesses).

@@ -50,7 +50,8 @@ struct StateCfg {
 template <class T, int DK, int DV>
 __global__ __launch_bounds__(256) void k_chunk_state(const T* __restrict__ K, const T* __restrict__ V,
                                                      int64_t ldk, int64_t ldv, T* __restrict__ dR,
-                                                     int BH, int N, int H, int chunk, int NC, HeadTab tab) {
+                                                     int BH, int N, int H, int chunk, int NC, HeadTab tab,
+                                                     int rev_in) {
   using C = StateCfg<T, DK, DV>;
   constexpr int TS = C::TS, WT = C::WT, KB = C::KB, LDT = C::LDT, UNITS = C::UNITS, UPT = C::UPT;
   __shared__ __attribute__((aligned(16))) T smem[C::STAGE];
@@ -74,8 +75,10 @@ __global__ __launch_bounds__(256) void k_chunk_state(const T* __restrict__ K, co
   const int wr = (wave >> 1) * 32 * WT;
   const int wc = (wave & 1) * 32 * WT;
   // uniform bases + small per-thread offsets; keys past the chunk end are
-  // clamped to a valid row and get zeta = 0, so they add nothing.
-  const size_t tok0 = (size_t)b * N + c0;
+  // clamped to a valid row and get zeta = 0, so they add nothing.  With
+  // rev_in key kc of the chunk is row N - 1 - c0 - kc: the base is the
+  // chunk's lowest row and the offset L - 1 - kc.
+  const size_t tok0 = (size_t)b * N + (rev_in ? N - c0 - L : c0);
   const T* Kb = K + (size_t)h * DK + tk * TS + tok0 * ldk;
   const T* Vb = V + (size_t)h * DV + tv * TS + tok0 * ldv;
 
@@ -92,10 +95,10 @@ __global__ __launch_bounds__(256) void k_chunk_state(const T* __restrict__ K, co
       const int key = u / (TS / 8), c8 = u % (TS / 8);
       if (UNITS % 256 == 0 || u < UNITS) {
         const int kk = kb + key;
-        const int kc = min(kk, L - 1);
+        const int kc = min(kk, L - 1), kr = rev_in ? L - 1 - kc : kc;
         Row8<T> rk, rv;
-        load_row8(rk, Kb + (uint32_t)(kc * (int)ldk + 8 * c8), true);
-        load_row8(rv, Vb + (uint32_t)(kc * (int)ldv + 8 * c8), true);
+        load_row8(rk, Kb + (uint32_t)(kr * (int)ldk + 8 * c8), true);
+        load_row8(rv, Vb + (uint32_t)(kr * (int)ldv + 8 * c8), true);
         scale_row8(rv, kk < L ? gpow(L - 1 - kk, lg2) : 0.f);
         store_row8(sK + key * LDT + 8 * c8, rk);
         store_row8(sV + key * LDT + 8 * c8, rv);
@@ -304,6 +307,8 @@ __global__ __launch_bounds__(64 * NW) void k_chunk_out(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, int64_t ldq, int64_t ldk,
     int64_t ldv, const T* __restrict__ Rx, int has_sin, const T* __restrict__ G, int64_t ldg, T* __restrict__ O,
     int64_t ldo, int BH, int N, int H, int chunk, int NC, int TPC, float scale, float eps, HeadTab tab, int rev) {
+  // rev bit 0: output row t to row N - 1 - t; bit 1: Q, K, V row t from row N - 1 - t
+  const bool rev_o = rev & 1, rev_i = rev & 2;
   using C = OutCfg<T, DK, DV, NW>;
   constexpr int NT = C::NT, KB = C::KB, SK = C::SK, LDK = C::LDK, LDV = C::LDV, LDR = C::LDR;
   constexpr int RT = 32 * NW;
@@ -329,7 +334,8 @@ __global__ __launch_bounds__(64 * NW) void k_chunk_out(
   Frag<T> qf[DK / 16];
   {
     // rows past the end are clamped (their outputs are never stored)
-    const T* p = Q + (tokb + min(q0 + lr, N - 1)) * ldq + (size_t)h * DK + 8 * hh;
+    const int qr = min(q0 + lr, N - 1);
+    const T* p = Q + (tokb + (rev_i ? N - 1 - qr : qr)) * ldq + (size_t)h * DK + 8 * hh;
 #pragma unroll
     for (int s = 0; s < DK / 16; ++s) qf[s] = load_frag(p + 16 * s);
   }
@@ -364,21 +370,25 @@ __global__ __launch_bounds__(64 * NW) void k_chunk_out(
   // 32-bit per-thread offsets inside a KB-row block (row < KB, so
   // row * stride fits easily); the block base is a uniform 64-bit pointer.
   const int ldk32 = (int)ldk, ldv32 = (int)ldv;
+  // With rev_i, key kb + r is row N - 1 - kb - r: the block's base is its
+  // lowest row, N - 1 - kb - lim, and key r sits lim - r rows above it.
   auto load_KV = [&](int kb) {
-    const int lim = N - 1 - kb;
-    const T* Kk = Kh + (size_t)kb * ldk;
-    const T* Vk = Vh + (size_t)kb * ldv;
+    const int lim = min(KB - 1, N - 1 - kb);
+    const int base = rev_i ? N - 1 - kb - lim : kb;
+    const T* Kk = Kh + (size_t)base * ldk;
+    const T* Vk = Vh + (size_t)base * ldv;
+    auto orow = [&](int row) { return rev_i ? lim - min(row, lim) : min(row, lim); };
 #pragma unroll
     for (int u = 0; u < C::KU; ++u) {
       const int idx = min(tid + NT * u, KB * (DK / 8) - 1);
       const int row = idx / (DK / 8), c8 = idx % (DK / 8);
-      load_row8(pre[u], Kk + (uint32_t)(min(row, lim) * ldk32 + 8 * c8), true);
+      load_row8(pre[u], Kk + (uint32_t)(orow(row) * ldk32 + 8 * c8), true);
     }
 #pragma unroll
     for (int u = 0; u < C::VU; ++u) {
       const int idx = min(tid + NT * u, KB * (DV / 8) - 1);
       const int row = idx / (DV / 8), c8 = idx % (DV / 8);
-      load_row8(pre[C::KU + u], Vk + (uint32_t)(min(row, lim) * ldv32 + 8 * c8), true);
+      load_row8(pre[C::KU + u], Vk + (uint32_t)(orow(row) * ldv32 + 8 * c8), true);
     }
   };
   auto store_KV = [&](T* sK) {
@@ -567,7 +577,7 @@ __global__ __launch_bounds__(64 * NW) void k_chunk_out(
         }
         Row8<T> o;
         pack_row8(o, z);
-        if (q < N) store_row8(O + (tokb + (rev ? N - 1 - q : q)) * ldo + (size_t)h * DV + 8 * c8, o);
+        if (q < N) store_row8(O + (tokb + (rev_o ? N - 1 - q : q)) * ldo + (size_t)h * DV + 8 * c8, o);
       }
       asm volatile("" ::: "memory");
     }
@@ -609,7 +619,7 @@ __global__ __launch_bounds__(64 * NW) void k_chunk_out(
         const int r = r0 + rr;
         const int q = q0 + 8 * (r >> 2) + 4 * hh + (r & 3);
         if (q < N) {
-          T* op = O + (tokb + (rev ? N - 1 - q : q)) * ldo + (size_t)h * DV + lr;
+          T* op = O + (tokb + (rev_o ? N - 1 - q : q)) * ldo + (size_t)h * DV + lr;
 #pragma unroll
           for (int j = 0; j < DV / 32; ++j) {
             const float sw = swish_fast(RawElt<T>::value(graw[rr][j]));
@@ -623,7 +633,7 @@ __global__ __launch_bounds__(64 * NW) void k_chunk_out(
     for (int r = 0; r < 16; ++r) {
       const int q = q0 + 8 * (r >> 2) + 4 * hh + (r & 3);
       if (q < N) {
-        T* op = O + (tokb + (rev ? N - 1 - q : q)) * ldo + (size_t)h * DV + lr;
+        T* op = O + (tokb + (rev_o ? N - 1 - q : q)) * ldo + (size_t)h * DV + lr;
 #pragma unroll
         for (int j = 0; j < DV / 32; ++j) op[32 * j] = (T)acc[j][r];
       }
@@ -679,6 +689,8 @@ __global__ __launch_bounds__(256) void k_chunk_dl(
     int64_t ldv, const bf16* __restrict__ Rx, int has_sin, const bf16* __restrict__ G, int64_t ldg,
     bf16* __restrict__ O, int64_t ldo, int BH, int N, int H, int chunk, int NC, int TPC, float scale, float eps,
     HeadTab tab, int rev) {
+  // rev bit 0: output row t to row N - 1 - t; bit 1: Q, K, V row t from row N - 1 - t
+  const bool rev_o = rev & 1, rev_i = rev & 2;
   using C = DlCfg<DK, DV>;
   constexpr int KB = C::KB, SK = C::SK, NS = C::NS, AHEAD = C::AHEAD, RT = C::RT;
   constexpr int CPK = C::CPK, CPV = C::CPV, CPR = C::CPR;
@@ -720,22 +732,26 @@ __global__ __launch_bounds__(256) void k_chunk_dl(
   // 64 ii .. 64 ii + 63 of the slot; slot u of a tile is row u / stride,
   // chunk u % stride (pad slots and slots past the tile copy chunk 0 of row
   // 0).  Keys past the end are clamped to the last row: they are in the
-  // future of every stored query, so they get weight 0.
+  // future of every stored query, so they get weight 0.  lim: the block's
+  // last valid key (KB - 1 for a whole block); with rev_i key r of a block
+  // is lim - r rows above the block's base (its lowest row).
   auto kv_off = [&](int t, int lim) -> uint32_t {
     const int ii = wave * C::LPW_KV + t;
     if (ii < C::IK) {
       const int u = ii * 64 + lane, row = u / C::SPK, c = u % C::SPK;
-      return row < KB && c < CPK ? (uint32_t)((min(row, lim) * ldk32 + 8 * c) * 2) : 0u;
+      const int r = rev_i ? lim - min(row, lim) : min(row, lim);
+      return row < KB && c < CPK ? (uint32_t)((r * ldk32 + 8 * c) * 2) : 0u;
     }
     const int u = (ii - C::IK) * 64 + lane, row = u / C::SPV, c = u % C::SPV;
-    return row < KB && c < CPV ? (uint32_t)((min(row, lim) * ldv32 + 8 * c) * 2) : 0u;
+    const int r = rev_i ? lim - min(row, lim) : min(row, lim);
+    return row < KB && c < CPV ? (uint32_t)((r * ldv32 + 8 * c) * 2) : 0u;
   };
   // Per-lane byte offsets of this wave's copies: they do not depend on the
   // stage, so they are computed once (only the sequence's last, partial key
   // block needs the clamp, computed when it comes).
   uint32_t okv[C::LPW_KV], orr[C::LPW_R];
 #pragma unroll
-  for (int t = 0; t < C::LPW_KV; ++t) okv[t] = kv_off(t, KB);
+  for (int t = 0; t < C::LPW_KV; ++t) okv[t] = kv_off(t, KB - 1);
 #pragma unroll
   for (int t = 0; t < C::LPW_R; ++t) {
     const int u = (wave * C::LPW_R + t) * 64 + lane, row = u / C::SPR, c = u % C::SPR;
@@ -758,15 +774,15 @@ __global__ __launch_bounds__(256) void k_chunk_dl(
       // block 0 and the last K of block nKV - 1 again: unused)
       const int j = idx - nR;
       const int kbk = c0 + min(j, nKV - 1) * KB, kbv = c0 + max(j - 1, 0) * KB;
-      c.src[0] = Kh + (size_t)kbk * ldk;
-      c.src[1] = Vh + (size_t)kbv * ldv;
-      if (kbk + KB <= N) {                       // no clamp needed (V's block is never later than K's)
+      const int limk = min(KB - 1, N - 1 - kbk), limv = min(KB - 1, N - 1 - kbv);
+      c.src[0] = Kh + (size_t)(rev_i ? N - 1 - kbk - limk : kbk) * ldk;
+      c.src[1] = Vh + (size_t)(rev_i ? N - 1 - kbv - limv : kbv) * ldv;
+      if (kbk + KB <= N) {                       // whole blocks (V's block is never later than K's)
 #pragma unroll
         for (int t = 0; t < C::LPW_KV; ++t) c.off[t] = okv[t];
       } else {
 #pragma unroll
-        for (int t = 0; t < C::LPW_KV; ++t)
-          c.off[t] = kv_off(t, N - 1 - (wave * C::LPW_KV + t < C::IK ? kbk : kbv));
+        for (int t = 0; t < C::LPW_KV; ++t) c.off[t] = kv_off(t, wave * C::LPW_KV + t < C::IK ? limk : limv);
       }
     }
   };
@@ -788,7 +804,8 @@ __global__ __launch_bounds__(256) void k_chunk_dl(
   // past the end clamped, never stored).
   Frag<bf16> qf[DK / 16];
   {
-    const bf16* p = Q + (tokb + min(q0 + lr, N - 1)) * ldq + (size_t)h * DK + 8 * hh;
+    const int qr = min(q0 + lr, N - 1);
+    const bf16* p = Q + (tokb + (rev_i ? N - 1 - qr : qr)) * ldq + (size_t)h * DK + 8 * hh;
 #pragma unroll
     for (int s = 0; s < DK / 16; ++s) qf[s] = load_frag(p + 16 * s);
   }
@@ -1019,7 +1036,7 @@ __global__ __launch_bounds__(256) void k_chunk_dl(
     for (int r = 0; r < 16; ++r) {
       const int qq = q0 + 8 * (r >> 2) + 4 * hh + (r & 3);
       if (qq < N) {
-        bf16* op = O + (tokb + (rev ? N - 1 - qq : qq)) * ldo + (size_t)h * DV + lr;
+        bf16* op = O + (tokb + (rev_o ? N - 1 - qq : qq)) * ldo + (size_t)h * DV + lr;
 #pragma unroll
         for (int j = 0; j < DV / 32; ++j) {
           const float sw = swish_fast(RawElt<bf16>::value(graw[r][j]));
@@ -1032,7 +1049,7 @@ __global__ __launch_bounds__(256) void k_chunk_dl(
     for (int r = 0; r < 16; ++r) {
       const int qq = q0 + 8 * (r >> 2) + 4 * hh + (r & 3);
       if (qq < N) {
-        bf16* op = O + (tokb + (rev ? N - 1 - qq : qq)) * ldo + (size_t)h * DV + lr;
+        bf16* op = O + (tokb + (rev_o ? N - 1 - qq : qq)) * ldo + (size_t)h * DV + lr;
 #pragma unroll
         for (int j = 0; j < DV / 32; ++j) op[32 * j] = (bf16)acc[j][r];
       }
@@ -1053,12 +1070,12 @@ static void launch_dl(const ChunkArgs& a, int chunk, int NC, int TPC, int has_si
     hipLaunchKernelGGL((k_chunk_dl<DK, DV, STATE, true>), grid, dim3(256), 0, st, (const bf16*)a.Q,
                        (const bf16*)a.K, (const bf16*)a.V, a.ldq, a.ldk, a.ldv, (const bf16*)a.Rx, has_sin,
                        (const bf16*)a.G, a.ldg, (bf16*)a.O, a.ldo, BH, a.seqlen, a.heads, chunk, NC, TPC, a.scale,
-                       a.eps, tab, a.rev_out ? 1 : 0);
+                       a.eps, tab, (a.rev_out ? 1 : 0) | (a.rev_in ? 2 : 0));
   else
     hipLaunchKernelGGL((k_chunk_dl<DK, DV, STATE, false>), grid, dim3(256), 0, st, (const bf16*)a.Q,
                        (const bf16*)a.K, (const bf16*)a.V, a.ldq, a.ldk, a.ldv, (const bf16*)a.Rx, has_sin,
                        (const bf16*)nullptr, (int64_t)0, (bf16*)a.O, a.ldo, BH, a.seqlen, a.heads, chunk, NC, TPC,
-                       a.scale, a.eps, tab, a.rev_out ? 1 : 0);
+                       a.scale, a.eps, tab, (a.rev_out ? 1 : 0) | (a.rev_in ? 2 : 0));
 }
 
 template <class T, int DK, int DV, int NW, bool STATE>
@@ -1070,12 +1087,12 @@ static void launch_out(const ChunkArgs& a, int chunk, int NC, int TPC, int has_s
     hipLaunchKernelGGL((k_chunk_out<T, DK, DV, NW, STATE, true>), grid, dim3(64 * NW), 0, st, (const T*)a.Q,
                        (const T*)a.K, (const T*)a.V, a.ldq, a.ldk, a.ldv, (const T*)a.Rx, has_sin, (const T*)a.G,
                        a.ldg, (T*)a.O, a.ldo, BH, a.seqlen, a.heads, chunk, NC, TPC, a.scale, a.eps, tab,
-                       a.rev_out ? 1 : 0);
+                       (a.rev_out ? 1 : 0) | (a.rev_in ? 2 : 0));
   else
     hipLaunchKernelGGL((k_chunk_out<T, DK, DV, NW, STATE, false>), grid, dim3(64 * NW), 0, st, (const T*)a.Q,
                        (const T*)a.K, (const T*)a.V, a.ldq, a.ldk, a.ldv, (const T*)a.Rx, has_sin,
                        (const T*)nullptr, (int64_t)0, (T*)a.O, a.ldo, BH, a.seqlen, a.heads, chunk, NC, TPC,
-                       a.scale, a.eps, tab, a.rev_out ? 1 : 0);
+                       a.scale, a.eps, tab, (a.rev_out ? 1 : 0) | (a.rev_in ? 2 : 0));
 }
 
 template <class T, int DK, int DV>
@@ -1089,7 +1106,7 @@ static hipError_t run_chunkwise(const ChunkArgs& a, const HeadTab& tab, hipStrea
     TraceScope ts("k_chunk_state", st);
     dim3 grid(((BH * NC + 7) / 8) * 8 * (DV / TS) * (DK / TS));
     hipLaunchKernelGGL((k_chunk_state<T, DK, DV>), grid, dim3(256), 0, st, (const T*)a.K, (const T*)a.V,
-                       a.ldk, a.ldv, (T*)a.dR, BH, N, H, Cn, NC, tab);
+                       a.ldk, a.ldv, (T*)a.dR, BH, N, H, Cn, NC, tab, a.rev_in ? 1 : 0);
   }
   {
     TraceScope ts("k_chunk_scan", st);

@@ -134,20 +134,14 @@ ChunkWs chunk_ws_layout(msr_dtype dt, const msr_dims& d, int32_t chunk, bool rop
 // inputs and the two state seeds.
 struct BwdWs {
   ChunkWs cw;
-  size_t chunk = 0, rq = 0, rk = 0, rv = 0, rdo = 0, sin_t = 0, dso = 0, total = 0;
+  size_t chunk = 0, sin_t = 0, dso = 0, total = 0;
 };
 BwdWs bwd_ws_layout(msr_dtype dt, const msr_dims& d, int32_t chunk, bool rope) {
   BwdWs w;
-  const size_t es = elt_size(dt);
-  const size_t rows = (size_t)d.batch * d.seqlen * d.heads * d.d_k * es;
   const size_t state = (size_t)d.batch * d.heads * d.d_k * d.d_v * sizeof(float);
   w.cw = chunk_ws_layout(dt, d, chunk, rope, true);
   size_t off = 0;
   w.chunk = off; off += align_up(w.cw.total);
-  w.rq = off; off += align_up(rows);
-  w.rk = off; off += align_up(rows);
-  w.rv = off; off += align_up(rows);
-  w.rdo = off; off += align_up(rows);
   w.sin_t = off; off += align_up(state);
   w.dso = off; off += align_up(state);
   w.total = off;
@@ -454,7 +448,6 @@ msr_status msr_chunkwise_bwd(msr_dtype dtype, msr_dims d, int32_t chunk, const d
   void* cws = at<void>(workspace, w.chunk);
   if (rope && (s = rotate_qk(dtype, d, rope_base, pos0, Q, K, cws, w.cw, st, &Q, &K))) return s;
   const Elt e = dtype == MSR_BF16 ? kBF16 : kF32;
-  const size_t es = elt_size(dtype);
   const int64_t ld = (int64_t)d.heads * d.d_k;   // d_k == d_v: one token stride for every tensor
   const HeadTab tab = make_tab(gamma, d.heads, chunk, d.seqlen);
   float* sin_t = at<float>(workspace, w.sin_t);
@@ -468,6 +461,8 @@ msr_status msr_chunkwise_bwd(msr_dtype dtype, msr_dims d, int32_t chunk, const d
     err = launch_state_xform(dS_out, dso, nbh, d.heads, d.d_k, d.d_v, false, hs, st);
   }
   if (err != hipSuccess) return from_hip(err, "msr_chunkwise_bwd(state seeds)");
+  // rev: the pass runs on the time-reversed sequence, reading its Q, K, V
+  // rows backwards and writing its output rows back in forward order
   auto pass = [&](const void* q, const void* k, const void* v, void* o, const float* sin, float* sout, bool rev,
                   bool reuse = false, bool seeded = false) {
     ChunkArgs a{};
@@ -481,6 +476,7 @@ msr_status msr_chunkwise_bwd(msr_dtype dtype, msr_dims d, int32_t chunk, const d
     a.dR = at<void>(cws, w.cw.dr);
     a.Rx = at<void>(cws, w.cw.rx);
     a.rev_out = rev;
+    a.rev_in = rev;
     a.reuse_rx = reuse;
     a.reuse_seeded = seeded;
     return launch_chunkwise(a, tab, st);
@@ -488,25 +484,9 @@ msr_status msr_chunkwise_bwd(msr_dtype dtype, msr_dims d, int32_t chunk, const d
   // dQ = causal retention of (dO, V, K) from S_in^T
   err = pass(dO, V, K, dQ, S_in ? sin_t : nullptr, nullptr, false);
   if (err != hipSuccess) return from_hip(err, "msr_chunkwise_bwd(dQ)");
-  // reversed K, Q, V, dO
-  RevJobs rj{};
-  const void* srcs[4] = {K, Q, V, dO};
-  const size_t offs[4] = {w.rk, w.rq, w.rv, w.rdo};
-  for (int j = 0; j < 4; ++j) {
-    rj.src[j] = static_cast<const char*>(srcs[j]);
-    rj.dst[j] = at<char>(workspace, offs[j]);
-    rj.lds[j] = rj.ldd[j] = ld * (int64_t)es;
-  }
-  const int row_bytes = (int)(ld * (int64_t)es);
-  err = launch_reverse_rows(rj, 4, d.batch, d.seqlen, row_bytes, st);
-  if (err != hipSuccess) return from_hip(err, "msr_chunkwise_bwd(reverse)");
-  const void* rk = at<void>(workspace, w.rk);
-  const void* rq = at<void>(workspace, w.rq);
-  const void* rv = at<void>(workspace, w.rv);
-  const void* rdo = at<void>(workspace, w.rdo);
   // dV = causal retention of (rev K, rev Q, rev dO), its rows written back in
   // forward time order; its last state gives dS_in
-  err = pass(rk, rq, rdo, dV, dS_out ? dso : nullptr, dS_in, true);
+  err = pass(K, Q, dO, dV, dS_out ? dso : nullptr, dS_in, true);
   if (err != hipSuccess) return from_hip(err, "msr_chunkwise_bwd(dV)");
   // dK = causal retention of (rev V, rev dO, rev Q), rows in forward order.
   // Its state is the transpose of the dV pass's, chunk by chunk (the sum of
@@ -515,7 +495,7 @@ msr_status msr_chunkwise_bwd(msr_dtype dtype, msr_dims d, int32_t chunk, const d
   const int NC = (d.seqlen + chunk - 1) / chunk;
   err = launch_transpose_blocks(e, at<void>(cws, w.cw.rx), d.d_k, (int64_t)nbh * NC, st);
   if (err != hipSuccess) return from_hip(err, "msr_chunkwise_bwd(state transpose)");
-  err = pass(rv, rdo, rq, dK, nullptr, nullptr, true, true, dS_out != nullptr);
+  err = pass(V, dO, Q, dK, nullptr, nullptr, true, true, dS_out != nullptr);
   if (err != hipSuccess) return from_hip(err, "msr_chunkwise_bwd(dK)");
   if (rope) {  // gradients with respect to the unrotated Q and K
     const float2* rtab = at<float2>(cws, w.cw.tab);

@@ -42,6 +42,7 @@ struct ChunkArgs {
   void* dR;                  // [B, H, NC, d_v, d_k] elt: each chunk's own state contribution
   void* Rx;                  // [B, H, NC, d_v, d_k] elt: R_{i-1} per chunk (aliases dR)
   bool rev_out;              // write output row t of each sequence to row seqlen-1-t
+  bool rev_in;               // read Q, K, V row t of each sequence from row seqlen-1-t
   // Rx already holds every chunk's R_{i-1} (state and scan kernels skipped);
   // reuse_seeded: chunk 0's R_{-1} is a seed (else zero)
   bool reuse_rx, reuse_seeded;
@@ -76,16 +77,6 @@ hipError_t launch_rglru_scan(Elt elt, const void* X, int64_t ldx, const void* G,
                              float c, const float* h0, float* hT, void* Y, int64_t ldy, int batch, int seqlen,
                              int width, hipStream_t stream);
 
-// Time reversal of token rows for the backward's anti-causal passes: up to
-// four jobs, byte row strides (multiples of 16), rows of row_bytes bytes
-// (a multiple of 16); dst row (b, seqlen-1-t) = src row (b, t).
-struct RevJobs {
-  const char* src[4];
-  char* dst[4];
-  int64_t lds[4], ldd[4];
-};
-hipError_t launch_reverse_rows(const RevJobs& jobs, int njobs, int batch, int seqlen, int row_bytes,
-                               hipStream_t stream);
 // In-place transpose of nblocks contiguous d x d blocks of elt (d % 32 == 0).
 hipError_t launch_transpose_blocks(Elt elt, void* base, int d, int64_t nblocks, hipStream_t stream);
 // Per-head factors of launch_state_xform.

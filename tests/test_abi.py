@@ -198,10 +198,11 @@ def test_workspace_sizes():
     assert base <= got <= base + up(8 * Bd * max(Hd * (2 * kd + 2 * vd), dm) * 4)
     assert msr.msr_layer_decode_workspace_bytes(1, 0, dm, Hd, kd, vd) == 0
     assert msr.msr_layer_decode_workspace_bytes(1, Bd, 100, Hd, kd, vd) == 0
-    # backward: the chunk workspace (with the rotated copies), four reversed inputs, two state seeds
+    # backward: the chunk workspace (with the rotated copies) and two state seeds (its reversed
+    # passes read their inputs backwards in place)
     cw = msr.msr_chunkwise_workspace_bytes(1, B, N, H, dk, dv, C, 1e4)
     assert msr.msr_chunkwise_bwd_workspace_bytes(1, B, N, H, dk, dv, C, 1e4) == (
-        up(cw) + 4 * up(B * N * H * dk * 2) + 2 * up(B * H * dk * dv * 4))
+        up(cw) + 2 * up(B * H * dk * dv * 4))
     # RetNet block: the layer's workspace, then LN(X) / LN(Y), Y and the hidden rows
     Bb, Nb, dmb, Hb, db, Cb, Fb = 2, 64, 256, 2, 64, 32, 512
     lay = msr.msr_layer_workspace_bytes(1, Bb, Nb, dmb, Hb, db, db, Cb)
