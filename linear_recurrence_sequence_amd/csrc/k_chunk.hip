@@ -47,11 +47,11 @@ struct StateCfg {
   static constexpr int STAGE = 2 * KB * LDT;                      // elements (V then K)
 };
 
-template <class T, int DK, int DV>
+template <class T, int DK, int DV, bool RV>
 __global__ __launch_bounds__(256) void k_chunk_state(const T* __restrict__ K, const T* __restrict__ V,
                                                      int64_t ldk, int64_t ldv, T* __restrict__ dR,
-                                                     int BH, int N, int H, int chunk, int NC, HeadTab tab,
-                                                     int rev_in) {
+                                                     int BH, int N, int H, int chunk, int NC, HeadTab tab) {
+  constexpr bool rev_in = RV;                        // read the sequence backwards
   using C = StateCfg<T, DK, DV>;
   constexpr int TS = C::TS, WT = C::WT, KB = C::KB, LDT = C::LDT, UNITS = C::UNITS, UPT = C::UPT;
   __shared__ __attribute__((aligned(16))) T smem[C::STAGE];
@@ -683,14 +683,15 @@ struct DlCfg {
   static_assert(LPW_KV == LPW_R, "equal copy counts per stage");
 };
 
-template <int DK, int DV, bool STATE, bool GN>
+template <int DK, int DV, bool STATE, bool GN, bool RV>
 __global__ __launch_bounds__(256) void k_chunk_dl(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V, int64_t ldq, int64_t ldk,
     int64_t ldv, const bf16* __restrict__ Rx, int has_sin, const bf16* __restrict__ G, int64_t ldg,
     bf16* __restrict__ O, int64_t ldo, int BH, int N, int H, int chunk, int NC, int TPC, float scale, float eps,
     HeadTab tab, int rev) {
-  // rev bit 0: output row t to row N - 1 - t; bit 1: Q, K, V row t from row N - 1 - t
-  const bool rev_o = rev & 1, rev_i = rev & 2;
+  // rev bit 0: output row t to row N - 1 - t; RV: Q, K, V row t from row N - 1 - t
+  const bool rev_o = rev & 1;
+  constexpr bool rev_i = RV;
   using C = DlCfg<DK, DV>;
   constexpr int KB = C::KB, SK = C::SK, NS = C::NS, AHEAD = C::AHEAD, RT = C::RT;
   constexpr int CPK = C::CPK, CPV = C::CPV, CPR = C::CPR;
@@ -1066,16 +1067,23 @@ static void launch_dl(const ChunkArgs& a, int chunk, int NC, int TPC, int has_si
   const int BH = a.batch * a.heads;
   const int U = NC * BH;
   dim3 grid(((U + 7) / 8) * 8 * TPC);
+  // the reversed reads (the backward's passes: no fused GroupNorm) are a
+  // compile-time variant, so the forward kernels carry none of their logic
   if (a.fuse_gn_gate)
-    hipLaunchKernelGGL((k_chunk_dl<DK, DV, STATE, true>), grid, dim3(256), 0, st, (const bf16*)a.Q,
+    hipLaunchKernelGGL((k_chunk_dl<DK, DV, STATE, true, false>), grid, dim3(256), 0, st, (const bf16*)a.Q,
                        (const bf16*)a.K, (const bf16*)a.V, a.ldq, a.ldk, a.ldv, (const bf16*)a.Rx, has_sin,
                        (const bf16*)a.G, a.ldg, (bf16*)a.O, a.ldo, BH, a.seqlen, a.heads, chunk, NC, TPC, a.scale,
-                       a.eps, tab, (a.rev_out ? 1 : 0) | (a.rev_in ? 2 : 0));
-  else
-    hipLaunchKernelGGL((k_chunk_dl<DK, DV, STATE, false>), grid, dim3(256), 0, st, (const bf16*)a.Q,
+                       a.eps, tab, a.rev_out ? 1 : 0);
+  else if (a.rev_in)
+    hipLaunchKernelGGL((k_chunk_dl<DK, DV, STATE, false, true>), grid, dim3(256), 0, st, (const bf16*)a.Q,
                        (const bf16*)a.K, (const bf16*)a.V, a.ldq, a.ldk, a.ldv, (const bf16*)a.Rx, has_sin,
                        (const bf16*)nullptr, (int64_t)0, (bf16*)a.O, a.ldo, BH, a.seqlen, a.heads, chunk, NC, TPC,
-                       a.scale, a.eps, tab, (a.rev_out ? 1 : 0) | (a.rev_in ? 2 : 0));
+                       a.scale, a.eps, tab, a.rev_out ? 1 : 0);
+  else
+    hipLaunchKernelGGL((k_chunk_dl<DK, DV, STATE, false, false>), grid, dim3(256), 0, st, (const bf16*)a.Q,
+                       (const bf16*)a.K, (const bf16*)a.V, a.ldq, a.ldk, a.ldv, (const bf16*)a.Rx, has_sin,
+                       (const bf16*)nullptr, (int64_t)0, (bf16*)a.O, a.ldo, BH, a.seqlen, a.heads, chunk, NC, TPC,
+                       a.scale, a.eps, tab, a.rev_out ? 1 : 0);
 }
 
 template <class T, int DK, int DV, int NW, bool STATE>
@@ -1105,8 +1113,12 @@ static hipError_t run_chunkwise(const ChunkArgs& a, const HeadTab& tab, hipStrea
   {
     TraceScope ts("k_chunk_state", st);
     dim3 grid(((BH * NC + 7) / 8) * 8 * (DV / TS) * (DK / TS));
-    hipLaunchKernelGGL((k_chunk_state<T, DK, DV>), grid, dim3(256), 0, st, (const T*)a.K, (const T*)a.V,
-                       a.ldk, a.ldv, (T*)a.dR, BH, N, H, Cn, NC, tab, a.rev_in ? 1 : 0);
+    if (a.rev_in)
+      hipLaunchKernelGGL((k_chunk_state<T, DK, DV, true>), grid, dim3(256), 0, st, (const T*)a.K, (const T*)a.V,
+                         a.ldk, a.ldv, (T*)a.dR, BH, N, H, Cn, NC, tab);
+    else
+      hipLaunchKernelGGL((k_chunk_state<T, DK, DV, false>), grid, dim3(256), 0, st, (const T*)a.K, (const T*)a.V,
+                         a.ldk, a.ldv, (T*)a.dR, BH, N, H, Cn, NC, tab);
   }
   {
     TraceScope ts("k_chunk_scan", st);
@@ -1157,6 +1169,7 @@ static hipError_t run_parallel(const ChunkArgs& a, const HeadTab& tab, hipStream
   if (a.d_k == 256 && a.d_v == 256) return FN<T, 256, 256>(__VA_ARGS__);
 
 hipError_t launch_chunkwise(const ChunkArgs& a, const HeadTab& tab, hipStream_t st) {
+  if (a.fuse_gn_gate && a.rev_in) return hipErrorInvalidValue;   // no reversed variant of the fused epilogue
   if (a.elt == kBF16) {
     MSR_DISPATCH_DIMS(run_chunkwise, bf16, a, tab, st)
     if (a.d_k == 256 && a.d_v == 512) return run_chunkwise<bf16, 256, 512>(a, tab, st);
