@@ -681,15 +681,19 @@ struct DlCfg {
   static constexpr int AHEAD = NS - 1;
   static_assert(NS == 4 && AHEAD == 3, "four ring slots, three stages in flight");
   static_assert(LPW_KV == LPW_R, "equal copy counts per stage");
+  // R_{i-1} itself ([d_k][d_v]) as the slab: SK rows of the V tile's stride
+  static constexpr int RSLT = r64(SK * SPV);
+  static_assert(RSLT / 64 <= 4 * LPW_KV, "a row slab fits the stage's copies");
 };
 
-template <int DK, int DV, bool STATE, bool GN, bool RV>
+template <int DK, int DV, bool STATE, bool GN, bool RV, bool RS>
 __global__ __launch_bounds__(256) void k_chunk_dl(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V, int64_t ldq, int64_t ldk,
     int64_t ldv, const bf16* __restrict__ Rx, int has_sin, const bf16* __restrict__ G, int64_t ldg,
     bf16* __restrict__ O, int64_t ldo, int BH, int N, int H, int chunk, int NC, int TPC, float scale, float eps,
     HeadTab tab, int rev) {
-  // rev bit 0: output row t to row N - 1 - t; RV: Q, K, V row t from row N - 1 - t
+  // rev bit 0: output row t to row N - 1 - t; RV: Q, K, V row t from row N - 1 - t;
+  // RS: Rx holds R_{i-1} itself ([DK][DV] per chunk) rather than its transpose
   const bool rev_o = rev & 1;
   constexpr bool rev_i = RV;
   using C = DlCfg<DK, DV>;
@@ -755,8 +759,14 @@ __global__ __launch_bounds__(256) void k_chunk_dl(
   for (int t = 0; t < C::LPW_KV; ++t) okv[t] = kv_off(t, KB - 1);
 #pragma unroll
   for (int t = 0; t < C::LPW_R; ++t) {
-    const int u = (wave * C::LPW_R + t) * 64 + lane, row = u / C::SPR, c = u % C::SPR;
-    orr[t] = row < DV && c < CPR ? (uint32_t)((row * DK + 8 * c) * 2) : 0u;
+    const int u = (wave * C::LPW_R + t) * 64 + lane;
+    if (RS) {                                      // rows of R_{i-1}: SK x DV, stride SPV
+      const int row = u / C::SPV, c = u % C::SPV;
+      orr[t] = row < SK && c < CPV ? (uint32_t)((row * DV + 8 * c) * 2) : 0u;
+    } else {                                       // rows of R^T: DV x SK, stride SPR
+      const int row = u / C::SPR, c = u % C::SPR;
+      orr[t] = row < DV && c < CPR ? (uint32_t)((row * DK + 8 * c) * 2) : 0u;
+    }
   }
   // The copies of one stage: wave-uniform source bases and LDS slot, and
   // this lane's offsets.  Stages past the last one copy the last stage
@@ -767,7 +777,7 @@ __global__ __launch_bounds__(256) void k_chunk_dl(
     const int idx = min(g, nst - 1);
     c.dst = slot(g) + wave * C::LPW_KV * 512;
     if (idx < nR) {
-      c.src[0] = c.src[1] = Rt + idx * SK;
+      c.src[0] = c.src[1] = Rt + idx * SK * (RS ? DV : 1);
 #pragma unroll
       for (int t = 0; t < C::LPW_KV; ++t) c.off[t] = orr[t];
     } else {
@@ -818,13 +828,30 @@ __global__ __launch_bounds__(256) void k_chunk_dl(
   // ---- Q R_{i-1} slab: acc[j] += Q[:, slab] R^T[32 j .., slab]^T; the rows
   // are scaled by scale * xi once all slabs are in (they come first) ----
   constexpr int NJ = DV / 32;
+  const int g4 = lane >> 4, i4 = lane & 15, cq = g4 & 1, jj4 = i4 >> 2, q4 = i4 & 3;
   auto compute_R = [&](const bf16* sR, const Frag<bf16>* qs, const Cp& cn) {
     constexpr int T = (SK / 16) * NJ;
     static_assert(T >= C::LPW_KV, "one copy per step at most");
     const bf16* rb0 = sR + lr * (8 * C::SPR) + 8 * hh;
+    // RS: the transposing read of V, on slab rows 16 s + 8 hh + 4 pp + jj4
+    // (the Q fragment's column order), chunk 4 j + 2 cq + q4 / 2
+    const bf16* rt0 = sR + (8 * hh + jj4) * (8 * C::SPV) + 8 * (2 * cq + (q4 >> 1)) + 4 * (q4 & 1);
     auto rd = [&](int t) {
-      const int s = t / NJ, j = t % NJ;            // row 32 j + lr, chunk 2 s + hh
-      return load_frag(rb0 + j * (32 * 8 * C::SPR) + 16 * s);
+      const int s = t / NJ, j = t % NJ;            // R^T row 32 j + lr, chunk 2 s + hh
+      if constexpr (RS) {
+        Frag<bf16> f;
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp) {
+          const bf16x4 r4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+              (__attribute__((address_space(3))) bf16x4*)(const lds_char*)(rt0 + (16 * s + 4 * pp) * (8 * C::SPV) +
+                                                                            32 * j));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) f.v[4 * pp + e] = r4[e];
+        }
+        return f;
+      } else {
+        return load_frag(rb0 + j * (32 * 8 * C::SPR) + 16 * s);
+      }
     };
     Frag<bf16> rb[3];
     rb[0] = rd(0);
@@ -839,7 +866,7 @@ __global__ __launch_bounds__(256) void k_chunk_dl(
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-      if (t + 2 < T) __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
+      if (t + 2 < T) __builtin_amdgcn_sched_group_barrier(SG_DS_READ, RS ? 2 : 1, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -858,7 +885,6 @@ __global__ __launch_bounds__(256) void k_chunk_dl(
   // P V uses the accumulator as the A operand; V fragments are read in that
   // key order (transposing read).
   constexpr int NSS = DK / 16, NPV = DV / 16, TKV = NSS > NPV ? NSS : NPV;
-  const int g4 = lane >> 4, i4 = lane & 15, cq = g4 & 1, jj4 = i4 >> 2, q4 = i4 & 3;
   const int kofs = lr * (8 * C::SPK) + 8 * hh;    // K: row lr, chunk 2 t + hh
   const int vofs = (4 * hh + jj4) * (8 * C::SPV) + 8 * (2 * cq + (q4 >> 1)) + 4 * (q4 & 1);
   auto rdK = [&](const bf16* sK, int t) { return load_frag(sK + kofs + 16 * t); };
@@ -1070,17 +1096,22 @@ static void launch_dl(const ChunkArgs& a, int chunk, int NC, int TPC, int has_si
   // the reversed reads (the backward's passes: no fused GroupNorm) are a
   // compile-time variant, so the forward kernels carry none of their logic
   if (a.fuse_gn_gate)
-    hipLaunchKernelGGL((k_chunk_dl<DK, DV, STATE, true, false>), grid, dim3(256), 0, st, (const bf16*)a.Q,
+    hipLaunchKernelGGL((k_chunk_dl<DK, DV, STATE, true, false, false>), grid, dim3(256), 0, st, (const bf16*)a.Q,
                        (const bf16*)a.K, (const bf16*)a.V, a.ldq, a.ldk, a.ldv, (const bf16*)a.Rx, has_sin,
                        (const bf16*)a.G, a.ldg, (bf16*)a.O, a.ldo, BH, a.seqlen, a.heads, chunk, NC, TPC, a.scale,
                        a.eps, tab, a.rev_out ? 1 : 0);
+  else if (STATE && a.rx_kv)   // with rev_in (checked by launch_chunkwise)
+    hipLaunchKernelGGL((k_chunk_dl<DK, DV, STATE, false, true, STATE>), grid, dim3(256), 0, st, (const bf16*)a.Q,
+                       (const bf16*)a.K, (const bf16*)a.V, a.ldq, a.ldk, a.ldv, (const bf16*)a.Rx, has_sin,
+                       (const bf16*)nullptr, (int64_t)0, (bf16*)a.O, a.ldo, BH, a.seqlen, a.heads, chunk, NC, TPC,
+                       a.scale, a.eps, tab, a.rev_out ? 1 : 0);
   else if (a.rev_in)
-    hipLaunchKernelGGL((k_chunk_dl<DK, DV, STATE, false, true>), grid, dim3(256), 0, st, (const bf16*)a.Q,
+    hipLaunchKernelGGL((k_chunk_dl<DK, DV, STATE, false, true, false>), grid, dim3(256), 0, st, (const bf16*)a.Q,
                        (const bf16*)a.K, (const bf16*)a.V, a.ldq, a.ldk, a.ldv, (const bf16*)a.Rx, has_sin,
                        (const bf16*)nullptr, (int64_t)0, (bf16*)a.O, a.ldo, BH, a.seqlen, a.heads, chunk, NC, TPC,
                        a.scale, a.eps, tab, a.rev_out ? 1 : 0);
   else
-    hipLaunchKernelGGL((k_chunk_dl<DK, DV, STATE, false, false>), grid, dim3(256), 0, st, (const bf16*)a.Q,
+    hipLaunchKernelGGL((k_chunk_dl<DK, DV, STATE, false, false, false>), grid, dim3(256), 0, st, (const bf16*)a.Q,
                        (const bf16*)a.K, (const bf16*)a.V, a.ldq, a.ldk, a.ldv, (const bf16*)a.Rx, has_sin,
                        (const bf16*)nullptr, (int64_t)0, (bf16*)a.O, a.ldo, BH, a.seqlen, a.heads, chunk, NC, TPC,
                        a.scale, a.eps, tab, a.rev_out ? 1 : 0);
@@ -1168,8 +1199,17 @@ static hipError_t run_parallel(const ChunkArgs& a, const HeadTab& tab, hipStream
   if (a.d_k == 128 && a.d_v == 128) return FN<T, 128, 128>(__VA_ARGS__);        \
   if (a.d_k == 256 && a.d_v == 256) return FN<T, 256, 256>(__VA_ARGS__);
 
+bool chunk_out_direct(Elt elt, int d_k, int d_v, int chunk) {
+  const bool dims = (d_k == 64 && d_v == 64) || (d_k == 128 && d_v == 128) || (d_k == 256 && d_v == 256);
+  return elt == kBF16 && dims && chunk % 128 == 0;
+}
+
 hipError_t launch_chunkwise(const ChunkArgs& a, const HeadTab& tab, hipStream_t st) {
   if (a.fuse_gn_gate && a.rev_in) return hipErrorInvalidValue;   // no reversed variant of the fused epilogue
+  // R_{i-1} itself in Rx: only stored states (no scan writing the transpose),
+  // read by the reversed direct-copy variant
+  if (a.rx_kv && !(a.reuse_rx && a.rev_in && chunk_out_direct(a.elt, a.d_k, a.d_v, a.chunk)))
+    return hipErrorInvalidValue;
   if (a.elt == kBF16) {
     MSR_DISPATCH_DIMS(run_chunkwise, bf16, a, tab, st)
     if (a.d_k == 256 && a.d_v == 512) return run_chunkwise<bf16, 256, 512>(a, tab, st);

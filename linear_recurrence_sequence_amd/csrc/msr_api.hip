@@ -464,7 +464,7 @@ msr_status msr_chunkwise_bwd(msr_dtype dtype, msr_dims d, int32_t chunk, const d
   // rev: the pass runs on the time-reversed sequence, reading its Q, K, V
   // rows backwards and writing its output rows back in forward order
   auto pass = [&](const void* q, const void* k, const void* v, void* o, const float* sin, float* sout, bool rev,
-                  bool reuse = false, bool seeded = false) {
+                  bool reuse = false, bool seeded = false, bool rx_kv = false) {
     ChunkArgs a{};
     a.elt = e;
     a.d_k = d.d_k; a.d_v = d.d_v; a.batch = d.batch; a.seqlen = d.seqlen; a.heads = d.heads;
@@ -479,6 +479,7 @@ msr_status msr_chunkwise_bwd(msr_dtype dtype, msr_dims d, int32_t chunk, const d
     a.rev_in = rev;
     a.reuse_rx = reuse;
     a.reuse_seeded = seeded;
+    a.rx_kv = rx_kv;
     return launch_chunkwise(a, tab, st);
   };
   // dQ = causal retention of (dO, V, K) from S_in^T
@@ -491,11 +492,16 @@ msr_status msr_chunkwise_bwd(msr_dtype dtype, msr_dims d, int32_t chunk, const d
   // dK = causal retention of (rev V, rev dO, rev Q), rows in forward order.
   // Its state is the transpose of the dV pass's, chunk by chunk (the sum of
   // rev dO^T rev Q against rev Q^T rev dO, seeded with dS_out^T against
-  // dS_out), so it reuses those per-chunk states transposed in place.
-  const int NC = (d.seqlen + chunk - 1) / chunk;
-  err = launch_transpose_blocks(e, at<void>(cws, w.cw.rx), d.d_k, (int64_t)nbh * NC, st);
-  if (err != hipSuccess) return from_hip(err, "msr_chunkwise_bwd(state transpose)");
-  err = pass(V, dO, Q, dK, nullptr, nullptr, true, true, dS_out != nullptr);
+  // dS_out), so it reuses those per-chunk states: the direct-copy output
+  // kernel reads them as they are (with the transposing LDS read), the
+  // others after an in-place transpose.
+  const bool rx_kv = chunk_out_direct(e, d.d_k, d.d_v, chunk);
+  if (!rx_kv) {
+    const int NC = (d.seqlen + chunk - 1) / chunk;
+    err = launch_transpose_blocks(e, at<void>(cws, w.cw.rx), d.d_k, (int64_t)nbh * NC, st);
+    if (err != hipSuccess) return from_hip(err, "msr_chunkwise_bwd(state transpose)");
+  }
+  err = pass(V, dO, Q, dK, nullptr, nullptr, true, true, dS_out != nullptr, rx_kv);
   if (err != hipSuccess) return from_hip(err, "msr_chunkwise_bwd(dK)");
   if (rope) {  // gradients with respect to the unrotated Q and K
     const float2* rtab = at<float2>(cws, w.cw.tab);

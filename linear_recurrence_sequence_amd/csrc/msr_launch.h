@@ -46,7 +46,15 @@ struct ChunkArgs {
   // Rx already holds every chunk's R_{i-1} (state and scan kernels skipped);
   // reuse_seeded: chunk 0's R_{-1} is a seed (else zero)
   bool reuse_rx, reuse_seeded;
+  // with reuse_rx and rev_in, on the direct-copy path only (chunk_out_direct):
+  // Rx holds each chunk's R_{i-1} itself, [d_k rows][d_v cols], instead of
+  // its transpose
+  bool rx_kv;
 };
+
+// Whether the chunkwise form of these dims and chunk runs the bf16
+// direct-copy output kernel (the one that can read Rx as R_{i-1} itself).
+bool chunk_out_direct(Elt elt, int d_k, int d_v, int chunk);
 
 // Chunkwise retention: state contributions, fp32 scan, outputs.
 hipError_t launch_chunkwise(const ChunkArgs& a, const HeadTab& tab, hipStream_t stream);

@@ -37,8 +37,8 @@ def _check(name, got, ref, tol):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("d,N,chunk", [(64, 200, 64), (64, 31, 32), (128, 300, 128), (256, 257, 128),
-                                       (256, 520, 256)])
+@pytest.mark.parametrize("d,N,chunk", [(64, 200, 64), (64, 31, 32), (64, 400, 128), (128, 300, 128),
+                                       (256, 257, 128), (256, 520, 256)])
 def test_backward(dtype, d, N, chunk):
     import torch
     msr = _msr()
