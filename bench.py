@@ -239,14 +239,15 @@ def bench_core(B, N, H, d, C, steps, warmup, parallel=False, dv=None):
         tr = traced(fn, steps)
         nc = -(-N // C)
         states = B * H * nc * dk * dv * 2
-        res["kernels"] = {
+        work = {
             # Q, K read, V read, O written, R_{i-1} read
-            "k_chunk_out": roof("k_chunk_out", B * N * H * (C * (dk + dv) + 2 * dk * dv), "mfma", tr, steps,
-                                bytes_per_step=B * N * H * (2 * dk + 2 * dv) * 2 + states),
-            "k_chunk_state": roof("k_chunk_state", B * N * H * 2 * dk * dv, "mfma", tr, steps,
-                                  bytes_per_step=B * N * H * (dk + dv) * 2 + states),
-            "k_chunk_scan": roof("k_chunk_scan", 2 * states, "hbm", tr, steps),
+            "k_chunk_out": (B * N * H * (C * (dk + dv) + 2 * dk * dv), "mfma",
+                            B * N * H * (2 * dk + 2 * dv) * 2 + states),
+            "k_chunk_state": (B * N * H * 2 * dk * dv, "mfma", B * N * H * (dk + dv) * 2 + states),
+            "k_chunk_scan": (2 * states, "hbm", None),
         }
+        res["kernels"] = {n: roof(n, wk, bd, tr, steps, bytes_per_step=by) for n, (wk, bd, by) in work.items()
+                          if n in tr}
     return res
 
 
