@@ -196,7 +196,8 @@ __device__ __forceinline__ void store_n(bf16* p, const float* x) {
 // 4 elements per thread).
 template <class T, int DK, int DV, int TS>
 __global__ __launch_bounds__(256) void k_chunk_scan(const T* dR, T* Rx, const float* __restrict__ S_in,
-                                                    float* __restrict__ S_out, int H, int NC, HeadTab tab) {
+                                                    float* __restrict__ S_out, int H, int NC, HeadTab tab,
+                                                    HeadScale so) {
   constexpr int E = TS * TS / 256;   // elements per thread
   constexpr int NTV = DV / TS;
   constexpr int NT = NTV * (DK / TS);
@@ -264,8 +265,9 @@ __global__ __launch_bounds__(256) void k_chunk_scan(const T* dR, T* Rx, const fl
     for (int e = 0; e < E; ++e) sT[col + e][row] = R[e];
     __syncthreads();
     float* o = S_out + (size_t)bh * DK * DV + (size_t)(tk * TS + row) * DV + tv * TS + col;
+    const float c = so.c[h];
 #pragma unroll
-    for (int e = 0; e < E; ++e) o[e] = sT[row][col + e];
+    for (int e = 0; e < E; ++e) o[e] = c * sT[row][col + e];
   }
 }
 
@@ -1153,16 +1155,18 @@ static hipError_t run_chunkwise(const ChunkArgs& a, const HeadTab& tab, hipStrea
   }
   {
     TraceScope ts("k_chunk_scan", st);
+    HeadScale so;
+    for (int h = 0; h < H; ++h) so.c[h] = a.sout_scale ? a.sout_scale[h] : 1.0f;
     // few (batch, head) pairs (one long sequence per head): 32 x 32 tiles, so
     // that enough workgroups walk the chunks
     if (DK >= 64 && DV >= 64 && BH * (DV / 64) * (DK / 64) >= 1024) {
       dim3 grid(BH * (DV / 64) * (DK / 64));
       hipLaunchKernelGGL((k_chunk_scan<T, DK, DV, 64>), grid, dim3(256), 0, st, (const T*)a.dR, (T*)a.Rx,
-                         a.S_in, a.S_out, H, NC, tab);
+                         a.S_in, a.S_out, H, NC, tab, so);
     } else {
       dim3 grid(BH * (DV / 32) * (DK / 32));
       hipLaunchKernelGGL((k_chunk_scan<T, DK, DV, 32>), grid, dim3(256), 0, st, (const T*)a.dR, (T*)a.Rx,
-                         a.S_in, a.S_out, H, NC, tab);
+                         a.S_in, a.S_out, H, NC, tab, so);
     }
   }
   }

@@ -461,6 +461,9 @@ msr_status msr_chunkwise_bwd(msr_dtype dtype, msr_dims d, int32_t chunk, const d
     err = launch_state_xform(dS_out, dso, nbh, d.heads, d.d_k, d.d_v, false, hs, st);
   }
   if (err != hipSuccess) return from_hip(err, "msr_chunkwise_bwd(state seeds)");
+  // dS_in = s gamma_h * the dV pass's last state, scaled as the scan writes it
+  float ds_scale[kMaxHeads];
+  for (int h = 0; h < d.heads; ++h) ds_scale[h] = (float)((double)qk_scale * gamma[h]);
   // rev: the pass runs on the time-reversed sequence, reading its Q, K, V
   // rows backwards and writing its output rows back in forward order
   auto pass = [&](const void* q, const void* k, const void* v, void* o, const float* sin, float* sout, bool rev,
@@ -473,6 +476,7 @@ msr_status msr_chunkwise_bwd(msr_dtype dtype, msr_dims d, int32_t chunk, const d
     a.ldq = a.ldk = a.ldv = a.ldo = ld;
     a.scale = qk_scale;
     a.S_in = sin; a.S_out = sout;
+    a.sout_scale = sout ? ds_scale : nullptr;
     a.dR = at<void>(cws, w.cw.dr);
     a.Rx = at<void>(cws, w.cw.rx);
     a.rev_out = rev;
@@ -510,11 +514,7 @@ msr_status msr_chunkwise_bwd(msr_dtype dtype, msr_dims d, int32_t chunk, const d
     if (err == hipSuccess) err = launch_rope_apply(e, dK, ld, dK, ld, rows, d.seqlen, d.heads, d.d_k, rtab, st, true);
     if (err != hipSuccess) return from_hip(err, "msr_chunkwise_bwd(rotation)");
   }
-  if (dS_in) {
-    for (int h = 0; h < d.heads; ++h) hs.c[h] = (float)((double)qk_scale * gamma[h]);
-    err = launch_state_xform(dS_in, dS_in, nbh, d.heads, d.d_k, d.d_v, false, hs, st);
-  }
-  return from_hip(err, "msr_chunkwise_bwd(dS_in)");
+  return ok();
 }
 
 size_t msr_rglru_workspace_bytes(msr_dtype dtype, int32_t batch, int32_t seqlen, int32_t width) {

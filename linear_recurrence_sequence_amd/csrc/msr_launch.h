@@ -39,6 +39,7 @@ struct ChunkArgs {
   float scale, eps;
   bool fuse_gn_gate;
   const float* S_in; float* S_out;
+  const float* sout_scale;   // host array [heads]: S_out = sout_scale[h] * final state (null: factor 1)
   void* dR;                  // [B, H, NC, d_v, d_k] elt: each chunk's own state contribution
   void* Rx;                  // [B, H, NC, d_v, d_k] elt: R_{i-1} per chunk (aliases dR)
   bool rev_out;              // write output row t of each sequence to row seqlen-1-t
