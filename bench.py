@@ -269,11 +269,18 @@ def bench_backward(B, N, H, d, C, steps, warmup):
     flops = 3 * B * N * H * (C * 2 * d + 4 * d * d)
     t = gpu_time(fn, steps, warmup)
     tr = traced(fn, steps)
+    # with the forward's per-chunk states kept (msr_chunkwise_fwd_save, outside the timed region)
+    R = torch.empty(msr.msr_chunkwise_states_shape(B, N, H, d, d, C), dtype=torch.bfloat16, device="cuda")
+    msr.msr_chunkwise_fwd_save(Q, K, V, g, C, R, qk_scale=s)
+    fs = lambda: msr.msr_chunkwise_bwd_saved(Q, K, V, dO, g, C, R, qk_scale=s, dS_in=dS_in, dQ=dQ, dK=dK, dV=dV,
+                                             workspace=ws)
+    ts = gpu_time(fs, steps, warmup)
     res = {"batch": B, "seqlen": N, "heads": H, "d": d, "chunk": C, "ms_per_step": round(t * 1e3, 4),
            "tokens_per_s": round(B * N / t, 1), "tflops": round(flops / t / 1e12, 1),
            "mfma_frac": round(flops / t / PEAK_BF16, 4),
-           "trace_ms_per_step": {k: round(v[0] / steps * 1e3, 4) for k, v in tr.items()}}
-    del Q, K, V, dO, dQ, dK, dV, ws
+           "trace_ms_per_step": {k: round(v[0] / steps * 1e3, 4) for k, v in tr.items()},
+           "saved_states_ms_per_step": round(ts * 1e3, 4), "saved_states_tokens_per_s": round(B * N / ts, 1)}
+    del Q, K, V, dO, dQ, dK, dV, ws, R
     torch.cuda.empty_cache()
     return res
 

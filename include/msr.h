@@ -101,6 +101,21 @@ msr_status msr_chunkwise_fwd(msr_dtype dtype, msr_dims dims, int32_t chunk,
 size_t msr_chunkwise_workspace_bytes(msr_dtype dtype, msr_dims dims, int32_t chunk,
                                      float rope_base);
 
+/* msr_chunkwise_fwd that also keeps, for msr_chunkwise_bwd_saved, the state
+ * each chunk starts from ([RN-zh] Eq. (7): R_{i-1}, with R_{-1} = S_in or
+ * zeros): R_chunks [batch, heads, ceil(seqlen / chunk), d_v, d_k] (dtype,
+ * caller-owned device memory, non-NULL unless there are no tokens) receives
+ * R_{i-1}^T of every chunk i, the states of the rotated K when rope_base >
+ * 0.  Costs nothing extra: the forward computes these states in any case
+ * and writes them there instead of into the workspace.  Arguments,
+ * workspace and errors otherwise as msr_chunkwise_fwd. */
+msr_status msr_chunkwise_fwd_save(msr_dtype dtype, msr_dims dims, int32_t chunk,
+                                  const double* gamma, float rope_base, int64_t pos0,
+                                  float qk_scale, const void* Q, const void* K,
+                                  const void* V, const float* S_in, float* S_out,
+                                  void* R_chunks, void* O, void* workspace,
+                                  size_t ws_bytes, void* stream);
+
 /* Backward of the chunkwise (equivalently parallel) form, for training
  * ([RN-zh] section "Retention 網路總體結構": training runs the parallel
  * form, Eq. (5), and the chunkwise form, Eq. (7)).  With Q, K rotated as in
@@ -129,6 +144,24 @@ msr_status msr_chunkwise_bwd(msr_dtype dtype, msr_dims dims, int32_t chunk,
                              void* stream);
 size_t msr_chunkwise_bwd_workspace_bytes(msr_dtype dtype, msr_dims dims, int32_t chunk,
                                          float rope_base);
+
+/* msr_chunkwise_bwd given the forward's per-chunk states R_chunks, as
+ * msr_chunkwise_fwd_save left them for the same dtype, dims, chunk, gamma,
+ * rope_base, pos0, Q, K, V and S_in (not checked; read only).  The dQ term
+ * is the causal retention of (dO, V, K) seeded with S_in^T, whose per-chunk
+ * states are exactly those transposed (sums of v^T k against k^T v), so it
+ * reads them instead of recomputing them -- on the bf16 path with d_k ==
+ * d_v in {64, 128, 256} and chunk a multiple of 128; elsewhere R_chunks is
+ * not read and the result is that of msr_chunkwise_bwd.  Arguments,
+ * workspace and errors otherwise as msr_chunkwise_bwd; R_chunks must be
+ * non-NULL unless there are no tokens. */
+msr_status msr_chunkwise_bwd_saved(msr_dtype dtype, msr_dims dims, int32_t chunk,
+                                   const double* gamma, float rope_base, int64_t pos0,
+                                   float qk_scale, const void* Q, const void* K,
+                                   const void* V, const void* dO, const float* S_in,
+                                   const float* dS_out, const void* R_chunks, void* dQ,
+                                   void* dK, void* dV, float* dS_in, void* workspace,
+                                   size_t ws_bytes, void* stream);
 
 /* RG-LRU, the gated diagonal linear recurrence of the page "Griffin ：將門控
  * 線性循環與局部注意力混合以實現高效的語言模型", section "實門線性循環單元

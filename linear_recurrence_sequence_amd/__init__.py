@@ -17,8 +17,9 @@ import os
 __all__ = [
     "MSR_F32", "MSR_BF16", "MsrError", "MsrLibraryMissing", "library_path", "lib",
     "msr_parallel_fwd", "msr_parallel_workspace_bytes",
-    "msr_chunkwise_fwd", "msr_chunkwise_workspace_bytes",
-    "msr_chunkwise_bwd", "msr_chunkwise_bwd_workspace_bytes", "msr_rglru_fwd", "msr_rglru_workspace_bytes",
+    "msr_chunkwise_fwd", "msr_chunkwise_workspace_bytes", "msr_chunkwise_fwd_save", "msr_chunkwise_states_shape",
+    "msr_chunkwise_bwd", "msr_chunkwise_bwd_workspace_bytes", "msr_chunkwise_bwd_saved",
+    "msr_rglru_fwd", "msr_rglru_workspace_bytes",
     "msr_recurrent_step", "msr_layer_fwd", "msr_layer_workspace_bytes",
     "msr_layer_decode_step", "msr_layer_decode_workspace_bytes",
     "msr_retnet_block_fwd", "msr_retnet_block_workspace_bytes",
@@ -29,7 +30,8 @@ __all__ = [
 MSR_F32, MSR_BF16 = 0, 1
 EXPORTS = (
     "msr_parallel_fwd", "msr_parallel_workspace_bytes", "msr_chunkwise_fwd",
-    "msr_chunkwise_workspace_bytes", "msr_chunkwise_bwd", "msr_chunkwise_bwd_workspace_bytes",
+    "msr_chunkwise_workspace_bytes", "msr_chunkwise_fwd_save", "msr_chunkwise_bwd",
+    "msr_chunkwise_bwd_workspace_bytes", "msr_chunkwise_bwd_saved",
     "msr_rglru_fwd", "msr_rglru_workspace_bytes", "msr_recurrent_step", "msr_layer_fwd",
     "msr_layer_workspace_bytes", "msr_layer_decode_step", "msr_layer_decode_workspace_bytes",
     "msr_retnet_block_fwd", "msr_retnet_block_workspace_bytes", "msr_status_str", "msr_last_error", "msr_trace_enable", "msr_trace_count", "msr_trace_get",
@@ -79,6 +81,10 @@ def lib():
         "msr_chunkwise_fwd": (_I32, [_I32, MsrDims, _I32, _DP, _F, _I64, _F, _P, _P, _P, _P, _P, _P, _P,
                                      _SZ, _P]),
         "msr_chunkwise_workspace_bytes": (_SZ, [_I32, MsrDims, _I32, _F]),
+        "msr_chunkwise_fwd_save": (_I32, [_I32, MsrDims, _I32, _DP, _F, _I64, _F, _P, _P, _P, _P, _P, _P, _P,
+                                          _P, _SZ, _P]),
+        "msr_chunkwise_bwd_saved": (_I32, [_I32, MsrDims, _I32, _DP, _F, _I64, _F, _P, _P, _P, _P, _P, _P, _P,
+                                           _P, _P, _P, _P, _P, _SZ, _P]),
         "msr_chunkwise_bwd": (_I32, [_I32, MsrDims, _I32, _DP, _F, _I64, _F, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                      _P, _P, _SZ, _P]),
         "msr_chunkwise_bwd_workspace_bytes": (_SZ, [_I32, MsrDims, _I32, _F]),
@@ -238,6 +244,31 @@ def msr_chunkwise_fwd(Q, K, V, gamma, chunk, *, rope_base=0.0, pos0=0, qk_scale=
     return O
 
 
+def msr_chunkwise_states_shape(B, N, H, d_k, d_v, chunk):
+    """Shape of the per-chunk states of msr_chunkwise_fwd_save: [B, H, NC, d_v, d_k]."""
+    return (B, H, -(-N // chunk), d_v, d_k)
+
+
+def msr_chunkwise_fwd_save(Q, K, V, gamma, chunk, R_chunks, *, rope_base=0.0, pos0=0, qk_scale=1.0, S_in=None,
+                           S_out=None, O=None, workspace=None, stream=None):
+    """msr_chunkwise_fwd that also writes every chunk's starting state
+    (transposed) into R_chunks (msr_chunkwise_states_shape, Q's dtype).
+    Returns O."""
+    B, N, H, dk = Q.shape
+    dv = V.shape[-1]
+    dt = _dtype_code(Q)
+    if O is None:
+        O = _torch().empty((B, N, H, dv), dtype=Q.dtype, device=Q.device)
+    _, gp = g = _gamma(gamma, H)
+    dims = MsrDims(B, N, H, dk, dv)
+    ws, wsb = _workspace(lib().msr_chunkwise_workspace_bytes(dt, dims, chunk, rope_base), workspace, Q.device)
+    _check("msr_chunkwise_fwd_save", lib().msr_chunkwise_fwd_save(dt, dims, chunk, gp, rope_base, pos0, qk_scale,
+                                                                  _ptr(Q), _ptr(K), _ptr(V), _ptr(S_in),
+                                                                  _ptr(S_out), _ptr(R_chunks), _ptr(O), _ptr(ws),
+                                                                  wsb, _stream(stream)))
+    return O
+
+
 def msr_chunkwise_bwd_workspace_bytes(dtype: int, batch, seqlen, heads, d_k, d_v, chunk, rope_base) -> int:
     return lib().msr_chunkwise_bwd_workspace_bytes(dtype, MsrDims(batch, seqlen, heads, d_k, d_v), chunk,
                                                    rope_base)
@@ -262,6 +293,27 @@ def msr_chunkwise_bwd(Q, K, V, dO, gamma, chunk, *, rope_base=0.0, pos0=0, qk_sc
                                                         _ptr(K), _ptr(V), _ptr(dO), _ptr(S_in), _ptr(dS_out),
                                                         _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(dS_in), _ptr(ws), wsb,
                                                         _stream(stream)))
+    return dQ, dK, dV
+
+
+def msr_chunkwise_bwd_saved(Q, K, V, dO, gamma, chunk, R_chunks, *, rope_base=0.0, pos0=0, qk_scale=1.0,
+                            S_in=None, dS_out=None, dS_in=None, dQ=None, dK=None, dV=None, workspace=None,
+                            stream=None):
+    """msr_chunkwise_bwd with the forward's per-chunk states (from
+    msr_chunkwise_fwd_save with the same arguments).  Returns (dQ, dK, dV)."""
+    B, N, H, dk = Q.shape
+    dv = V.shape[-1]
+    dt = _dtype_code(Q)
+    t = _torch()
+    dQ = t.empty_like(Q) if dQ is None else dQ
+    dK = t.empty_like(K) if dK is None else dK
+    dV = t.empty_like(V) if dV is None else dV
+    _, gp = g = _gamma(gamma, H)
+    dims = MsrDims(B, N, H, dk, dv)
+    ws, wsb = _workspace(lib().msr_chunkwise_bwd_workspace_bytes(dt, dims, chunk, rope_base), workspace, Q.device)
+    _check("msr_chunkwise_bwd_saved", lib().msr_chunkwise_bwd_saved(
+        dt, dims, chunk, gp, rope_base, pos0, qk_scale, _ptr(Q), _ptr(K), _ptr(V), _ptr(dO), _ptr(S_in),
+        _ptr(dS_out), _ptr(R_chunks), _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(dS_in), _ptr(ws), wsb, _stream(stream)))
     return dQ, dK, dV
 
 

@@ -1102,7 +1102,12 @@ static void launch_dl(const ChunkArgs& a, int chunk, int NC, int TPC, int has_si
                        (const bf16*)a.K, (const bf16*)a.V, a.ldq, a.ldk, a.ldv, (const bf16*)a.Rx, has_sin,
                        (const bf16*)a.G, a.ldg, (bf16*)a.O, a.ldo, BH, a.seqlen, a.heads, chunk, NC, TPC, a.scale,
                        a.eps, tab, a.rev_out ? 1 : 0);
-  else if (STATE && a.rx_kv)   // with rev_in (checked by launch_chunkwise)
+  else if (STATE && a.rx_kv && !a.rev_in)
+    hipLaunchKernelGGL((k_chunk_dl<DK, DV, STATE, false, false, STATE>), grid, dim3(256), 0, st, (const bf16*)a.Q,
+                       (const bf16*)a.K, (const bf16*)a.V, a.ldq, a.ldk, a.ldv, (const bf16*)a.Rx, has_sin,
+                       (const bf16*)nullptr, (int64_t)0, (bf16*)a.O, a.ldo, BH, a.seqlen, a.heads, chunk, NC, TPC,
+                       a.scale, a.eps, tab, a.rev_out ? 1 : 0);
+  else if (STATE && a.rx_kv)
     hipLaunchKernelGGL((k_chunk_dl<DK, DV, STATE, false, true, STATE>), grid, dim3(256), 0, st, (const bf16*)a.Q,
                        (const bf16*)a.K, (const bf16*)a.V, a.ldq, a.ldk, a.ldv, (const bf16*)a.Rx, has_sin,
                        (const bf16*)nullptr, (int64_t)0, (bf16*)a.O, a.ldo, BH, a.seqlen, a.heads, chunk, NC, TPC,
@@ -1211,8 +1216,8 @@ bool chunk_out_direct(Elt elt, int d_k, int d_v, int chunk) {
 hipError_t launch_chunkwise(const ChunkArgs& a, const HeadTab& tab, hipStream_t st) {
   if (a.fuse_gn_gate && a.rev_in) return hipErrorInvalidValue;   // no reversed variant of the fused epilogue
   // R_{i-1} itself in Rx: only stored states (no scan writing the transpose),
-  // read by the reversed direct-copy variant
-  if (a.rx_kv && !(a.reuse_rx && a.rev_in && chunk_out_direct(a.elt, a.d_k, a.d_v, a.chunk)))
+  // read by the direct-copy output kernel
+  if (a.rx_kv && !(a.reuse_rx && !a.fuse_gn_gate && chunk_out_direct(a.elt, a.d_k, a.d_v, a.chunk)))
     return hipErrorInvalidValue;
   if (a.elt == kBF16) {
     MSR_DISPATCH_DIMS(run_chunkwise, bf16, a, tab, st)

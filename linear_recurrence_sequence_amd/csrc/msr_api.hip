@@ -353,10 +353,11 @@ msr_status msr_parallel_fwd(msr_dtype dtype, msr_dims d, const double* gamma, fl
   return from_hip(launch_parallel(a, tab, st), "msr_parallel_fwd");
 }
 
-msr_status msr_chunkwise_fwd(msr_dtype dtype, msr_dims d, int32_t chunk, const double* gamma, float rope_base,
-                             int64_t pos0, float qk_scale, const void* Q, const void* K, const void* V,
-                             const float* S_in, float* S_out, void* O, void* workspace, size_t ws_bytes,
-                             void* stream) {
+// R_chunks (nullable): where the per-chunk states R_{i-1}^T go (else the workspace)
+static msr_status chunkwise_fwd(msr_dtype dtype, msr_dims d, int32_t chunk, const double* gamma, float rope_base,
+                                int64_t pos0, float qk_scale, const void* Q, const void* K, const void* V,
+                                const float* S_in, float* S_out, void* R_chunks, void* O, void* workspace,
+                                size_t ws_bytes, void* stream) {
   msr_status s;
   if ((s = check_dtype(dtype))) return s;
   if ((s = check_heads(d.batch, d.seqlen, d.heads, d.d_k, d.d_v))) return s;
@@ -391,10 +392,27 @@ msr_status msr_chunkwise_fwd(msr_dtype dtype, msr_dims d, int32_t chunk, const d
   a.ldv = a.ldo = (int64_t)d.heads * d.d_v;
   a.scale = qk_scale;
   a.S_in = S_in; a.S_out = S_out;
-  a.dR = at<void>(workspace, w.dr);
-  a.Rx = at<void>(workspace, w.rx);
+  // the state kernel's contributions and the scan's R_{i-1} share one buffer
+  a.dR = a.Rx = R_chunks ? R_chunks : at<void>(workspace, w.rx);
   const HeadTab tab = make_tab(gamma, d.heads, chunk, d.seqlen);
   return from_hip(launch_chunkwise(a, tab, st), "msr_chunkwise_fwd");
+}
+
+msr_status msr_chunkwise_fwd(msr_dtype dtype, msr_dims d, int32_t chunk, const double* gamma, float rope_base,
+                             int64_t pos0, float qk_scale, const void* Q, const void* K, const void* V,
+                             const float* S_in, float* S_out, void* O, void* workspace, size_t ws_bytes,
+                             void* stream) {
+  return chunkwise_fwd(dtype, d, chunk, gamma, rope_base, pos0, qk_scale, Q, K, V, S_in, S_out, nullptr, O,
+                       workspace, ws_bytes, stream);
+}
+
+msr_status msr_chunkwise_fwd_save(msr_dtype dtype, msr_dims d, int32_t chunk, const double* gamma, float rope_base,
+                                  int64_t pos0, float qk_scale, const void* Q, const void* K, const void* V,
+                                  const float* S_in, float* S_out, void* R_chunks, void* O, void* workspace,
+                                  size_t ws_bytes, void* stream) {
+  if (!R_chunks && d.batch > 0 && d.seqlen > 0) return fail(MSR_ERR_NULL, "R_chunks must be non-NULL");
+  return chunkwise_fwd(dtype, d, chunk, gamma, rope_base, pos0, qk_scale, Q, K, V, S_in, S_out, R_chunks, O,
+                       workspace, ws_bytes, stream);
 }
 
 size_t msr_chunkwise_bwd_workspace_bytes(msr_dtype dtype, msr_dims dims, int32_t chunk, float rope_base) {
@@ -408,10 +426,14 @@ size_t msr_chunkwise_bwd_workspace_bytes(msr_dtype dtype, msr_dims dims, int32_t
 // transpose (the dK pass's per-chunk states are the dV pass's transposed),
 // whose output kernels write their rows back in forward time order;
 // dS_in = scale gamma times the last state of the dV pass.
-msr_status msr_chunkwise_bwd(msr_dtype dtype, msr_dims d, int32_t chunk, const double* gamma, float rope_base,
-                             int64_t pos0, float qk_scale, const void* Q, const void* K, const void* V,
-                             const void* dO, const float* S_in, const float* dS_out, void* dQ, void* dK, void* dV,
-                             float* dS_in, void* workspace, size_t ws_bytes, void* stream) {
+// R_chunks (nullable): the forward's per-chunk states R_{i-1}^T, which are the
+// dQ pass's states R_{i-1} themselves; read in place by the direct-copy
+// output kernel, ignored elsewhere (the dQ pass computes its own)
+static msr_status chunkwise_bwd(msr_dtype dtype, msr_dims d, int32_t chunk, const double* gamma, float rope_base,
+                                int64_t pos0, float qk_scale, const void* Q, const void* K, const void* V,
+                                const void* dO, const float* S_in, const float* dS_out, const void* R_chunks,
+                                void* dQ, void* dK, void* dV, float* dS_in, void* workspace, size_t ws_bytes,
+                                void* stream) {
   msr_status s;
   if ((s = check_dtype(dtype))) return s;
   if ((s = check_heads(d.batch, d.seqlen, d.heads, d.d_k, d.d_v))) return s;
@@ -455,7 +477,9 @@ msr_status msr_chunkwise_bwd(msr_dtype dtype, msr_dims d, int32_t chunk, const d
   hipError_t err = hipSuccess;
   // state seeds
   std::fill(hs.c, hs.c + kMaxHeads, 1.0f);
-  if (S_in) err = launch_state_xform(S_in, sin_t, nbh, d.heads, d.d_v, d.d_k, true, hs, st);
+  const bool direct = chunk_out_direct(e, d.d_k, d.d_v, chunk);
+  const bool saved = R_chunks && direct;          // the dQ pass reads the forward's states
+  if (S_in && !saved) err = launch_state_xform(S_in, sin_t, nbh, d.heads, d.d_v, d.d_k, true, hs, st);
   if (dS_out && err == hipSuccess) {
     for (int h = 0; h < d.heads; ++h) hs.c[h] = (float)(1.0 / ((double)qk_scale * gamma[h]));
     err = launch_state_xform(dS_out, dso, nbh, d.heads, d.d_k, d.d_v, false, hs, st);
@@ -467,7 +491,7 @@ msr_status msr_chunkwise_bwd(msr_dtype dtype, msr_dims d, int32_t chunk, const d
   // rev: the pass runs on the time-reversed sequence, reading its Q, K, V
   // rows backwards and writing its output rows back in forward order
   auto pass = [&](const void* q, const void* k, const void* v, void* o, const float* sin, float* sout, bool rev,
-                  bool reuse = false, bool seeded = false, bool rx_kv = false) {
+                  bool reuse = false, bool seeded = false, bool rx_kv = false, const void* rx = nullptr) {
     ChunkArgs a{};
     a.elt = e;
     a.d_k = d.d_k; a.d_v = d.d_v; a.batch = d.batch; a.seqlen = d.seqlen; a.heads = d.heads;
@@ -478,7 +502,7 @@ msr_status msr_chunkwise_bwd(msr_dtype dtype, msr_dims d, int32_t chunk, const d
     a.S_in = sin; a.S_out = sout;
     a.sout_scale = sout ? ds_scale : nullptr;
     a.dR = at<void>(cws, w.cw.dr);
-    a.Rx = at<void>(cws, w.cw.rx);
+    a.Rx = rx ? const_cast<void*>(rx) : at<void>(cws, w.cw.rx);   // a given rx is only read
     a.rev_out = rev;
     a.rev_in = rev;
     a.reuse_rx = reuse;
@@ -486,8 +510,13 @@ msr_status msr_chunkwise_bwd(msr_dtype dtype, msr_dims d, int32_t chunk, const d
     a.rx_kv = rx_kv;
     return launch_chunkwise(a, tab, st);
   };
-  // dQ = causal retention of (dO, V, K) from S_in^T
-  err = pass(dO, V, K, dQ, S_in ? sin_t : nullptr, nullptr, false);
+  // dQ = causal retention of (dO, V, K) from S_in^T; its per-chunk states
+  // are the forward's transposed (sums of V^T K against K^T V, seeded with
+  // S_in^T against S_in)
+  if (saved)
+    err = pass(dO, V, K, dQ, nullptr, nullptr, false, true, S_in != nullptr, true, R_chunks);
+  else
+    err = pass(dO, V, K, dQ, S_in ? sin_t : nullptr, nullptr, false);
   if (err != hipSuccess) return from_hip(err, "msr_chunkwise_bwd(dQ)");
   // dV = causal retention of (rev K, rev Q, rev dO), its rows written back in
   // forward time order; its last state gives dS_in
@@ -499,7 +528,7 @@ msr_status msr_chunkwise_bwd(msr_dtype dtype, msr_dims d, int32_t chunk, const d
   // dS_out), so it reuses those per-chunk states: the direct-copy output
   // kernel reads them as they are (with the transposing LDS read), the
   // others after an in-place transpose.
-  const bool rx_kv = chunk_out_direct(e, d.d_k, d.d_v, chunk);
+  const bool rx_kv = direct;
   if (!rx_kv) {
     const int NC = (d.seqlen + chunk - 1) / chunk;
     err = launch_transpose_blocks(e, at<void>(cws, w.cw.rx), d.d_k, (int64_t)nbh * NC, st);
@@ -515,6 +544,24 @@ msr_status msr_chunkwise_bwd(msr_dtype dtype, msr_dims d, int32_t chunk, const d
     if (err != hipSuccess) return from_hip(err, "msr_chunkwise_bwd(rotation)");
   }
   return ok();
+}
+
+msr_status msr_chunkwise_bwd(msr_dtype dtype, msr_dims d, int32_t chunk, const double* gamma, float rope_base,
+                             int64_t pos0, float qk_scale, const void* Q, const void* K, const void* V,
+                             const void* dO, const float* S_in, const float* dS_out, void* dQ, void* dK, void* dV,
+                             float* dS_in, void* workspace, size_t ws_bytes, void* stream) {
+  return chunkwise_bwd(dtype, d, chunk, gamma, rope_base, pos0, qk_scale, Q, K, V, dO, S_in, dS_out, nullptr, dQ,
+                       dK, dV, dS_in, workspace, ws_bytes, stream);
+}
+
+msr_status msr_chunkwise_bwd_saved(msr_dtype dtype, msr_dims d, int32_t chunk, const double* gamma, float rope_base,
+                                   int64_t pos0, float qk_scale, const void* Q, const void* K, const void* V,
+                                   const void* dO, const float* S_in, const float* dS_out, const void* R_chunks,
+                                   void* dQ, void* dK, void* dV, float* dS_in, void* workspace, size_t ws_bytes,
+                                   void* stream) {
+  if (!R_chunks && d.batch > 0 && d.seqlen > 0) return fail(MSR_ERR_NULL, "R_chunks must be non-NULL");
+  return chunkwise_bwd(dtype, d, chunk, gamma, rope_base, pos0, qk_scale, Q, K, V, dO, S_in, dS_out, R_chunks, dQ,
+                       dK, dV, dS_in, workspace, ws_bytes, stream);
 }
 
 size_t msr_rglru_workspace_bytes(msr_dtype dtype, int32_t batch, int32_t seqlen, int32_t width) {

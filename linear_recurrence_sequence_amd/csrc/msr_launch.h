@@ -47,9 +47,9 @@ struct ChunkArgs {
   // Rx already holds every chunk's R_{i-1} (state and scan kernels skipped);
   // reuse_seeded: chunk 0's R_{-1} is a seed (else zero)
   bool reuse_rx, reuse_seeded;
-  // with reuse_rx and rev_in, on the direct-copy path only (chunk_out_direct):
-  // Rx holds each chunk's R_{i-1} itself, [d_k rows][d_v cols], instead of
-  // its transpose
+  // with reuse_rx, on the direct-copy path only (chunk_out_direct): Rx
+  // holds each chunk's R_{i-1} itself, [d_k rows][d_v cols], instead of its
+  // transpose
   bool rx_kv;
 };
 

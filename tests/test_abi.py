@@ -141,6 +141,26 @@ def test_backward_validation():
     assert bwd(dims=(2, 64, 2, 64, 64), gam=zp, ws=16) == 5     # gamma = 0 is fine without dS_out
 
 
+def test_saved_state_entry_points_validation():
+    """The forward that keeps its per-chunk states and the backward that
+    reads them need R_chunks when there are tokens, and otherwise validate
+    like msr_chunkwise_fwd / msr_chunkwise_bwd."""
+    L = msr.lib()
+    g, gp = _gamma(2)
+    fwd = lambda dims=(1, 64, 2, 64, 64), R=FAKE, dtype=1, ws=1 << 40: L.msr_chunkwise_fwd_save(
+        dtype, msr.MsrDims(*dims), 32, gp, 0.0, 0, 1.0, FAKE, FAKE, FAKE, None, None, R, FAKE, FAKE, ws, None)
+    assert fwd(R=None) == 1 and "R_chunks" in msr.msr_last_error()
+    assert fwd(dims=(0, 64, 2, 64, 64), R=None) == 0              # no tokens: nothing to keep
+    assert fwd(dtype=3) == 3
+    assert fwd(ws=16) == 5
+    bwd = lambda dims=(1, 64, 2, 64, 64), R=FAKE, dtype=1, ws=1 << 40: L.msr_chunkwise_bwd_saved(
+        dtype, msr.MsrDims(*dims), 32, gp, 0.0, 0, 1.0, FAKE, FAKE, FAKE, FAKE, None, None, R, FAKE, FAKE, FAKE,
+        None, FAKE, ws, None)
+    assert bwd(R=None) == 1 and "R_chunks" in msr.msr_last_error()
+    assert bwd(dims=(1, 64, 2, 256, 512)) == 4                   # d_k != d_v
+    assert bwd(ws=16) == 5
+
+
 def test_rglru_validation():
     L = msr.lib()
     rg = lambda B=2, T=16, D=128, c=8.0, X=FAKE, lam=FAKE, h0=None, hT=None, ws=1 << 40, dtype=1: L.msr_rglru_fwd(

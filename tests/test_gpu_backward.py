@@ -132,3 +132,55 @@ def test_backward_headline_core_shape_sampled():
         _check(f"dK[{b},{h}]", sl(dK), oracle.rotary_adjoint(rk, 0, 1e4), TOL["bf16"])
         _check(f"dV[{b},{h}]", sl(dV), rv, TOL["bf16"])
         assert oracle.max_rel_err(host(dS_in[b, h]), rS[0, 0]) < STATE_TOL["bf16"]
+
+
+@pytest.mark.parametrize("dtype,d,N,chunk", [("bf16", 128, 300, 128), ("bf16", 64, 400, 128),
+                                             ("bf16", 256, 520, 256), ("bf16", 64, 200, 64), ("f32", 64, 200, 64)])
+def test_backward_with_saved_forward_states(dtype, d, N, chunk):
+    """msr_chunkwise_fwd_save then msr_chunkwise_bwd_saved, with rotation and
+    both seeds: O is msr_chunkwise_fwd's bit for bit, the kept states are
+    the oracle's per-chunk starting states (of the rotated K), and the
+    gradients match the oracle.  On the direct-copy path (bf16, chunk a
+    multiple of 128) the dQ pass reads the kept states, so only the dV pass
+    runs the state kernel; elsewhere they are not read."""
+    import torch
+    msr = _msr()
+    B, H = 2, 3
+    q, k, v = workloads.core_inputs(41 + d, B, N, H, d, d, dtype)
+    rng = np.random.default_rng(42 + d)
+    dO = workloads.normal(rng, (B, N, H, d), 1.0, dtype)
+    S0 = rng.standard_normal((B, H, d, d)).astype(np.float32)
+    dS = rng.standard_normal((B, H, d, d)).astype(np.float32)
+    g = np.array([0.9, 1 - 2.0 ** -5, 1 - 2.0 ** -12])
+    scale, pos0, base = 1 / math.sqrt(d), 3, 10000.0
+    Q, K, V, S0d = dev(q, dtype), dev(k, dtype), dev(v, dtype), torch.from_numpy(S0).cuda()
+    R = torch.empty(msr.msr_chunkwise_states_shape(B, N, H, d, d, chunk), dtype=Q.dtype, device="cuda")
+    say("saved states", dtype, d, N, chunk)
+    O_plain = msr.msr_chunkwise_fwd(Q, K, V, g, chunk, rope_base=base, pos0=pos0, qk_scale=scale, S_in=S0d)
+    O = msr.msr_chunkwise_fwd_save(Q, K, V, g, chunk, R, rope_base=base, pos0=pos0, qk_scale=scale, S_in=S0d)
+    torch.cuda.synchronize()
+    assert torch.equal(O, O_plain)
+    qr, kr = oracle.rotary(q, pos0, base), oracle.rotary(k, pos0, base)
+    Rh = host(R)
+    for i in range(R.shape[2]):
+        c0 = i * chunk
+        ref = S0 if c0 == 0 else oracle.retention_chunkwise(qr[:, :c0], kr[:, :c0], v[:, :c0], g, chunk, scale,
+                                                            S0=S0)[1]
+        err = _state_err(np.swapaxes(Rh[:, :, i], -1, -2), ref)
+        assert err < STATE_TOL[dtype], (i, err)
+    dS_in = torch.empty((B, H, d, d), device="cuda")
+    msr.msr_trace_enable(True)
+    try:
+        dQ, dK, dV = msr.msr_chunkwise_bwd_saved(Q, K, V, dev(dO, dtype), g, chunk, R, rope_base=base, pos0=pos0,
+                                                 qk_scale=scale, S_in=S0d, dS_out=torch.from_numpy(dS).cuda(),
+                                                 dS_in=dS_in)
+        torch.cuda.synchronize()
+        launches = msr.trace_totals()["k_chunk_state"][1]
+    finally:
+        msr.msr_trace_enable(False)
+    assert launches == (1 if dtype == "bf16" and chunk % 128 == 0 else 2)
+    rq, rk, rv, rS = oracle.retention_grad(qr, kr, v, dO, g, scale, S0=S0, dS=dS)
+    _check("dQ", host(dQ), oracle.rotary_adjoint(rq, pos0, base), TOL[dtype])
+    _check("dK", host(dK), oracle.rotary_adjoint(rk, pos0, base), TOL[dtype])
+    _check("dV", host(dV), rv, TOL[dtype])
+    assert _state_err(host(dS_in), rS) < STATE_TOL[dtype]
