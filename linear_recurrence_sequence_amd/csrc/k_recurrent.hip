@@ -16,11 +16,18 @@ namespace msr {
 // (cos, sin) of p * theta_j, theta_j = base^(-2j/d).  The angle is reduced in
 // double precision (p can be ~1e4 radians, where float32 would lose ~1e-3 of
 // absolute accuracy) and evaluated as sincospi of the reduced half-turns.
-__device__ __forceinline__ void rope_cs(int64_t p, int j, int d, float base, float* c, float* s) {
-  const double w = exp2(-2.0 * (double)j / (double)d * log2((double)base)) * 0.31830988618379067154;  // theta/pi
+// theta_j / pi of pair j
+__device__ __forceinline__ double rope_w(int j, int d, float base) {
+  return exp2(-2.0 * (double)j / (double)d * log2((double)base)) * 0.31830988618379067154;
+}
+// cos and sin of p theta_j, given w = theta_j / pi
+__device__ __forceinline__ void rope_cs_w(int64_t p, double w, float* c, float* s) {
   double t = (double)p * w;
   t -= 2.0 * rint(0.5 * t);
   sincospif((float)t, s, c);
+}
+__device__ __forceinline__ void rope_cs(int64_t p, int j, int d, float base, float* c, float* s) {
+  rope_cs_w(p, rope_w(j, d, base), c, s);
 }
 
 template <class T> __device__ __forceinline__ float ld1(const T* p) { return (float)*p; }
@@ -183,18 +190,26 @@ hipError_t launch_gn_gate(Elt elt, int d_v, int batch, int heads, const float* o
 // ---------------------------------------------------------------------------
 // Rotation: a (cos, sin) table per call, then an elementwise pass.
 // ---------------------------------------------------------------------------
+// One lane per (pair j, RPL consecutive positions): theta_j / pi (float64
+// exp2 and log2) once per lane; lanes of a wave take consecutive pairs, so
+// every store of a position is one contiguous row segment.
+constexpr int RPL = 4;
 __global__ void k_rope_table(float2* tab, int npos, int d, int64_t pos0, float base) {
   const int half = d / 2;
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= (int64_t)npos * half) return;
-  const int n = (int)(i / half), j = (int)(i % half);
-  float c, s;
-  rope_cs(pos0 + n, j, d, base, &c, &s);
-  tab[i] = make_float2(c, s);
+  const int64_t nblk = (npos + RPL - 1) / RPL;
+  if (i >= nblk * half) return;
+  const int j = (int)(i % half), n0 = (int)(i / half) * RPL;
+  const double w = rope_w(j, d, base);
+  for (int u = 0; u < RPL && n0 + u < npos; ++u) {
+    float c, s;
+    rope_cs_w(pos0 + n0 + u, w, &c, &s);
+    tab[(int64_t)(n0 + u) * half + j] = make_float2(c, s);
+  }
 }
 
 hipError_t launch_rope_table(float2* tab, int npos, int d, int64_t pos0, float base, hipStream_t st) {
-  const int64_t n = (int64_t)npos * (d / 2);
+  const int64_t n = (int64_t)((npos + RPL - 1) / RPL) * (d / 2);
   if (n == 0) return hipSuccess;
   TraceScope ts("k_rope_table", st);
   hipLaunchKernelGGL(k_rope_table, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, tab, npos, d, pos0, base);
