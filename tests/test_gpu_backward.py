@@ -184,3 +184,31 @@ def test_backward_with_saved_forward_states(dtype, d, N, chunk):
     _check("dK", host(dK), oracle.rotary_adjoint(rk, pos0, base), TOL[dtype])
     _check("dV", host(dV), rv, TOL[dtype])
     assert _state_err(host(dS_in), rS) < STATE_TOL[dtype]
+
+
+@pytest.mark.slow
+def test_saved_states_backward_headline_core_shape_sampled():
+    """The kept-state path at the shape bench.py times it (batch 8, 2048
+    tokens, 8 heads of 256, bf16, chunk 256, gammas 1 - 2^(-5-h), scale 1/16,
+    no rotation): O of msr_chunkwise_fwd_save equals msr_chunkwise_fwd's,
+    and (batch, head) slices (1, 2), (6, 7) of dQ, dK, dV and dS_in from
+    msr_chunkwise_bwd_saved match the oracle."""
+    import torch
+    msr = _msr()
+    B, N, H, d, C = 8, 2048, 8, 256, 256
+    g = workloads.gammas(H)
+    say("saved-state backward headline core shape")
+    q, k, v, dO = (workloads.device_normal((B, N, H, d), seed=950 + i).to(torch.bfloat16) for i in range(4))
+    R = torch.empty(msr.msr_chunkwise_states_shape(B, N, H, d, d, C), dtype=torch.bfloat16, device="cuda")
+    O = msr.msr_chunkwise_fwd_save(q, k, v, g, C, R, qk_scale=1 / 16)
+    assert torch.equal(O, msr.msr_chunkwise_fwd(q, k, v, g, C, qk_scale=1 / 16))
+    dS_in = torch.empty((B, H, d, d), device="cuda")
+    dQ, dK, dV = msr.msr_chunkwise_bwd_saved(q, k, v, dO, g, C, R, qk_scale=1 / 16, dS_in=dS_in)
+    torch.cuda.synchronize()
+    for b, h in ((1, 2), (6, 7)):
+        sl = lambda t: host(t[b:b + 1, :, h:h + 1])
+        rq, rk, rv, rS = oracle.retention_grad(sl(q), sl(k), sl(v), sl(dO), g[h:h + 1], 1 / 16)
+        _check(f"dQ[{b},{h}]", sl(dQ), rq, TOL["bf16"])
+        _check(f"dK[{b},{h}]", sl(dK), rk, TOL["bf16"])
+        _check(f"dV[{b},{h}]", sl(dV), rv, TOL["bf16"])
+        assert oracle.max_rel_err(host(dS_in[b, h]), rS[0, 0]) < STATE_TOL["bf16"]
