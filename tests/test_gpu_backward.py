@@ -212,3 +212,31 @@ def test_saved_states_backward_headline_core_shape_sampled():
         _check(f"dK[{b},{h}]", sl(dK), rk, TOL["bf16"])
         _check(f"dV[{b},{h}]", sl(dV), rv, TOL["bf16"])
         assert oracle.max_rel_err(host(dS_in[b, h]), rS[0, 0]) < STATE_TOL["bf16"]
+
+
+@pytest.mark.parametrize("dtype,dk,dv,N,chunk", [("bf16", 256, 512, 200, 64), ("f32", 128, 128, 97, 32)])
+def test_kept_states_of_the_forward(dtype, dk, dv, N, chunk):
+    """msr_chunkwise_fwd_save's R_chunks = the oracle's state at the start of
+    every chunk (transposed), also where d_k != d_v and for a ragged last
+    chunk; O and S_out are msr_chunkwise_fwd's bit for bit."""
+    import torch
+    msr = _msr()
+    B, H = 2, 2
+    q, k, v = workloads.core_inputs(61 + dk, B, N, H, dk, dv, dtype)
+    S0 = np.random.default_rng(62).standard_normal((B, H, dk, dv)).astype(np.float32)
+    g = np.array([0.95, 1 - 2.0 ** -9])
+    Q, K, V, S0d = dev(q, dtype), dev(k, dtype), dev(v, dtype), torch.from_numpy(S0).cuda()
+    R = torch.empty(msr.msr_chunkwise_states_shape(B, N, H, dk, dv, chunk), dtype=Q.dtype, device="cuda")
+    S1, S2 = (torch.empty((B, H, dk, dv), device="cuda") for _ in range(2))
+    say("kept states", dtype, dk, dv, N, chunk)
+    O1 = msr.msr_chunkwise_fwd(Q, K, V, g, chunk, qk_scale=0.1, S_in=S0d, S_out=S1)
+    O2 = msr.msr_chunkwise_fwd_save(Q, K, V, g, chunk, R, qk_scale=0.1, S_in=S0d, S_out=S2)
+    torch.cuda.synchronize()
+    assert torch.equal(O1, O2) and torch.equal(S1, S2)
+    Rh = host(R)
+    for i in range(R.shape[2]):
+        c0 = i * chunk
+        ref = S0 if c0 == 0 else oracle.retention_chunkwise(q[:, :c0], k[:, :c0], v[:, :c0], g, chunk, 0.1,
+                                                            S0=S0)[1]
+        err = _state_err(np.swapaxes(Rh[:, :, i], -1, -2), ref)
+        assert err < STATE_TOL[dtype], (i, err)
