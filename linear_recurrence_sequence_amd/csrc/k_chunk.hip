@@ -229,13 +229,14 @@ __global__ __launch_bounds__(256) void k_chunk_scan(const T* dR, T* Rx, const fl
   const T* src = dR + off;
   T* dst = Rx + off;
   const float gB = tab.gchunk[h], gL = tab.glast[h];
-  // Contributions of the next PF chunks in flight, kept raw (unconverted) in a
+  // Contributions of the next PF chunks in flight (8 with the 32 x 32 tiles,
+  // whose loads are 8 bytes per lane), kept raw (unconverted) in a
   // statically indexed ring: converting right after the load would make the
   // load complete at once.  Chunk ci's slot is reloaded with chunk ci + PF
   // right after it has been read.  The reloads are unconditional, clamped to
   // the last chunk (a re-read whose value is never used), so no slot has to
   // be kept across a branch; chunk NC - 1 is loaded before it is written.
-  constexpr int PF = 4;
+  constexpr int PF = TS == 32 ? 8 : 4;
   RawN<T, E> ring[PF];
   // (issued in slot order, as in the loop, so that the wait counts at the
   // loop head are the steady-state ones)
