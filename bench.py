@@ -50,10 +50,10 @@ PEAK_HBM = 8.0e12                      # bytes/s
 # it was taken with: the sha256 prefix of those files is recorded, and a
 # kernel whose sources have changed since reports null.
 MEASURED_TRAFFIC = {  # (workload, kernel): (bytes per launch, sources, sha256[:16])
-    ("layer_bf16_b8_n2048", "k_gemm"): (6.881e+08, ('k_gemm.hip', 'msr_device.h'), "a06455c014b88a49"),
-    ("layer_bf16_b8_n2048", "k_chunk_out"): (3.95e+08, ('k_chunk.hip', 'msr_device.h'), "4880aa4d1754a5d6"),
-    ("layer_bf16_b8_n2048", "k_chunk_state"): (2.028e+08, ('k_chunk.hip', 'msr_device.h'), "4880aa4d1754a5d6"),
-    ("layer_bf16_b8_n2048", "k_chunk_scan"): (1.347e+08, ('k_chunk.hip', 'msr_device.h'), "4880aa4d1754a5d6"),
+    ("layer_bf16_b8_n2048", "k_gemm"): (6.882e+08, ('k_gemm.hip', 'msr_device.h'), "a06455c014b88a49"),
+    ("layer_bf16_b8_n2048", "k_chunk_out"): (3.951e+08, ('k_chunk.hip', 'msr_device.h'), "e199c3d1b03234b4"),
+    ("layer_bf16_b8_n2048", "k_chunk_state"): (2.029e+08, ('k_chunk.hip', 'msr_device.h'), "e199c3d1b03234b4"),
+    ("layer_bf16_b8_n2048", "k_chunk_scan"): (1.347e+08, ('k_chunk.hip', 'msr_device.h'), "e199c3d1b03234b4"),
     ("decode_fp32_b128_h16", "k_recurrent_step"): (1.086e+09, ('k_recurrent.hip', 'msr_device.h'), "e6d672c087335737"),
     ("rglru_bf16_b8_n2048_d2048", "k_gemm"): (5.374e+08, ('k_gemm.hip', 'msr_device.h'), "a06455c014b88a49"),
     ("rglru_bf16_b8_n2048_d2048", "k_rglru_scan"): (2.686e+08, ('k_rglru.hip', 'msr_device.h'), "12a096c3dad145c9"),
