@@ -3,26 +3,32 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--only a,b,...] [--no-cpu]
 
-Headline (the JSON line's "value"): forward of one gated multi-scale
-retention layer (bf16, fp32 accumulate) on batch 8 x 2048 tokens,
-d_model 2048, 8 heads of 256, chunk 256 -- tokens per second, inputs and
-weights resident in HBM, W untimed warm-up steps then exactly K timed steps
-between two stream synchronisations.  The same line carries:
+Headline (the JSON line's "value"): forward of the full gated multi-scale
+retention layer (X W_Q/W_K/W_V, rotation, chunkwise retention, GroupNorm,
+swish(X W_G) gate, W_O; bf16 with float32 accumulation) on batch 4 x 8192
+tokens, d_model 4096, 16 heads, q/k head dim 256, v head dim 512, chunk 512
+-- tokens per second, inputs and weights resident in HBM, W untimed warm-up
+steps then exactly K timed steps between two stream synchronisations.  The
+same line carries:
 
 * roofline   -- the dominant kernel's achieved rate over the timed steps,
                 from HIP events bracketing each of its launches (msr_trace)
                 against the MI355X peak;
-* kernels    -- the same for every kernel of the step;
+* chunkwise  -- the same for the chunkwise retention kernels of the step,
+                alone and together (the core's share of the MFMA peak);
+* kernels    -- every kernel of the step;
 * decode     -- recurrent decode, batch 128, 16 heads of 256, fp32 state
                 (512 MiB) prefilled from an 8192-token context, 512 timed
                 steps: steps/s and fraction of HBM peak; also a 1024-token
                 context for the length-independence check;
+* layer_decode -- the whole layer's decode step at that shape, 512 steps;
+* layer_b8_n2048 -- the layer at batch 8 x 2048, d_model 2048, 8 heads of
+                256, chunk 256;
 * long       -- chunkwise core (batch 2, 16384 tokens, 10 heads of 256,
                 chunk 512) and a sequence-length sweep of chunkwise vs
                 parallel form, plus that layer;
-* block      -- the gated MSR block (batch 4, 8192 tokens, d_model 4096,
-                16 heads, q/k 256, v 512, chunk 512);
-* cpu_baseline -- the float64 oracle timed on this host on a bounded sample.
+* cpu_baseline -- the float64 oracle timed on this host on a bounded sample
+                of the headline workload.
 
 There is one GPU: --gpus above 1 exits with a message.
 """
@@ -207,15 +213,34 @@ def bench_layer(w, steps, warmup, device_inputs=False):
     res = {"s_per_step": t, "s_per_step_median": med, "s_per_step_min": mn, "tokens_per_s": B * N / t,
            "flops_per_step": proj + core,
            "tflops": (proj + core) / t / 1e12, "mfma_frac": (proj + core) / t / PEAK_BF16, "kernels": kern,
-           "trace_s_per_step": {k: v[0] / steps for k, v in tr.items()}}
+           "trace_s_per_step": {k: v[0] / steps for k, v in tr.items()},
+           "chunkwise": chunkwise_summary(tr, steps, core, kern)}
     return res
 
 
-def bench_core(B, N, H, d, C, steps, warmup, parallel=False, dv=None):
+CHUNK_KERNELS = ("k_chunk_state", "k_chunk_scan", "k_chunk_out")
+
+
+def chunkwise_summary(tr, steps, core_flops, kern):
+    """The chunkwise retention kernels of a step together: the core's
+    algorithmic flops (causal intra-chunk products, Q R and the state
+    contributions) over their summed launch time, against the bf16 peak;
+    and each kernel's own roofline entry."""
+    t = sum(tr[n][0] for n in CHUNK_KERNELS if n in tr) / steps
+    if t <= 0:
+        return None
+    ach = core_flops / t
+    return {"bound": "mfma", "achieved": round(ach / 1e12, 2), "peak": round(PEAK_BF16 / 1e12, 1),
+            "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16, 4), "us_per_step": round(t * 1e6, 2),
+            "flops_per_step": core_flops, "kernels": {n: kern[n] for n in CHUNK_KERNELS if n in kern}}
+
+
+def bench_core(B, N, H, d, C, steps, warmup, parallel=False, dv=None, rope_base=0.0):
     """Chunkwise (or parallel) retention core on projected bf16 Q, K, V of
-    [B, N, H, d] (V and O [B, N, H, dv]); algorithmic flops count the causal
-    half of the intra-chunk products: per token and head C (d_k + d_v) +
-    4 d_k d_v (chunkwise), N (d_k + d_v) on average (parallel)."""
+    [B, N, H, d] (V and O [B, N, H, dv]), rotated inside the call when
+    rope_base > 0; algorithmic flops count the causal half of the
+    intra-chunk products: per token and head C (d_k + d_v) + 4 d_k d_v
+    (chunkwise), N (d_k + d_v) on average (parallel)."""
     import torch
     import linear_recurrence_sequence_amd as msr
     import workloads
@@ -226,12 +251,14 @@ def bench_core(B, N, H, d, C, steps, warmup, parallel=False, dv=None):
     g = workloads.gammas(H)
     s = 1 / math.sqrt(dk)
     if parallel:
-        fn = lambda: msr.msr_parallel_fwd(Q, K, V, g, qk_scale=s, O=O)
+        wp = torch.empty(max(1, msr.msr_parallel_workspace_bytes(1, B, N, H, dk, dv, rope_base)), dtype=torch.uint8,
+                         device="cuda")
+        fn = lambda: msr.msr_parallel_fwd(Q, K, V, g, qk_scale=s, rope_base=rope_base, O=O, workspace=wp)
         flops = B * N * H * N * (dk + dv)
     else:
-        ws = torch.empty(msr.msr_chunkwise_workspace_bytes(1, B, N, H, dk, dv, C, 0.0), dtype=torch.uint8,
+        ws = torch.empty(msr.msr_chunkwise_workspace_bytes(1, B, N, H, dk, dv, C, rope_base), dtype=torch.uint8,
                          device="cuda")
-        fn = lambda: msr.msr_chunkwise_fwd(Q, K, V, g, C, qk_scale=s, O=O, workspace=ws)
+        fn = lambda: msr.msr_chunkwise_fwd(Q, K, V, g, C, qk_scale=s, rope_base=rope_base, O=O, workspace=ws)
         flops = B * N * H * (C * (dk + dv) + 4 * dk * dv)
     t = gpu_time(fn, steps, warmup)
     res = {"N": N, "s": t, "tokens_per_s": B * N / t, "tflops": flops / t / 1e12, "mfma_frac": flops / t / PEAK_BF16}
@@ -248,6 +275,7 @@ def bench_core(B, N, H, d, C, steps, warmup, parallel=False, dv=None):
         }
         res["kernels"] = {n: roof(n, wk, bd, tr, steps, bytes_per_step=by) for n, (wk, bd, by) in work.items()
                           if n in tr}
+        res["trace_us_per_step"] = {k: round(v[0] / steps * 1e6, 2) for k, v in tr.items()}
     return res
 
 
@@ -368,7 +396,10 @@ def bench_decode(steps_timed, warmup):
 def bench_layer_decode(n_steps, warmup):
     """Gated layer decode step at the decode workload's shape (batch 128,
     d_model 4096, 16 heads of 256; bf16 tokens and weights, float32 state):
-    projections, rotation, state update, GroupNorm, gate, W_O per step."""
+    projections, rotation, state update, GroupNorm, gate, W_O per step.
+    n_steps consecutive steps between two events (the rate), then the same
+    steps with an event pair around each (the median step) and the host's
+    issue time per step (wall time to enqueue the steps, before waiting)."""
     import torch
     import linear_recurrence_sequence_amd as msr
     import workloads
@@ -390,16 +421,23 @@ def bench_layer_decode(n_steps, warmup):
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
+    h0 = time.perf_counter()
     for t in range(n_steps):
         step(t)
+    host_issue = (time.perf_counter() - h0) / n_steps
     e1.record()
     torch.cuda.synchronize()
     ts = e0.elapsed_time(e1) * 1e-3 / n_steps
+    med, mn = step_stats(lambda: step(0), n_steps)
     tr = traced(lambda: step(0), n_steps)
     wbytes = (dm * (2 * H * dk + 2 * H * dv) + H * dv * dm) * 2
     byts = B * H * dk * dv * 4 * 2 + wbytes + B * dm * 2 * 2
+    ksum = sum(v[0] for v in tr.values()) / n_steps
     res = {"batch": B, "d_model": dm, "heads": H, "d_k": dk, "d_v": dv, "steps": n_steps,
-           "us_per_step": round(ts * 1e6, 2), "steps_per_s": round(1 / ts, 1), "tokens_per_s": round(B / ts, 1),
+           "us_per_step": round(ts * 1e6, 2), "us_per_step_median": round(med * 1e6, 2),
+           "us_per_step_min": round(mn * 1e6, 2), "host_issue_us_per_step": round(host_issue * 1e6, 2),
+           "kernel_sum_us_per_step": round(ksum * 1e6, 2),
+           "steps_per_s": round(1 / ts, 1), "tokens_per_s": round(B / ts, 1),
            "GB_per_s": round(byts / ts / 1e9, 1), "hbm_frac": round(byts / ts / PEAK_HBM, 4), "bytes_per_step": byts,
            "trace_us_per_step": {k: round(v[0] / n_steps * 1e6, 2) for k, v in tr.items()}}
     del W, WO, S, xs, out, ws
@@ -452,11 +490,11 @@ def bench_copy(nbytes=1 << 30, reps=8):
             "GB_per_s": round(2 * nbytes / t / 1e9, 1)}
 
 
-def cpu_baseline(budget_s=12.0):
-    """The float64 oracle on a bounded sample of the headline workload: the
-    layer on one batch element (2048 tokens) at a time, cycling through the
-    batch, until at least budget_s seconds of CPU work are done."""
-    import numpy as np
+def cpu_baseline(budget_s=10.0):
+    """The float64 oracle on a bounded sample of the headline workload:
+    the whole layer on batch element 0 (8192 tokens; causal, so it is the
+    exact first quarter of the batch), repeated until at least budget_s
+    seconds of CPU work are done."""
     import oracle
     import workloads
     try:
@@ -464,14 +502,15 @@ def cpu_baseline(budget_s=12.0):
         threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
     except Exception:
         threads = None
-    w = workloads.WORKLOADS["layer_bf16_b8_n2048"]
-    X, WQ, WK, WV, WG, WO = workloads.layer_inputs(w)
+    w = workloads.WORKLOADS["block_bf16_b4_n8192"]
+    # the workload's recipe drawn at batch 1: the same shapes and
+    # distributions (the cost of the oracle does not depend on the values)
+    X, WQ, WK, WV, WG, WO = workloads.layer_inputs(w, batch=1)
     g = workloads.gammas(w.heads)
     t0 = time.perf_counter()
     done = 0
     while True:
-        b = done % w.batch
-        oracle.msr_layer(X[b:b + 1], WQ, WK, WV, WG, WO, g, w.heads, w.d_k, w.d_v, w.chunk, rope_base=w.rope_base,
+        oracle.msr_layer(X[0:1], WQ, WK, WV, WG, WO, g, w.heads, w.d_k, w.d_v, w.chunk, rope_base=w.rope_base,
                          eps=1e-5)
         done += 1
         if time.perf_counter() - t0 >= budget_s:
@@ -479,8 +518,8 @@ def cpu_baseline(budget_s=12.0):
     t = time.perf_counter() - t0
     return {"value": round(done * w.seqlen / t, 1), "unit": "tokens/s", "cores": threads,
             "host_cpus": len(os.sched_getaffinity(0)), "kind": "oracle",
-            "sample": f"{done} batch-element passes ({done * w.seqlen} tokens, cycling over the {w.batch} "
-                      f"elements) of the layer workload, float64 numpy, {t:.1f} s"}
+            "sample": f"{done} pass(es) of the whole layer over one batch element ({w.seqlen} tokens, the "
+                      f"headline workload's recipe drawn at batch 1) of {w.name}, float64 numpy, {t:.1f} s"}
 
 
 def main():
@@ -488,7 +527,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--only", default="layer,decode,long,block,retnet,backward,rglru,cpu")
+    ap.add_argument("--only", default="layer,decode,small,long,retnet,backward,rglru,cpu")
     ap.add_argument("--no-cpu", action="store_true")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -505,16 +544,17 @@ def main():
     props = torch.cuda.get_device_properties(0)
     log(f"device {props.name} CUs={props.multi_processor_count}")
 
-    w = workloads.WORKLOADS["layer_bf16_b8_n2048"]
+    w = workloads.WORKLOADS["block_bf16_b4_n8192"]
     line = {"metric": "MSR fwd tokens/s + %MFMA peak (chunkwise); decode steps/s + %HBM peak",
             "value": None, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
             "ms_per_step": None, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
             "data": "synthetic (seeded Gaussian inputs and random-init weights)",
             "config": {"workload": w.name, "batch": w.batch, "seqlen": w.seqlen, "d_model": w.d_model,
-                       "heads": w.heads, "d_k": w.d_k, "d_v": w.d_v, "chunk": w.chunk, "form": "chunkwise"}}
+                       "heads": w.heads, "d_k": w.d_k, "d_v": w.d_v, "chunk": w.chunk, "form": "chunkwise",
+                       "step": "gated MSR layer forward"}}
     if "layer" in parts:
         log("layer", w.name)
-        r = bench_layer(w, args.steps, args.warmup)
+        r = bench_layer(w, args.steps, args.warmup, device_inputs=True)
         line["value"] = round(r["tokens_per_s"], 1)
         line["ms_per_step"] = round(r["s_per_step"] * 1e3, 4)
         line["ms_per_step_median"] = round(r["s_per_step_median"] * 1e3, 4)   # single-call events, a pass after
@@ -525,18 +565,33 @@ def main():
         dom = max(k, key=lambda n: r["trace_s_per_step"].get(n, 0))
         line["roofline"] = {x: k[dom][x] for x in ("bound", "achieved", "peak", "unit", "frac", "traffic")}
         line["roofline"]["kernel"] = dom
+        line["chunkwise"] = r["chunkwise"]
         line["kernels"] = k
         line["trace_ms_per_step"] = {n: round(v * 1e3, 4) for n, v in r["trace_s_per_step"].items()}
+        # the chunkwise core alone at this shape (projected Q, K, V; d_v = 512)
+        bc = bench_core(w.batch, w.seqlen, w.heads, w.d_k, w.chunk, max(3, args.steps // 2), 2, dv=w.d_v)
+        line["core_chunkwise"] = {
+            "tokens_per_s": round(bc["tokens_per_s"], 1), "us_per_step": round(bc["s"] * 1e6, 1),
+            "tflops": round(bc["tflops"], 1), "mfma_frac": round(bc["mfma_frac"], 4), "kernels": bc["kernels"]}
     if "decode" in parts:
         log("decode")
         line["decode"] = bench_decode(512, 16)
         log("layer decode")
-        line["layer_decode"] = bench_layer_decode(64, 8)
+        line["layer_decode"] = bench_layer_decode(512, 16)
+    if "small" in parts:
+        sw = workloads.WORKLOADS["layer_bf16_b8_n2048"]
+        log("layer", sw.name)
+        r = bench_layer(sw, args.steps, args.warmup)
+        line["layer_b8_n2048"] = {"tokens_per_s": round(r["tokens_per_s"], 1), "mfma_frac": round(r["mfma_frac"], 4),
+                                  "ms_per_step": round(r["s_per_step"] * 1e3, 4), "tflops": round(r["tflops"], 1),
+                                  "chunkwise": r["chunkwise"], "kernels": r["kernels"]}
     if "long" in parts:
         log("long")
         lw = workloads.WORKLOADS["long_bf16_b2_n16384"]
         long = {"core_chunkwise": bench_core(lw.batch, lw.seqlen, lw.heads, lw.d_k, lw.chunk, args.steps,
-                                             args.warmup)}
+                                             args.warmup),
+                "core_chunkwise_rotated": bench_core(lw.batch, lw.seqlen, lw.heads, lw.d_k, lw.chunk, args.steps,
+                                                     args.warmup, rope_base=lw.rope_base)}
         sweep = []
         for N in (1024, 2048, 4096, 8192, 16384):
             c = bench_core(lw.batch, N, lw.heads, lw.d_k, lw.chunk, 5, 2)
@@ -546,20 +601,8 @@ def main():
         long["sweep"] = sweep
         lr = bench_layer(lw, max(3, args.steps // 4), 2, device_inputs=True)
         long["layer"] = {"tokens_per_s": round(lr["tokens_per_s"], 1), "mfma_frac": round(lr["mfma_frac"], 4),
-                         "ms_per_step": round(lr["s_per_step"] * 1e3, 3)}
+                         "ms_per_step": round(lr["s_per_step"] * 1e3, 3), "chunkwise": lr["chunkwise"]}
         line["long"] = long
-    if "block" in parts:
-        log("block")
-        bw = workloads.WORKLOADS["block_bf16_b4_n8192"]
-        br = bench_layer(bw, max(3, args.steps // 4), 2, device_inputs=True)
-        line["block"] = {"tokens_per_s": round(br["tokens_per_s"], 1), "mfma_frac": round(br["mfma_frac"], 4),
-                         "ms_per_step": round(br["s_per_step"] * 1e3, 3), "tflops": round(br["tflops"], 1),
-                         "kernels": br["kernels"]}
-        # the chunkwise core alone at the block workload's shape (d_v = 512)
-        bc = bench_core(bw.batch, bw.seqlen, bw.heads, bw.d_k, bw.chunk, max(3, args.steps // 4), 2, dv=bw.d_v)
-        line["block"]["core_chunkwise"] = {
-            "tokens_per_s": round(bc["tokens_per_s"], 1), "us_per_step": round(bc["s"] * 1e6, 1),
-            "tflops": round(bc["tflops"], 1), "mfma_frac": round(bc["mfma_frac"], 4), "kernels": bc["kernels"]}
     if "retnet" in parts:
         log("retnet block")
         line["retnet_block"] = bench_retnet_block(max(3, args.steps // 2), 2)

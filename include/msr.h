@@ -62,10 +62,22 @@ typedef enum {
   MSR_ERR_DTYPE = 3,        /* unknown dtype */
   MSR_ERR_UNSUPPORTED = 4,  /* valid but not implemented (head dim, chunk) */
   MSR_ERR_WORKSPACE = 5,    /* workspace missing or too small */
-  MSR_ERR_HIP = 6           /* the HIP runtime reported an error */
+  MSR_ERR_HIP = 6,          /* the HIP runtime reported an error */
+  /* range markers, never returned: any int32 is a valid value of the type */
+  MSR_STATUS_RANGE_MIN_ = -2147483647 - 1,
+  MSR_STATUS_RANGE_MAX_ = 2147483647
 } msr_status;
 
-typedef enum { MSR_F32 = 0, MSR_BF16 = 1 } msr_dtype;
+/* The two range markers are not dtypes (they are rejected as
+ * MSR_ERR_DTYPE); they give the enum the full int32 range, so that any
+ * integer a caller passes is a valid value of the type and can be checked
+ * (in C++ a value outside an enum's range is undefined behaviour). */
+typedef enum {
+  MSR_F32 = 0,
+  MSR_BF16 = 1,
+  MSR_DTYPE_RANGE_MIN_ = -2147483647 - 1,
+  MSR_DTYPE_RANGE_MAX_ = 2147483647
+} msr_dtype;
 
 typedef struct {
   int32_t batch, seqlen, heads, d_k, d_v;

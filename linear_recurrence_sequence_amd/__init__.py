@@ -1,8 +1,9 @@
 """Python binding of libmsr (multi-scale retention on MI355X / gfx950).
 
-Argument marshalling only: every function below validates nothing beyond
-what it needs to build the C call, and every step of the computation runs in
-the HIP kernels of ``libmsr.so``.  PyTorch supplies device memory and the
+Argument marshalling only: every function below checks the dtype, shape and
+device of the tensors it is given (so that no wrong buffer reaches a
+kernel) and builds the C call; every step of the computation runs in the
+HIP kernels of ``libmsr.so``.  PyTorch supplies device memory and the
 current stream.  The C functions carry the same names; their contracts are
 documented in ``include/msr.h``.
 
@@ -41,7 +42,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 
 
 def library_path() -> str:
-    return os.path.join(_HERE, "libmsr.so")
+    """The in-tree libmsr.so, or the build named by MSR_LIBRARY (e.g. the
+    host-sanitizer build of build_sanitized.py)."""
+    return os.environ.get("MSR_LIBRARY") or os.path.join(_HERE, "libmsr.so")
 
 
 class MsrError(RuntimeError):
@@ -174,6 +177,26 @@ def _ptr(t):
     return t.data_ptr()
 
 
+def _need(name, t, shape, dtype, device=None):
+    """Check a caller's tensor before any pointer reaches the library: its
+    dtype, exact shape and device (a wrong buffer would let a kernel read
+    or write past the allocation).  None is allowed by the caller only
+    where the argument is optional, so it is not checked here."""
+    if t is None:
+        return
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _need_ws(workspace, device):
+    if workspace is not None and (workspace.device != device or not workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous tensor on the inputs' device")
+
+
 def _gamma(gamma, heads):
     import numpy as np
     g = np.ascontiguousarray(np.asarray(gamma, dtype=np.float64).reshape(-1))
@@ -216,6 +239,10 @@ def msr_parallel_fwd(Q, K, V, gamma, *, rope_base=0.0, pos0=0, qk_scale=1.0, O=N
     B, N, H, dk = Q.shape
     dv = V.shape[-1]
     dt = _dtype_code(Q)
+    _need("K", K, Q.shape, Q.dtype, Q.device)
+    _need("V", V, (B, N, H, dv), Q.dtype, Q.device)
+    _need("O", O, (B, N, H, dv), Q.dtype, Q.device)
+    _need_ws(workspace, Q.device)
     if O is None:
         O = _torch().empty((B, N, H, dv), dtype=Q.dtype, device=Q.device)
     _, gp = g = _gamma(gamma, H)
@@ -233,6 +260,7 @@ def msr_chunkwise_fwd(Q, K, V, gamma, chunk, *, rope_base=0.0, pos0=0, qk_scale=
     B, N, H, dk = Q.shape
     dv = V.shape[-1]
     dt = _dtype_code(Q)
+    _check_core(Q, K, V, O, S_in, S_out, workspace)
     if O is None:
         O = _torch().empty((B, N, H, dv), dtype=Q.dtype, device=Q.device)
     _, gp = g = _gamma(gamma, H)
@@ -242,6 +270,21 @@ def msr_chunkwise_fwd(Q, K, V, gamma, chunk, *, rope_base=0.0, pos0=0, qk_scale=
                                                         _ptr(K), _ptr(V), _ptr(S_in), _ptr(S_out), _ptr(O),
                                                         _ptr(ws), wsb, _stream(stream)))
     return O
+
+
+def _check_core(Q, K, V, O, S_in, S_out, workspace, R_chunks=None, chunk=None):
+    """Shapes, dtypes and devices of a chunkwise call's tensors."""
+    torch = _torch()
+    B, N, H, dk = Q.shape
+    dv = V.shape[-1]
+    _need("K", K, Q.shape, Q.dtype, Q.device)
+    _need("V", V, (B, N, H, dv), Q.dtype, Q.device)
+    _need("O", O, (B, N, H, dv), Q.dtype, Q.device)
+    _need("S_in", S_in, (B, H, dk, dv), torch.float32, Q.device)
+    _need("S_out", S_out, (B, H, dk, dv), torch.float32, Q.device)
+    if chunk is not None and chunk > 0:
+        _need("R_chunks", R_chunks, msr_chunkwise_states_shape(B, N, H, dk, dv, chunk), Q.dtype, Q.device)
+    _need_ws(workspace, Q.device)
 
 
 def msr_chunkwise_states_shape(B, N, H, d_k, d_v, chunk):
@@ -257,6 +300,9 @@ def msr_chunkwise_fwd_save(Q, K, V, gamma, chunk, R_chunks, *, rope_base=0.0, po
     B, N, H, dk = Q.shape
     dv = V.shape[-1]
     dt = _dtype_code(Q)
+    if R_chunks is None:
+        raise ValueError("R_chunks is required")
+    _check_core(Q, K, V, O, S_in, S_out, workspace, R_chunks, chunk)
     if O is None:
         O = _torch().empty((B, N, H, dv), dtype=Q.dtype, device=Q.device)
     _, gp = g = _gamma(gamma, H)
@@ -282,6 +328,7 @@ def msr_chunkwise_bwd(Q, K, V, dO, gamma, chunk, *, rope_base=0.0, pos0=0, qk_sc
     B, N, H, dk = Q.shape
     dv = V.shape[-1]
     dt = _dtype_code(Q)
+    _check_bwd(Q, K, V, dO, S_in, dS_out, dS_in, dQ, dK, dV, workspace)
     t = _torch()
     dQ = t.empty_like(Q) if dQ is None else dQ
     dK = t.empty_like(K) if dK is None else dK
@@ -296,6 +343,19 @@ def msr_chunkwise_bwd(Q, K, V, dO, gamma, chunk, *, rope_base=0.0, pos0=0, qk_sc
     return dQ, dK, dV
 
 
+def _check_bwd(Q, K, V, dO, S_in, dS_out, dS_in, dQ, dK, dV, workspace, R_chunks=None, chunk=None):
+    torch = _torch()
+    B, N, H, dk = Q.shape
+    dv = V.shape[-1]
+    _check_core(Q, K, V, None, S_in, None, workspace, R_chunks, chunk)
+    _need("dO", dO, (B, N, H, dv), Q.dtype, Q.device)
+    _need("dS_out", dS_out, (B, H, dk, dv), torch.float32, Q.device)
+    _need("dS_in", dS_in, (B, H, dk, dv), torch.float32, Q.device)
+    _need("dQ", dQ, Q.shape, Q.dtype, Q.device)
+    _need("dK", dK, Q.shape, Q.dtype, Q.device)
+    _need("dV", dV, (B, N, H, dv), Q.dtype, Q.device)
+
+
 def msr_chunkwise_bwd_saved(Q, K, V, dO, gamma, chunk, R_chunks, *, rope_base=0.0, pos0=0, qk_scale=1.0,
                             S_in=None, dS_out=None, dS_in=None, dQ=None, dK=None, dV=None, workspace=None,
                             stream=None):
@@ -304,6 +364,9 @@ def msr_chunkwise_bwd_saved(Q, K, V, dO, gamma, chunk, R_chunks, *, rope_base=0.
     B, N, H, dk = Q.shape
     dv = V.shape[-1]
     dt = _dtype_code(Q)
+    if R_chunks is None:
+        raise ValueError("R_chunks is required")
+    _check_bwd(Q, K, V, dO, S_in, dS_out, dS_in, dQ, dK, dV, workspace, R_chunks, chunk)
     t = _torch()
     dQ = t.empty_like(Q) if dQ is None else dQ
     dK = t.empty_like(K) if dK is None else dK
@@ -328,6 +391,15 @@ def msr_rglru_fwd(X, W_a, b_a, W_x, b_x, Lambda, *, c=8.0, h0=None, h_last=None,
     Returns Y [B, T, width]."""
     B, T, D = X.shape
     dt = _dtype_code(X)
+    f32 = _torch().float32
+    _need("W_a", W_a, (D, D), X.dtype, X.device)
+    _need("W_x", W_x, (D, D), X.dtype, X.device)
+    for name, t in (("b_a", b_a), ("b_x", b_x), ("Lambda", Lambda)):
+        _need(name, t, (D,), f32, X.device)
+    _need("h0", h0, (B, D), f32, X.device)
+    _need("h_last", h_last, (B, D), f32, X.device)
+    _need("Y", Y, X.shape, X.dtype, X.device)
+    _need_ws(workspace, X.device)
     Y = _torch().empty_like(X) if Y is None else Y
     ws, wsb = _workspace(lib().msr_rglru_workspace_bytes(dt, B, T, D), workspace, X.device)
     _check("msr_rglru_fwd", lib().msr_rglru_fwd(dt, B, T, D, c, _ptr(X), _ptr(W_a), _ptr(b_a), _ptr(W_x), _ptr(b_x),
@@ -342,6 +414,12 @@ def msr_recurrent_step(q, k, v, S, gamma, *, pos, rope_base=0.0, qk_scale=1.0, o
     B, H, dk = q.shape
     dv = v.shape[-1]
     dt = _dtype_code(q)
+    if S is None:
+        raise ValueError("S is required")
+    _need("k", k, q.shape, q.dtype, q.device)
+    _need("v", v, (B, H, dv), q.dtype, q.device)
+    _need("S", S, (B, H, dk, dv), _torch().float32, q.device)
+    _need("o", o, (B, H, dv), q.dtype, q.device)
     if o is None:
         o = _torch().empty((B, H, dv), dtype=q.dtype, device=q.device)
     _, gp = g = _gamma(gamma, H)
@@ -356,6 +434,9 @@ def msr_layer_fwd(X, W_Q, W_K, W_V, W_G, W_O, gamma, heads, d_k, d_v, chunk, *, 
     """Gated MSR layer (Eq. 8).  X: [B, N, d_model]; returns [B, N, d_model]."""
     B, N, dm = X.shape
     dt = _dtype_code(X)
+    _check_layer_weights(X, dm, heads, d_k, d_v, W_Q, W_K, W_V, W_G, W_O)
+    _need("out", out, X.shape, X.dtype, X.device)
+    _need_ws(workspace, X.device)
     if out is None:
         out = _torch().empty((B, N, dm), dtype=X.dtype, device=X.device)
     _, gp = g = _gamma(gamma, heads)
@@ -365,6 +446,15 @@ def msr_layer_fwd(X, W_Q, W_K, W_V, W_G, W_O, gamma, heads, d_k, d_v, chunk, *, 
                                                 _ptr(X), _ptr(W_Q), _ptr(W_K), _ptr(W_V), _ptr(W_G), _ptr(W_O),
                                                 _ptr(out), _ptr(ws), wsb, _stream(stream)))
     return out
+
+
+def _check_layer_weights(X, dm, heads, d_k, d_v, W_Q, W_K, W_V, W_G, W_O):
+    for name, t, shape in (("W_Q", W_Q, (dm, heads * d_k)), ("W_K", W_K, (dm, heads * d_k)),
+                           ("W_V", W_V, (dm, heads * d_v)), ("W_G", W_G, (dm, heads * d_v)),
+                           ("W_O", W_O, (heads * d_v, dm))):
+        if t is None:
+            raise ValueError(f"{name} is required")
+        _need(name, t, shape, X.dtype, X.device)
 
 
 def msr_retnet_block_workspace_bytes(dtype, batch, seqlen, d_model, heads, d_k, d_v, chunk, d_ffn):
@@ -377,6 +467,11 @@ def msr_retnet_block_fwd(X, W_Q, W_K, W_V, W_G, W_O, W_1, W_2, gamma, heads, d_k
     B, N, dm = X.shape
     d_ffn = W_1.shape[1]
     dt = _dtype_code(X)
+    _check_layer_weights(X, dm, heads, d_k, d_v, W_Q, W_K, W_V, W_G, W_O)
+    _need("W_1", W_1, (dm, d_ffn), X.dtype, X.device)
+    _need("W_2", W_2, (d_ffn, dm), X.dtype, X.device)
+    _need("out", out, X.shape, X.dtype, X.device)
+    _need_ws(workspace, X.device)
     if out is None:
         out = _torch().empty((B, N, dm), dtype=X.dtype, device=X.device)
     _, gp = g = _gamma(gamma, heads)
@@ -399,8 +494,12 @@ def msr_layer_decode_step(X, W_Q, W_K, W_V, W_G, W_O, S, gamma, heads, d_k, d_v,
     sequence); S: [B, heads, d_k, d_v] float32, updated in place; returns out [B, d_model]."""
     B, dm = X.shape
     dt = _dtype_code(X)
-    if S.dtype != _torch().float32:
-        raise TypeError("S must be float32")
+    _check_layer_weights(X, dm, heads, d_k, d_v, W_Q, W_K, W_V, W_G, W_O)
+    if S is None:
+        raise ValueError("S is required")
+    _need("S", S, (B, heads, d_k, d_v), _torch().float32, X.device)
+    _need("out", out, X.shape, X.dtype, X.device)
+    _need_ws(workspace, X.device)
     if out is None:
         out = _torch().empty((B, dm), dtype=X.dtype, device=X.device)
     _, gp = g = _gamma(gamma, heads)

@@ -291,6 +291,7 @@ const char* msr_status_str(msr_status s) {
     case MSR_ERR_UNSUPPORTED: return "MSR_ERR_UNSUPPORTED";
     case MSR_ERR_WORKSPACE: return "MSR_ERR_WORKSPACE";
     case MSR_ERR_HIP: return "MSR_ERR_HIP";
+    default: break;
   }
   return "MSR_ERR_UNKNOWN";
 }

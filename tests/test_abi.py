@@ -37,6 +37,8 @@ def test_status_strings():
     names = [msr.msr_status_str(i) for i in range(7)]
     assert names == ["MSR_OK", "MSR_ERR_NULL", "MSR_ERR_SHAPE", "MSR_ERR_DTYPE", "MSR_ERR_UNSUPPORTED",
                      "MSR_ERR_WORKSPACE", "MSR_ERR_HIP"]
+    # any int32 is a value of the enum: out-of-range codes are named, not undefined
+    assert msr.msr_status_str(99) == msr.msr_status_str(-2 ** 31) == "MSR_ERR_UNKNOWN"
 
 
 def _gamma(n):
@@ -57,6 +59,8 @@ def _chunkwise(dtype=0, dims=(1, 64, 2, 64, 64), chunk=32, gamma=True, ws=(FAKE,
 
 def test_chunkwise_validation():
     assert _chunkwise(dtype=7) == 3                               # dtype
+    assert _chunkwise(dtype=-1) == 3
+    assert _chunkwise(dtype=2 ** 31 - 1) == 3
     assert _chunkwise(dims=(1, 64, 2, 64, 96)) == 4               # unsupported head dims
     assert _chunkwise(dims=(1, 64, 2, 48, 48)) == 4
     assert _chunkwise(dims=(-1, 64, 2, 64, 64)) == 2              # negative size
@@ -235,3 +239,55 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(msr, "library_path", lambda: str(tmp_path / "missing.so"))
     with pytest.raises(msr.MsrLibraryMissing):
         msr.lib()
+
+
+def test_binding_rejects_wrong_tensors_before_the_call():
+    """The binding checks dtype, shape and device of every tensor it is
+    given before any pointer reaches the library (CPU tensors here: the
+    checks run first, so no GPU is touched, and a correct set of shapes
+    gets as far as the device check)."""
+    import torch
+    B, N, H, d, C = 1, 64, 2, 64, 32
+    bf = torch.bfloat16
+    Q, K, V = (torch.zeros((B, N, H, d), dtype=bf) for _ in range(3))
+    g = np.full(H, 0.9)
+    bad = [
+        (dict(S_in=torch.zeros((B, H, d, d), dtype=bf)), "S_in must be torch.float32"),
+        (dict(S_out=torch.zeros((B, H, d, d + 1))), "S_out must have shape"),
+        (dict(O=torch.zeros((B, N, H, d), dtype=torch.float32)), "O must be torch.bfloat16"),
+    ]
+    for kw, msg in bad:
+        with pytest.raises(ValueError, match=msg):
+            msr.msr_chunkwise_fwd(Q, K, V, g, C, **kw)
+    with pytest.raises(ValueError, match="K must have shape"):
+        msr.msr_chunkwise_fwd(Q, K[:, :32], V, g, C)
+    with pytest.raises(ValueError, match="V must be torch.bfloat16"):
+        msr.msr_parallel_fwd(Q, K, V.float(), g)
+    with pytest.raises(ValueError, match="R_chunks must have shape"):
+        msr.msr_chunkwise_fwd_save(Q, K, V, g, C, torch.zeros((B, H, 3, d, d), dtype=bf))
+    with pytest.raises(ValueError, match="R_chunks must be torch.bfloat16"):
+        msr.msr_chunkwise_fwd_save(Q, K, V, g, C, torch.zeros(msr.msr_chunkwise_states_shape(B, N, H, d, d, C)))
+    with pytest.raises(ValueError, match="dS_out must be torch.float32"):
+        msr.msr_chunkwise_bwd(Q, K, V, Q, g, C, dS_out=torch.zeros((B, H, d, d), dtype=bf))
+    with pytest.raises(ValueError, match="dV must have shape"):
+        msr.msr_chunkwise_bwd(Q, K, V, Q, g, C, dV=torch.zeros((B, N, H, 2 * d), dtype=bf))
+    q1 = torch.zeros((B, H, d), dtype=bf)
+    with pytest.raises(ValueError, match="S must be torch.float32"):
+        msr.msr_recurrent_step(q1, q1, q1, torch.zeros((B, H, d, d), dtype=bf), g, pos=0)
+    with pytest.raises(ValueError, match="S must have shape"):
+        msr.msr_recurrent_step(q1, q1, q1, torch.zeros((B, H, d, 2 * d)), g, pos=0)
+    dm = 192
+    X = torch.zeros((B, N, dm), dtype=bf)
+    W = [torch.zeros(s, dtype=bf) for s in ((dm, H * d),) * 4 + ((H * d, dm),)]
+    with pytest.raises(ValueError, match="W_O must have shape"):
+        msr.msr_layer_fwd(X, *W[:4], W[0], g, H, d, d, C)
+    with pytest.raises(ValueError, match="W_G must be torch.bfloat16"):
+        msr.msr_layer_fwd(X, *W[:3], W[3].float(), W[4], g, H, d, d, C)
+    with pytest.raises(ValueError, match="S must have shape"):
+        msr.msr_layer_decode_step(X[:, 0], *W, torch.zeros((B, H, d, d + 2)), g, H, d, d, 0)
+    with pytest.raises(ValueError, match="Lambda must be torch.float32"):
+        Wsq = torch.zeros((dm, dm), dtype=bf)
+        msr.msr_rglru_fwd(X, Wsq, torch.zeros(dm), Wsq, torch.zeros(dm), torch.zeros(dm, dtype=bf))
+    # shapes and dtypes right: the next check is the device
+    with pytest.raises(ValueError, match="on the GPU"):
+        msr.msr_chunkwise_fwd(Q, K, V, g, C, S_out=torch.zeros((B, H, d, d)))

@@ -2,14 +2,16 @@
 layer, residual, LayerNorm, gelu feed-forward network, residual) against the
 float64 oracle: small shapes in both precisions with a ragged sequence, and
 the b8 x 2048 layer shape with a 4096-wide feed-forward network on a sampled
-batch element.  Rows whose layer-internal GroupNorm is ill-conditioned (the
-same criterion as the layer tests) are excluded and counted."""
+batch element.  Row 0 of a batch element is left out where the rounding of
+its single scores can move the layer inside the block by more than half the
+tolerance (the layer tests' criterion, on the LayerNorm output); such rows
+must still be finite."""
 import numpy as np
 import pytest
 
 import oracle
 import workloads
-from gpu_util import TOL, dev, host, layer_err, say
+from gpu_util import TOL, dev, host, first_token_bound, layer_err, say
 
 pytestmark = pytest.mark.gpu
 
@@ -26,14 +28,14 @@ def _weights(rng, dm, H, dk, dv, F, dtype):
             n((F, dm), F ** -0.5))
 
 
-def _check(X, Ws, g, H, dk, dv, C, got, dtype, limit):
+def _check(X, Ws, g, H, dk, dv, C, got, dtype):
     WQ, WK, WV, WG, WO, W1, W2 = Ws
     ref = oracle.retnet_block(X, WQ, WK, WV, WG, WO, W1, W2, g, H, dk, dv, C, gn_eps=1e-5, ln_eps=1e-5)
-    _, gv = oracle.msr_layer(oracle.layer_norm(X, 1e-5), WQ, WK, WV, WG, WO, g, H, dk, dv, C, eps=1e-5,
-                             return_gn_var=True)
-    err, excluded = layer_err(got, ref, gv, 1e-5)
-    print(f"block err {err:.2e} (excluded rows {excluded:.2e})", flush=True)
-    assert err < TOL[dtype] and excluded < limit
+    bound0 = first_token_bound(oracle.layer_norm(X, 1e-5), WQ, WK, WV, WG, WO, H, dk, dv, dtype, 1e-5,
+                               rounded_input=dtype == "bf16")
+    err, excluded = layer_err(got, ref, bound0, dtype, row0_bound=False)
+    print(f"block err {err:.2e} (excluded first-token rows {excluded})", flush=True)
+    assert err < TOL[dtype]
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -47,7 +49,7 @@ def test_block_small(dtype):
     say("retnet block", dtype, B, N, dm, F)
     out = msr.msr_retnet_block_fwd(dev(X, dtype), *(dev(w, dtype) for w in Ws), g, H, d, d, C, rope_base=1e4,
                                    gn_eps=1e-5, ln_eps=1e-5)
-    _check(X, Ws, g, H, d, d, C, host(out), dtype, 1e-2)
+    _check(X, Ws, g, H, d, d, C, host(out), dtype)
 
 
 @pytest.mark.slow
@@ -68,5 +70,4 @@ def test_block_b8_n2048_sampled():
                                    w.d_v, w.chunk, rope_base=w.rope_base, gn_eps=1e-5, ln_eps=1e-5)
     torch.cuda.synchronize()
     b = 5
-    _check(X[b:b + 1], (WQ, WK, WV, WG, WO, W1, W2), g, w.heads, w.d_k, w.d_v, w.chunk, host(out)[b:b + 1], "bf16",
-           1e-3)
+    _check(X[b:b + 1], (WQ, WK, WV, WG, WO, W1, W2), g, w.heads, w.d_k, w.d_v, w.chunk, host(out)[b:b + 1], "bf16")

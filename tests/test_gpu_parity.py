@@ -8,7 +8,7 @@ import pytest
 
 import oracle
 import workloads
-from gpu_util import TOL, dev, host, layer_err, say
+from gpu_util import TOL, dev, host, first_token_bound, layer_err, say
 
 pytestmark = pytest.mark.gpu
 
@@ -144,10 +144,11 @@ def test_layer(dtype, B, N, dm, H, dk, dv, chunk):
     out = msr.msr_layer_fwd(*(dev(a, dtype) for a in (X, WQ, WK, WV, WG, WO)), g, H, dk, dv, chunk,
                             rope_base=10000.0, gn_eps=1e-5)
     torch.cuda.synchronize()
-    ref, gv = oracle.msr_layer(X, WQ, WK, WV, WG, WO, g, H, dk, dv, chunk, rope_base=10000.0, eps=1e-5,
-                               return_gn_var=True)
-    err, excluded = layer_err(host(out), ref, gv, 1e-5)
-    assert err < TOL[dtype] and excluded < 1e-2
+    ref = oracle.msr_layer(X, WQ, WK, WV, WG, WO, g, H, dk, dv, chunk, rope_base=10000.0, eps=1e-5)
+    bound0 = first_token_bound(X, WQ, WK, WV, WG, WO, H, dk, dv, dtype, 1e-5)
+    err, excluded = layer_err(host(out), ref, bound0, dtype)
+    print(f"layer {dtype} err {err:.2e}, excluded first-token rows {excluded}", flush=True)
+    assert err < TOL[dtype]
 
 
 def test_fp32_workload_three_forms():

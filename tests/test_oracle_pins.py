@@ -599,3 +599,100 @@ def test_rglru_input_recipe():
     ac = np.exp(8.0 * oracle.log_sigmoid(lam.astype(np.float64)))
     assert ac.min() >= 0.9 - 1e-6 and ac.max() <= 0.999 + 1e-6
     assert 0.93 < ac.mean() < 0.97
+
+
+# ------------------------------------------------------- Eq. (8), by hand --
+# A two-token, two-head layer small enough to work out on paper ([RN-zh]
+# "門控多尺度 Retention", Eq. (8): Y = GroupNorm_h(Concat_h head_h),
+# MSR(X) = (swish(X W_G) (.) Y) W_O).  X is the 2 x 2 identity, so row n of
+# each weight matrix is token n's projection; head h owns columns 2h, 2h+1.
+# No rotation, score scale s = 1/sqrt(d_k) = 1/sqrt(2), eps = 1/2,
+# gamma = (1/2, 1/4).
+#
+#   token 0: q = (1, 0 | 1, 1)   k = (1, 0 | 1, 1)   v = (2, 0 | 1, 3)   g = (1, -1 | 0, 2)
+#   token 1: q = (1, 1 | 2, 0)   k = (1, 1 | 1, 1)   v = (0, 4 | -1, 1)  g = (2, 0 | -2, 1)
+#
+# Retention, o_n = s sum_{m <= n} gamma^(n-m) (q_n . k_m) v_m:
+#   head 0: o_0 = s (2, 0);   o_1 = s [ 1/2 * 1 * (2, 0) + 2 * (0, 4) ] = s (1, 8)
+#   head 1: o_0 = s 2 (1, 3) = s (2, 6);   o_1 = s [ 1/4 * 2 * (1, 3) + 2 * (-1, 1) ] = s (-3/2, 7/2)
+# GroupNorm of a pair (a, b): deviations +-(a - b)/2, variance ((a - b)/2)^2,
+#   y = (a - b)/2 / sqrt(((a - b)/2)^2 + eps) * (1, -1):
+#   head 0, token 0: (a-b)/2 = s,       var 1/2   -> y = (1, -1) / sqrt(2)
+#   head 0, token 1: (a-b)/2 = -7s/2,   var 49/8  -> y = (-7, 7) / sqrt(53)
+#   head 1, token 0: (a-b)/2 = -2s,     var 2     -> y = (-2, 2) / sqrt(5)
+#   head 1, token 1: (a-b)/2 = -5s/2,   var 25/8  -> y = (-5, 5) / sqrt(29)
+# Gate z = swish(g) (.) y, then out = z W_O with W_O rows (1,0), (0,1), (1,1), (0,-1):
+#   out_n = (z0 + z2, z1 + z2 - z3).
+_EQ8_W = {
+    "WQ": [[1, 0, 1, 1], [1, 1, 2, 0]],
+    "WK": [[1, 0, 1, 1], [1, 1, 1, 1]],
+    "WV": [[2, 0, 1, 3], [0, 4, -1, 1]],
+    "WG": [[1, -1, 0, 2], [2, 0, -2, 1]],
+    "WO": [[1, 0], [0, 1], [1, 1], [0, -1]],
+}
+_EQ8_GAMMA = np.array([0.5, 0.25])
+
+
+def _sw(x):
+    return x / (1.0 + math.exp(-x))
+
+
+def _eq8_by_hand():
+    r2, r5, r29, r53 = math.sqrt(2), math.sqrt(5), math.sqrt(29), math.sqrt(53)
+    z0 = [_sw(1) / r2, _sw(-1) * (-1 / r2), _sw(0) * (-2 / r5), _sw(2) * (2 / r5)]
+    z1 = [_sw(2) * (-7 / r53), _sw(0) * (7 / r53), _sw(-2) * (-5 / r29), _sw(1) * (5 / r29)]
+    out = [[z[0] + z[2], z[1] + z[2] - z[3]] for z in (z0, z1)]
+    # state after both tokens, S_h = gamma_h k_0^T v_0 + k_1^T v_1
+    S = [[[0.5 * 2 + 0, 0 + 4], [0 + 0, 0 + 4]],
+         [[0.25 * 1 - 1, 0.25 * 3 + 1], [0.25 * 1 - 1, 0.25 * 3 + 1]]]
+    return np.array([out]), np.array([S])
+
+
+def _eq8_weights():
+    return [np.array(_EQ8_W[n], dtype=np.float64) for n in ("WQ", "WK", "WV", "WG", "WO")]
+
+
+def test_layer_composition_by_hand():
+    """oracle.msr_layer (all three retention forms) and two decode steps of
+    oracle.msr_layer_decode_step equal the hand-derived values above."""
+    want, S_want = _eq8_by_hand()
+    X = np.eye(2)[None]
+    W = _eq8_weights()
+    for form, chunk in (("parallel", None), ("recurrent", None), ("chunkwise", 1), ("chunkwise", 2)):
+        got = oracle.msr_layer(X, *W, _EQ8_GAMMA, 2, 2, 2, chunk=chunk, rope_base=0.0, eps=0.5, form=form)
+        assert np.max(np.abs(got - want)) < 1e-14, form
+    S = np.zeros((1, 2, 2, 2))
+    for n in range(2):
+        out, S = oracle.msr_layer_decode_step(X[:, n], S, *W, _EQ8_GAMMA, 2, 2, 2, pos=n, rope_base=0.0, eps=0.5)
+        assert np.max(np.abs(out - want[:, n])) < 1e-14
+    assert np.max(np.abs(S - S_want)) < 1e-15
+
+
+def test_layer_composition_pin_rejects_misreadings():
+    """The hand-derived value separates Eq. (8) from plausible misreadings
+    of it, each built here from the oracle's own parts: the gate applied
+    before the GroupNorm, swish taken of the normalised heads instead of the
+    gate branch, no swish, a sigmoid gate, one GroupNorm over all heads, and
+    the heads' rows of W_O exchanged."""
+    want, _ = _eq8_by_hand()
+    X = np.eye(2)[None]
+    WQ, WK, WV, WG, WO = _eq8_weights()
+    s = 1 / math.sqrt(2)
+    q = (X @ WQ).reshape(1, 2, 2, 2)
+    k = (X @ WK).reshape(1, 2, 2, 2)
+    v = (X @ WV).reshape(1, 2, 2, 2)
+    g = X @ WG
+    o = oracle.retention_parallel(q, k, v, _EQ8_GAMMA, s)
+    gn = lambda t: oracle.group_norm_heads(t, 0.5).reshape(1, 2, 4)
+    wrong = {
+        "gate before GroupNorm": gn(oracle.swish(g).reshape(1, 2, 2, 2) * o) @ WO,
+        "swish of the heads": (g * oracle.swish(gn(o))) @ WO,
+        "no swish": (g * gn(o)) @ WO,
+        "sigmoid gate": ((1 / (1 + np.exp(-g))) * gn(o)) @ WO,
+        "one group": (oracle.swish(g) * oracle.group_norm_heads(o.reshape(1, 2, 1, 4), 0.5).reshape(1, 2, 4)) @ WO,
+        "heads swapped in W_O": (oracle.swish(g) * gn(o)) @ WO[[2, 3, 0, 1]],
+    }
+    right = (oracle.swish(g) * gn(o)) @ WO
+    assert np.max(np.abs(right - want)) < 1e-14
+    for name, val in wrong.items():
+        assert np.max(np.abs(val - want)) > 1e-2, name
