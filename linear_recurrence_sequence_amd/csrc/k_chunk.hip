@@ -1179,6 +1179,8 @@ static hipError_t run_chunkwise(const ChunkArgs& a, const HeadTab& tab, hipStrea
   {
     TraceScope ts("k_chunk_out", st);
     const int has_sin = a.reuse_rx ? (int)a.reuse_seeded : (int)(a.S_in != nullptr);
+    if (chunk_out_o16(a.elt, DK, DV, Cn) && !a.rev_in && !a.rev_out && !a.rx_kv)
+      return launch_out_o16(a, true, Cn, NC, Cn / 128, has_sin, tab, st);
     if constexpr (sizeof(T) == 2 && DV <= 256) {
       if (Cn % 128 == 0) {
         launch_dl<DK, DV, true>(a, Cn, NC, Cn / 128, has_sin, tab, st);
@@ -1197,6 +1199,8 @@ template <class T, int DK, int DV>
 static hipError_t run_parallel(const ChunkArgs& a, const HeadTab& tab, hipStream_t st) {
   const int TPC = (a.seqlen + 127) / 128;
   TraceScope ts("k_chunk_out", st);
+  if (chunk_out_o16(a.elt, DK, DV, TPC * 128) && !a.rev_in && !a.rev_out)
+    return launch_out_o16(a, false, TPC * 128, 1, TPC, 0, tab, st);
   if constexpr (sizeof(T) == 2 && DV <= 256)
     launch_dl<DK, DV, false>(a, TPC * 128, 1, TPC, 0, tab, st);
   else

@@ -51,11 +51,23 @@ struct ChunkArgs {
   // holds each chunk's R_{i-1} itself, [d_k rows][d_v cols], instead of its
   // transpose
   bool rx_kv;
+  // (cos, sin) table [seqlen][d_k / 2] of the positions of the sequence's
+  // rows: the output kernel rotates Q with it as it loads Q (only where
+  // chunk_out_o16 holds; K must then already be rotated); null: Q as given
+  const float2* q_rope_tab;
 };
 
 // Whether the chunkwise form of these dims and chunk runs the bf16
 // direct-copy output kernel (the one that can read Rx as R_{i-1} itself).
 bool chunk_out_direct(Elt elt, int d_k, int d_v, int chunk);
+
+// Whether the forward output kernel with 16 query rows per wave runs these
+// dims and chunk (bf16, d_k 256, d_v 256 or 512, chunk a multiple of 128).
+bool chunk_out_o16(Elt elt, int d_k, int d_v, int chunk);
+// That kernel: the chunkwise form's outputs (state: Rx holds R_{i-1}^T per
+// chunk) or the parallel form's (one chunk of chunk = TPC * 128 rows).
+hipError_t launch_out_o16(const ChunkArgs& a, bool state, int chunk, int NC, int TPC, int has_sin,
+                          const HeadTab& tab, hipStream_t stream);
 
 // Chunkwise retention: state contributions, fp32 scan, outputs.
 hipError_t launch_chunkwise(const ChunkArgs& a, const HeadTab& tab, hipStream_t stream);

@@ -50,7 +50,10 @@ def test_recurrent_steps(dtype, dk, dv):
 
 
 # ------------------------------------------------------------- chunkwise ---
-CHUNK_CASES = [(200, 64), (256, 128), (97, 32), (300, 96), (1, 32), (513, 256)]
+# (the bf16 d_k 256 forms with a chunk that is a multiple of 128 run the
+# 16-rows-per-wave output kernel: 130 leaves a second row tile with two rows,
+# most of its waves without any; 777 / 384 three row tiles and a ragged chunk)
+CHUNK_CASES = [(200, 64), (256, 128), (97, 32), (300, 96), (1, 32), (513, 256), (130, 128), (777, 384)]
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -134,6 +137,8 @@ def _layer(dtype, B, N, dm, H, dk, dv, chunk, seed):
     ("f32", 2, 150, 128, 2, 64, 64, 32),
     ("bf16", 2, 300, 256, 2, 128, 128, 128),
     ("bf16", 1, 200, 256, 2, 256, 512, 64),
+    ("bf16", 2, 300, 256, 2, 256, 512, 128),     # GroupNorm + gate fused, 512-wide value heads
+    ("bf16", 1, 260, 256, 3, 256, 256, 256),
 ])
 def test_layer(dtype, B, N, dm, H, dk, dv, chunk):
     import torch
