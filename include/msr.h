@@ -28,8 +28,9 @@
  *           Eq. (3)-(4), xPos).  rope_base <= 0: no rotation.
  * Memory.   Every pointer except `gamma` is device memory allocated by the
  *           caller; the library allocates nothing and, apart from the
- *           opt-in msr_trace_* diagnostics, keeps no mutable global state
- *           (it is thread safe).  Outputs must not alias
+ *           opt-in msr_trace_* diagnostics and the static scratch of
+ *           msr_layer_decode_step_noalloc, keeps no mutable global state
+ *           (it is thread safe; that one entry point is not, per GPU).  Outputs must not alias
  *           inputs, except S of msr_recurrent_step and
  *           msr_layer_decode_step, which is updated in place.
  * Streams.  `stream` is a hipStream_t (NULL = the null stream).  Every call
@@ -274,6 +275,28 @@ msr_status msr_layer_decode_step(msr_dtype dtype, int32_t batch, int32_t d_model
 size_t msr_layer_decode_workspace_bytes(msr_dtype dtype, int32_t batch,
                                         int32_t d_model, int32_t heads,
                                         int32_t d_k, int32_t d_v);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation):
+ * msr_layer_decode_step with its workspace in a static device array of
+ * msr_layer_decode_noalloc_max_bytes() bytes (64 MiB) that each GPU holds
+ * from the time the library is loaded on it until the process ends.  Same
+ * arguments and results as msr_layer_decode_step, without the workspace;
+ * the array of the current device is used (the stream must belong to it).
+ * It allocates nothing and calls no allocating routine; the first call on a
+ * device looks up that device's copy of the array (hipGetSymbolAddress).
+ * Returns MSR_ERR_WORKSPACE, before anything is enqueued, when the step
+ * needs more than the array holds (msr_layer_decode_workspace_bytes() >
+ * msr_layer_decode_noalloc_max_bytes(), e.g. batch 256 at d_model 4096 with
+ * 16 heads of 256).  Every call on a GPU shares that GPU's array: calls that
+ * overlap on one GPU (several streams, several host threads) race. */
+msr_status msr_layer_decode_step_noalloc(msr_dtype dtype, int32_t batch, int32_t d_model,
+                                         int32_t heads, int32_t d_k, int32_t d_v,
+                                         const double* gamma, float rope_base, float gn_eps,
+                                         int64_t pos, const void* X, const void* W_Q,
+                                         const void* W_K, const void* W_V, const void* W_G,
+                                         const void* W_O, float* S, void* out, void* stream);
+size_t msr_layer_decode_noalloc_max_bytes(void);
 
 /* Diagnostics for benchmarks: per-kernel timing with HIP events.
  * msr_trace_enable(1) clears earlier totals and from then on brackets every

@@ -23,6 +23,7 @@ __all__ = [
     "msr_rglru_fwd", "msr_rglru_workspace_bytes",
     "msr_recurrent_step", "msr_layer_fwd", "msr_layer_workspace_bytes",
     "msr_layer_decode_step", "msr_layer_decode_workspace_bytes",
+    "msr_layer_decode_step_noalloc", "msr_layer_decode_noalloc_max_bytes",
     "msr_retnet_block_fwd", "msr_retnet_block_workspace_bytes",
     "msr_status_str", "msr_last_error", "msr_trace_enable", "msr_trace_count", "msr_trace_get",
     "trace_totals",
@@ -35,6 +36,7 @@ EXPORTS = (
     "msr_chunkwise_bwd_workspace_bytes", "msr_chunkwise_bwd_saved",
     "msr_rglru_fwd", "msr_rglru_workspace_bytes", "msr_recurrent_step", "msr_layer_fwd",
     "msr_layer_workspace_bytes", "msr_layer_decode_step", "msr_layer_decode_workspace_bytes",
+    "msr_layer_decode_step_noalloc", "msr_layer_decode_noalloc_max_bytes",
     "msr_retnet_block_fwd", "msr_retnet_block_workspace_bytes", "msr_status_str", "msr_last_error", "msr_trace_enable", "msr_trace_count", "msr_trace_get",
 )
 
@@ -101,6 +103,9 @@ def lib():
         "msr_layer_decode_step": (_I32, [_I32, _I32, _I32, _I32, _I32, _I32, _DP, _F, _F, _I64, _P, _P, _P, _P,
                                          _P, _P, _P, _P, _P, _SZ, _P]),
         "msr_layer_decode_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32]),
+        "msr_layer_decode_step_noalloc": (_I32, [_I32, _I32, _I32, _I32, _I32, _I32, _DP, _F, _F, _I64, _P, _P, _P,
+                                                 _P, _P, _P, _P, _P, _P]),
+        "msr_layer_decode_noalloc_max_bytes": (_SZ, []),
         "msr_retnet_block_fwd": (_I32, [_I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _DP, _F, _F, _F,
                                         _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
         "msr_retnet_block_workspace_bytes": (_SZ, [_I32] * 9),
@@ -509,4 +514,30 @@ def msr_layer_decode_step(X, W_Q, W_K, W_V, W_G, W_O, S, gamma, heads, d_k, d_v,
            lib().msr_layer_decode_step(dt, B, dm, heads, d_k, d_v, gp, rope_base, gn_eps, int(pos), _ptr(X),
                                        _ptr(W_Q), _ptr(W_K), _ptr(W_V), _ptr(W_G), _ptr(W_O), _ptr(S), _ptr(out),
                                        _ptr(ws), wsb, _stream(stream)))
+    return out
+
+
+def msr_layer_decode_noalloc_max_bytes() -> int:
+    return lib().msr_layer_decode_noalloc_max_bytes()
+
+
+def msr_layer_decode_step_noalloc(X, W_Q, W_K, W_V, W_G, W_O, S, gamma, heads, d_k, d_v, pos, *,
+                                  rope_base=10000.0, gn_eps=1e-5, out=None, stream=None):
+    """msr_layer_decode_step on the library's static scratch (no workspace;
+    the C call allocates nothing -- pass `out` to allocate nothing here
+    either).  Calls that overlap on one GPU race."""
+    B, dm = X.shape
+    dt = _dtype_code(X)
+    _check_layer_weights(X, dm, heads, d_k, d_v, W_Q, W_K, W_V, W_G, W_O)
+    if S is None:
+        raise ValueError("S is required")
+    _need("S", S, (B, heads, d_k, d_v), _torch().float32, X.device)
+    _need("out", out, X.shape, X.dtype, X.device)
+    if out is None:
+        out = _torch().empty((B, dm), dtype=X.dtype, device=X.device)
+    _, gp = g = _gamma(gamma, heads)
+    _check("msr_layer_decode_step_noalloc",
+           lib().msr_layer_decode_step_noalloc(dt, B, dm, heads, d_k, d_v, gp, rope_base, gn_eps, int(pos), _ptr(X),
+                                               _ptr(W_Q), _ptr(W_K), _ptr(W_V), _ptr(W_G), _ptr(W_O), _ptr(S),
+                                               _ptr(out), _stream(stream)))
     return out

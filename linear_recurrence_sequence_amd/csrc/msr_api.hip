@@ -5,6 +5,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "../../include/msr.h"
@@ -641,11 +642,9 @@ size_t msr_layer_decode_workspace_bytes(msr_dtype dtype, int32_t batch, int32_t 
   return decode_ws_layout(dtype, batch, d_model, heads, d_k, d_v).total;
 }
 
-msr_status msr_layer_decode_step(msr_dtype dtype, int32_t batch, int32_t d_model, int32_t heads, int32_t d_k,
-                                 int32_t d_v, const double* gamma, float rope_base, float gn_eps, int64_t pos,
-                                 const void* X, const void* W_Q, const void* W_K, const void* W_V, const void* W_G,
-                                 const void* W_O, float* S, void* out, void* workspace, size_t ws_bytes,
-                                 void* stream) {
+// Validation shared by the two layer decode step entry points.
+static msr_status decode_check(msr_dtype dtype, int32_t batch, int32_t d_model, int32_t heads, int32_t d_k,
+                               int32_t d_v, const double* gamma, float gn_eps, int64_t pos) {
   msr_status s;
   if ((s = check_dtype(dtype))) return s;
   if ((s = check_heads(batch, 1, heads, d_k, d_v))) return s;
@@ -654,13 +653,17 @@ msr_status msr_layer_decode_step(msr_dtype dtype, int32_t batch, int32_t d_model
   if (d_model % 64) return fail(MSR_ERR_UNSUPPORTED, "d_model = %d is not a multiple of 64", d_model);
   if (!(gn_eps >= 0.f)) return fail(MSR_ERR_SHAPE, "gn_eps must be >= 0");
   if (pos < 0) return fail(MSR_ERR_SHAPE, "pos = %lld is negative", (long long)pos);
-  if (batch == 0) return ok();
-  if (!X || !W_Q || !W_K || !W_V || !W_G || !W_O || !S || !out)
-    return fail(MSR_ERR_NULL, "X, W_Q, W_K, W_V, W_G, W_O, S and out must be non-NULL");
   if ((int64_t)batch * heads > (int64_t)INT32_MAX) return fail(MSR_ERR_UNSUPPORTED, "batch*heads too large");
-  const DecodeWs w = decode_ws_layout(dtype, batch, d_model, heads, d_k, d_v);
-  if (!workspace || ws_bytes < w.total)
-    return fail(MSR_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", w.total, workspace ? ws_bytes : 0);
+  return MSR_OK;
+}
+
+// The layer decode step's launches on validated arguments and a workspace
+// of the layout decode_ws_layout gives.
+static msr_status decode_launch(msr_dtype dtype, int32_t batch, int32_t d_model, int32_t heads, int32_t d_k,
+                                int32_t d_v, const double* gamma, float rope_base, float gn_eps, int64_t pos,
+                                const void* X, const void* W_Q, const void* W_K, const void* W_V, const void* W_G,
+                                const void* W_O, float* S, void* out, const DecodeWs& w, void* workspace,
+                                void* stream) {
   hipStream_t st = (hipStream_t)stream;
   const Elt e = dtype == MSR_BF16 ? kBF16 : kF32;
   const size_t es = elt_size(dtype);
@@ -698,6 +701,85 @@ msr_status msr_layer_decode_step(msr_dtype dtype, int32_t batch, int32_t d_model
   return from_hip(err, "msr_layer_decode_step(output projection)");
 }
 
+msr_status msr_layer_decode_step(msr_dtype dtype, int32_t batch, int32_t d_model, int32_t heads, int32_t d_k,
+                                 int32_t d_v, const double* gamma, float rope_base, float gn_eps, int64_t pos,
+                                 const void* X, const void* W_Q, const void* W_K, const void* W_V, const void* W_G,
+                                 const void* W_O, float* S, void* out, void* workspace, size_t ws_bytes,
+                                 void* stream) {
+  msr_status s;
+  if ((s = decode_check(dtype, batch, d_model, heads, d_k, d_v, gamma, gn_eps, pos))) return s;
+  if (batch == 0) return ok();
+  if (!X || !W_Q || !W_K || !W_V || !W_G || !W_O || !S || !out)
+    return fail(MSR_ERR_NULL, "X, W_Q, W_K, W_V, W_G, W_O, S and out must be non-NULL");
+  const DecodeWs w = decode_ws_layout(dtype, batch, d_model, heads, d_k, d_v);
+  if (!workspace || ws_bytes < w.total)
+    return fail(MSR_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", w.total, workspace ? ws_bytes : 0);
+  return decode_launch(dtype, batch, d_model, heads, d_k, d_v, gamma, rope_base, gn_eps, pos, X, W_Q, W_K, W_V, W_G,
+                       W_O, S, out, w, workspace, stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Allocation-free layer decode step: the same launches on a workspace in a
+// file-scope device array.  Each GPU holds its own copy of `scratch` from the
+// moment the library's code object is loaded on it until the process ends;
+// its device address is looked up once per device (hipGetSymbolAddress, with
+// that device current) and kept.  In host code the array's name is only a
+// stand-in, never a device address: only that looked-up pointer is passed to
+// kernels.  Every call on a GPU reuses that GPU's array (nothing in it has to
+// start at zero: each call writes every element it later reads), so calls
+// that overlap on one GPU race.
+// ---------------------------------------------------------------------------
+namespace {
+constexpr size_t kScratchBytes = size_t(64) << 20;
+constexpr int kScratchDevices = 64;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kScratchDevices] = {};
+
+msr_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return from_hip(e, "msr_layer_decode_step_noalloc(current device)");
+  if (dev < 0 || dev >= kScratchDevices)
+    return fail(MSR_ERR_UNSUPPORTED, "device %d is beyond the %d the static scratch is kept for", dev, kScratchDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return from_hip(e != hipSuccess ? e : hipErrorInvalidSymbol,
+                                               "msr_layer_decode_step_noalloc(scratch address)");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MSR_OK;
+}
+}  // namespace
+
+extern "C" {
+
+size_t msr_layer_decode_noalloc_max_bytes(void) { return kScratchBytes; }
+
+msr_status msr_layer_decode_step_noalloc(msr_dtype dtype, int32_t batch, int32_t d_model, int32_t heads,
+                                         int32_t d_k, int32_t d_v, const double* gamma, float rope_base,
+                                         float gn_eps, int64_t pos, const void* X, const void* W_Q, const void* W_K,
+                                         const void* W_V, const void* W_G, const void* W_O, float* S, void* out,
+                                         void* stream) {
+  msr_status s;
+  if ((s = decode_check(dtype, batch, d_model, heads, d_k, d_v, gamma, gn_eps, pos))) return s;
+  if (batch == 0) return ok();
+  if (!X || !W_Q || !W_K || !W_V || !W_G || !W_O || !S || !out)
+    return fail(MSR_ERR_NULL, "X, W_Q, W_K, W_V, W_G, W_O, S and out must be non-NULL");
+  const DecodeWs w = decode_ws_layout(dtype, batch, d_model, heads, d_k, d_v);
+  if (w.total > kScratchBytes)
+    return fail(MSR_ERR_WORKSPACE, "this step needs %zu bytes of scratch; the static scratch holds %zu "
+                "(msr_layer_decode_step takes a caller workspace of any size)", w.total, kScratchBytes);
+  void* ws = nullptr;
+  if ((s = scratch_of_current_device(&ws))) return s;
+  return decode_launch(dtype, batch, d_model, heads, d_k, d_v, gamma, rope_base, gn_eps, pos, X, W_Q, W_K, W_V, W_G,
+                       W_O, S, out, w, ws, stream);
+}
 
 size_t msr_layer_workspace_bytes(msr_dtype dtype, int32_t batch, int32_t seqlen, int32_t d_model, int32_t heads,
                                  int32_t d_k, int32_t d_v, int32_t chunk) {

@@ -291,3 +291,27 @@ def test_binding_rejects_wrong_tensors_before_the_call():
     # shapes and dtypes right: the next check is the device
     with pytest.raises(ValueError, match="on the GPU"):
         msr.msr_chunkwise_fwd(Q, K, V, g, C, S_out=torch.zeros((B, H, d, d)))
+
+
+def test_noalloc_decode_step_limits():
+    """The allocation-free decode step rejects, before anything reaches the
+    GPU, a step whose workspace exceeds its static scratch, and validates
+    like msr_layer_decode_step."""
+    L = msr.lib()
+    cap = msr.msr_layer_decode_noalloc_max_bytes()
+    assert cap == 64 << 20
+    g, gp = _gamma(16)
+    big = (1, 256, 4096, 16, 256, 256)            # batch 256 at d_model 4096: 78 MiB
+    assert msr.msr_layer_decode_workspace_bytes(*big) > cap
+    assert msr.msr_layer_decode_workspace_bytes(1, 128, 4096, 16, 256, 256) <= cap
+    call = lambda dtype, B, dm, H, dk, dv, pos=0: L.msr_layer_decode_step_noalloc(
+        dtype, B, dm, H, dk, dv, gp, 1e4, 1e-5, pos, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None)
+    assert call(*big) == 5                                        # MSR_ERR_WORKSPACE
+    assert "static scratch" in msr.msr_last_error()
+    assert call(7, 2, 256, 16, 256, 256) == 3                     # dtype
+    assert call(1, 2, 100, 16, 256, 256) == 4                     # d_model not a multiple of 64
+    assert call(1, 2, 256, 16, 256, 96) == 4                      # head dims
+    assert call(1, 2, 256, 16, 256, 256, pos=-1) == 2             # position
+    assert call(1, 0, 256, 16, 256, 256) == 0                     # empty batch: nothing to do
+    assert L.msr_layer_decode_step_noalloc(1, 2, 256, 16, 256, 256, gp, 1e4, 1e-5, 0, None, FAKE, FAKE, FAKE,
+                                           FAKE, FAKE, FAKE, FAKE, None) == 1
