@@ -47,10 +47,16 @@ struct StateCfg {
   static constexpr int STAGE = 2 * KB * LDT;                      // elements (V then K)
 };
 
+// With a (cos, sin) table (forward only), the K rows are rotated as they
+// are staged ([RN-zh] section "Retention", Eq. (3)-(4)) and the tiles with
+// tv == 0 (which together stage every K column once) also write the rotated
+// rows to Krot, for the output kernel.
 template <class T, int DK, int DV, bool RV>
 __global__ __launch_bounds__(256) void k_chunk_state(const T* __restrict__ K, const T* __restrict__ V,
                                                      int64_t ldk, int64_t ldv, T* __restrict__ dR,
-                                                     int BH, int N, int H, int chunk, int NC, HeadTab tab) {
+                                                     int BH, int N, int H, int chunk, int NC, HeadTab tab,
+                                                     const float2* __restrict__ rtab, T* __restrict__ Krot,
+                                                     int64_t ldkr) {
   constexpr bool rev_in = RV;                        // read the sequence backwards
   using C = StateCfg<T, DK, DV>;
   constexpr int TS = C::TS, WT = C::WT, KB = C::KB, LDT = C::LDT, UNITS = C::UNITS, UPT = C::UPT;
@@ -99,6 +105,11 @@ __global__ __launch_bounds__(256) void k_chunk_state(const T* __restrict__ K, co
         Row8<T> rk, rv;
         load_row8(rk, Kb + (uint32_t)(kr * (int)ldk + 8 * c8), true);
         load_row8(rv, Vb + (uint32_t)(kr * (int)ldv + 8 * c8), true);
+        if (rtab != nullptr) {                         // uniform
+          rotate_row8(rk, rtab + (size_t)(c0 + kr) * (DK / 2) + (tk * TS + 8 * c8) / 2);
+          if (tv == 0 && kk < L)
+            store_row8(Krot + ((size_t)b * N + c0 + kr) * ldkr + (size_t)h * DK + tk * TS + 8 * c8, rk);
+        }
         scale_row8(rv, kk < L ? gpow(L - 1 - kk, lg2) : 0.f);
         store_row8(sK + key * LDT + 8 * c8, rk);
         store_row8(sV + key * LDT + 8 * c8, rv);
@@ -309,8 +320,11 @@ template <class T, int DK, int DV, int NW, bool STATE, bool GN>
 __global__ __launch_bounds__(64 * NW) void k_chunk_out(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, int64_t ldq, int64_t ldk,
     int64_t ldv, const T* __restrict__ Rx, int has_sin, const T* __restrict__ G, int64_t ldg, T* __restrict__ O,
-    int64_t ldo, int BH, int N, int H, int chunk, int NC, int TPC, float scale, float eps, HeadTab tab, int rev) {
+    int64_t ldo, int BH, int N, int H, int chunk, int NC, int TPC, float scale, float eps, HeadTab tab, int rev,
+    const float2* __restrict__ qtab) {
   // rev bit 0: output row t to row N - 1 - t; bit 1: Q, K, V row t from row N - 1 - t
+  // qtab: (cos, sin) table of the rows' positions; Q is rotated as it is
+  // loaded (forward only)
   const bool rev_o = rev & 1, rev_i = rev & 2;
   using C = OutCfg<T, DK, DV, NW>;
   constexpr int NT = C::NT, KB = C::KB, SK = C::SK, LDK = C::LDK, LDV = C::LDV, LDR = C::LDR;
@@ -341,6 +355,10 @@ __global__ __launch_bounds__(64 * NW) void k_chunk_out(
     const T* p = Q + (tokb + (rev_i ? N - 1 - qr : qr)) * ldq + (size_t)h * DK + 8 * hh;
 #pragma unroll
     for (int s = 0; s < DK / 16; ++s) qf[s] = load_frag(p + 16 * s);
+    if (qtab != nullptr) {                           // uniform; element t is column 16 s + 8 hh + t
+#pragma unroll
+      for (int s = 0; s < DK / 16; ++s) rotate_frag(qf[s], qtab + (size_t)qr * (DK / 2) + 8 * s + 4 * hh);
+    }
   }
   f32x16 acc[DV / 32];
 #pragma unroll
@@ -1134,12 +1152,12 @@ static void launch_out(const ChunkArgs& a, int chunk, int NC, int TPC, int has_s
     hipLaunchKernelGGL((k_chunk_out<T, DK, DV, NW, STATE, true>), grid, dim3(64 * NW), 0, st, (const T*)a.Q,
                        (const T*)a.K, (const T*)a.V, a.ldq, a.ldk, a.ldv, (const T*)a.Rx, has_sin, (const T*)a.G,
                        a.ldg, (T*)a.O, a.ldo, BH, a.seqlen, a.heads, chunk, NC, TPC, a.scale, a.eps, tab,
-                       (a.rev_out ? 1 : 0) | (a.rev_in ? 2 : 0));
+                       (a.rev_out ? 1 : 0) | (a.rev_in ? 2 : 0), a.q_rope_tab);
   else
     hipLaunchKernelGGL((k_chunk_out<T, DK, DV, NW, STATE, false>), grid, dim3(64 * NW), 0, st, (const T*)a.Q,
                        (const T*)a.K, (const T*)a.V, a.ldq, a.ldk, a.ldv, (const T*)a.Rx, has_sin,
                        (const T*)nullptr, (int64_t)0, (T*)a.O, a.ldo, BH, a.seqlen, a.heads, chunk, NC, TPC,
-                       a.scale, a.eps, tab, (a.rev_out ? 1 : 0) | (a.rev_in ? 2 : 0));
+                       a.scale, a.eps, tab, (a.rev_out ? 1 : 0) | (a.rev_in ? 2 : 0), a.q_rope_tab);
 }
 
 template <class T, int DK, int DV>
@@ -1154,10 +1172,11 @@ static hipError_t run_chunkwise(const ChunkArgs& a, const HeadTab& tab, hipStrea
     dim3 grid(((BH * NC + 7) / 8) * 8 * (DV / TS) * (DK / TS));
     if (a.rev_in)
       hipLaunchKernelGGL((k_chunk_state<T, DK, DV, true>), grid, dim3(256), 0, st, (const T*)a.K, (const T*)a.V,
-                         a.ldk, a.ldv, (T*)a.dR, BH, N, H, Cn, NC, tab);
+                         a.ldk, a.ldv, (T*)a.dR, BH, N, H, Cn, NC, tab, (const float2*)nullptr, (T*)nullptr,
+                         (int64_t)0);
     else
       hipLaunchKernelGGL((k_chunk_state<T, DK, DV, false>), grid, dim3(256), 0, st, (const T*)a.K, (const T*)a.V,
-                         a.ldk, a.ldv, (T*)a.dR, BH, N, H, Cn, NC, tab);
+                         a.ldk, a.ldv, (T*)a.dR, BH, N, H, Cn, NC, tab, a.k_rope_tab, (T*)a.k_rot, a.ld_k_rot);
   }
   {
     TraceScope ts("k_chunk_scan", st);
@@ -1179,18 +1198,21 @@ static hipError_t run_chunkwise(const ChunkArgs& a, const HeadTab& tab, hipStrea
   {
     TraceScope ts("k_chunk_out", st);
     const int has_sin = a.reuse_rx ? (int)a.reuse_seeded : (int)(a.S_in != nullptr);
+    ChunkArgs ao = a;                                // the output kernel reads the rotated K rows
+    if (a.k_rope_tab) { ao.K = a.k_rot; ao.ldk = a.ld_k_rot; }
     if (chunk_out_o16(a.elt, DK, DV, Cn) && !a.rev_in && !a.rev_out && !a.rx_kv)
-      return launch_out_o16(a, true, Cn, NC, Cn / 128, has_sin, tab, st);
+      return launch_out_o16(ao, true, Cn, NC, Cn / 128, has_sin, tab, st);
     if constexpr (sizeof(T) == 2 && DV <= 256) {
       if (Cn % 128 == 0) {
-        launch_dl<DK, DV, true>(a, Cn, NC, Cn / 128, has_sin, tab, st);
+        if (a.q_rope_tab) return hipErrorInvalidValue;   // this kernel does not rotate Q
+        launch_dl<DK, DV, true>(ao, Cn, NC, Cn / 128, has_sin, tab, st);
         return hipGetLastError();
       }
     }
     if (Cn % 128 == 0)
-      launch_out<T, DK, DV, 4, true>(a, Cn, NC, Cn / 128, has_sin, tab, st);
+      launch_out<T, DK, DV, 4, true>(ao, Cn, NC, Cn / 128, has_sin, tab, st);
     else
-      launch_out<T, DK, DV, 1, true>(a, Cn, NC, Cn / 32, has_sin, tab, st);
+      launch_out<T, DK, DV, 1, true>(ao, Cn, NC, Cn / 32, has_sin, tab, st);
   }
   return hipGetLastError();
 }
@@ -1199,8 +1221,12 @@ template <class T, int DK, int DV>
 static hipError_t run_parallel(const ChunkArgs& a, const HeadTab& tab, hipStream_t st) {
   const int TPC = (a.seqlen + 127) / 128;
   TraceScope ts("k_chunk_out", st);
-  if (chunk_out_o16(a.elt, DK, DV, TPC * 128) && !a.rev_in && !a.rev_out)
+  // the 16-rows-per-wave kernel for the 512-wide value heads only: with one
+  // long chunk the work is all matrix-core steps, where the 32-row kernel
+  // of d_v <= 256 is the faster one
+  if (chunk_out_o16(a.elt, DK, DV, TPC * 128) && DV > 256 && !a.rev_in && !a.rev_out)
     return launch_out_o16(a, false, TPC * 128, 1, TPC, 0, tab, st);
+  if (a.q_rope_tab && sizeof(T) == 2 && DV <= 256) return hipErrorInvalidValue;
   if constexpr (sizeof(T) == 2 && DV <= 256)
     launch_dl<DK, DV, false>(a, TPC * 128, 1, TPC, 0, tab, st);
   else
@@ -1212,6 +1238,11 @@ static hipError_t run_parallel(const ChunkArgs& a, const HeadTab& tab, hipStream
   if (a.d_k == 64 && a.d_v == 64) return FN<T, 64, 64>(__VA_ARGS__);            \
   if (a.d_k == 128 && a.d_v == 128) return FN<T, 128, 128>(__VA_ARGS__);        \
   if (a.d_k == 256 && a.d_v == 256) return FN<T, 256, 256>(__VA_ARGS__);
+
+bool chunk_out_rotates_q(Elt elt, int d_k, int d_v, int chunk) {
+  if (chunk_out_o16(elt, d_k, d_v, chunk)) return true;
+  return !(elt == kBF16 && d_v <= 256 && chunk % 128 == 0);
+}
 
 bool chunk_out_direct(Elt elt, int d_k, int d_v, int chunk) {
   const bool dims = (d_k == 64 && d_v == 64) || (d_k == 128 && d_v == 128) || (d_k == 256 && d_v == 256);

@@ -309,6 +309,9 @@ size_t msr_parallel_workspace_bytes(msr_dtype dtype, msr_dims dims, float rope_b
   return chunk_ws_layout(dtype, dims, 0, rope_base > 0.f, false).total;
 }
 
+// The (cos, sin) table of positions pos0 .. pos0 + seqlen - 1 into the
+// workspace, and rotated copies of Q and K (either may be null: not rotated
+// here) into it; *Qo / *Ko then point at the copies.
 static msr_status rotate_qk(msr_dtype dtype, const msr_dims& d, float rope_base, int64_t pos0, const void* Q,
                             const void* K, void* ws, const ChunkWs& w, hipStream_t st, const void** Qo,
                             const void** Ko) {
@@ -317,12 +320,12 @@ static msr_status rotate_qk(msr_dtype dtype, const msr_dims& d, float rope_base,
   const int64_t ld = (int64_t)d.heads * d.d_k;
   const int rows = d.batch * d.seqlen;
   hipError_t err = launch_rope_table(tab, d.seqlen, d.d_k, pos0, rope_base, st);
-  if (err == hipSuccess)
+  if (err == hipSuccess && Q)
     err = launch_rope_apply(e, Q, ld, at<void>(ws, w.qr), ld, rows, d.seqlen, d.heads, d.d_k, tab, st);
-  if (err == hipSuccess)
+  if (err == hipSuccess && K)
     err = launch_rope_apply(e, K, ld, at<void>(ws, w.kr), ld, rows, d.seqlen, d.heads, d.d_k, tab, st);
-  *Qo = at<void>(ws, w.qr);
-  *Ko = at<void>(ws, w.kr);
+  if (Q) *Qo = at<void>(ws, w.qr);
+  if (K) *Ko = at<void>(ws, w.kr);
   return from_hip(err, "rotation");
 }
 
@@ -343,13 +346,21 @@ msr_status msr_parallel_fwd(msr_dtype dtype, msr_dims d, const double* gamma, fl
   if (w.total > 0 && (!workspace || ws_bytes < w.total))
     return fail(MSR_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", w.total, workspace ? ws_bytes : 0);
   hipStream_t st = (hipStream_t)stream;
-  if (rope && (s = rotate_qk(dtype, d, rope_base, pos0, Q, K, workspace, w, st, &Q, &K))) return s;
   ChunkArgs a{};
   a.elt = dtype == MSR_BF16 ? kBF16 : kF32;
   a.d_k = d.d_k; a.d_v = d.d_v; a.batch = d.batch; a.seqlen = d.seqlen; a.heads = d.heads;
-  a.Q = Q; a.K = K; a.V = V; a.O = O;
   a.ldq = a.ldk = (int64_t)d.heads * d.d_k;
   a.ldv = a.ldo = (int64_t)d.heads * d.d_v;
+  if (rope) {
+    // K rotated by a pass (no state kernel stages it here); Q by the output
+    // kernel as it loads it where that kernel can, else by the pass too
+    const int tpc = (d.seqlen + 127) / 128;
+    const bool q_in_kernel = chunk_out_rotates_q(a.elt, d.d_k, d.d_v, tpc * 128) &&
+                             !(a.elt == kBF16 && d.d_v <= 256);
+    if ((s = rotate_qk(dtype, d, rope_base, pos0, q_in_kernel ? nullptr : Q, K, workspace, w, st, &Q, &K))) return s;
+    if (q_in_kernel) a.q_rope_tab = at<float2>(workspace, w.tab);
+  }
+  a.Q = Q; a.K = K; a.V = V; a.O = O;
   a.scale = qk_scale;
   const HeadTab tab = make_tab(gamma, d.heads, 0, d.seqlen);
   return from_hip(launch_parallel(a, tab, st), "msr_parallel_fwd");
@@ -384,9 +395,22 @@ static msr_status chunkwise_fwd(msr_dtype dtype, msr_dims d, int32_t chunk, cons
   if (!workspace || ws_bytes < w.total)
     return fail(MSR_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", w.total, workspace ? ws_bytes : 0);
   (void)tok;
-  if (rope && (s = rotate_qk(dtype, d, rope_base, pos0, Q, K, workspace, w, st, &Q, &K))) return s;
   ChunkArgs a{};
   a.elt = dtype == MSR_BF16 ? kBF16 : kF32;
+  if (rope) {
+    // K is rotated by the state kernel as it stages it (which writes the
+    // rotated rows for the output kernel), Q by the output kernel as it
+    // loads it -- or, for the one output kernel that cannot, by a pass
+    const bool q_in_kernel = chunk_out_rotates_q(a.elt, d.d_k, d.d_v, chunk);
+    if ((s = rotate_qk(dtype, d, rope_base, pos0, q_in_kernel ? nullptr : Q, nullptr, workspace, w, st, &Q,
+                       nullptr)))
+      return s;
+    const float2* tab = at<float2>(workspace, w.tab);
+    if (q_in_kernel) a.q_rope_tab = tab;
+    a.k_rope_tab = tab;
+    a.k_rot = at<void>(workspace, w.kr);
+    a.ld_k_rot = (int64_t)d.heads * d.d_k;
+  }
   a.d_k = d.d_k; a.d_v = d.d_v; a.batch = d.batch; a.seqlen = d.seqlen; a.heads = d.heads;
   a.chunk = chunk;
   a.Q = Q; a.K = K; a.V = V; a.O = O;

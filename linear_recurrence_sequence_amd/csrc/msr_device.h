@@ -197,6 +197,36 @@ __device__ __forceinline__ void unpack_row8(float* v, const Row8<float>& r) {
   for (int i = 0; i < 8; ++i) v[i] = __uint_as_float(w[i]);
 }
 
+// Rotate the 4 interleaved pairs (x[2p], x[2p+1]) of an 8-element row (or
+// fragment) by the angles whose (cos, sin) are cs[0..3] (32-byte aligned):
+// ([RN-zh] section "Retention", Eq. (3)-(4)): (x0, x1) -> (x0 c - x1 s, x0 s + x1 c).
+__device__ __forceinline__ void rotate8(float* x, const float2* __restrict__ cs) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(cs), b = *reinterpret_cast<const f32x4*>(cs + 2);
+  const float c[4] = {a[0], a[2], b[0], b[2]}, sn[4] = {a[1], a[3], b[1], b[3]};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float x0 = x[2 * q], x1 = x[2 * q + 1];
+    x[2 * q] = x0 * c[q] - x1 * sn[q];
+    x[2 * q + 1] = x0 * sn[q] + x1 * c[q];
+  }
+}
+template <class T>
+__device__ __forceinline__ void rotate_row8(Row8<T>& r, const float2* __restrict__ cs) {
+  float x[8];
+  unpack_row8(x, r);
+  rotate8(x, cs);
+  pack_row8(r, x);
+}
+template <class T>
+__device__ __forceinline__ void rotate_frag(Frag<T>& f, const float2* __restrict__ cs) {
+  float x[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = (float)f.v[e];
+  rotate8(x, cs);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f.v[e] = (T)x[e];
+}
+
 // Multiply the 8 elements of a row by s (rounding back to the storage type).
 __device__ __forceinline__ void scale_row8(Row8<bf16>& r, float s) {
   uint32_t w[4] = {r.u.x, r.u.y, r.u.z, r.u.w};

@@ -55,7 +55,18 @@ struct ChunkArgs {
   // rows: the output kernel rotates Q with it as it loads Q (only where
   // chunk_out_o16 holds; K must then already be rotated); null: Q as given
   const float2* q_rope_tab;
+  // (cos, sin) table of the rows' positions for K (forward passes only):
+  // the state kernel rotates the K rows it stages with it and writes them
+  // to k_rot (row stride ld_k_rot), which the output kernel then reads in
+  // place of K; null: K as given
+  const float2* k_rope_tab;
+  void* k_rot; int64_t ld_k_rot;
 };
+
+// Whether the forward output kernel for these dims and chunk rotates Q
+// itself from ChunkArgs::q_rope_tab (all but the bf16 direct-copy kernel
+// of d_v <= 256).
+bool chunk_out_rotates_q(Elt elt, int d_k, int d_v, int chunk);
 
 // Whether the chunkwise form of these dims and chunk runs the bf16
 // direct-copy output kernel (the one that can read Rx as R_{i-1} itself).
