@@ -1166,7 +1166,14 @@ static hipError_t run_chunkwise(const ChunkArgs& a, const HeadTab& tab, hipStrea
   const int NC = (N + Cn - 1) / Cn;
   const int BH = B * H;
   constexpr int TS = StateCfg<T, DK, DV>::TS;
-  if (!a.reuse_rx) {
+  HeadScale so;
+  for (int h = 0; h < H; ++h) so.c[h] = a.sout_scale ? a.sout_scale[h] : 1.0f;
+  if (!a.reuse_rx && !a.rev_in && !a.k_rope_tab && chunk_rscan_ok(a.elt, DK, DV, Cn, BH)) {
+    // every chunk's R_{i-1} in one pass over the keys
+    TraceScope ts("k_chunk_rscan", st);
+    const hipError_t err = launch_chunk_rscan(a, tab, so, st);
+    if (err != hipSuccess) return err;
+  } else if (!a.reuse_rx) {
   {
     TraceScope ts("k_chunk_state", st);
     dim3 grid(((BH * NC + 7) / 8) * 8 * (DV / TS) * (DK / TS));
@@ -1180,8 +1187,6 @@ static hipError_t run_chunkwise(const ChunkArgs& a, const HeadTab& tab, hipStrea
   }
   {
     TraceScope ts("k_chunk_scan", st);
-    HeadScale so;
-    for (int h = 0; h < H; ++h) so.c[h] = a.sout_scale ? a.sout_scale[h] : 1.0f;
     // few (batch, head) pairs (one long sequence per head): 32 x 32 tiles, so
     // that enough workgroups walk the chunks
     if (DK >= 64 && DV >= 64 && BH * (DV / 64) * (DK / 64) >= 1024) {

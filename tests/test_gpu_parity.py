@@ -101,6 +101,52 @@ def test_chunkwise_special_gammas_no_state(dtype):
     assert oracle.max_rel_err(host(S_out), Sref) < (1e-4 if dtype == "f32" else 1e-2)
 
 
+# Shapes with enough (batch, head) pairs for the one-pass state kernel (no
+# rotation; every state tile walks the chunks in order): 256 x 128 and
+# 128 x 128 tiles, d_k 128 and 256, ragged last chunks (also shorter than a
+# key block), the degenerate decays.
+STATE_WALK_CASES = [(256, 512, 4, 16, 1000, 256), (256, 256, 2, 24, 700, 128), (128, 128, 16, 12, 333, 64),
+                    (256, 512, 2, 12, 260, 128)]
+
+
+@pytest.mark.parametrize("dk,dv,B,H,N,chunk", STATE_WALK_CASES)
+def test_chunkwise_state_walk(dk, dv, B, H, N, chunk):
+    """bf16 msr_chunkwise_fwd_save with an initial state and the final
+    state: the run takes the one-pass state kernel (no separate scan), and on
+    sampled (batch, head) slices -- heads with gamma 1 - 2^-5, 0.5, 1, 0 --
+    O, every kept chunk state R_{i-1} and S_out match the oracle."""
+    import torch
+    msr = _msr()
+    q, k, v = workloads.core_inputs(17 + dk + dv, B, N, H, dk, dv, "bf16")
+    S0 = np.random.default_rng(18).standard_normal((B, H, dk, dv)).astype(np.float32)
+    g = _gam(H)
+    scale = 1 / math.sqrt(dk)
+    R = torch.empty(msr.msr_chunkwise_states_shape(B, N, H, dk, dv, chunk), dtype=torch.bfloat16, device="cuda")
+    S_out = torch.empty((B, H, dk, dv), device="cuda")
+    say("state walk", dk, dv, B, H, N, chunk)
+    msr.msr_trace_enable(True)
+    try:
+        O = msr.msr_chunkwise_fwd_save(dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16"), g, chunk, R, qk_scale=scale,
+                                       S_in=torch.from_numpy(S0).cuda(), S_out=S_out)
+        torch.cuda.synchronize()
+        tot = msr.trace_totals()
+    finally:
+        msr.msr_trace_enable(False)
+    assert "k_chunk_rscan" in tot and "k_chunk_scan" not in tot and "k_chunk_state" not in tot
+    for b, h in ((0, 0), (B - 1, 1), (1, 2), (B // 2, 4), (B - 1, H - 1)):
+        sl = lambda a: a[b:b + 1, :, h:h + 1]
+        S0s = S0[b:b + 1, h:h + 1]
+        Oref, Sref = oracle.retention_chunkwise(sl(q), sl(k), sl(v), g[h:h + 1], chunk, scale, S0s)
+        assert oracle.max_rel_err_per_head(host(O[b:b + 1, :, h:h + 1]), Oref) < TOL["bf16"], (b, h)
+        assert oracle.max_rel_err(host(S_out[b:b + 1, h:h + 1]), Sref) < 1e-2, (b, h)
+        for i in range(R.shape[2]):
+            c0 = i * chunk
+            ref = S0s if c0 == 0 else oracle.retention_chunkwise(sl(q)[:, :c0], sl(k)[:, :c0], sl(v)[:, :c0],
+                                                                 g[h:h + 1], chunk, scale, S0s)[1]
+            got = np.swapaxes(host(R[b:b + 1, h:h + 1, i]), -1, -2)
+            assert oracle.max_rel_err(got, ref) < 1e-2, (b, h, i)
+
+
 # -------------------------------------------------------------- parallel ---
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("dk,dv", DIMS)
