@@ -56,13 +56,13 @@ PEAK_HBM = 8.0e12                      # bytes/s
 # it was taken with: the sha256 prefix of those files is recorded, and a
 # kernel whose sources have changed since reports null.
 MEASURED_TRAFFIC = {  # (workload, kernel): (bytes per launch, sources, sha256[:16])
-    ("layer_bf16_b8_n2048", "k_gemm"): (6.882e+08, ('k_gemm.hip', 'msr_device.h'), "a06455c014b88a49"),
-    ("layer_bf16_b8_n2048", "k_chunk_out"): (3.951e+08, ('k_chunk.hip', 'msr_device.h'), "e199c3d1b03234b4"),
-    ("layer_bf16_b8_n2048", "k_chunk_state"): (2.029e+08, ('k_chunk.hip', 'msr_device.h'), "e199c3d1b03234b4"),
-    ("layer_bf16_b8_n2048", "k_chunk_scan"): (1.347e+08, ('k_chunk.hip', 'msr_device.h'), "e199c3d1b03234b4"),
-    ("decode_fp32_b128_h16", "k_recurrent_step"): (1.086e+09, ('k_recurrent.hip', 'msr_device.h'), "e6d672c087335737"),
-    ("rglru_bf16_b8_n2048_d2048", "k_gemm"): (5.374e+08, ('k_gemm.hip', 'msr_device.h'), "a06455c014b88a49"),
-    ("rglru_bf16_b8_n2048_d2048", "k_rglru_scan"): (2.686e+08, ('k_rglru.hip', 'msr_device.h'), "12a096c3dad145c9"),
+    ("block_bf16_b4_n8192", "k_gemm"): (7.450e+09, ('k_gemm.hip', 'msr_device.h'), "186b5773627ab6e6"),
+    ("block_bf16_b4_n8192", "k_chunk_out"): (3.364e+09, ('k_chunk_o16.hip', 'msr_device.h'), "85d8bc921c411554"),
+    ("block_bf16_b4_n8192", "k_chunk_rscan"): (1.076e+09, ('k_chunk_rscan.hip', 'msr_device.h'), "3aeea8c58fc6b4dc"),
+    ("block_bf16_b4_n8192:core", "k_chunk_out"): (2.953e+09, ('k_chunk_o16.hip', 'msr_device.h'),
+                                                  "85d8bc921c411554"),
+    ("block_bf16_b4_n8192:core", "k_chunk_rscan"): (1.076e+09, ('k_chunk_rscan.hip', 'msr_device.h'),
+                                                    "3aeea8c58fc6b4dc"),
 }
 CSRC = os.path.join(ROOT, "linear_recurrence_sequence_amd", "csrc")
 
@@ -204,6 +204,8 @@ def bench_layer(w, steps, warmup, device_inputs=False):
         "k_chunk_out": (B * N * H * (C * (dk + dv) + 2 * dk * dv), "mfma", M * (ntot + hv) * es + states),
         "k_chunk_state": (B * N * H * 2 * dk * dv, "mfma", M * (hk + hv) * es + states),
         "k_chunk_scan": (2 * states, "hbm", None),     # read dR_i, write R_{i-1} (element type)
+        # one pass: read K and V, write every R_{i-1}
+        "k_chunk_rscan": (B * N * H * 2 * dk * dv, "mfma", M * (hk + hv) * es + states),
         "k_rope_table": (N * dk // 2 * 8, "hbm", None),
     }
     kern = {n: roof(n, wk, bd, tr, steps, workload=w.name, bytes_per_step=by) for n, (wk, bd, by) in work.items()
@@ -218,7 +220,7 @@ def bench_layer(w, steps, warmup, device_inputs=False):
     return res
 
 
-CHUNK_KERNELS = ("k_chunk_state", "k_chunk_scan", "k_chunk_out")
+CHUNK_KERNELS = ("k_chunk_state", "k_chunk_scan", "k_chunk_rscan", "k_chunk_out")
 
 
 def chunkwise_summary(tr, steps, core_flops, kern):
@@ -235,7 +237,7 @@ def chunkwise_summary(tr, steps, core_flops, kern):
             "flops_per_step": core_flops, "kernels": {n: kern[n] for n in CHUNK_KERNELS if n in kern}}
 
 
-def bench_core(B, N, H, d, C, steps, warmup, parallel=False, dv=None, rope_base=0.0):
+def bench_core(B, N, H, d, C, steps, warmup, parallel=False, dv=None, rope_base=0.0, workload=None):
     """Chunkwise (or parallel) retention core on projected bf16 Q, K, V of
     [B, N, H, d] (V and O [B, N, H, dv]), rotated inside the call when
     rope_base > 0; algorithmic flops count the causal half of the
@@ -272,9 +274,10 @@ def bench_core(B, N, H, d, C, steps, warmup, parallel=False, dv=None, rope_base=
                             B * N * H * (2 * dk + 2 * dv) * 2 + states),
             "k_chunk_state": (B * N * H * 2 * dk * dv, "mfma", B * N * H * (dk + dv) * 2 + states),
             "k_chunk_scan": (2 * states, "hbm", None),
+            "k_chunk_rscan": (B * N * H * 2 * dk * dv, "mfma", B * N * H * (dk + dv) * 2 + states),
         }
-        res["kernels"] = {n: roof(n, wk, bd, tr, steps, bytes_per_step=by) for n, (wk, bd, by) in work.items()
-                          if n in tr}
+        res["kernels"] = {n: roof(n, wk, bd, tr, steps, workload=workload, bytes_per_step=by)
+                          for n, (wk, bd, by) in work.items() if n in tr}
         res["trace_us_per_step"] = {k: round(v[0] / steps * 1e6, 2) for k, v in tr.items()}
     return res
 
@@ -569,7 +572,8 @@ def main():
         line["kernels"] = k
         line["trace_ms_per_step"] = {n: round(v * 1e3, 4) for n, v in r["trace_s_per_step"].items()}
         # the chunkwise core alone at this shape (projected Q, K, V; d_v = 512)
-        bc = bench_core(w.batch, w.seqlen, w.heads, w.d_k, w.chunk, max(3, args.steps // 2), 2, dv=w.d_v)
+        bc = bench_core(w.batch, w.seqlen, w.heads, w.d_k, w.chunk, max(3, args.steps // 2), 2, dv=w.d_v,
+                        workload=w.name + ":core")
         line["core_chunkwise"] = {
             "tokens_per_s": round(bc["tokens_per_s"], 1), "us_per_step": round(bc["s"] * 1e6, 1),
             "tflops": round(bc["tflops"], 1), "mfma_frac": round(bc["mfma_frac"], 4), "kernels": bc["kernels"]}
@@ -603,6 +607,19 @@ def main():
         long["layer"] = {"tokens_per_s": round(lr["tokens_per_s"], 1), "mfma_frac": round(lr["mfma_frac"], 4),
                          "ms_per_step": round(lr["s_per_step"] * 1e3, 3), "chunkwise": lr["chunkwise"]}
         line["long"] = long
+    # single cores for counter passes: the chunkwise and the parallel form at
+    # the long workload's and the headline workload's shapes
+    for tag, wname, par in (("core3", "long_bf16_b2_n16384", False), ("core5", "block_bf16_b4_n8192", False),
+                            ("par3", "long_bf16_b2_n16384", True), ("par5", "block_bf16_b4_n8192", True)):
+        if tag in parts:
+            cw = workloads.WORKLOADS[wname]
+            log(tag, cw.name)
+            r = bench_core(cw.batch, cw.seqlen, cw.heads, cw.d_k, cw.chunk, args.steps, args.warmup, parallel=par,
+                           dv=cw.d_v)
+            line.setdefault("cores", {})[tag] = {
+                "workload": cw.name, "form": "parallel" if par else "chunkwise", "us_per_step": round(r["s"] * 1e6, 1),
+                "tflops": round(r["tflops"], 1), "mfma_frac": round(r["mfma_frac"], 4),
+                "trace_us_per_step": r.get("trace_us_per_step")}
     if "retnet" in parts:
         log("retnet block")
         line["retnet_block"] = bench_retnet_block(max(3, args.steps // 2), 2)
