@@ -536,7 +536,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on one GPU only (asked for {max(args.gpus, world)}): this library has no "
-              f"multi-GPU path; the sharding design is described in DESIGN.md.", file=sys.stderr)
+              f"multi-GPU path (one process, one GPU).", file=sys.stderr)
         sys.exit(2)
     import torch
     import workloads
