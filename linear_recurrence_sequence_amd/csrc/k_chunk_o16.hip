@@ -98,6 +98,7 @@ struct O16Cfg {
   static_assert(NS * STG <= 160 * 1024, "ring fits in LDS");
   static_assert(NW * 2 * SLD * 4 <= STG, "epilogue staging (2 rows per wave) fits in one slot");
   static_assert(64 * CPK / 64 <= NCP, "a Q stage (64 rows) fits the stage's copies");
+  static_assert(KCH % (64 * NW) == 0 && CPK % NW == 0, "each part of a stage fills whole rounds of copies");
 };
 
 }  // namespace
@@ -155,32 +156,35 @@ __global__ __launch_bounds__(512) void k_chunk_o16(
 
   // ---- the copy stream: every stage of every tile of this workgroup ----
   // Per-lane byte offsets (from the stage's first row) of copy t of this
-  // wave, which fills 16-byte slots 64 (wave LPW + t) + lane of the stage;
-  // rows past the sequence end are clamped to its last row (lim): such keys
-  // are in the future of every stored query (weight 0), such query rows are
-  // never stored.  Unsigned arithmetic: the divisions are shifts.
+  // wave, which fills 16-byte slots 64 (NW t + wave) + lane of the stage
+  // (copies strided over the waves: which part of the stage -- K or V, data
+  // or pad -- a copy fills then depends on t alone, so each copy's formula
+  // is fixed at compile time); rows past the sequence end are clamped to its
+  // last row (lim): such keys are in the future of every stored query
+  // (weight 0), such query rows are never stored.  Unsigned arithmetic: the
+  // divisions are shifts.
   auto kv_off = [&](uint32_t ln, int t, int lim) -> uint32_t {
-    const uint32_t u = (uint32_t)((wave * LPW + t) * 64) + ln;
+    const uint32_t u = (uint32_t)((t * C::NW + wave) * 64) + ln;
     const uint32_t ul = (uint32_t)lim;
     const uint32_t rk = u / C::CPK, ck = (u % C::CPK) ^ (rk & 15u);
     const uint32_t v = u - C::KCH, rv = v / C::CPV, cv = (v % C::CPV) ^ (2u * (rv & 7u));
     const uint32_t ok = (min(rk, ul) * (uint32_t)ldk32 + 8u * ck) * 2u;
     const uint32_t ov = (min(rv, ul) * (uint32_t)ldv32 + 8u * cv) * 2u;
-    return u < (uint32_t)C::KCH ? ok : ov;
+    return t < C::KCH / 64 / C::NW ? ok : ov;
   };
   // Q stages: 64 rows x 32 chunks, K's swizzle; R stages: rows of the R^T
   // slab.  Copies past the data (d_v = 512) re-read its first 16 bytes into
   // the unused tail of the slot, so that every stage issues LPW copies.
   auto q_off = [&](uint32_t ln, int t, int lim) -> uint32_t {
-    const uint32_t u = (uint32_t)((wave * LPW + t) * 64) + ln;
+    const uint32_t u = (uint32_t)((t * C::NW + wave) * 64) + ln;
     const uint32_t r = u / C::CPK, c = (u % C::CPK) ^ (r & 15u);
-    return ((min(r, (uint32_t)lim) * (uint32_t)ldq32 + 8u * c) * 2u) & (0u - (uint32_t)(u < 64u * C::CPK));
+    return t < 64 * C::CPK / 64 / C::NW ? (min(r, (uint32_t)lim) * (uint32_t)ldq32 + 8u * c) * 2u : 0u;
   };
   auto r_off = [&](uint32_t ln, int t) -> uint32_t {
-    const uint32_t u = (uint32_t)((wave * LPW + t) * 64) + ln;
+    const uint32_t u = (uint32_t)((t * C::NW + wave) * 64) + ln;
     const uint32_t r = u / C::CPR, p = u % C::CPR;
     const uint32_t c = DV > 256 ? (p ^ ((r >> 2) & 3u)) : (p ^ ((r >> 1) & 7u));
-    return ((r * DK + 8u * c) * 2u) & (0u - (uint32_t)(u < (uint32_t)C::RCH));
+    return t < C::RCH / 64 / C::NW ? (r * DK + 8u * c) * 2u : 0u;
   };
   // The prefetch position (tile iteration pk, its stage pl) runs AHEAD
   // stages ahead of the consumed one; past the last stage of the last tile
@@ -191,7 +195,7 @@ __global__ __launch_bounds__(512) void k_chunk_o16(
   Tile pt = tile_at(0);
   const bool any = pt.ok;
   auto prep_next = [&](Cp& c) {
-    c.dst = (uint32_t)(uintptr_t)slot(pg) + wave * LPW * 1024;
+    c.dst = (uint32_t)(uintptr_t)slot(pg) + wave * 1024;
     ++pg;
     const int b = pt.bh / H, h = pt.bh % H;
     const size_t tokb = (size_t)b * N;
@@ -226,9 +230,8 @@ __global__ __launch_bounds__(512) void k_chunk_o16(
     }
   };
   auto cp = [&](const Cp& c, int t) {
-    const int ii = wave * LPW + t;                   // wave-uniform
-    copy16_to_lds(uniform_ptr(ii < C::KCH / 64 ? c.src[0] : c.src[1]), c.off[t],
-                  __builtin_amdgcn_readfirstlane(c.dst + t * 1024));
+    copy16_to_lds(uniform_ptr(t < C::KCH / 64 / C::NW ? c.src[0] : c.src[1]), c.off[t],
+                  __builtin_amdgcn_readfirstlane(c.dst + t * C::NW * 1024));
   };
   if (!any) return;
   Cp cn;
