@@ -163,28 +163,42 @@ __global__ __launch_bounds__(512) void k_chunk_o16(
   // last row (lim): such keys are in the future of every stored query
   // (weight 0), such query rows are never stored.  Unsigned arithmetic: the
   // divisions are shifts.
-  auto kv_off = [&](uint32_t ln, int t, int lim) -> uint32_t {
-    const uint32_t u = (uint32_t)((t * C::NW + wave) * 64) + ln;
+  // Slot u = 512 t + w64 (w64 = 64 wave + lane) of a stage splits into a
+  // part that depends on t alone and one that depends on the lane alone:
+  //   K, Q rows (32 chunks each): row 16 t + w64 / 32, chunk (w64 % 32) ^ (row & 15)
+  //   V rows (CPV chunks):        row (t - KR) 512 / CPV + w64 / CPV,
+  //                               chunk (w64 % CPV) ^ (2 (row & 7))
+  //   R^T rows (CPR chunks):      row 512 t / CPR + w64 / CPR, chunk p ^ f(row)
+  // (512 / CPV is a multiple of 8 and 512 / CPR of 32, so the swizzles only
+  // see the lane part).  The lane parts, kept in five registers:
+  struct LaneOff { uint32_t rk, ck, rv, cv, ro; };
+  LaneOff lo0;
+  {
+    const uint32_t w64 = (uint32_t)(wave * 64 + lane);
+    lo0.rk = w64 / C::CPK;
+    lo0.ck = 16u * ((w64 % C::CPK) ^ (lo0.rk & 15u));
+    lo0.rv = w64 / C::CPV;
+    lo0.cv = 16u * ((w64 % C::CPV) ^ (2u * (lo0.rv & 7u)));
+    const uint32_t r = w64 / C::CPR, p = w64 % C::CPR;
+    const uint32_t c = DV > 256 ? (p ^ ((r >> 2) & 3u)) : (p ^ ((r >> 1) & 7u));
+    lo0.ro = (r * DK + 8u * c) * 2u;
+  }
+  constexpr int KR = C::KCH / 64 / C::NW;            // rounds of copies holding K
+  auto kv_off = [&](const LaneOff& lo, int t, int lim) -> uint32_t {
     const uint32_t ul = (uint32_t)lim;
-    const uint32_t rk = u / C::CPK, ck = (u % C::CPK) ^ (rk & 15u);
-    const uint32_t v = u - C::KCH, rv = v / C::CPV, cv = (v % C::CPV) ^ (2u * (rv & 7u));
-    const uint32_t ok = (min(rk, ul) * (uint32_t)ldk32 + 8u * ck) * 2u;
-    const uint32_t ov = (min(rv, ul) * (uint32_t)ldv32 + 8u * cv) * 2u;
-    return t < C::KCH / 64 / C::NW ? ok : ov;
+    if (t < KR) return min(lo.rk + 16u * t, ul) * (uint32_t)(2 * ldk32) + lo.ck;
+    return min(lo.rv + (uint32_t)((t - KR) * (512 / C::CPV)), ul) * (uint32_t)(2 * ldv32) + lo.cv;
   };
   // Q stages: 64 rows x 32 chunks, K's swizzle; R stages: rows of the R^T
   // slab.  Copies past the data (d_v = 512) re-read its first 16 bytes into
   // the unused tail of the slot, so that every stage issues LPW copies.
-  auto q_off = [&](uint32_t ln, int t, int lim) -> uint32_t {
-    const uint32_t u = (uint32_t)((t * C::NW + wave) * 64) + ln;
-    const uint32_t r = u / C::CPK, c = (u % C::CPK) ^ (r & 15u);
-    return t < 64 * C::CPK / 64 / C::NW ? (min(r, (uint32_t)lim) * (uint32_t)ldq32 + 8u * c) * 2u : 0u;
+  auto q_off = [&](const LaneOff& lo, int t, int lim) -> uint32_t {
+    if (t < 64 * C::CPK / 64 / C::NW) return min(lo.rk + 16u * t, (uint32_t)lim) * (uint32_t)(2 * ldq32) + lo.ck;
+    return 0u;
   };
-  auto r_off = [&](uint32_t ln, int t) -> uint32_t {
-    const uint32_t u = (uint32_t)((t * C::NW + wave) * 64) + ln;
-    const uint32_t r = u / C::CPR, p = u % C::CPR;
-    const uint32_t c = DV > 256 ? (p ^ ((r >> 2) & 3u)) : (p ^ ((r >> 1) & 7u));
-    return t < C::RCH / 64 / C::NW ? (r * DK + 8u * c) * 2u : 0u;
+  auto r_off = [&](const LaneOff& lo, int t) -> uint32_t {
+    if (t < C::RCH / 64 / C::NW) return lo.ro + (uint32_t)(t * (512 / C::CPR) * DK * 2);
+    return 0u;
   };
   // The prefetch position (tile iteration pk, its stage pl) runs AHEAD
   // stages ahead of the consumed one; past the last stage of the last tile
@@ -199,27 +213,27 @@ __global__ __launch_bounds__(512) void k_chunk_o16(
     ++pg;
     const int b = pt.bh / H, h = pt.bh % H;
     const size_t tokb = (size_t)b * N;
-    // the lane index made opaque: otherwise the compiler keeps every
-    // stage kind's per-lane offsets live across the whole tile loop
-    uint32_t ln = (uint32_t)lane;
-    asm volatile("" : "+v"(ln));
+    // the lane parts made opaque here: otherwise the compiler keeps every
+    // stage kind's per-copy offsets live across the whole tile loop
+    LaneOff lo = lo0;
+    asm volatile("" : "+v"(lo.rk), "+v"(lo.ck), "+v"(lo.rv), "+v"(lo.cv), "+v"(lo.ro));
     if (pl < 2) {                                    // Q rows r0 + 64 pl ..
       const int base = min(pt.r0 + 64 * pl, N - 1);
       c.src[0] = c.src[1] = Q + (tokb + base) * ldq + (size_t)h * DK;
       const int lim = min(63, N - 1 - base);
 #pragma unroll
-      for (int t = 0; t < LPW; ++t) c.off[t] = q_off(ln, t, lim);
+      for (int t = 0; t < LPW; ++t) c.off[t] = q_off(lo, t, lim);
     } else if (pl < 2 + pt.nR) {                     // R_{i-1}^T slab
       c.src[0] = c.src[1] = Rx + ((size_t)pt.bh * NC + pt.ci) * DV * DK + (pl - 2) * C::SK;
 #pragma unroll
-      for (int t = 0; t < LPW; ++t) c.off[t] = r_off(ln, t);
+      for (int t = 0; t < LPW; ++t) c.off[t] = r_off(lo, t);
     } else {                                         // keys kb .. kb + 31
       const int kb = pt.c0 + (pl - 2 - pt.nR) * KB;
       const int lim = min(KB - 1, N - 1 - kb);
       c.src[0] = K + (size_t)h * DK + (tokb + kb) * ldk;
       c.src[1] = V + (size_t)h * DV + (tokb + kb) * ldv;
 #pragma unroll
-      for (int t = 0; t < LPW; ++t) c.off[t] = kv_off(ln, t, lim);
+      for (int t = 0; t < LPW; ++t) c.off[t] = kv_off(lo, t, lim);
     }
     // advance the position, unless this was the very last stage
     if (pl + 1 < nst_of(pt)) {
