@@ -92,11 +92,11 @@ struct O16Cfg {
   // (one 16x16x32 step is 16 cycles, an LDS read under load several times
   // that)
   static constexpr int PF = DV > 256 ? 3 : 6;
-  static constexpr int SLD = DV + 8;                  // epilogue staging row (floats): 4 lane groups
-                                                      // writing rows 2 apart hit disjoint banks
+  static constexpr int SLH = DV / 2 + 16;             // epilogue staging row (floats, half of d_v): the 4 lane
+                                                      // groups' rows, 16 banks apart, hit disjoint banks
   static_assert(NCP % NW == 0 && RCH % (64 * NW) == 0 && RCH / 64 <= NCP, "whole copies per wave");
   static_assert(NS * STG <= 160 * 1024, "ring fits in LDS");
-  static_assert(NW * 2 * SLD * 4 <= STG, "epilogue staging (2 rows per wave) fits in one slot");
+  static_assert(NW * 4 * SLH * 4 <= STG, "epilogue staging (4 half rows per wave) fits in one slot");
   static_assert(64 * CPK / 64 <= NCP, "a Q stage (64 rows) fits the stage's copies");
   static_assert(KCH % (64 * NW) == 0 && CPK % NW == 0, "each part of a stage fills whole rounds of copies");
 };
@@ -463,13 +463,13 @@ __global__ __launch_bounds__(512) void k_chunk_o16(
     }
 
     // ---- epilogue: lane holds column 16 jt + i16 of rows q0 + 4 g + r.
-    // Rows go through this wave's part of the last stage's slot, 2 at a
-    // time (register r of lane groups 2 h2, 2 h2 + 1), so that each lane
-    // then takes whole 8-column chunks: 16-byte gate loads and output
-    // stores.  The slot is free once every wave is past that stage (the
-    // barrier; the copies in flight, which it does not wait for, fill the
-    // other slots) and until the next stage's barrier.  Waves with no rows
-    // skip the rest. ----
+    // Pass p stages the rows q0 + 4 g + p / 2 (all four lane groups) over
+    // the column half p % 2 in this wave's part of the last stage's slot,
+    // so that each lane then takes whole 8-column chunks: 16-byte gate loads
+    // and output stores.  The slot is free once every wave is past that
+    // stage (the barrier; the copies in flight, which it does not wait for,
+    // fill the other slots) and until the next stage's barrier.  Waves with
+    // no rows skip the rest. ----
     copies_wait_barrier<AHEAD * LPW>();
     if (active) {
       float mu[4], rs[4];
@@ -490,41 +490,42 @@ __global__ __launch_bounds__(512) void k_chunk_o16(
             sum += d * d;
           }
           rs[r] = rsqrtf(row16_sum(sum) * (1.0f / DV) + eps);
+          mu[r] *= -rs[r];                           // y = x rs - mu rs, one fused multiply-add
         }
       }
-      lds_float* stg = (lds_float*)slot(gs - 1) + wave * 2 * C::SLD;
-      constexpr int CH = 2 * (DV / 8) / 64;          // 8-column chunks per lane per pass
+      lds_float* stg = (lds_float*)slot(gs - 1) + wave * 4 * C::SLH;
+      constexpr int NCH = DV / 16;                   // 8-column chunks per half row
+      constexpr int CH = 4 * NCH / 64;               // per lane per pass
       auto gate = [&](int pass, Row8<bf16>* gv) {
-        const int r = pass >> 1, h2 = pass & 1;
+        const int r = pass >> 1, hv = pass & 1;
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
-          const int id = lane + 64 * c, sr = id / (DV / 8), c8 = id % (DV / 8);
-          const int q = min(q0 + 4 * (2 * h2 + sr) + r, N - 1);
-          load_row8(gv[c], G + (tokb + q) * ldg + (size_t)h * DV + 8 * c8, true);
+          const int id = lane + 64 * c, sr = id / NCH, c8 = id % NCH;
+          const int q = min(q0 + 4 * sr + r, N - 1);
+          load_row8(gv[c], G + (tokb + q) * ldg + (size_t)h * DV + hv * (DV / 2) + 8 * c8, true);
         }
       };
       Row8<bf16> gv[2][CH];
       if constexpr (GN) gate(0, gv[0]);
 #pragma unroll
       for (int pass = 0; pass < 8; ++pass) {
-        const int r = pass >> 1, h2 = pass & 1;
+        const int r = pass >> 1, hv = pass & 1;
         if constexpr (GN) {
           if (pass + 1 < 8) gate(pass + 1, gv[(pass + 1) & 1]);
         }
-        if ((g >> 1) == h2) {
 #pragma unroll
-          for (int jt = 0; jt < NJ; ++jt) {
-            const float y = GN ? (acc[jt][r] - mu[r]) * rs[r] : acc[jt][r];
-            stg[(g & 1) * C::SLD + 16 * jt + i16] = y;
-          }
+        for (int jh = 0; jh < NJ / 2; ++jh) {
+          const int jt = hv * (NJ / 2) + jh;
+          const float y = GN ? fmaf(acc[jt][r], rs[r], mu[r]) : acc[jt][r];
+          stg[g * C::SLH + 16 * jh + i16] = y;
         }
         asm volatile("" ::: "memory");
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
-          const int id = lane + 64 * c, sr = id / (DV / 8), c8 = id % (DV / 8);
-          const int q = q0 + 4 * (2 * h2 + sr) + r;
-          const f32x4 y0 = *(const lds_f32x4*)(stg + sr * C::SLD + 8 * c8);
-          const f32x4 y1 = *(const lds_f32x4*)(stg + sr * C::SLD + 8 * c8 + 4);
+          const int id = lane + 64 * c, sr = id / NCH, c8 = id % NCH;
+          const int q = q0 + 4 * sr + r;
+          const f32x4 y0 = *(const lds_f32x4*)(stg + sr * C::SLH + 8 * c8);
+          const f32x4 y1 = *(const lds_f32x4*)(stg + sr * C::SLH + 8 * c8 + 4);
           float z[8] = {y0[0], y0[1], y0[2], y0[3], y1[0], y1[1], y1[2], y1[3]};
           if constexpr (GN) {
             float gg[8];
@@ -534,7 +535,7 @@ __global__ __launch_bounds__(512) void k_chunk_o16(
           }
           Row8<bf16> o;
           pack_row8(o, z);
-          if (q < N) store_row8(O + (tokb + q) * ldo + (size_t)h * DV + 8 * c8, o);
+          if (q < N) store_row8(O + (tokb + q) * ldo + (size_t)h * DV + hv * (DV / 2) + 8 * c8, o);
         }
         asm volatile("" ::: "memory");
       }
