@@ -173,9 +173,12 @@ __device__ __forceinline__ void store_row8_nt(float* p, const Row8<float>& r) {
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+// Two floats rounded (to nearest even) to a bf16 pair in one 32-bit word:
+// written as a vector conversion, one v_cvt_pk_bf16_f32.
+typedef float f32x2_pk __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_pk __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-  bf16 a = (bf16)lo, b = (bf16)hi;
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_pk){lo, hi}, bf16x2_pk));
 }
 
 __device__ __forceinline__ void pack_row8(Row8<bf16>& r, const float* v) {
