@@ -9,7 +9,7 @@
 // R_{-1} = the initial state (or zero).  The output kernel needs every
 // R_{i-1}; they are stored transposed, [d_v][d_k] per chunk, in bf16.
 //
-// One workgroup (4 waves) owns a TK x TV tile of the state of one (batch,
+// One workgroup (8 waves, two per SIMD) owns a TK x TV tile of the state of one (batch,
 // head) and walks its chunks in order with the tile in float32 matrix-core
 // accumulators: before a chunk's first key block it stores the tile as that
 // chunk's R_{i-1}, multiplies it by gamma^L, then adds the chunk's keys.  The
@@ -45,20 +45,21 @@ struct RsCfg {
   static constexpr int CPK = TK / 8, CPV = TV / 8;     // 16-byte chunks per K / V row of the tile
   static constexpr int KCH = KB * CPK, VCH = KB * CPV; // chunks per block
   static constexpr int NCP = (KCH + VCH) / 64;         // 1 KiB copies per block
-  static constexpr int CPW = NCP / 4;                  // per wave
+  static constexpr int NWV = 8;                        // waves: 4 along d_k x 2 along d_v, two per SIMD
+  static constexpr int CPW = NCP / NWV;                // copies per wave
   static constexpr int STG = NCP * 1024;               // bytes per ring slot
   // ring slots: one block being multiplied, one being scaled, the rest in
   // flight (a deeper ring measured slower)
   static constexpr int NS = 4;
-  static constexpr int WTM = TK / 64, WTN = TV / 64;   // 32x32 tiles per wave (d_k, d_v)
-  static constexpr int VPT = VCH / 256;                // V chunks per thread in the scaling pass
-  static_assert(NCP % 4 == 0 && KCH % 64 == 0 && VCH % 256 == 0, "whole copies per wave");
+  static constexpr int WTM = TK / 128, WTN = TV / 64;  // 32x32 tiles per wave (d_k, d_v)
+  static constexpr int VPT = VCH / (64 * NWV);         // V chunks per thread in the scaling pass
+  static_assert(NCP % NWV == 0 && KCH % 64 == 0 && VCH % (64 * NWV) == 0 && WTM >= 1, "whole copies per wave");
   static_assert(CPK >= 16 && CPV >= 8, "rows of at least 256 (K) and 128 (V) bytes");
   // staging of the state tile on its way out: per wave one 32-row (d_v)
-  // slice of its TK / 2 d_k columns at a time, rows padded by 16 bytes
-  static constexpr int SROW = TK + 16;                 // bytes per staged row
+  // slice of its TK / 4 d_k columns at a time, rows padded by 16 bytes
+  static constexpr int SROW = TK / 2 + 16;             // bytes per staged row
   static constexpr int SWAVE = 32 * SROW;              // bytes per wave
-  static_assert(NS >= 3 && NS * STG + 4 * SWAVE <= 160 * 1024, "ring and staging fit in LDS");
+  static_assert(NS >= 3 && NS * STG + NWV * SWAVE <= 160 * 1024, "ring and staging fit in LDS");
 };
 
 template <int CPR>
@@ -82,7 +83,7 @@ typedef __attribute__((address_space(3))) rs_u32x2 lds_u32x2_t;
 }  // namespace
 
 template <int DK, int DV, int TK, int TV>
-__global__ __launch_bounds__(256) void k_chunk_rscan(const bf16* __restrict__ K, const bf16* __restrict__ V,
+__global__ __launch_bounds__(512) void k_chunk_rscan(const bf16* __restrict__ K, const bf16* __restrict__ V,
                                                      int64_t ldk, int64_t ldv, bf16* __restrict__ Rx,
                                                      const float* __restrict__ S_in, float* __restrict__ S_out,
                                                      HeadScale so, int BH, int N, int H, int chunk, int NC,
@@ -90,12 +91,12 @@ __global__ __launch_bounds__(256) void k_chunk_rscan(const bf16* __restrict__ K,
   using C = RsCfg<TK, TV>;
   constexpr int KB = C::KB, NS = C::NS, CPW = C::CPW, WTM = C::WTM, WTN = C::WTN;
   constexpr int CPK = C::CPK, CPV = C::CPV, KCH = C::KCH;
-  __shared__ __attribute__((aligned(1024))) char smem[NS * C::STG + 4 * C::SWAVE];
+  __shared__ __attribute__((aligned(1024))) char smem[NS * C::STG + C::NWV * C::SWAVE];
   lds_char* const lds = (lds_char*)smem;
 
   const int tid = threadIdx.x, lane = tid & 63, lr = lane & 31, hh = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;           // wave's d_k half, d_v half of the tile
+  const int wm = wave >> 1, wn = wave & 1;           // wave's d_k quarter, d_v half of the tile
   constexpr int NTV = DV / TV, NT = NTV * (DK / TK);
   const int xg = blockIdx.x & 7, yg = blockIdx.x >> 3;
   const int tile = yg % NT, bh = (yg / NT) * 8 + xg;
@@ -144,7 +145,7 @@ __global__ __launch_bounds__(256) void k_chunk_rscan(const bf16* __restrict__ K,
   // ---- accumulators: tile (i, j) of this wave holds, in lane lr + 32 hh,
   // register r, D[dkw + 32 i + 8 (r / 4) + 4 hh + r % 4][dvw + 32 j + lr] ----
   f32x16 acc[WTM][WTN];
-  const int dkw = tk * TK + wm * (TK / 2), dvw = tv * TV + wn * (TV / 2);
+  const int dkw = tk * TK + wm * (TK / 4), dvw = tv * TV + wn * (TV / 2);
   if (S_in != nullptr) {                             // S_in [dk][dv] float32
     const float* sp = S_in + (size_t)bh * DK * DV;
 #pragma unroll
@@ -171,7 +172,7 @@ __global__ __launch_bounds__(256) void k_chunk_rscan(const bf16* __restrict__ K,
 #pragma unroll
   for (int i = 0; i < WTM; ++i)
     ka[i] = (uint32_t)((8 * hh + jr) * (TK * 2)) +
-            16u * ((((uint32_t)(wm * (TK / 2) + 32 * i) >> 3) ^ kswz) + 2 * c16 + (q4 >> 1)) + 8u * (q4 & 1);
+            16u * ((((uint32_t)(wm * (TK / 4) + 32 * i) >> 3) ^ kswz) + 2 * c16 + (q4 >> 1)) + 8u * (q4 & 1);
 #pragma unroll
   for (int j = 0; j < WTN; ++j)
     vb[j] = (uint32_t)(KCH * 16) + (uint32_t)((8 * hh + jr) * (TV * 2)) +
@@ -184,7 +185,7 @@ __global__ __launch_bounds__(256) void k_chunk_rscan(const bf16* __restrict__ K,
     lds_char* sl = lds + (m % NS) * C::STG;
 #pragma unroll
     for (int v = 0; v < C::VPT; ++v) {
-      const int s = tid + 256 * v, r = s / CPV;
+      const int s = tid + 64 * C::NWV * v, r = s / CPV;
       const float z = kb + r < N ? __builtin_amdgcn_exp2f((float)(L - 1 - (kb - c0 + r)) * lg2f) : 0.0f;
       lds_u32x4_t* p = (lds_u32x4_t*)(sl + KCH * 16 + 16 * s);
       rs_u32x4 w = *p;
@@ -214,7 +215,7 @@ __global__ __launch_bounds__(256) void k_chunk_rscan(const bf16* __restrict__ K,
     // by gamma^L of this chunk
     if (kb == c0) {                                  // uniform
       // Rx[dv][dk] rows: each 32-column d_v tile j of the wave goes through
-      // its staging area ([32 dv][TK / 2 dk] bf16), then out as whole
+      // its staging area ([32 dv][TK / 4 dk] bf16), then out as whole
       // 16-byte pieces of TK-byte row segments
       bf16* rp = Rx + ((size_t)bh * NC + ci) * DV * DK;
       lds_char* stg = lds + NS * C::STG + wave * C::SWAVE;
@@ -230,7 +231,7 @@ __global__ __launch_bounds__(256) void k_chunk_rscan(const bf16* __restrict__ K,
             *(lds_u32x2_t*)(stg + lr * C::SROW + 2 * (32 * i + 8 * r4 + 4 * hh)) = w;
           }
         asm volatile("" ::: "memory");
-        constexpr int CPR = TK / 16;                 // 16-byte pieces per staged row
+        constexpr int CPR = TK / 32;                 // 16-byte pieces per staged row
 #pragma unroll
         for (int u = 0; u < 32 * CPR / 64; ++u) {
           const int id = lane + 64 * u, row = id / CPR, pc = id % CPR;
@@ -307,7 +308,7 @@ static void launch_rs_t(const ChunkArgs& a, int NC, const HeadTab& tab, const He
   const int BH = a.batch * a.heads;
   constexpr int NT = (DK / TK) * (DV / TV);
   dim3 grid(((BH + 7) / 8) * 8 * NT);
-  hipLaunchKernelGGL((k_chunk_rscan<DK, DV, TK, TV>), grid, dim3(256), 0, st, (const bf16*)a.K, (const bf16*)a.V,
+  hipLaunchKernelGGL((k_chunk_rscan<DK, DV, TK, TV>), grid, dim3(64 * RsCfg<TK, TV>::NWV), 0, st, (const bf16*)a.K, (const bf16*)a.V,
                      a.ldk, a.ldv, (bf16*)a.Rx, a.S_in, a.S_out, so, BH, a.seqlen, a.heads, a.chunk, NC, tab);
 }
 
