@@ -56,13 +56,13 @@ PEAK_HBM = 8.0e12                      # bytes/s
 # it was taken with: the sha256 prefix of those files is recorded, and a
 # kernel whose sources have changed since reports null.
 MEASURED_TRAFFIC = {  # (workload, kernel): (bytes per launch, sources, sha256[:16])
-    ("block_bf16_b4_n8192", "k_gemm"): (7.450e+09, ('k_gemm.hip', 'msr_device.h'), "186b5773627ab6e6"),
-    ("block_bf16_b4_n8192", "k_chunk_out"): (3.364e+09, ('k_chunk_o16.hip', 'msr_device.h'), "85d8bc921c411554"),
-    ("block_bf16_b4_n8192", "k_chunk_rscan"): (1.076e+09, ('k_chunk_rscan.hip', 'msr_device.h'), "3aeea8c58fc6b4dc"),
-    ("block_bf16_b4_n8192:core", "k_chunk_out"): (2.953e+09, ('k_chunk_o16.hip', 'msr_device.h'),
-                                                  "85d8bc921c411554"),
-    ("block_bf16_b4_n8192:core", "k_chunk_rscan"): (1.076e+09, ('k_chunk_rscan.hip', 'msr_device.h'),
-                                                    "3aeea8c58fc6b4dc"),
+    ("block_bf16_b4_n8192", "k_gemm"): (7.450e+09, ('k_gemm.hip', 'msr_device.h'), "fb18439e637715b7"),
+    ("block_bf16_b4_n8192", "k_chunk_out"): (3.383e+09, ('k_chunk_o16.hip', 'msr_device.h'), "9569f51a94b6b6d9"),
+    ("block_bf16_b4_n8192", "k_chunk_rscan"): (1.075e+09, ('k_chunk_rscan.hip', 'msr_device.h'), "c9607021fa616eaa"),
+    ("block_bf16_b4_n8192:core", "k_chunk_out"): (2.773e+09, ('k_chunk_o16.hip', 'msr_device.h'),
+                                                  "9569f51a94b6b6d9"),
+    ("block_bf16_b4_n8192:core", "k_chunk_rscan"): (1.075e+09, ('k_chunk_rscan.hip', 'msr_device.h'),
+                                                    "c9607021fa616eaa"),
 }
 CSRC = os.path.join(ROOT, "linear_recurrence_sequence_amd", "csrc")
 
