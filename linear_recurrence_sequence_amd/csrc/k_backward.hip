@@ -31,12 +31,13 @@ __device__ __forceinline__ void store4(float* p, const float* v) {
 }
 }  // namespace
 
-// In-place transpose of nblocks contiguous d x d blocks (d a multiple of 32):
-// workgroup (block, tile pair I <= J) reads tiles (I, J) and (J, I) through
-// LDS and writes each one transposed into the other's place.  Workgroups
-// touch disjoint tile pairs, and each reads both tiles before writing.
+// Transpose of nblocks contiguous d x d blocks (d a multiple of 32) from src
+// to dst, in place when they are equal: workgroup (block, tile pair I <= J)
+// reads tiles (I, J) and (J, I) through LDS and writes each one transposed
+// into the other's place.  Workgroups touch disjoint tile pairs, and each
+// reads both tiles before writing.
 template <class T>
-__global__ __launch_bounds__(256) void k_transpose_blocks(T* base, int d, int npairs) {
+__global__ __launch_bounds__(256) void k_transpose_blocks(const T* src, T* dst, int d, int npairs) {
   __shared__ float ta[32][33], tb[32][33];
   const int nt = d / 32;
   const int64_t blk = blockIdx.x / npairs;
@@ -46,7 +47,8 @@ __global__ __launch_bounds__(256) void k_transpose_blocks(T* base, int d, int np
     ++I;
   }
   const int J = I + pr;
-  T* m = base + blk * d * d;
+  const T* m = src + blk * d * d;
+  T* o = dst + blk * d * d;
   // each thread moves 4 consecutive elements of one tile row: 8 threads per
   // row, 32 rows per pass
   const int r = threadIdx.x >> 3, c4 = (threadIdx.x & 7) * 4;
@@ -64,11 +66,11 @@ __global__ __launch_bounds__(256) void k_transpose_blocks(T* base, int d, int np
     x[e] = ta[c4 + e][r];
     y[e] = tb[c4 + e][r];
   }
-  store4(m + (size_t)(32 * J + r) * d + 32 * I + c4, x);   // tile (I, J) transposed into (J, I)
-  if (I != J) store4(m + (size_t)(32 * I + r) * d + 32 * J + c4, y);
+  store4(o + (size_t)(32 * J + r) * d + 32 * I + c4, x);   // tile (I, J) transposed into (J, I)
+  if (I != J) store4(o + (size_t)(32 * I + r) * d + 32 * J + c4, y);
 }
 
-hipError_t launch_transpose_blocks(Elt elt, void* base, int d, int64_t nblocks, hipStream_t st) {
+hipError_t launch_transpose_blocks_to(Elt elt, const void* src, void* dst, int d, int64_t nblocks, hipStream_t st) {
   if (d % 32 || d <= 0) return hipErrorInvalidValue;
   const int nt = d / 32, npairs = nt * (nt + 1) / 2;
   const int64_t wgs = nblocks * npairs;
@@ -76,10 +78,15 @@ hipError_t launch_transpose_blocks(Elt elt, void* base, int d, int64_t nblocks, 
   if (wgs > INT32_MAX) return hipErrorInvalidValue;
   TraceScope ts("k_transpose_blocks", st);
   if (elt == kBF16)
-    hipLaunchKernelGGL(k_transpose_blocks<bf16>, dim3((unsigned)wgs), dim3(256), 0, st, (bf16*)base, d, npairs);
+    hipLaunchKernelGGL(k_transpose_blocks<bf16>, dim3((unsigned)wgs), dim3(256), 0, st, (const bf16*)src, (bf16*)dst, d,
+                       npairs);
   else
-    hipLaunchKernelGGL(k_transpose_blocks<float>, dim3((unsigned)wgs), dim3(256), 0, st, (float*)base, d, npairs);
+    hipLaunchKernelGGL(k_transpose_blocks<float>, dim3((unsigned)wgs), dim3(256), 0, st, (const float*)src,
+                       (float*)dst, d, npairs);
   return hipGetLastError();
+}
+hipError_t launch_transpose_blocks(Elt elt, void* base, int d, int64_t nblocks, hipStream_t st) {
+  return launch_transpose_blocks_to(elt, base, base, d, nblocks, st);
 }
 
 // dst[bh] (rows x cols) = c_h * src[bh] or c_h * src[bh]^T (src cols x rows),

@@ -1205,7 +1205,9 @@ static hipError_t run_chunkwise(const ChunkArgs& a, const HeadTab& tab, hipStrea
     const int has_sin = a.reuse_rx ? (int)a.reuse_seeded : (int)(a.S_in != nullptr);
     ChunkArgs ao = a;                                // the output kernel reads the rotated K rows
     if (a.k_rope_tab) { ao.K = a.k_rot; ao.ldk = a.ld_k_rot; }
-    if (chunk_out_o16(a.elt, DK, DV, Cn) && !a.rev_in && !a.rev_out && !a.rx_kv)
+    // (reversed reads come with reversed writes: the backward's passes,
+    // which rotate Q and K beforehand)
+    if (chunk_out_o16(a.elt, DK, DV, Cn) && a.rev_in == a.rev_out && !a.rx_kv && !(a.rev_in && a.q_rope_tab))
       return launch_out_o16(ao, true, Cn, NC, Cn / 128, has_sin, tab, st);
     if constexpr (sizeof(T) == 2 && DV <= 256) {
       if (Cn % 128 == 0) {

@@ -9,6 +9,9 @@
 // the parallel form (section "1) Retention 的並行表征", Eq. (5)) is one chunk
 // spanning the sequence with no state.  Optionally followed by the per-head
 // GroupNorm and the swish gate of section "門控多尺度 Retention", Eq. (8).
+// The reversed variant (REV, for the backward's anti-causal passes) runs the
+// same recurrence on the time-reversed sequence: row t of Q, K, V is read
+// from row N - 1 - t and output row t written to row N - 1 - t.
 //
 // Work split: tiles of (batch, head, chunk, 128 query rows), run by a
 // persistent grid of one workgroup of 8 waves (two per SIMD) per CU; each
@@ -103,7 +106,7 @@ struct O16Cfg {
 
 }  // namespace
 
-template <int DV, bool STATE, bool GN, bool ROPE>
+template <int DV, bool STATE, bool GN, bool ROPE, bool REV>
 __global__ __launch_bounds__(512) void k_chunk_o16(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V, int64_t ldq, int64_t ldk,
     int64_t ldv, const bf16* __restrict__ Rx, const bf16* __restrict__ G, int64_t ldg,
@@ -184,16 +187,20 @@ __global__ __launch_bounds__(512) void k_chunk_o16(
     lo0.ro = (r * DK + 8u * c) * 2u;
   }
   constexpr int KR = C::KCH / 64 / C::NW;            // rounds of copies holding K
+  // row r of a stage (clamped to lim) lies r rows after the stage's base
+  // row, or, reversed, lim - r rows after it (the base is then the stage's
+  // last row in time order, the lowest in memory)
+  auto srow = [&](uint32_t r, uint32_t ul) { return REV ? ul - min(r, ul) : min(r, ul); };
   auto kv_off = [&](const LaneOff& lo, int t, int lim) -> uint32_t {
     const uint32_t ul = (uint32_t)lim;
-    if (t < KR) return min(lo.rk + 16u * t, ul) * (uint32_t)(2 * ldk32) + lo.ck;
-    return min(lo.rv + (uint32_t)((t - KR) * (512 / C::CPV)), ul) * (uint32_t)(2 * ldv32) + lo.cv;
+    if (t < KR) return srow(lo.rk + 16u * t, ul) * (uint32_t)(2 * ldk32) + lo.ck;
+    return srow(lo.rv + (uint32_t)((t - KR) * (512 / C::CPV)), ul) * (uint32_t)(2 * ldv32) + lo.cv;
   };
   // Q stages: 64 rows x 32 chunks, K's swizzle; R stages: rows of the R^T
   // slab.  Copies past the data (d_v = 512) re-read its first 16 bytes into
   // the unused tail of the slot, so that every stage issues LPW copies.
   auto q_off = [&](const LaneOff& lo, int t, int lim) -> uint32_t {
-    if (t < 64 * C::CPK / 64 / C::NW) return min(lo.rk + 16u * t, (uint32_t)lim) * (uint32_t)(2 * ldq32) + lo.ck;
+    if (t < 64 * C::CPK / 64 / C::NW) return srow(lo.rk + 16u * t, (uint32_t)lim) * (uint32_t)(2 * ldq32) + lo.ck;
     return 0u;
   };
   auto r_off = [&](const LaneOff& lo, int t) -> uint32_t {
@@ -219,8 +226,8 @@ __global__ __launch_bounds__(512) void k_chunk_o16(
     asm volatile("" : "+v"(lo.rk), "+v"(lo.ck), "+v"(lo.rv), "+v"(lo.cv), "+v"(lo.ro));
     if (pl < 2) {                                    // Q rows r0 + 64 pl ..
       const int base = min(pt.r0 + 64 * pl, N - 1);
-      c.src[0] = c.src[1] = Q + (tokb + base) * ldq + (size_t)h * DK;
       const int lim = min(63, N - 1 - base);
+      c.src[0] = c.src[1] = Q + (tokb + (REV ? N - 1 - base - lim : base)) * ldq + (size_t)h * DK;
 #pragma unroll
       for (int t = 0; t < LPW; ++t) c.off[t] = q_off(lo, t, lim);
     } else if (pl < 2 + pt.nR) {                     // R_{i-1}^T slab
@@ -230,8 +237,9 @@ __global__ __launch_bounds__(512) void k_chunk_o16(
     } else {                                         // keys kb .. kb + 31
       const int kb = pt.c0 + (pl - 2 - pt.nR) * KB;
       const int lim = min(KB - 1, N - 1 - kb);
-      c.src[0] = K + (size_t)h * DK + (tokb + kb) * ldk;
-      c.src[1] = V + (size_t)h * DV + (tokb + kb) * ldv;
+      const int row = REV ? N - 1 - kb - lim : kb;
+      c.src[0] = K + (size_t)h * DK + (tokb + row) * ldk;
+      c.src[1] = V + (size_t)h * DV + (tokb + row) * ldv;
 #pragma unroll
       for (int t = 0; t < LPW; ++t) c.off[t] = kv_off(lo, t, lim);
     }
@@ -535,7 +543,7 @@ __global__ __launch_bounds__(512) void k_chunk_o16(
           }
           Row8<bf16> o;
           pack_row8(o, z);
-          if (q < N) store_row8(O + (tokb + q) * ldo + (size_t)h * DV + hv * (DV / 2) + 8 * c8, o);
+          if (q < N) store_row8(O + (tokb + (REV ? N - 1 - q : q)) * ldo + (size_t)h * DV + hv * (DV / 2) + 8 * c8, o);
         }
         asm volatile("" ::: "memory");
       }
@@ -568,14 +576,14 @@ static int o16_per_xcd(int U, int TPC) {
   return P < need ? P : need;
 }
 
-template <int DV, bool STATE, bool GN, bool ROPE>
+template <int DV, bool STATE, bool GN, bool ROPE, bool REV = false>
 static void launch_o16_t(const ChunkArgs& a, int chunk, int NC, int TPC, int has_sin, const HeadTab& tab,
                          hipStream_t st) {
   const int BH = a.batch * a.heads;
   const int U = NC * BH;
   const int P = o16_per_xcd(U, TPC);
   dim3 grid(8 * P);
-  hipLaunchKernelGGL((k_chunk_o16<DV, STATE, GN, ROPE>), grid, dim3(512), 0, st, (const bf16*)a.Q,
+  hipLaunchKernelGGL((k_chunk_o16<DV, STATE, GN, ROPE, REV>), grid, dim3(512), 0, st, (const bf16*)a.Q,
                      (const bf16*)a.K, (const bf16*)a.V, a.ldq, a.ldk, a.ldv, (const bf16*)a.Rx,
                      (const bf16*)a.G, a.ldg, (bf16*)a.O, a.ldo, BH, a.seqlen, a.heads, chunk, NC, TPC, P, a.scale,
                      a.eps, tab, a.q_rope_tab);
@@ -584,6 +592,12 @@ static void launch_o16_t(const ChunkArgs& a, int chunk, int NC, int TPC, int has
 template <int DV, bool STATE>
 static void launch_o16_d(const ChunkArgs& a, int chunk, int NC, int TPC, int has_sin, const HeadTab& tab,
                          hipStream_t st) {
+  // the reversed passes (the backward's) carry neither the fused epilogue
+  // nor the rotation
+  if (a.rev_in) {
+    launch_o16_t<DV, STATE, false, false, true>(a, chunk, NC, TPC, has_sin, tab, st);
+    return;
+  }
   if (a.fuse_gn_gate) {
     if (a.q_rope_tab) launch_o16_t<DV, STATE, true, true>(a, chunk, NC, TPC, has_sin, tab, st);
     else launch_o16_t<DV, STATE, true, false>(a, chunk, NC, TPC, has_sin, tab, st);

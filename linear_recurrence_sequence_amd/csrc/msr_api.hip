@@ -536,13 +536,22 @@ static msr_status chunkwise_bwd(msr_dtype dtype, msr_dims d, int32_t chunk, cons
     a.rx_kv = rx_kv;
     return launch_chunkwise(a, tab, st);
   };
+  // the 16-rows-per-wave output kernel (d_k = d_v = 256) reads each chunk's
+  // state in the layout the scans write; the direct-copy kernel of the
+  // other dims also reads it transposed
+  const bool o16 = chunk_out_o16(e, d.d_k, d.d_v, chunk);
+  const int NC = (d.seqlen + chunk - 1) / chunk;
   // dQ = causal retention of (dO, V, K) from S_in^T; its per-chunk states
   // are the forward's transposed (sums of V^T K against K^T V, seeded with
   // S_in^T against S_in)
-  if (saved)
+  if (saved && o16) {
+    err = launch_transpose_blocks_to(e, R_chunks, at<void>(cws, w.cw.rx), d.d_k, (int64_t)nbh * NC, st);
+    if (err == hipSuccess) err = pass(dO, V, K, dQ, nullptr, nullptr, false, true, S_in != nullptr);
+  } else if (saved) {
     err = pass(dO, V, K, dQ, nullptr, nullptr, false, true, S_in != nullptr, true, R_chunks);
-  else
+  } else {
     err = pass(dO, V, K, dQ, S_in ? sin_t : nullptr, nullptr, false);
+  }
   if (err != hipSuccess) return from_hip(err, "msr_chunkwise_bwd(dQ)");
   // dV = causal retention of (rev K, rev Q, rev dO), its rows written back in
   // forward time order; its last state gives dS_in
@@ -552,11 +561,10 @@ static msr_status chunkwise_bwd(msr_dtype dtype, msr_dims d, int32_t chunk, cons
   // Its state is the transpose of the dV pass's, chunk by chunk (the sum of
   // rev dO^T rev Q against rev Q^T rev dO, seeded with dS_out^T against
   // dS_out), so it reuses those per-chunk states: the direct-copy output
-  // kernel reads them as they are (with the transposing LDS read), the
-  // others after an in-place transpose.
-  const bool rx_kv = direct;
+  // kernel of d_k <= 128 reads them as they are (with the transposing LDS
+  // read), the others after an in-place transpose.
+  const bool rx_kv = direct && !o16;
   if (!rx_kv) {
-    const int NC = (d.seqlen + chunk - 1) / chunk;
     err = launch_transpose_blocks(e, at<void>(cws, w.cw.rx), d.d_k, (int64_t)nbh * NC, st);
     if (err != hipSuccess) return from_hip(err, "msr_chunkwise_bwd(state transpose)");
   }

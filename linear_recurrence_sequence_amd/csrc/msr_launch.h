@@ -76,7 +76,9 @@ bool chunk_out_direct(Elt elt, int d_k, int d_v, int chunk);
 // dims and chunk (bf16, d_k 256, d_v 256 or 512, chunk a multiple of 128).
 bool chunk_out_o16(Elt elt, int d_k, int d_v, int chunk);
 // That kernel: the chunkwise form's outputs (state: Rx holds R_{i-1}^T per
-// chunk) or the parallel form's (one chunk of chunk = TPC * 128 rows).
+// chunk) or the parallel form's (one chunk of chunk = TPC * 128 rows); with
+// rev_in (and rev_out) set, those of the time-reversed sequence (no fused
+// GroupNorm or rotation).
 hipError_t launch_out_o16(const ChunkArgs& a, bool state, int chunk, int NC, int TPC, int has_sin,
                           const HeadTab& tab, hipStream_t stream);
 
@@ -111,6 +113,8 @@ hipError_t launch_rglru_scan(Elt elt, const void* X, int64_t ldx, const void* G,
 
 // In-place transpose of nblocks contiguous d x d blocks of elt (d % 32 == 0).
 hipError_t launch_transpose_blocks(Elt elt, void* base, int d, int64_t nblocks, hipStream_t stream);
+// The same from src to dst (disjoint, or equal for the in-place transpose).
+hipError_t launch_transpose_blocks_to(Elt elt, const void* src, void* dst, int d, int64_t nblocks, hipStream_t stream);
 // Per-head factors of launch_state_xform.
 struct HeadScale {
   float c[kMaxHeads];
