@@ -1168,7 +1168,7 @@ static hipError_t run_chunkwise(const ChunkArgs& a, const HeadTab& tab, hipStrea
   constexpr int TS = StateCfg<T, DK, DV>::TS;
   HeadScale so;
   for (int h = 0; h < H; ++h) so.c[h] = a.sout_scale ? a.sout_scale[h] : 1.0f;
-  if (!a.reuse_rx && !a.rev_in && !a.k_rope_tab && chunk_rscan_ok(a.elt, DK, DV, Cn, BH)) {
+  if (!a.reuse_rx && !a.k_rope_tab && chunk_rscan_ok(a.elt, DK, DV, Cn, BH)) {
     // every chunk's R_{i-1} in one pass over the keys
     TraceScope ts("k_chunk_rscan", st);
     const hipError_t err = launch_chunk_rscan(a, tab, so, st);

@@ -7,7 +7,9 @@
 // a chunk,
 //   R_i = gamma^L R_{i-1} + K_[i]^T (V_[i] (.) zeta),  zeta_s = gamma^(L-1-s),
 // R_{-1} = the initial state (or zero).  The output kernel needs every
-// R_{i-1}; they are stored transposed, [d_v][d_k] per chunk, in bf16.
+// R_{i-1}; they are stored transposed, [d_v][d_k] per chunk, in bf16.  The
+// reversed variant (REV, the backward's anti-causal passes) runs on the
+// time-reversed sequence: key t is read from row N - 1 - t.
 //
 // One workgroup (8 waves, two per SIMD) owns a TK x TV tile of the state of one (batch,
 // head) and walks its chunks in order with the tile in float32 matrix-core
@@ -82,7 +84,7 @@ typedef __attribute__((address_space(3))) rs_u32x2 lds_u32x2_t;
 
 }  // namespace
 
-template <int DK, int DV, int TK, int TV>
+template <int DK, int DV, int TK, int TV, bool REV>
 __global__ __launch_bounds__(512) void k_chunk_rscan(const bf16* __restrict__ K, const bf16* __restrict__ V,
                                                      int64_t ldk, int64_t ldv, bf16* __restrict__ Rx,
                                                      const float* __restrict__ S_in, float* __restrict__ S_out,
@@ -127,18 +129,21 @@ __global__ __launch_bounds__(512) void k_chunk_rscan(const bf16* __restrict__ K,
       ccol[t] = 16u * (pc ^ rs_swz<CPV>(r));
     }
   }
+  // (reversed: key kb + r of the block is row N - 1 - kb - r, i.e. lim - r
+  // rows after the block's lowest row in memory)
   auto issue = [&](int n) {                          // copies of key block n (clamped) into its slot
     const int nb = min(n, NB - 1), kb = nb * KB;
     const uint32_t lim = (uint32_t)min(KB - 1, N - 1 - kb);
+    const int row0 = REV ? N - 1 - kb - (int)lim : kb;
     const uint32_t slot = (uint32_t)(uintptr_t)(lds + (n % NS) * C::STG);
 #pragma unroll
     for (int t = 0; t < CPW; ++t) {
       const int idx = wave * CPW + t;
       const bool isk = idx < KCH / 64;
       const uint32_t ld = (uint32_t)(isk ? ldk : ldv);
-      const bf16* base = isk ? Kb + (size_t)kb * ldk : Vb + (size_t)kb * ldv;
-      copy16_to_lds(rs_uniform(base), min(crow[t], lim) * ld * 2u + ccol[t],
-                    __builtin_amdgcn_readfirstlane(slot + (uint32_t)idx * 1024u));
+      const bf16* base = isk ? Kb + (size_t)row0 * ldk : Vb + (size_t)row0 * ldv;
+      const uint32_t r = REV ? lim - min(crow[t], lim) : min(crow[t], lim);
+      copy16_to_lds(rs_uniform(base), r * ld * 2u + ccol[t], __builtin_amdgcn_readfirstlane(slot + (uint32_t)idx * 1024u));
     }
   };
 
@@ -308,8 +313,14 @@ static void launch_rs_t(const ChunkArgs& a, int NC, const HeadTab& tab, const He
   const int BH = a.batch * a.heads;
   constexpr int NT = (DK / TK) * (DV / TV);
   dim3 grid(((BH + 7) / 8) * 8 * NT);
-  hipLaunchKernelGGL((k_chunk_rscan<DK, DV, TK, TV>), grid, dim3(64 * RsCfg<TK, TV>::NWV), 0, st, (const bf16*)a.K, (const bf16*)a.V,
-                     a.ldk, a.ldv, (bf16*)a.Rx, a.S_in, a.S_out, so, BH, a.seqlen, a.heads, a.chunk, NC, tab);
+  if (a.rev_in)
+    hipLaunchKernelGGL((k_chunk_rscan<DK, DV, TK, TV, true>), grid, dim3(64 * RsCfg<TK, TV>::NWV), 0, st,
+                       (const bf16*)a.K, (const bf16*)a.V, a.ldk, a.ldv, (bf16*)a.Rx, a.S_in, a.S_out, so, BH,
+                       a.seqlen, a.heads, a.chunk, NC, tab);
+  else
+    hipLaunchKernelGGL((k_chunk_rscan<DK, DV, TK, TV, false>), grid, dim3(64 * RsCfg<TK, TV>::NWV), 0, st,
+                       (const bf16*)a.K, (const bf16*)a.V, a.ldk, a.ldv, (bf16*)a.Rx, a.S_in, a.S_out, so, BH,
+                       a.seqlen, a.heads, a.chunk, NC, tab);
 }
 
 // Tile: 256 x 128 (d_k x d_v) where that still gives about 200 workgroups,

@@ -122,7 +122,8 @@ struct HeadScale {
 // Every chunk's R_{i-1} (Rx, [B, H, NC, d_v, d_k]) and the final state in
 // one kernel that walks the chunks of each state tile in order (bf16,
 // (d_k, d_v) in {(128, 128), (256, 256), (256, 512)}, chunk a multiple of
-// 64, enough (batch, head) pairs bh; forward order, K as given).
+// 64, enough (batch, head) pairs bh; K as given; rev_in: the time-reversed
+// sequence).
 bool chunk_rscan_ok(Elt elt, int dk, int dv, int chunk, int bh);
 hipError_t launch_chunk_rscan(const ChunkArgs& a, const HeadTab& tab, const HeadScale& so, hipStream_t st);
 // dst[bh] (rows x cols float32) = c[bh % heads] * (transpose ? src[bh]^T :

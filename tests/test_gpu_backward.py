@@ -240,3 +240,45 @@ def test_kept_states_of_the_forward(dtype, dk, dv, N, chunk):
                                                             S0=S0)[1]
         err = _state_err(np.swapaxes(Rh[:, :, i], -1, -2), ref)
         assert err < STATE_TOL[dtype], (i, err)
+
+
+def test_backward_one_pass_states_reversed_ragged_sampled():
+    """Enough (batch, head) pairs for the one-pass state kernel in both of the
+    backward's state computations (the dQ pass forward, the dV pass on the
+    time-reversed sequence), with a ragged last chunk, both seeds and the
+    rotation: batch 4, 700 tokens, 16 heads of 256, bf16, chunk 128; the
+    library's trace shows the one-pass kernel twice and no chunk-parallel
+    state kernel, and (batch, head) slices (0, 0), (2, 7), (3, 15) of dQ,
+    dK, dV and dS_in match the oracle."""
+    import torch
+    msr = _msr()
+    B, N, H, d, C = 4, 700, 16, 256, 128
+    g = workloads.gammas(H)
+    q, k, v = workloads.core_inputs(61, B, N, H, d, d, "bf16")
+    rng = np.random.default_rng(62)
+    dO = workloads.normal(rng, (B, N, H, d), 1.0, "bf16")
+    S0 = rng.standard_normal((B, H, d, d)).astype(np.float32)
+    dS = rng.standard_normal((B, H, d, d)).astype(np.float32)
+    scale, pos0, base = 1 / math.sqrt(d), 7, 10000.0
+    dS_in = torch.empty((B, H, d, d), device="cuda")
+    say("backward one-pass states, reversed, ragged")
+    msr.msr_trace_enable(True)
+    try:
+        dQ, dK, dV = msr.msr_chunkwise_bwd(dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16"), dev(dO, "bf16"), g, C,
+                                           rope_base=base, pos0=pos0, qk_scale=scale,
+                                           S_in=torch.from_numpy(S0).cuda(), dS_out=torch.from_numpy(dS).cuda(),
+                                           dS_in=dS_in)
+        torch.cuda.synchronize()
+        tot = msr.trace_totals()
+    finally:
+        msr.msr_trace_enable(False)
+    assert tot["k_chunk_rscan"][1] == 2 and "k_chunk_state" not in tot, tot
+    for b, h in ((0, 0), (2, 7), (3, 15)):
+        sl = lambda a: a[b:b + 1, :, h:h + 1]
+        qs, ks = oracle.rotary(sl(q), pos0, base), oracle.rotary(sl(k), pos0, base)
+        rq, rk, rv, rS = oracle.retention_grad(qs, ks, sl(v), sl(dO), g[h:h + 1], scale, S0=S0[b:b + 1, h:h + 1],
+                                               dS=dS[b:b + 1, h:h + 1])
+        _check(f"dQ[{b},{h}]", host(dQ)[b:b + 1, :, h:h + 1], oracle.rotary_adjoint(rq, pos0, base), TOL["bf16"])
+        _check(f"dK[{b},{h}]", host(dK)[b:b + 1, :, h:h + 1], oracle.rotary_adjoint(rk, pos0, base), TOL["bf16"])
+        _check(f"dV[{b},{h}]", host(dV)[b:b + 1, :, h:h + 1], rv, TOL["bf16"])
+        assert oracle.max_rel_err(host(dS_in[b, h]), rS[0, 0]) < STATE_TOL["bf16"]
