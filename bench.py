@@ -57,12 +57,12 @@ PEAK_HBM = 8.0e12                      # bytes/s
 # kernel whose sources have changed since reports null.
 MEASURED_TRAFFIC = {  # (workload, kernel): (bytes per launch, sources, sha256[:16])
     ("block_bf16_b4_n8192", "k_gemm"): (7.450e+09, ('k_gemm.hip', 'msr_device.h'), "fb18439e637715b7"),
-    ("block_bf16_b4_n8192", "k_chunk_out"): (3.383e+09, ('k_chunk_o16.hip', 'msr_device.h'), "9569f51a94b6b6d9"),
-    ("block_bf16_b4_n8192", "k_chunk_rscan"): (1.075e+09, ('k_chunk_rscan.hip', 'msr_device.h'), "c9607021fa616eaa"),
-    ("block_bf16_b4_n8192:core", "k_chunk_out"): (2.773e+09, ('k_chunk_o16.hip', 'msr_device.h'),
-                                                  "9569f51a94b6b6d9"),
-    ("block_bf16_b4_n8192:core", "k_chunk_rscan"): (1.075e+09, ('k_chunk_rscan.hip', 'msr_device.h'),
-                                                    "c9607021fa616eaa"),
+    ("block_bf16_b4_n8192", "k_chunk_out"): (3.361e+09, ('k_chunk_o16.hip', 'msr_device.h'), "0b62dd6ed4d8c45e"),
+    ("block_bf16_b4_n8192", "k_chunk_rscan"): (1.076e+09, ('k_chunk_rscan.hip', 'msr_device.h'), "137bae01dfdbb700"),
+    ("block_bf16_b4_n8192:core", "k_chunk_out"): (2.878e+09, ('k_chunk_o16.hip', 'msr_device.h'),
+                                                  "0b62dd6ed4d8c45e"),
+    ("block_bf16_b4_n8192:core", "k_chunk_rscan"): (1.076e+09, ('k_chunk_rscan.hip', 'msr_device.h'),
+                                                    "137bae01dfdbb700"),
 }
 CSRC = os.path.join(ROOT, "linear_recurrence_sequence_amd", "csrc")
 
