@@ -66,19 +66,20 @@ def test_backward(dtype, d, N, chunk):
     assert err < STATE_TOL[dtype]
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_backward_degenerate_decays_without_states(dtype):
+@pytest.mark.parametrize("dtype,d,chunk", [("f32", 64, 64), ("bf16", 64, 64), ("bf16", 256, 128)])
+def test_backward_degenerate_decays_without_states(dtype, d, chunk):
     """gamma = 0, 0.5 and 1, no S_in, no dS_out, no rotation, scale 1,
-    ragged sequence; dS_in still returned."""
+    ragged sequence over several chunks (d 256: the 16-row output kernel's
+    reversed passes); dS_in still returned."""
     import torch
     msr = _msr()
-    B, N, H, d = 2, 161, 3, 64
+    B, N, H = 2, 161 if d == 64 else 300, 3
     q, k, v = workloads.core_inputs(31, B, N, H, d, d, dtype)
     dO = workloads.normal(np.random.default_rng(32), (B, N, H, d), 1.0, dtype)
     g = np.array([0.0, 0.5, 1.0])
     dS_in = torch.empty((B, H, d, d), device="cuda")
-    say("backward degenerate", dtype)
-    dQ, dK, dV = msr.msr_chunkwise_bwd(dev(q, dtype), dev(k, dtype), dev(v, dtype), dev(dO, dtype), g, 64,
+    say("backward degenerate", dtype, d, chunk)
+    dQ, dK, dV = msr.msr_chunkwise_bwd(dev(q, dtype), dev(k, dtype), dev(v, dtype), dev(dO, dtype), g, chunk,
                                        dS_in=dS_in)
     torch.cuda.synchronize()
     rq, rk, rv, rS = oracle.retention_grad(q, k, v, dO, g, 1.0)
