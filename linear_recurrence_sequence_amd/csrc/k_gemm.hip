@@ -70,10 +70,35 @@ __device__ __forceinline__ void gemm_epilogue(f32x16 (&acc)[TM][TN], float* stg0
     row = min(row0, M - 1);
     col = min(col0, N - 8);
   };
-  // (cos, sin) of the 4 column pairs of an 8-column group at its row's position
-  auto rope_cs = [&](int row, int col, int sg) {
-    return reinterpret_cast<const float4*>(bp.rope_tab + (size_t)(row % bp.seqlen) * (bp.rope_d / 2) +
-                                           (((col - bp.start[sg]) % bp.rope_d) >> 1));
+  // (cos, sin) of the 4 column pairs of an 8-column group at its row's
+  // position.  A lane's 8 columns are the same in every iteration, so its
+  // segment, rotation flag and pair offset are found once; the wave's rows
+  // are consecutive, so row 32 i + rr of the wave sits at pos0 + 32 i + rr,
+  // wrapped once at seqlen when seqlen covers the wave's rows (no integer
+  // division per row: each costs a dozen instructions and a quarter-rate
+  // reciprocal).
+  static_assert(64 % (WCOLS / 8) == 0, "a lane's column group is the same in every iteration");
+  bool rot = false;
+  int cpair = 0, pos0 = 0;
+  if constexpr ((EPI & kEpiRope) != 0) {
+    int row, col;
+    bool ok;
+    where(0, 0, row, col, ok);
+    const int sg = seg_of(col);
+    rot = sg < bp.rope_segs && !bp.part;
+    cpair = ((col - sel(sg, bp.start[0], bp.start[1], bp.start[2], bp.start[3])) % bp.rope_d) >> 1;
+    pos0 = (m0 + wm * (BM / WM)) % bp.seqlen;
+  }
+  auto rope_cs = [&](int i, int it) {
+    const int rr = (lane + 64 * it) / (WCOLS / 8);
+    int p;
+    if (bp.seqlen >= BM / WM) {
+      p = pos0 + 32 * i + rr;
+      p = p >= bp.seqlen ? p - bp.seqlen : p;
+    } else {
+      p = min(m0 + wm * (BM / WM) + 32 * i + rr, M - 1) % bp.seqlen;
+    }
+    return reinterpret_cast<const float4*>(bp.rope_tab + (size_t)p * (bp.rope_d / 2) + cpair);
   };
   constexpr bool PRE = (EPI & kEpiRope) && ITER <= 4;   // table values loaded before the staging
 #pragma unroll
@@ -82,12 +107,8 @@ __device__ __forceinline__ void gemm_epilogue(f32x16 (&acc)[TM][TN], float* stg0
     if constexpr (PRE) {
 #pragma unroll
       for (int it = 0; it < ITER; ++it) {
-        int row, col;
-        bool ok;
-        where(i, it, row, col, ok);
-        const int sg = seg_of(col);
-        if (sg < bp.rope_segs && !bp.part) {
-          const float4* cs = rope_cs(row, col, sg);
+        if (rot) {
+          const float4* cs = rope_cs(i, it);
           csv[it][0] = cs[0];
           csv[it][1] = cs[1];
         }
@@ -111,13 +132,13 @@ __device__ __forceinline__ void gemm_epilogue(f32x16 (&acc)[TM][TN], float* stg0
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[e] = src[e];
       const int sg = seg_of(col);
-      if ((EPI & kEpiRope) && sg < bp.rope_segs && !bp.part) {
+      if ((EPI & kEpiRope) && rot) {
         float4 c0, c1;
         if constexpr (PRE) {
           c0 = csv[PRE ? it : 0][0];
           c1 = csv[PRE ? it : 0][1];
         } else {
-          const float4* cs = rope_cs(row, col, sg);
+          const float4* cs = rope_cs(i, it);
           c0 = cs[0];
           c1 = cs[1];
         }

@@ -185,6 +185,10 @@ def _layer(dtype, B, N, dm, H, dk, dv, chunk, seed):
     ("bf16", 1, 200, 256, 2, 256, 512, 64),
     ("bf16", 2, 300, 256, 2, 256, 512, 128),     # GroupNorm + gate fused, 512-wide value heads
     ("bf16", 1, 260, 256, 3, 256, 256, 256),
+    # sequences shorter than a projection wave's 128 rows: the rotation's
+    # table row is then taken per row rather than from the wave's first one
+    ("bf16", 4, 40, 256, 2, 128, 128, 32),
+    ("f32", 3, 60, 128, 2, 64, 64, 32),
 ])
 def test_layer(dtype, B, N, dm, H, dk, dv, chunk):
     import torch
