@@ -155,7 +155,10 @@ __global__ __launch_bounds__(512) void k_chunk_o16(
   // LDS addresses are 32-bit (so that constant parts fold into the
   // instructions' offsets)
   lds_char* const lds = (lds_char*)smem;
-  auto slot = [&](int s) { return lds + (s % NS) * C::STG; };
+  // ring slots by byte offset, stepped with a compare instead of a modulo
+  // by NS (a multiply-high sequence per use for NS = 3)
+  auto next_off = [&](uint32_t o) { return o + C::STG == (uint32_t)(NS * C::STG) ? 0u : o + C::STG; };
+  auto prev_off = [&](uint32_t o) { return o == 0u ? (uint32_t)((NS - 1) * C::STG) : o - C::STG; };
 
   // ---- the copy stream: every stage of every tile of this workgroup ----
   // Per-lane byte offsets (from the stage's first row) of copy t of this
@@ -191,16 +194,19 @@ __global__ __launch_bounds__(512) void k_chunk_o16(
   // row, or, reversed, lim - r rows after it (the base is then the stage's
   // last row in time order, the lowest in memory)
   auto srow = [&](uint32_t r, uint32_t ul) { return REV ? ul - min(r, ul) : min(r, ul); };
+  // row (< 64) times the row stride in bytes on the full-rate 24-bit
+  // multiplier: the strides are below 2^20 bytes (a token row of the widest
+  // buffer, heads (2 d_k + 2 d_v) elements, stays below 2^19)
   auto kv_off = [&](const LaneOff& lo, int t, int lim) -> uint32_t {
     const uint32_t ul = (uint32_t)lim;
-    if (t < KR) return srow(lo.rk + 16u * t, ul) * (uint32_t)(2 * ldk32) + lo.ck;
-    return srow(lo.rv + (uint32_t)((t - KR) * (512 / C::CPV)), ul) * (uint32_t)(2 * ldv32) + lo.cv;
+    if (t < KR) return __umul24(srow(lo.rk + 16u * t, ul), (uint32_t)(2 * ldk32)) + lo.ck;
+    return __umul24(srow(lo.rv + (uint32_t)((t - KR) * (512 / C::CPV)), ul), (uint32_t)(2 * ldv32)) + lo.cv;
   };
   // Q stages: 64 rows x 32 chunks, K's swizzle; R stages: rows of the R^T
   // slab.  Copies past the data (d_v = 512) re-read its first 16 bytes into
   // the unused tail of the slot, so that every stage issues LPW copies.
   auto q_off = [&](const LaneOff& lo, int t, int lim) -> uint32_t {
-    if (t < 64 * C::CPK / 64 / C::NW) return srow(lo.rk + 16u * t, (uint32_t)lim) * (uint32_t)(2 * ldq32) + lo.ck;
+    if (t < 64 * C::CPK / 64 / C::NW) return __umul24(srow(lo.rk + 16u * t, (uint32_t)lim), (uint32_t)(2 * ldq32)) + lo.ck;
     return 0u;
   };
   auto r_off = [&](const LaneOff& lo, int t) -> uint32_t {
@@ -212,14 +218,27 @@ __global__ __launch_bounds__(512) void k_chunk_o16(
   // it re-copies that stage into a free slot, so that every stage issues
   // the same copies and the waits are fixed.
   struct Cp { const bf16* src[2]; uint32_t dst; uint32_t off[LPW]; };
-  int pk = 0, pl = 0, pg = 0;                        // prefetch tile iteration, stage in it, global stage
+  int pk = 0, pl = 0;                                // prefetch tile iteration, stage in it
+  uint32_t pgo = 0;                                  // its ring slot (byte offset)
   Tile pt = tile_at(0);
   const bool any = pt.ok;
-  auto prep_next = [&](Cp& c) {
-    c.dst = (uint32_t)(uintptr_t)slot(pg) + wave * 1024;
-    ++pg;
-    const int b = pt.bh / H, h = pt.bh % H;
+  // Bases of the prefetch position's tile, set once when it enters the
+  // tile (not per stage: the (batch, head) split is a scalar division and
+  // the row products 64-bit): Q, K, V at row 0 of its sequence and head,
+  // and its R_{i-1}^T.
+  const bf16 *pqb, *pkb, *pvb, *prb;
+  auto enter = [&](const Tile& t) {
+    const int b = t.bh / H, h = t.bh % H;
     const size_t tokb = (size_t)b * N;
+    pqb = Q + tokb * ldq + (size_t)h * DK;
+    pkb = K + tokb * ldk + (size_t)h * DK;
+    pvb = V + tokb * ldv + (size_t)h * DV;
+    prb = STATE ? Rx + ((size_t)t.bh * NC + t.ci) * DV * DK : nullptr;
+  };
+  enter(pt);
+  auto prep_next = [&](Cp& c) {
+    c.dst = (uint32_t)(uintptr_t)(lds + pgo) + wave * 1024;
+    pgo = next_off(pgo);
     // the lane parts made opaque here: otherwise the compiler keeps every
     // stage kind's per-copy offsets live across the whole tile loop
     LaneOff lo = lo0;
@@ -227,19 +246,19 @@ __global__ __launch_bounds__(512) void k_chunk_o16(
     if (pl < 2) {                                    // Q rows r0 + 64 pl ..
       const int base = min(pt.r0 + 64 * pl, N - 1);
       const int lim = min(63, N - 1 - base);
-      c.src[0] = c.src[1] = Q + (tokb + (REV ? N - 1 - base - lim : base)) * ldq + (size_t)h * DK;
+      c.src[0] = c.src[1] = pqb + (uint64_t)(uint32_t)(REV ? N - 1 - base - lim : base) * (uint32_t)ldq32;
 #pragma unroll
       for (int t = 0; t < LPW; ++t) c.off[t] = q_off(lo, t, lim);
     } else if (pl < 2 + pt.nR) {                     // R_{i-1}^T slab
-      c.src[0] = c.src[1] = Rx + ((size_t)pt.bh * NC + pt.ci) * DV * DK + (pl - 2) * C::SK;
+      c.src[0] = c.src[1] = prb + (pl - 2) * C::SK;
 #pragma unroll
       for (int t = 0; t < LPW; ++t) c.off[t] = r_off(lo, t);
     } else {                                         // keys kb .. kb + 31
       const int kb = pt.c0 + (pl - 2 - pt.nR) * KB;
       const int lim = min(KB - 1, N - 1 - kb);
       const int row = REV ? N - 1 - kb - lim : kb;
-      c.src[0] = K + (size_t)h * DK + (tokb + row) * ldk;
-      c.src[1] = V + (size_t)h * DV + (tokb + row) * ldv;
+      c.src[0] = pkb + (uint64_t)(uint32_t)row * (uint32_t)ldk32;
+      c.src[1] = pvb + (uint64_t)(uint32_t)row * (uint32_t)ldv32;
 #pragma unroll
       for (int t = 0; t < LPW; ++t) c.off[t] = kv_off(lo, t, lim);
     }
@@ -248,7 +267,7 @@ __global__ __launch_bounds__(512) void k_chunk_o16(
       ++pl;
     } else if (pk + 1 < iters) {
       const Tile t2 = tile_at(pk + 1);
-      if (t2.ok) { ++pk; pt = t2; pl = 0; }
+      if (t2.ok) { ++pk; pt = t2; pl = 0; enter(pt); }
     }
   };
   auto cp = [&](const Cp& c, int t) {
@@ -263,9 +282,10 @@ __global__ __launch_bounds__(512) void k_chunk_o16(
 #pragma unroll
     for (int t = 0; t < LPW; ++t) cp(cn, t);
   }
-  int gs = 0;                                        // global index of the stage being consumed
-  // wait for stage gs's copies, then prepare those of stage gs + AHEAD into
-  // the slot of stage gs - 1, which every wave is past (issued during stage gs)
+  uint32_t gso = 0;                                  // ring slot (byte offset) of the stage being consumed
+  // wait for the consumed stage's copies, then prepare those of the stage
+  // AHEAD after it into the slot of the stage before it, which every wave
+  // is past (issued during the consumed stage)
   auto advance = [&]() {
     copies_wait_barrier<(AHEAD - 1) * LPW>();
     prep_next(cn);
@@ -289,14 +309,14 @@ __global__ __launch_bounds__(512) void k_chunk_o16(
     // of fragment s is column 32 s + 8 g + e of row q0 + i16) ----
     bf16x8 qf[DK / 32];
 #pragma unroll
-    for (int qs = 0; qs < 2; ++qs, ++gs) {
+    for (int qs = 0; qs < 2; ++qs, gso = next_off(gso)) {
       advance();
 #pragma unroll
       for (int tt = 0; tt < LPW; ++tt) cp(cn, tt);
       if ((wave >> 2) == qs) {
         uint32_t kb_l = kbase + (uint32_t)((wave & 3) * 16 * (C::CPK * 16));
         asm volatile("" : "+v"(kb_l));
-        const lds_char* sq = slot(gs);
+        const lds_char* sq = lds + gso;
 #pragma unroll
         for (int s = 0; s < DK / 32; ++s)
           qf[s] = *(const lds_bf16x8*)(sq + kb_l + 16 * ((4 * (s & 3) + g) ^ i16) + (s >> 2) * 256);
@@ -333,7 +353,7 @@ __global__ __launch_bounds__(512) void k_chunk_o16(
         for (int s2 = 0; s2 < C::SK / 32; ++s2) rl[s2] = (uint32_t)(i16 * (C::CPR * 16) + 16 * ((4 * s2 + g) ^ fr));
         asm volatile("" : "+v"(rl[0]));
         if constexpr (C::SK / 32 > 1) asm volatile("" : "+v"(rl[C::SK / 32 - 1]));
-        const lds_char* sR = slot(gs);
+        const lds_char* sR = lds + gso;
         constexpr int T = NJ * (C::SK / 32);
         auto rd = [&](int tt) {
           const int jt = tt / (C::SK / 32), s2 = tt % (C::SK / 32);
@@ -356,7 +376,7 @@ __global__ __launch_bounds__(512) void k_chunk_o16(
           __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
-        ++gs;
+        gso = next_off(gso);
       });
       // rows scaled by scale * xi_t = scale * gamma^(t + 1), t = row in the chunk
 #pragma unroll
@@ -381,9 +401,9 @@ __global__ __launch_bounds__(512) void k_chunk_o16(
     float wk[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) wk[e] = scale * pw(ex0 - 16 * (e >> 2) - (e & 3));
-    for (int kv = 0; kv < t.nKV; ++kv, ++gs) {
+    for (int kv = 0; kv < t.nKV; ++kv, gso = next_off(gso)) {
       advance();
-      const lds_char* sb = slot(gs);
+      const lds_char* sb = lds + gso;
       const int kb = t.c0 + kv * KB;
       // per-lane bases made opaque each stage: otherwise every (lane part +
       // constant) sum of the unrolled reads is hoisted out of the loop into
@@ -501,7 +521,7 @@ __global__ __launch_bounds__(512) void k_chunk_o16(
           mu[r] *= -rs[r];                           // y = x rs - mu rs, one fused multiply-add
         }
       }
-      lds_float* stg = (lds_float*)slot(gs - 1) + wave * 4 * C::SLH;
+      lds_float* stg = (lds_float*)(lds + prev_off(gso)) + wave * 4 * C::SLH;
       constexpr int NCH = DV / 16;                   // 8-column chunks per half row
       constexpr int CH = 4 * NCH / 64;               // per lane per pass
       auto gate = [&](int pass, Row8<bf16>* gv) {
