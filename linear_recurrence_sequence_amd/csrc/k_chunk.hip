@@ -202,30 +202,32 @@ __device__ __forceinline__ void store_n(bf16* p, const float* x) {
   }
 }
 
-// TS x TS state tile per workgroup (TS = 64: 16 elements per thread; TS =
-// 32 for shapes with few (batch, head) pairs: four times the workgroups,
-// 4 elements per thread).
-template <class T, int DK, int DV, int TS>
+// TR x TC state tile per workgroup (d_v rows x d_k columns): 64 x 64 (16
+// elements per thread), or, for shapes with few (batch, head) pairs, 16 x 64
+// (four times the workgroups, 4 elements per thread).  Every row segment a
+// thread group reads or writes is 128 bytes (bf16), a whole L2 line, so no
+// line is shared with a neighbouring tile's workgroup on another XCD.
+template <class T, int DK, int DV, int TR, int TC>
 __global__ __launch_bounds__(256) void k_chunk_scan(const T* dR, T* Rx, const float* __restrict__ S_in,
                                                     float* __restrict__ S_out, int H, int NC, HeadTab tab,
                                                     HeadScale so) {
-  constexpr int E = TS * TS / 256;   // elements per thread
-  constexpr int NTV = DV / TS;
-  constexpr int NT = NTV * (DK / TS);
+  constexpr int E = TR * TC / 256;   // elements per thread
+  constexpr int NTV = DV / TR;
+  constexpr int NT = NTV * (DK / TC);
+  static_assert(E >= 4 && TC % E == 0 && 256 % (TC / E) == 0, "whole rows per thread group");
   const int bh = blockIdx.x / NT, tile = blockIdx.x % NT;
   const int h = bh % H;
   const int tv = tile % NTV, tk = tile / NTV;
   const int tid = threadIdx.x;
-  const int row = tid / (TS / E);       // d_v index inside the tile
-  const int col = (tid % (TS / E)) * E; // first of E d_k indices inside the tile
-  __shared__ float sT[TS][TS + 1];
+  const int row = tid / (TC / E);       // d_v index inside the tile
+  const int col = (tid % (TC / E)) * E; // first of E d_k indices inside the tile
+  __shared__ float sT[TC][TR + 1];      // the tile as [d_k][d_v] (the float32 states' layout)
 
   float R[E];
   if (S_in != nullptr) {
-    // S_in is [dk][dv]; stage the tile and read it transposed.
-    const float* src = S_in + (size_t)bh * DK * DV + (size_t)(tk * TS + row) * DV + tv * TS + col;
-#pragma unroll
-    for (int e = 0; e < E; ++e) sT[row][col + e] = src[e];
+    // S_in is [dk][dv]: stage the tile in that order, read it transposed
+    const float* src = S_in + (size_t)bh * DK * DV + (size_t)(tk * TC) * DV + tv * TR;
+    for (int i = tid; i < TR * TC; i += 256) sT[i / TR][i % TR] = src[(size_t)(i / TR) * DV + i % TR];
     __syncthreads();
 #pragma unroll
     for (int e = 0; e < E; ++e) R[e] = sT[col + e][row];
@@ -236,18 +238,18 @@ __global__ __launch_bounds__(256) void k_chunk_scan(const T* dR, T* Rx, const fl
   }
 
   const size_t cstride = (size_t)DV * DK;
-  const size_t off = (size_t)bh * NC * cstride + (size_t)(tv * TS + row) * DK + tk * TS + col;
+  const size_t off = (size_t)bh * NC * cstride + (size_t)(tv * TR + row) * DK + tk * TC + col;
   const T* src = dR + off;
   T* dst = Rx + off;
   const float gB = tab.gchunk[h], gL = tab.glast[h];
-  // Contributions of the next PF chunks in flight (8 with the 32 x 32 tiles,
+  // Contributions of the next PF chunks in flight (8 with the 16 x 64 tiles,
   // whose loads are 8 bytes per lane), kept raw (unconverted) in a
   // statically indexed ring: converting right after the load would make the
   // load complete at once.  Chunk ci's slot is reloaded with chunk ci + PF
   // right after it has been read.  The reloads are unconditional, clamped to
   // the last chunk (a re-read whose value is never used), so no slot has to
   // be kept across a branch; chunk NC - 1 is loaded before it is written.
-  constexpr int PF = TS == 32 ? 8 : 4;
+  constexpr int PF = E == 4 ? 8 : 4;
   RawN<T, E> ring[PF];
   // (issued in slot order, as in the loop, so that the wait counts at the
   // loop head are the steady-state ones)
@@ -276,10 +278,9 @@ __global__ __launch_bounds__(256) void k_chunk_scan(const T* dR, T* Rx, const fl
 #pragma unroll
     for (int e = 0; e < E; ++e) sT[col + e][row] = R[e];
     __syncthreads();
-    float* o = S_out + (size_t)bh * DK * DV + (size_t)(tk * TS + row) * DV + tv * TS + col;
+    float* o = S_out + (size_t)bh * DK * DV + (size_t)(tk * TC) * DV + tv * TR;
     const float c = so.c[h];
-#pragma unroll
-    for (int e = 0; e < E; ++e) o[e] = c * sT[row][col + e];
+    for (int i = tid; i < TR * TC; i += 256) o[(size_t)(i / TR) * DV + i % TR] = c * sT[i / TR][i % TR];
   }
 }
 
@@ -1187,15 +1188,15 @@ static hipError_t run_chunkwise(const ChunkArgs& a, const HeadTab& tab, hipStrea
   }
   {
     TraceScope ts("k_chunk_scan", st);
-    // few (batch, head) pairs (one long sequence per head): 32 x 32 tiles, so
+    // few (batch, head) pairs (one long sequence per head): 16 x 64 tiles, so
     // that enough workgroups walk the chunks
     if (DK >= 64 && DV >= 64 && BH * (DV / 64) * (DK / 64) >= 1024) {
       dim3 grid(BH * (DV / 64) * (DK / 64));
-      hipLaunchKernelGGL((k_chunk_scan<T, DK, DV, 64>), grid, dim3(256), 0, st, (const T*)a.dR, (T*)a.Rx,
+      hipLaunchKernelGGL((k_chunk_scan<T, DK, DV, 64, 64>), grid, dim3(256), 0, st, (const T*)a.dR, (T*)a.Rx,
                          a.S_in, a.S_out, H, NC, tab, so);
     } else {
-      dim3 grid(BH * (DV / 32) * (DK / 32));
-      hipLaunchKernelGGL((k_chunk_scan<T, DK, DV, 32>), grid, dim3(256), 0, st, (const T*)a.dR, (T*)a.Rx,
+      dim3 grid(BH * (DV / 16) * (DK / 64));
+      hipLaunchKernelGGL((k_chunk_scan<T, DK, DV, 16, 64>), grid, dim3(256), 0, st, (const T*)a.dR, (T*)a.Rx,
                          a.S_in, a.S_out, H, NC, tab, so);
     }
   }
