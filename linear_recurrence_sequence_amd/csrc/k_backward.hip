@@ -31,15 +31,17 @@ __device__ __forceinline__ void store4(float* p, const float* v) {
 }
 }  // namespace
 
-// Transpose of nblocks contiguous d x d blocks (d a multiple of 32) from src
-// to dst, in place when they are equal: workgroup (block, tile pair I <= J)
-// reads tiles (I, J) and (J, I) through LDS and writes each one transposed
-// into the other's place.  Workgroups touch disjoint tile pairs, and each
-// reads both tiles before writing.
-template <class T>
+// Transpose of nblocks contiguous d x d blocks from src to dst, in place
+// when they are equal: workgroup (block, tile pair I <= J) reads tiles
+// (I, J) and (J, I) through LDS and writes each one transposed into the
+// other's place.  Workgroups touch disjoint tile pairs, and each reads both
+// tiles before writing.  Tiles are TT x TT with TT elements = 128 bytes (64
+// for bf16, 32 for float32), so each row segment is a whole L2 line and no
+// line is shared with another workgroup (on another XCD).
+template <class T, int TT>
 __global__ __launch_bounds__(256) void k_transpose_blocks(const T* src, T* dst, int d, int npairs) {
-  __shared__ float ta[32][33], tb[32][33];
-  const int nt = d / 32;
+  __shared__ float ta[TT][TT + 1], tb[TT][TT + 1];
+  const int nt = d / TT;
   const int64_t blk = blockIdx.x / npairs;
   int pr = blockIdx.x % npairs, I = 0;
   while (pr >= nt - I) {   // row-major upper triangle of the tile grid
@@ -49,39 +51,51 @@ __global__ __launch_bounds__(256) void k_transpose_blocks(const T* src, T* dst, 
   const int J = I + pr;
   const T* m = src + blk * d * d;
   T* o = dst + blk * d * d;
-  // each thread moves 4 consecutive elements of one tile row: 8 threads per
-  // row, 32 rows per pass
-  const int r = threadIdx.x >> 3, c4 = (threadIdx.x & 7) * 4;
-  float x[4], y[4];
-  load4(x, m + (size_t)(32 * I + r) * d + 32 * J + c4);
-  load4(y, m + (size_t)(32 * J + r) * d + 32 * I + c4);
+  // each thread moves 4 consecutive elements of a tile row at a time: TT / 4
+  // threads per row, 1024 / TT rows per pass
+  constexpr int TPR = TT / 4, RPP = 256 / TPR, NP = TT / RPP;
+  const int r = threadIdx.x / TPR, c4 = (threadIdx.x % TPR) * 4;
+  float x[NP][4], y[NP][4];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    ta[r][c4 + e] = x[e];
-    tb[r][c4 + e] = y[e];
+  for (int p = 0; p < NP; ++p) {
+    load4(x[p], m + (size_t)(TT * I + r + RPP * p) * d + TT * J + c4);
+    load4(y[p], m + (size_t)(TT * J + r + RPP * p) * d + TT * I + c4);
   }
+#pragma unroll
+  for (int p = 0; p < NP; ++p)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      ta[r + RPP * p][c4 + e] = x[p][e];
+      tb[r + RPP * p][c4 + e] = y[p][e];
+    }
   __syncthreads();
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    x[e] = ta[c4 + e][r];
-    y[e] = tb[c4 + e][r];
+  for (int p = 0; p < NP; ++p)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[p][e] = ta[c4 + e][r + RPP * p];
+      y[p][e] = tb[c4 + e][r + RPP * p];
+    }
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    store4(o + (size_t)(TT * J + r + RPP * p) * d + TT * I + c4, x[p]);   // tile (I, J) transposed into (J, I)
+    if (I != J) store4(o + (size_t)(TT * I + r + RPP * p) * d + TT * J + c4, y[p]);
   }
-  store4(o + (size_t)(32 * J + r) * d + 32 * I + c4, x);   // tile (I, J) transposed into (J, I)
-  if (I != J) store4(o + (size_t)(32 * I + r) * d + 32 * J + c4, y);
 }
 
 hipError_t launch_transpose_blocks_to(Elt elt, const void* src, void* dst, int d, int64_t nblocks, hipStream_t st) {
-  if (d % 32 || d <= 0) return hipErrorInvalidValue;
-  const int nt = d / 32, npairs = nt * (nt + 1) / 2;
+  const int TT = elt == kBF16 ? 64 : 32;
+  if (d % TT || d <= 0) return hipErrorInvalidValue;
+  const int nt = d / TT, npairs = nt * (nt + 1) / 2;
   const int64_t wgs = nblocks * npairs;
   if (wgs == 0) return hipSuccess;
   if (wgs > INT32_MAX) return hipErrorInvalidValue;
   TraceScope ts("k_transpose_blocks", st);
   if (elt == kBF16)
-    hipLaunchKernelGGL(k_transpose_blocks<bf16>, dim3((unsigned)wgs), dim3(256), 0, st, (const bf16*)src, (bf16*)dst, d,
-                       npairs);
+    hipLaunchKernelGGL((k_transpose_blocks<bf16, 64>), dim3((unsigned)wgs), dim3(256), 0, st, (const bf16*)src,
+                       (bf16*)dst, d, npairs);
   else
-    hipLaunchKernelGGL(k_transpose_blocks<float>, dim3((unsigned)wgs), dim3(256), 0, st, (const float*)src,
+    hipLaunchKernelGGL((k_transpose_blocks<float, 32>), dim3((unsigned)wgs), dim3(256), 0, st, (const float*)src,
                        (float*)dst, d, npairs);
   return hipGetLastError();
 }

@@ -111,7 +111,8 @@ hipError_t launch_rglru_scan(Elt elt, const void* X, int64_t ldx, const void* G,
                              float c, const float* h0, float* hT, void* Y, int64_t ldy, int batch, int seqlen,
                              int width, hipStream_t stream);
 
-// In-place transpose of nblocks contiguous d x d blocks of elt (d % 32 == 0).
+// In-place transpose of nblocks contiguous d x d blocks of elt (d a multiple
+// of 64 for bf16, of 32 for float32).
 hipError_t launch_transpose_blocks(Elt elt, void* base, int d, int64_t nblocks, hipStream_t stream);
 // The same from src to dst (disjoint, or equal for the in-place transpose).
 hipError_t launch_transpose_blocks_to(Elt elt, const void* src, void* dst, int d, int64_t nblocks, hipStream_t stream);
