@@ -134,16 +134,19 @@ __global__ __launch_bounds__(512) void k_chunk_rscan(const bf16* __restrict__ K,
   auto issue = [&](int n) {                          // copies of key block n (clamped) into its slot
     const int nb = min(n, NB - 1), kb = nb * KB;
     const uint32_t lim = (uint32_t)min(KB - 1, N - 1 - kb);
-    const int row0 = REV ? N - 1 - kb - (int)lim : kb;
+    const uint32_t row0 = (uint32_t)(REV ? N - 1 - kb - (int)lim : kb);
     const uint32_t slot = (uint32_t)(uintptr_t)(lds + (n % NS) * C::STG);
 #pragma unroll
     for (int t = 0; t < CPW; ++t) {
       const int idx = wave * CPW + t;
       const bool isk = idx < KCH / 64;
       const uint32_t ld = (uint32_t)(isk ? ldk : ldv);
-      const bf16* base = isk ? Kb + (size_t)row0 * ldk : Vb + (size_t)row0 * ldv;
+      // 32 x 32-bit row products, and the lane's row (< 64) times the byte
+      // stride on the 24-bit multiplier (strides stay below 2^20 bytes)
+      const bf16* base = (isk ? Kb : Vb) + (uint64_t)row0 * ld;
       const uint32_t r = REV ? lim - min(crow[t], lim) : min(crow[t], lim);
-      copy16_to_lds(rs_uniform(base), r * ld * 2u + ccol[t], __builtin_amdgcn_readfirstlane(slot + (uint32_t)idx * 1024u));
+      copy16_to_lds(rs_uniform(base), __umul24(r, 2u * ld) + ccol[t],
+                    __builtin_amdgcn_readfirstlane(slot + (uint32_t)idx * 1024u));
     }
   };
 
@@ -185,8 +188,8 @@ __global__ __launch_bounds__(512) void k_chunk_rscan(const bf16* __restrict__ K,
 
   // scale block m's V rows by zeta_s = gamma^(L - 1 - s) in place (s = key
   // index in its chunk; keys past the sequence end: 0)
-  auto scale_v = [&](int m) {
-    const int kb = m * KB, c0 = (kb / chunk) * chunk, L = min(chunk, N - c0);
+  auto scale_v = [&](int m, int c0) {               // c0: first key of block m's chunk
+    const int kb = m * KB, L = min(chunk, N - c0);
     lds_char* sl = lds + (m % NS) * C::STG;
 #pragma unroll
     for (int v = 0; v < C::VPT; ++v) {
@@ -208,10 +211,14 @@ __global__ __launch_bounds__(512) void k_chunk_rscan(const bf16* __restrict__ K,
 #pragma unroll
   for (int a = 0; a < NS - 1; ++a) issue(a);
   copies_wait_barrier<(NS - 2) * CPW>();
-  scale_v(0);
+  scale_v(0, 0);
 
+  // chunk index and first key of the current block, stepped (a chunk is a
+  // whole number of blocks) rather than divided per block
+  int ci = 0, c0 = 0;
   for (int n = 0; n < NB; ++n) {
-    const int kb = n * KB, ci = kb / chunk, c0 = ci * chunk;
+    const int kb = n * KB;
+    if (kb == c0 + chunk) { ++ci; c0 += chunk; }     // uniform
     lds_char* sl = lds + (n % NS) * C::STG;
     copies_wait_barrier<(NS - 3) * CPW>();
     issue(n + NS - 1);
@@ -281,7 +288,7 @@ __global__ __launch_bounds__(512) void k_chunk_rscan(const bf16* __restrict__ K,
       for (int i = 0; i < WTM; ++i)
 #pragma unroll
         for (int j = 0; j < WTN; ++j) mma16(acc[i][j], af[i], bfr[j]);
-      if (ks == 0 && n + 1 < NB) scale_v(n + 1);     // uniform
+      if (ks == 0 && n + 1 < NB) scale_v(n + 1, kb + KB == c0 + chunk ? c0 + chunk : c0);   // uniform
     }
   }
 
