@@ -1229,10 +1229,12 @@ template <class T, int DK, int DV>
 static hipError_t run_parallel(const ChunkArgs& a, const HeadTab& tab, hipStream_t st) {
   const int TPC = (a.seqlen + 127) / 128;
   TraceScope ts("k_chunk_out", st);
-  // the 16-rows-per-wave kernel for the 512-wide value heads only: with one
-  // long chunk the work is all matrix-core steps, where the 32-row kernel
-  // of d_v <= 256 is the faster one
-  if (chunk_out_o16(a.elt, DK, DV, TPC * 128) && DV > 256 && !a.rev_in && !a.rev_out)
+  // the 16-rows-per-wave kernel for the 512-wide value heads, and for d_v
+  // 256 up to 32 row tiles (4096 tokens): longer single chunks are mostly
+  // matrix-core steps, where the 32-row kernel of d_v <= 256 is the faster
+  // one (at d_v 256, b2 x 10 heads: 41 / 82 / 274 us against 46 / 97 / 281 us
+  // at 1024 / 2048 / 4096 tokens, 3554 against 3111 us at 16384)
+  if (chunk_out_o16(a.elt, DK, DV, TPC * 128) && (DV > 256 || TPC <= 32) && !a.rev_in && !a.rev_out)
     return launch_out_o16(a, false, TPC * 128, 1, TPC, 0, tab, st);
   if (a.q_rope_tab && sizeof(T) == 2 && DV <= 256) return hipErrorInvalidValue;
   if constexpr (sizeof(T) == 2 && DV <= 256)
