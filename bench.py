@@ -57,12 +57,15 @@ PEAK_HBM = 8.0e12                      # bytes/s
 # kernel whose sources have changed since reports null.
 MEASURED_TRAFFIC = {  # (workload, kernel): (bytes per launch, sources, sha256[:16])
     ("block_bf16_b4_n8192", "k_gemm"): (7.450e+09, ('k_gemm.hip', 'msr_device.h'), "d6d1fb4f84103cf7"),
-    ("block_bf16_b4_n8192", "k_chunk_out"): (3.422e+09, ('k_chunk_o16.hip', 'msr_device.h'), "0b62dd6ed4d8c45e"),
-    ("block_bf16_b4_n8192", "k_chunk_rscan"): (1.075e+09, ('k_chunk_rscan.hip', 'msr_device.h'), "137bae01dfdbb700"),
-    ("block_bf16_b4_n8192:core", "k_chunk_out"): (2.843e+09, ('k_chunk_o16.hip', 'msr_device.h'),
-                                                  "0b62dd6ed4d8c45e"),
-    ("block_bf16_b4_n8192:core", "k_chunk_rscan"): (1.075e+09, ('k_chunk_rscan.hip', 'msr_device.h'),
-                                                    "137bae01dfdbb700"),
+    ("block_bf16_b4_n8192", "k_chunk_out"): (3.342e+09, ('k_chunk_o16.hip', 'msr_device.h'), "d363d9876734f0d8"),
+    ("block_bf16_b4_n8192", "k_chunk_rscan"): (1.079e+09, ('k_chunk_rscan.hip', 'msr_device.h'), "f884352b01858490"),
+    ("block_bf16_b4_n8192:core", "k_chunk_out"): (1.880e+09, ('k_chunk_o16.hip', 'msr_device.h'),
+                                                  "d363d9876734f0d8"),
+    ("block_bf16_b4_n8192:core", "k_chunk_rscan"): (1.079e+09, ('k_chunk_rscan.hip', 'msr_device.h'),
+                                                    "f884352b01858490"),
+    ("long_bf16_b2_n16384:core", "k_chunk_out"): (7.554e+08, ('k_chunk_o16.hip', 'msr_device.h'), "d363d9876734f0d8"),
+    ("long_bf16_b2_n16384:core", "k_chunk_state"): (4.213e+08, ('k_chunk.hip', 'msr_device.h'), "6d4c12e791058fb3"),
+    ("long_bf16_b2_n16384:core", "k_chunk_scan"): (1.678e+08, ('k_chunk.hip', 'msr_device.h'), "6d4c12e791058fb3"),
 }
 CSRC = os.path.join(ROOT, "linear_recurrence_sequence_amd", "csrc")
 
@@ -593,7 +596,7 @@ def main():
         log("long")
         lw = workloads.WORKLOADS["long_bf16_b2_n16384"]
         long = {"core_chunkwise": bench_core(lw.batch, lw.seqlen, lw.heads, lw.d_k, lw.chunk, args.steps,
-                                             args.warmup),
+                                             args.warmup, workload=lw.name + ":core"),
                 "core_chunkwise_rotated": bench_core(lw.batch, lw.seqlen, lw.heads, lw.d_k, lw.chunk, args.steps,
                                                      args.warmup, rope_base=lw.rope_base)}
         sweep = []
