@@ -91,6 +91,30 @@ def test_long_core_chunkwise_vs_oracle_and_parallel():
     assert oracle.max_rel_err(host(S_out)[1:], Sref) < 1e-2
 
 
+def test_block_core_parallel_vs_chunkwise_and_oracle():
+    """The block workload's core shape (batch 4 x 8192 tokens, 16 heads,
+    d_k 256, d_v 512) through the parallel form -- one chunk of 64 row tiles
+    on the paired 16-row output kernel, as bench.py times it -- against the
+    chunkwise form everywhere and against the oracle on batch element 2."""
+    import torch
+    msr = _msr()
+    w = workloads.WORKLOADS["block_bf16_b4_n8192"]
+    B, N, H, dk, dv = w.batch, w.seqlen, w.heads, w.d_k, w.d_v
+    q, k, v = workloads.core_inputs(33, B, N, H, dk, dv, "bf16")
+    g = workloads.gammas(H)
+    s = 1 / math.sqrt(dk)
+    say("block core parallel vs chunkwise")
+    Qd, Kd, Vd = dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16")
+    o_p = msr.msr_parallel_fwd(Qd, Kd, Vd, g, qk_scale=s)
+    o_c = msr.msr_chunkwise_fwd(Qd, Kd, Vd, g, w.chunk, qk_scale=s)
+    torch.cuda.synchronize()
+    e_pc = oracle.max_rel_err_per_head(host(o_p), host(o_c))
+    ref, _ = oracle.retention_chunkwise(q[2:3], k[2:3], v[2:3], g, w.chunk, s)
+    e_p = oracle.max_rel_err_per_head(host(o_p)[2:3], ref)
+    print(f"block core: parallel vs chunkwise {e_pc:.3e}, parallel vs oracle (batch 2) {e_p:.3e}", flush=True)
+    assert e_pc < TOL["bf16"] and e_p < TOL["bf16"]
+
+
 def test_layer_b8_n2048_chunkwise_equals_parallel():
     """The bf16 b8 x 2048 workload's core shape through both forms on the
     GPU (the layer runs the chunkwise one), each against the oracle on
