@@ -83,6 +83,34 @@ def test_chunkwise(dtype, dk, dv, N, chunk):
     assert oracle.max_rel_err(host(S_out), Sref) < (1e-4 if dtype == "f32" else 1e-2)
 
 
+@pytest.mark.parametrize("dv,chunk", [(512, 512), (256, 256)])
+def test_chunkwise_paired_tiles_ragged(dv, chunk):
+    """Enough (batch, head, chunk) units that each workgroup of the 16-row
+    output kernel walks several tiles, so that the backward-walked row tiles
+    (key blocks from the diagonal down, Q R_{i-1} last with Q pre-scaled)
+    run beside the forward-walked ones, with a ragged last chunk and an
+    initial state: batch 4, 3000 tokens, 16 heads, d_k 256, bf16, no
+    rotation; the last batch element against the oracle (outputs per head,
+    final states)."""
+    import torch
+    msr = _msr()
+    B, N, H, dk = 4, 3000, 16, 256
+    q, k, v = workloads.core_inputs(71, B, N, H, dk, dv, "bf16")
+    S0 = np.random.default_rng(72).standard_normal((B, H, dk, dv)).astype(np.float32)
+    g = workloads.gammas(H)
+    scale = 1 / math.sqrt(dk)
+    S_out = torch.empty((B, H, dk, dv), device="cuda")
+    say("chunkwise paired tiles, ragged", dv, chunk)
+    O = msr.msr_chunkwise_fwd(dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16"), g, chunk, qk_scale=scale,
+                              S_in=torch.from_numpy(S0).cuda(), S_out=S_out)
+    torch.cuda.synchronize()
+    Oref, Sref = oracle.retention_chunkwise(q[3:], k[3:], v[3:], g, chunk, scale, S0[3:])
+    err = oracle.max_rel_err_per_head(host(O)[3:], Oref)
+    print(f"paired tiles d_v {dv} chunk {chunk}: max rel err per head {err:.3e}", flush=True)
+    assert err < TOL["bf16"]
+    assert oracle.max_rel_err(host(S_out)[3:], Sref) < 1e-2
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_chunkwise_special_gammas_no_state(dtype):
     """gamma = 0, 0.5 and 1 (the degenerate decays), no initial state, no
