@@ -548,6 +548,129 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_dc(const bf16* __restrict__ A,
   gemm_epilogue<bf16, BM, BN, WM, WN, EPI>(acc, reinterpret_cast<float*>(smem), bp, C, ldc, M, N, m0, n0, wave, lane);
 }
 
+// ---------------------------------------------------------------------------
+// k_gemm_sk: bf16 C = A B for at most 128 rows of A (one token per sequence
+// in decode), where the product is a stream of the weights B: 128 x 128
+// output tiles, 64-deep K slabs of both operands copied straight to LDS
+// (direct 16-byte copies) through a ring of NS slots, NS - 1 slabs in
+// flight, so that each CU keeps about 48 KiB of the weight stream in
+// flight.  8 waves (two per SIMD), wave w: rows 32 (w % 4), columns
+// 64 (w / 4) as two 32 x 32 tiles.  Plain bf16 output or float32 split-K
+// partials (blockIdx.z = split), no other epilogue.
+//   A slab: 128 rows x 8 chunks (8 k each), chunk c of row r in slot
+//   c ^ ((r / 2) % 8): the 16 rows that one LDS pass of a fragment read
+//   serves fall on 16 different 16-byte bank groups.
+//   B slab: 64 k-rows x 16 chunks (8 columns each), chunk c of k-row r in
+//   slot c ^ (4 (r % 4)): the four k-rows that one pass of the transposing
+//   read serves fall on four different 64-byte bank groups.
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8_t;
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4_t;
+
+template <bool PART>
+__global__ __launch_bounds__(512) void k_gemm_sk(const bf16* __restrict__ A, int64_t lda, GemmB bp,
+                                                 bf16* __restrict__ C, int64_t ldc, int M, int N, int K) {
+  constexpr int BM = 128, BN = 128, BK = 64, NS = 4, AHEAD = NS - 1, NW = 8;
+  constexpr int ASL = BM * BK / 8, BSL = BK * BN / 8;  // 16-byte slots of the A and B slabs (1024 each)
+  constexpr int STG = (ASL + BSL) * 16;              // bytes per ring slot
+  constexpr int CPW = (ASL + BSL) / 64 / NW;         // copies per wave per slab (4)
+  constexpr int ACP = ASL / 64 / NW;                 // of which A (2)
+  static_assert(CPW * 64 * NW == ASL + BSL && ACP * 64 * NW == ASL, "whole copies per wave");
+  __shared__ __attribute__((aligned(1024))) char smem[NS * STG];
+
+  const int tid = threadIdx.x, lane = tid & 63, lr = lane & 31, hh = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n0 = blockIdx.x * BN;
+  const int kz = blockIdx.z * K;                     // this split's first K row
+  const int KT = K / BK;
+  // the tile lies inside one weight segment (checked by the launcher)
+  const int sg = (n0 >= bp.start[1]) + (n0 >= bp.start[2]) + (n0 >= bp.start[3]);
+  auto sel = [&](auto a0, auto a1, auto a2, auto a3) { return sg == 0 ? a0 : (sg == 1 ? a1 : (sg == 2 ? a2 : a3)); };
+  const bf16* Bs = reinterpret_cast<const bf16*>(sel(bp.ptr[0], bp.ptr[1], bp.ptr[2], bp.ptr[3]));
+  const int64_t ldb = sel(bp.ld[0], bp.ld[1], bp.ld[2], bp.ld[3]);
+  const bf16* Bt = Bs + (n0 - sel(bp.start[0], bp.start[1], bp.start[2], bp.start[3])) + (size_t)kz * ldb;
+  const bf16* At = A + kz;
+
+  // Per-lane source offsets (elements) of this wave's copies; copy t fills
+  // slots 64 (NW t + wave) + lane of the slab (A for t < ACP, then B).
+  uint32_t off[CPW];
+#pragma unroll
+  for (int t = 0; t < CPW; ++t) {
+    const int u = 64 * (NW * t + wave) + lane;
+    if (t < ACP) {
+      const int r = u / 8, c = (u % 8) ^ ((r >> 1) & 7);
+      off[t] = (uint32_t)(min(r, M - 1) * lda + 8 * c);
+    } else {
+      const int v = u - ASL, r = v / 16, c = (v % 16) ^ (4 * (r & 3));
+      off[t] = (uint32_t)(r * ldb + 8 * c);
+    }
+  }
+  lds_char* const lds = (lds_char*)smem;
+  // copies of slab j into its slot (slabs past the last re-copy the last
+  // one, into a slot no wave reads again, so that every slab issues CPW
+  // copies and the waits are fixed)
+  auto issue = [&](int j) {
+    const int jj = min(j, KT - 1);
+    const uint32_t dst = (uint32_t)(uintptr_t)(lds + (j % NS) * STG) + wave * 1024;
+    const bf16* a = At + (size_t)jj * BK;
+    const bf16* b = Bt + (size_t)jj * BK * ldb;
+#pragma unroll
+    for (int t = 0; t < CPW; ++t)
+      copy16_to_lds(t < ACP ? a : b, 2 * off[t], __builtin_amdgcn_readfirstlane(dst + t * NW * 1024));
+  };
+#pragma unroll
+  for (int j = 0; j < AHEAD; ++j) issue(j);
+
+  // fragment offsets within a slot: A row 32 (w % 4) + lr, chunk 2 s + hh;
+  // B (transposing read, as load_frag_rm): k-row 16 s + 8 hh' + 4 p + jj,
+  // columns 64 (w / 4) + 32 tj + 16 c + 4 q
+  const int ar = 32 * (wave & 3) + lr;
+  const uint32_t abase = (uint32_t)(ar * 128);
+  const int af = (ar >> 1) & 7;
+  const int g = lane >> 4, i16 = lane & 15, bh = g >> 1, bc = g & 1, jj = i16 >> 2, q = i16 & 3;
+  f32x16 acc[2] = {(f32x16){}, (f32x16){}};
+  for (int j = 0; j < KT; ++j) {
+    copies_wait_barrier<(AHEAD - 1) * CPW>();
+    issue(j + AHEAD);
+    const lds_char* sa = lds + (j % NS) * STG;
+    const lds_char* sb = sa + ASL * 16;
+#pragma unroll
+    for (int s = 0; s < BK / 16; ++s) {
+      Frag<bf16> a;
+      a.v = *(const lds_bf16x8_t*)(sa + abase + 16 * ((2 * s + hh) ^ af));
+#pragma unroll
+      for (int tj = 0; tj < 2; ++tj) {
+        Frag<bf16> b;
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          const int kr = 16 * s + 8 * bh + 4 * p + jj;
+          const int col = 64 * (wave >> 2) + 32 * tj + 16 * bc + 4 * q;
+          const int ch = (col >> 3) ^ (4 * (kr & 3));
+          const bf16x4 r4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+              (lds_bf16x4_t*)(sb + kr * 256 + 16 * ch + 2 * (col & 7)));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) b.v[4 * p + e] = r4[e];
+        }
+        mma16(acc[tj], a, b);
+      }
+    }
+  }
+  copies_wait_barrier<0>();                          // the trailing copies landed
+  // epilogue: lane holds column lr of each 32 x 32 tile, rows 8 (r / 4) + 4 hh + r % 4
+#pragma unroll
+  for (int tj = 0; tj < 2; ++tj) {
+    const int n = n0 + 64 * (wave >> 2) + 32 * tj + lr;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int m = 32 * (wave & 3) + 8 * (r >> 2) + 4 * hh + (r & 3);
+      if (m < M) {
+        if constexpr (PART) bp.part[(size_t)blockIdx.z * M * ldc + (size_t)m * ldc + n] = acc[tj][r];
+        else C[(size_t)m * ldc + n] = (bf16)acc[tj][r];
+      }
+    }
+  }
+}
+
 // Sum of the split-K partials, rounded once: 8 consecutive columns per thread.
 template <class T>
 __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__ part, int splits,
@@ -575,6 +698,13 @@ static bool skinny(Elt elt, int M) { return elt == kBF16 && M <= 128; }
 
 
 int gemm_splits(Elt elt, int M, int N, int K) {
+  if (skinny(elt, M) && N % 128 == 0) {
+    // k_gemm_sk: one workgroup per CU, at most 8 slices
+    const int tiles = N / 128;
+    int s = 1;
+    while (s < 8 && tiles * s < 256 && K % (64 * 2 * s) == 0) s *= 2;
+    return s;
+  }
   if (skinny(elt, M)) {
     // at least two workgroups per CU, at most 4 slices (more only adds partials traffic)
     const int tiles = (N + 63) / 64;
@@ -659,7 +789,14 @@ static void launch_dc(dim3 grid, const bf16* A, int64_t lda, const GemmB& b, bf1
 // bf16 and f32 products on their usual tiles, or on the skinny tiles.
 static void launch_any(Elt elt, const void* A, int64_t lda, const GemmB& b, void* C, int64_t ldc, int M, int N,
                        int K, int splits, hipStream_t st) {
-  if (skinny(elt, M)) {
+  const int epi = epilogue_set(b);
+  if (skinny(elt, M) && N % 128 == 0 && K % 64 == 0 && (epi == 0 || epi == kEpiPart) && uniform_segments(b, N, 128)) {
+    const dim3 grid(N / 128, 1, splits);
+    if (epi == kEpiPart)
+      hipLaunchKernelGGL((k_gemm_sk<true>), grid, dim3(512), 0, st, (const bf16*)A, lda, b, (bf16*)C, ldc, M, N, K);
+    else
+      hipLaunchKernelGGL((k_gemm_sk<false>), grid, dim3(512), 0, st, (const bf16*)A, lda, b, (bf16*)C, ldc, M, N, K);
+  } else if (skinny(elt, M)) {
     launch_tiles<bf16, 128, 64, 64, 2, 2>(dim3((N + 63) / 64, 1, splits), (const bf16*)A, lda, b, (bf16*)C, ldc, M,
                                           N, K, st);
   } else if (elt == kBF16 && uniform_segments(b, N, 256)) {
