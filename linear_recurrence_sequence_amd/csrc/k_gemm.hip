@@ -550,32 +550,42 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_dc(const bf16* __restrict__ A,
 
 // ---------------------------------------------------------------------------
 // k_gemm_sk: bf16 C = A B for at most 128 rows of A (one token per sequence
-// in decode), where the product is a stream of the weights B: 128 x 128
+// in decode), where the product is a stream of the weights B: 128 x 64
 // output tiles, 64-deep K slabs of both operands copied straight to LDS
-// (direct 16-byte copies) through a ring of NS slots, NS - 1 slabs in
-// flight, so that each CU keeps about 48 KiB of the weight stream in
-// flight.  8 waves (two per SIMD), wave w: rows 32 (w % 4), columns
-// 64 (w / 4) as two 32 x 32 tiles.  Plain bf16 output or float32 split-K
-// partials (blockIdx.z = split), no other epilogue.
+// (direct 16-byte copies) through a ring of 5 slots, 4 slabs (32 KiB of
+// the weight stream) in flight per CU.  8 waves (two per SIMD), wave w:
+// rows 32 (w % 4), columns 32 (w / 4).  Plain bf16 output or float32
+// split-K partials (blockIdx.z = split), no other epilogue.
 //   A slab: 128 rows x 8 chunks (8 k each), chunk c of row r in slot
 //   c ^ ((r / 2) % 8): the 16 rows that one LDS pass of a fragment read
 //   serves fall on 16 different 16-byte bank groups.
-//   B slab: 64 k-rows x 16 chunks (8 columns each), chunk c of k-row r in
-//   slot c ^ (4 (r % 4)): the four k-rows that one pass of the transposing
-//   read serves fall on four different 64-byte bank groups.
+//   B slab: 64 k-rows x 8 chunks (8 columns each), chunk c of k-row r in
+//   slot c ^ 4 ((r / 2) % 2): the four k-rows that one pass of the
+//   transposing read serves fall on four different 64-byte bank groups.
 // ---------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8_t;
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4_t;
 
+struct SkCfg {
+  static constexpr int BM = 128, BN = 64, BK = 64, NW = 8;
+  static constexpr int NS = 5;                       // ring slots (120 KiB)
+  static constexpr int TJ = BN / 64;                 // 32 x 32 tiles per wave
+  static constexpr int CPR = BN / 8;                 // chunks per B k-row
+  static constexpr int ASL = BM * BK / 8, BSL = BK * BN / 8;   // 16-byte slots of the A and B slabs
+  static constexpr int STG = (ASL + BSL) * 16;       // bytes per ring slot
+  static constexpr int CPW = (ASL + BSL) / 64 / NW;  // copies per wave per slab
+  static constexpr int ACP = ASL / 64 / NW;          // of which A
+  static_assert(CPW * 64 * NW == ASL + BSL && ACP * 64 * NW == ASL, "whole copies per wave");
+  static_assert(NS * STG <= 160 * 1024, "ring fits in LDS");
+  static __device__ __forceinline__ int bsw(int r) { return 4 * ((r >> 1) & 1); }
+};
+
 template <bool PART>
 __global__ __launch_bounds__(512) void k_gemm_sk(const bf16* __restrict__ A, int64_t lda, GemmB bp,
                                                  bf16* __restrict__ C, int64_t ldc, int M, int N, int K) {
-  constexpr int BM = 128, BN = 128, BK = 64, NS = 4, AHEAD = NS - 1, NW = 8;
-  constexpr int ASL = BM * BK / 8, BSL = BK * BN / 8;  // 16-byte slots of the A and B slabs (1024 each)
-  constexpr int STG = (ASL + BSL) * 16;              // bytes per ring slot
-  constexpr int CPW = (ASL + BSL) / 64 / NW;         // copies per wave per slab (4)
-  constexpr int ACP = ASL / 64 / NW;                 // of which A (2)
-  static_assert(CPW * 64 * NW == ASL + BSL && ACP * 64 * NW == ASL, "whole copies per wave");
+  using SC = SkCfg;
+  constexpr int BN = SC::BN, BK = SC::BK, NS = SC::NS, AHEAD = NS - 1, NW = SC::NW, TJ = SC::TJ, CPW = SC::CPW, ACP = SC::ACP;
+  constexpr int ASL = SC::ASL, STG = SC::STG, CPR = SC::CPR;
   __shared__ __attribute__((aligned(1024))) char smem[NS * STG];
 
   const int tid = threadIdx.x, lane = tid & 63, lr = lane & 31, hh = lane >> 5;
@@ -601,7 +611,7 @@ __global__ __launch_bounds__(512) void k_gemm_sk(const bf16* __restrict__ A, int
       const int r = u / 8, c = (u % 8) ^ ((r >> 1) & 7);
       off[t] = (uint32_t)(min(r, M - 1) * lda + 8 * c);
     } else {
-      const int v = u - ASL, r = v / 16, c = (v % 16) ^ (4 * (r & 3));
+      const int v = u - ASL, r = v / CPR, c = (v % CPR) ^ SC::bsw(r);
       off[t] = (uint32_t)(r * ldb + 8 * c);
     }
   }
@@ -623,12 +633,14 @@ __global__ __launch_bounds__(512) void k_gemm_sk(const bf16* __restrict__ A, int
 
   // fragment offsets within a slot: A row 32 (w % 4) + lr, chunk 2 s + hh;
   // B (transposing read, as load_frag_rm): k-row 16 s + 8 hh' + 4 p + jj,
-  // columns 64 (w / 4) + 32 tj + 16 c + 4 q
+  // columns (BN / 2) (w / 4) + 32 tj + 16 c + 4 q
   const int ar = 32 * (wave & 3) + lr;
   const uint32_t abase = (uint32_t)(ar * 128);
   const int af = (ar >> 1) & 7;
   const int g = lane >> 4, i16 = lane & 15, bh = g >> 1, bc = g & 1, jj = i16 >> 2, q = i16 & 3;
-  f32x16 acc[2] = {(f32x16){}, (f32x16){}};
+  f32x16 acc[TJ];
+#pragma unroll
+  for (int tj = 0; tj < TJ; ++tj) acc[tj] = (f32x16){};
   for (int j = 0; j < KT; ++j) {
     copies_wait_barrier<(AHEAD - 1) * CPW>();
     issue(j + AHEAD);
@@ -639,15 +651,15 @@ __global__ __launch_bounds__(512) void k_gemm_sk(const bf16* __restrict__ A, int
       Frag<bf16> a;
       a.v = *(const lds_bf16x8_t*)(sa + abase + 16 * ((2 * s + hh) ^ af));
 #pragma unroll
-      for (int tj = 0; tj < 2; ++tj) {
+      for (int tj = 0; tj < TJ; ++tj) {
         Frag<bf16> b;
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
           const int kr = 16 * s + 8 * bh + 4 * p + jj;
-          const int col = 64 * (wave >> 2) + 32 * tj + 16 * bc + 4 * q;
-          const int ch = (col >> 3) ^ (4 * (kr & 3));
+          const int col = (BN / 2) * (wave >> 2) + 32 * tj + 16 * bc + 4 * q;
+          const int ch = (col >> 3) ^ SC::bsw(kr);
           const bf16x4 r4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-              (lds_bf16x4_t*)(sb + kr * 256 + 16 * ch + 2 * (col & 7)));
+              (lds_bf16x4_t*)(sb + kr * (BN * 2) + 16 * ch + 2 * (col & 7)));
 #pragma unroll
           for (int e = 0; e < 4; ++e) b.v[4 * p + e] = r4[e];
         }
@@ -658,8 +670,8 @@ __global__ __launch_bounds__(512) void k_gemm_sk(const bf16* __restrict__ A, int
   copies_wait_barrier<0>();                          // the trailing copies landed
   // epilogue: lane holds column lr of each 32 x 32 tile, rows 8 (r / 4) + 4 hh + r % 4
 #pragma unroll
-  for (int tj = 0; tj < 2; ++tj) {
-    const int n = n0 + 64 * (wave >> 2) + 32 * tj + lr;
+  for (int tj = 0; tj < TJ; ++tj) {
+    const int n = n0 + (BN / 2) * (wave >> 2) + 32 * tj + lr;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int m = 32 * (wave & 3) + 8 * (r >> 2) + 4 * hh + (r & 3);
@@ -698,9 +710,9 @@ static bool skinny(Elt elt, int M) { return elt == kBF16 && M <= 128; }
 
 
 int gemm_splits(Elt elt, int M, int N, int K) {
-  if (skinny(elt, M) && N % 128 == 0) {
+  if (skinny(elt, M) && N % 64 == 0) {
     // k_gemm_sk: one workgroup per CU, at most 8 slices
-    const int tiles = N / 128;
+    const int tiles = N / 64;
     int s = 1;
     while (s < 8 && tiles * s < 256 && K % (64 * 2 * s) == 0) s *= 2;
     return s;
@@ -790,8 +802,8 @@ static void launch_dc(dim3 grid, const bf16* A, int64_t lda, const GemmB& b, bf1
 static void launch_any(Elt elt, const void* A, int64_t lda, const GemmB& b, void* C, int64_t ldc, int M, int N,
                        int K, int splits, hipStream_t st) {
   const int epi = epilogue_set(b);
-  if (skinny(elt, M) && N % 128 == 0 && K % 64 == 0 && (epi == 0 || epi == kEpiPart) && uniform_segments(b, N, 128)) {
-    const dim3 grid(N / 128, 1, splits);
+  if (skinny(elt, M) && N % 64 == 0 && K % 64 == 0 && (epi == 0 || epi == kEpiPart) && uniform_segments(b, N, 64)) {
+    const dim3 grid(N / 64, 1, splits);
     if (epi == kEpiPart)
       hipLaunchKernelGGL((k_gemm_sk<true>), grid, dim3(512), 0, st, (const bf16*)A, lda, b, (bf16*)C, ldc, M, N, K);
     else
