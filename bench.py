@@ -56,15 +56,15 @@ PEAK_HBM = 8.0e12                      # bytes/s
 # it was taken with: the sha256 prefix of those files is recorded, and a
 # kernel whose sources have changed since reports null.
 MEASURED_TRAFFIC = {  # (workload, kernel): (bytes per launch, sources, sha256[:16])
-    ("block_bf16_b4_n8192", "k_gemm"): (7.450e+09, ('k_gemm.hip', 'msr_device.h'), "d6d1fb4f84103cf7"),
-    ("block_bf16_b4_n8192", "k_chunk_out"): (3.342e+09, ('k_chunk_o16.hip', 'msr_device.h'), "d363d9876734f0d8"),
-    ("block_bf16_b4_n8192", "k_chunk_rscan"): (1.079e+09, ('k_chunk_rscan.hip', 'msr_device.h'), "f884352b01858490"),
+    ("block_bf16_b4_n8192", "k_gemm"): (7.450e+09, ('k_gemm.hip', 'msr_device.h'), "905f7dd4a6237cbf"),
+    ("block_bf16_b4_n8192", "k_chunk_out"): (3.316e+09, ('k_chunk_o16.hip', 'msr_device.h'), "d363d9876734f0d8"),
+    ("block_bf16_b4_n8192", "k_chunk_rscan"): (1.078e+09, ('k_chunk_rscan.hip', 'msr_device.h'), "f884352b01858490"),
     ("block_bf16_b4_n8192:core", "k_chunk_out"): (1.880e+09, ('k_chunk_o16.hip', 'msr_device.h'),
                                                   "d363d9876734f0d8"),
-    ("block_bf16_b4_n8192:core", "k_chunk_rscan"): (1.079e+09, ('k_chunk_rscan.hip', 'msr_device.h'),
+    ("block_bf16_b4_n8192:core", "k_chunk_rscan"): (1.078e+09, ('k_chunk_rscan.hip', 'msr_device.h'),
                                                     "f884352b01858490"),
     ("long_bf16_b2_n16384:core", "k_chunk_out"): (7.554e+08, ('k_chunk_o16.hip', 'msr_device.h'), "d363d9876734f0d8"),
-    ("long_bf16_b2_n16384:core", "k_chunk_state"): (4.213e+08, ('k_chunk.hip', 'msr_device.h'), "6d4c12e791058fb3"),
+    ("long_bf16_b2_n16384:core", "k_chunk_state"): (4.212e+08, ('k_chunk.hip', 'msr_device.h'), "6d4c12e791058fb3"),
     ("long_bf16_b2_n16384:core", "k_chunk_scan"): (1.678e+08, ('k_chunk.hip', 'msr_device.h'), "6d4c12e791058fb3"),
 }
 CSRC = os.path.join(ROOT, "linear_recurrence_sequence_amd", "csrc")
