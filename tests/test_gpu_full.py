@@ -115,6 +115,29 @@ def test_block_core_parallel_vs_chunkwise_and_oracle():
     assert e_pc < TOL["bf16"] and e_p < TOL["bf16"]
 
 
+def test_parallel_dv256_4096_tokens_paired_tiles():
+    """The parallel form at d_v 256 and 4096 tokens -- one chunk of 32 row
+    tiles on the paired 16-row output kernel -- at the long workload's head
+    shape (batch 2, 10 heads of 256): batch element 1 against the oracle,
+    everything against the GPU chunkwise form (chunk 512)."""
+    import torch
+    msr = _msr()
+    B, N, H, d = 2, 4096, 10, 256
+    q, k, v = workloads.core_inputs(34, B, N, H, d, d, "bf16")
+    g = workloads.gammas(H)
+    s = 1 / math.sqrt(d)
+    say("parallel d_v 256, 4096 tokens")
+    Qd, Kd, Vd = dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16")
+    o_p = msr.msr_parallel_fwd(Qd, Kd, Vd, g, qk_scale=s)
+    o_c = msr.msr_chunkwise_fwd(Qd, Kd, Vd, g, 512, qk_scale=s)
+    torch.cuda.synchronize()
+    e_pc = oracle.max_rel_err_per_head(host(o_p), host(o_c))
+    ref, _ = oracle.retention_chunkwise(q[1:], k[1:], v[1:], g, 512, s)
+    e_p = oracle.max_rel_err_per_head(host(o_p)[1:], ref)
+    print(f"parallel d_v 256 N 4096: vs chunkwise {e_pc:.3e}, vs oracle (batch 1) {e_p:.3e}", flush=True)
+    assert e_pc < TOL["bf16"] and e_p < TOL["bf16"]
+
+
 def test_layer_b8_n2048_chunkwise_equals_parallel():
     """The bf16 b8 x 2048 workload's core shape through both forms on the
     GPU (the layer runs the chunkwise one), each against the oracle on
