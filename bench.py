@@ -56,7 +56,7 @@ PEAK_HBM = 8.0e12                      # bytes/s
 # it was taken with: the sha256 prefix of those files is recorded, and a
 # kernel whose sources have changed since reports null.
 MEASURED_TRAFFIC = {  # (workload, kernel): (bytes per launch, sources, sha256[:16])
-    ("block_bf16_b4_n8192", "k_gemm"): (7.450e+09, ('k_gemm.hip', 'msr_device.h'), "905f7dd4a6237cbf"),
+    ("block_bf16_b4_n8192", "k_gemm"): (7.450e+09, ('k_gemm.hip', 'msr_device.h'), "ada3023b46f5318f"),
     ("block_bf16_b4_n8192", "k_chunk_out"): (3.316e+09, ('k_chunk_o16.hip', 'msr_device.h'), "d363d9876734f0d8"),
     ("block_bf16_b4_n8192", "k_chunk_rscan"): (1.078e+09, ('k_chunk_rscan.hip', 'msr_device.h'), "f884352b01858490"),
     ("block_bf16_b4_n8192:core", "k_chunk_out"): (1.880e+09, ('k_chunk_o16.hip', 'msr_device.h'),

@@ -404,7 +404,9 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm(const T* __restrict__ A, 
 // between the two steps, so the first fragments of a slab are read before
 // its first MFMA is due.
 // ---------------------------------------------------------------------------
-template <int EPI, int NS, int NW>
+// PRIO > 0: each k16 step's fragment reads and matrix-core instructions run
+// at that wave priority, the waits and barriers between them at 0.
+template <int EPI, int NS, int NW, int PRIO>
 __global__ __launch_bounds__(64 * NW) void k_gemm_dc(const bf16* __restrict__ A, int64_t lda, GemmB bp,
                                                      bf16* __restrict__ C, int64_t ldc, int M, int N, int K) {
   constexpr int BM = 256, BN = 256, BK = 32, WM = 2, WN = NW / 2, TM = 4, TN = 4 / (NW / 4);
@@ -506,6 +508,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_dc(const bf16* __restrict__ A,
   for (int kt = 0; kt < KT; ++kt) {
     const bf16* slab = smem + (kt % NS) * SLOTS * 8;
     // step 0: read step 1's fragments, MFMAs of step 0
+    if constexpr (PRIO) __builtin_amdgcn_s_setprio(PRIO);
     rd(slab, 1, af[1], bfr[1]);
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -520,12 +523,14 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_dc(const bf16* __restrict__ A,
     }
     __builtin_amdgcn_sched_group_barrier(SG_MFMA, TM * TN - NRD, 0);
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
     // slab kt + 1 landed (this wave's copies, then everyone's), every wave
     // is past slab kt - 1: its slot takes slab kt + NS - 1
     copies_wait_barrier<CPW * (NS - 3)>();
     // step 1: the next slab's step-0 fragments (after the last slab: a
     // harmless read of a slot nobody writes) and the refill copies between
     // the MFMAs of step 1
+    if constexpr (PRIO) __builtin_amdgcn_s_setprio(PRIO);
     rd(smem + ((kt + 1) % NS) * SLOTS * 8, 0, af[0], bfr[0]);
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
@@ -543,6 +548,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_dc(const bf16* __restrict__ A,
     }
     __builtin_amdgcn_sched_group_barrier(SG_MFMA, TM * TN - NRD, 0);
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
   }
   copies_wait_barrier<0>();                          // the trailing copies landed, every wave is done with the ring
   gemm_epilogue<bf16, BM, BN, WM, WN, EPI>(acc, reinterpret_cast<float*>(smem), bp, C, ldc, M, N, m0, n0, wave, lane);
@@ -779,12 +785,18 @@ static void launch_tiles(dim3 grid, const T* A, int64_t lda, const GemmB& b, T* 
 // The direct-copy bf16 product on 256 x 256 tiles, instantiated for the
 // epilogue option set as launch_tiles does.  8 waves and four ring slots:
 // the fastest of 4 / 8 waves x 3 / 4 / 5 slots on the layer's projection
-// shapes.
+// shapes.  Products of at most 8192 columns raise the waves' issue priority
+// while they issue matrix-core work (M 32768, N 4096, K 8192: 4.5 % faster;
+// M 16384, N 8192, K 2048: 10 %; at N 24576, K 4096 it was 0.6 % slower).
 static void launch_dc(dim3 grid, const bf16* A, int64_t lda, const GemmB& b, bf16* C, int64_t ldc, int M, int N, int K,
                       hipStream_t st) {
   constexpr int NS = 4, NW = 8;
+  const bool prio = N <= 8192;
 #define MSR_GEMM_BT(E)                                                                                         \
-  hipLaunchKernelGGL((k_gemm_dc<E, NS, NW>), grid, dim3(64 * NW), 0, st, A, lda, b, C, ldc, M, N, K);         \
+  if (prio)                                                                                                    \
+    hipLaunchKernelGGL((k_gemm_dc<E, NS, NW, 1>), grid, dim3(64 * NW), 0, st, A, lda, b, C, ldc, M, N, K);    \
+  else                                                                                                         \
+    hipLaunchKernelGGL((k_gemm_dc<E, NS, NW, 0>), grid, dim3(64 * NW), 0, st, A, lda, b, C, ldc, M, N, K);    \
   return;
   switch (epilogue_set(b)) {
     case 0: MSR_GEMM_BT(0)
